@@ -1,0 +1,156 @@
+/*
+ * kq.h -- C ABI of libkq, the k-quant decode matvec library for AMD MI355X
+ * (gfx950).
+ *
+ * The operations come from "How to Write an Inference Engine -- the Muser
+ * book":
+ *   - the decode matvec y = W x over quantized weight rows (Ch 1 "The problem:
+ *     why inference is a memory problem", section 1.3; Ch 19 "The down
+ *     projection + residual", section 19.1, operation 1);
+ *   - the Q4_K and Q6_K 256-weight superblocks of 144 and 210 bytes (Ch 19,
+ *     section 19.3) with per-block scale (and min) (Ch 5 "Quantization from
+ *     scratch", section 5.5);
+ *   - the speculative-verify batch of up to 16 activation rows (Ch 10 "The
+ *     forward pass at a glance", section 10.1; Ch 36 "Prefill vs decode",
+ *     section 36.4, Y = W X);
+ *   - the SiLU-gated FFN product (Ch 10, section 10.3, box 11);
+ *   - the fused dual-epsilon residual tail (Ch 19, sections 19.1 and 19.4;
+ *     Ch 10, section 10.4, Figure 10.2).
+ *
+ * Superblock layouts (the pages give only the sizes; this library adopts the
+ * common k-quant packing):
+ *   Q4_K, 144 B: d f16 @0, dmin f16 @2, 12 B of packed 6-bit scales and mins
+ *     for 8 sub-blocks of 32 @4, 128 B of 4-bit quants @16.
+ *     weight = d * scale_s * q - dmin * min_s.
+ *   Q6_K, 210 B: low 4 bits @0 (128 B), high 2 bits @128 (64 B), 16 int8
+ *     scales for sub-blocks of 16 @192, d f16 @208.
+ *     weight = d * scale_s * (q - 32).
+ *   A weight matrix with n_rows outputs and k inputs is stored row-major:
+ *   row r is k/256 consecutive superblocks starting at byte
+ *   r * (k/256) * block_bytes, and superblock b of a row covers inputs
+ *   256b .. 256b+255.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer (hipMalloc or a PyTorch ROCm
+ *     tensor).  The caller owns every buffer; the library allocates nothing.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  They enqueue kernels and return; they do
+ *     no host<->device copy and no synchronization.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     any error the call returns a negative kq_status and enqueues nothing, so
+ *     outputs are left untouched.  A failed kernel launch returns
+ *     KQ_ERR_LAUNCH.  Unsupported shapes return KQ_ERR_UNSUPPORTED; there is no
+ *     slower fallback path.
+ *   - Outputs must not overlap inputs (KQ_ERR_ALIAS), except that the tail
+ *     updates `residual` in place.
+ *   - Results are deterministic: every reduction runs in a fixed order and no
+ *     output is written with atomics, so identical inputs give identical bits.
+ *   - Accuracy: a matvec row agrees with the exact (binary64) result within
+ *     1e-3 * sum_i |w_i x_i|; the tail's outputs within 2e-3 absolute.
+ *   - The library holds no state across calls and is safe to call from
+ *     several host threads on different streams.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int kq_status;
+
+#define KQ_OK 0
+#define KQ_ERR_NULL (-1)        /* a required pointer is NULL */
+#define KQ_ERR_SHAPE (-2)       /* a size is out of range or inconsistent */
+#define KQ_ERR_ALIGN (-3)       /* a pointer is not aligned as required */
+#define KQ_ERR_ALIAS (-4)       /* an output overlaps an input */
+#define KQ_ERR_UNSUPPORTED (-5) /* valid but not supported (e.g. k too large) */
+#define KQ_ERR_LAUNCH (-6)      /* the HIP runtime refused the launch */
+#define KQ_ERR_DEVICE (-7)      /* the current device is not usable */
+
+#define KQ_QTYPE_Q4K 1
+#define KQ_QTYPE_Q6K 2
+
+#define KQ_QK 256           /* weights per superblock */
+#define KQ_Q4K_BLOCK_BYTES 144
+#define KQ_Q6K_BLOCK_BYTES 210
+#define KQ_MAX_K 40960      /* largest k (inputs per row) any matvec accepts */
+#define KQ_MAX_M 16         /* largest activation batch of kq_matmul_small_m */
+#define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
+
+/*
+ * Q4_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows, with an
+ * optional SiLU-gated epilogue y[r] = silu(silu_gate[r]) * (W x)[r] where
+ * silu(z) = z / (1 + exp(-z)).
+ *   W          [n_rows * (k/256) * 144] bytes, 16-byte aligned.
+ *   x          [k] f32, 16-byte aligned.
+ *   y          [n_rows] f32 output, 4-byte aligned; must not overlap W, x or
+ *              silu_gate.
+ *   n_rows     >= 0 (0 enqueues nothing and returns KQ_OK), < 2^31.
+ *   k          multiple of 256, 256 <= k <= KQ_MAX_K.
+ *   silu_gate  NULL, or [n_rows] f32 (4-byte aligned).
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS,
+ * KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
+ */
+kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        const float *silu_gate, void *stream);
+
+/*
+ * Q6_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows.
+ *   W   [n_rows * (k/256) * 210] bytes, 4-byte aligned (a 210-byte superblock
+ *       keeps only 2-byte alignment, and rows keep 4-byte alignment).
+ *   x   [k] f32, 16-byte aligned.   y [n_rows] f32 output, 4-byte aligned,
+ *       must not overlap W or x.
+ *   n_rows >= 0, k multiple of 256 with 256 <= k <= KQ_MAX_K.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        void *stream);
+
+/*
+ * Small-M matmul for the speculative-verify batch: for m < M and r < n_rows,
+ *   Y[m * ldy + r] = sum_i w[r,i] * X[m * ldx + i].
+ * Each weight is read from memory once and applied to all M rows.
+ *   qtype   KQ_QTYPE_Q4K or KQ_QTYPE_Q6K.
+ *   W       weight bytes as for the matvec of that qtype (same alignment).
+ *   X       [M][ldx] f32, ldx >= k and ldx % 4 == 0, 16-byte aligned.
+ *   Y       [M][ldy] f32 output, ldy >= n_rows, 4-byte aligned; must not
+ *           overlap W or X.
+ *   n_rows  >= 0; k as for the matvec; 1 <= m <= KQ_MAX_M.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ldx, float *Y,
+                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *stream);
+
+/*
+ * Fused dual-epsilon residual tail, rows independent:
+ *   residual[r] += rms_norm(projected[r], eps_post) * g_post
+ *   next_in[r]   = rms_norm(residual[r], eps_next) * g_next
+ * with rms_norm(v, eps)_i = v_i / sqrt(mean_j(v_j^2) + eps).  The second norm
+ * sees the f32 residual after the add, which is also what is stored.
+ *   residual   [rows][n] f32, updated in place, 16-byte aligned.
+ *   projected  [rows][n] f32, 16-byte aligned.
+ *   next_in    [rows][n] f32 output, 16-byte aligned; must not overlap
+ *              residual, projected, g_post or g_next.
+ *   g_post, g_next  [n] f32 gains shared by all rows, 16-byte aligned.
+ *   rows >= 0; n % 4 == 0 with 4 <= n <= KQ_MAX_TAIL_N; eps >= 0 and finite.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS,
+ * KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
+ */
+kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,
+                                 const float *g_post, const float *g_next, int64_t rows,
+                                 int64_t n, float eps_post, float eps_next, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *kq_status_string(kq_status s);
+
+/* Static text naming the build: kernel variants, gfx target, HIP version. */
+const char *kq_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

@@ -1,0 +1,13 @@
+"""k-quant decode matvec for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libkq.so`` (C ABI in ``include/kq.h``);
+``_binding`` marshals arguments to it.  ``inputs`` generates the seeded
+synthetic workloads.  Build the library with
+``python -m quant_weight_matvec_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    KQ_ERR_ALIAS, KQ_ERR_ALIGN, KQ_ERR_DEVICE, KQ_ERR_LAUNCH, KQ_ERR_NULL, KQ_ERR_SHAPE,
+    KQ_ERR_UNSUPPORTED, KQ_MAX_K, KQ_MAX_M, KQ_MAX_TAIL_N, KQ_OK, KQ_QTYPE_Q4K, KQ_QTYPE_Q6K,
+    KQError, KQLibraryMissing, kq_build_info, kq_fused_residual_norm, kq_matmul_small_m,
+    kq_matvec_q4k, kq_matvec_q6k, kq_status_string, kq_tune_get_shape, kq_tune_set_shape, lib,
+)

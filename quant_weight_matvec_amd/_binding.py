@@ -1,0 +1,143 @@
+"""ctypes binding of libkq (include/kq.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of ``libkq.so``; this module only
+turns tensors into device pointers and streams into handles, and turns a
+non-zero status into an exception.  There is no fallback: if the built
+library is missing, importing the functions raises ``KQLibraryMissing``.
+
+Pointer arguments accept a ``torch.Tensor`` (its ``data_ptr()``), a plain
+integer address, or ``None`` (NULL).  ``stream`` accepts a
+``torch.cuda.Stream``, a raw handle, or ``None`` for torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkq.so")
+
+KQ_OK = 0
+KQ_ERR_NULL = -1
+KQ_ERR_SHAPE = -2
+KQ_ERR_ALIGN = -3
+KQ_ERR_ALIAS = -4
+KQ_ERR_UNSUPPORTED = -5
+KQ_ERR_LAUNCH = -6
+KQ_ERR_DEVICE = -7
+KQ_QTYPE_Q4K = 1
+KQ_QTYPE_Q6K = 2
+KQ_MAX_K = 40960
+KQ_MAX_M = 16
+KQ_MAX_TAIL_N = 32768
+
+
+class KQLibraryMissing(RuntimeError):
+    pass
+
+
+class KQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib: C.CDLL | None = None
+_vp = C.c_void_p
+_i64 = C.c_int64
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KQLibraryMissing(
+            f"{LIB_PATH} is not built; run `python -m quant_weight_matvec_amd.build` "
+            "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    L.kq_matvec_q4k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp]
+    L.kq_matvec_q6k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
+    L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp]
+    L.kq_fused_residual_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, C.c_float,
+                                         C.c_float, _vp]
+    L.kq_status_string.argtypes = [C.c_int]
+    L.kq_status_string.restype = C.c_char_p
+    L.kq_build_info.argtypes = []
+    L.kq_build_info.restype = C.c_char_p
+    L.kq_tune_set_shape.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int]
+    L.kq_tune_get_shape.argtypes = [C.c_int, _i64, _i64, C.POINTER(C.c_int),
+                                    C.POINTER(C.c_int), C.POINTER(C.c_int)]
+    for fn in ("kq_matvec_q4k", "kq_matvec_q6k", "kq_matmul_small_m", "kq_fused_residual_norm",
+               "kq_tune_set_shape", "kq_tune_get_shape"):
+        getattr(L, fn).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _ptr(a) -> int | None:
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != KQ_OK:
+        raise KQError(rc, f"{what}: {kq_status_string(rc)}")
+
+
+def kq_status_string(status: int) -> str:
+    return lib().kq_status_string(int(status)).decode()
+
+
+def kq_build_info() -> str:
+    return lib().kq_build_info().decode()
+
+
+def kq_matvec_q4k(W, x, y, n_rows: int, k: int, silu_gate=None, stream=None) -> None:
+    rc = lib().kq_matvec_q4k(_ptr(W), _ptr(x), _ptr(y), int(n_rows), int(k), _ptr(silu_gate),
+                             _stream(stream))
+    _check(rc, "kq_matvec_q4k")
+
+
+def kq_matvec_q6k(W, x, y, n_rows: int, k: int, stream=None) -> None:
+    rc = lib().kq_matvec_q6k(_ptr(W), _ptr(x), _ptr(y), int(n_rows), int(k), _stream(stream))
+    _check(rc, "kq_matvec_q6k")
+
+
+def kq_matmul_small_m(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: int, m: int,
+                      stream=None) -> None:
+    rc = lib().kq_matmul_small_m(int(qtype), _ptr(W), _ptr(X), int(ldx), _ptr(Y), int(ldy),
+                                 int(n_rows), int(k), int(m), _stream(stream))
+    _check(rc, "kq_matmul_small_m")
+
+
+def kq_fused_residual_norm(residual, projected, next_in, g_post, g_next, rows: int, n: int,
+                           eps_post: float = 1e-8, eps_next: float = 1e-5, stream=None) -> None:
+    rc = lib().kq_fused_residual_norm(_ptr(residual), _ptr(projected), _ptr(next_in),
+                                      _ptr(g_post), _ptr(g_next), int(rows), int(n),
+                                      float(eps_post), float(eps_next), _stream(stream))
+    _check(rc, "kq_fused_residual_norm")
+
+
+def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0) -> None:
+    _check(lib().kq_tune_set_shape(int(qtype), int(lanes), int(waves), int(grid)),
+           "kq_tune_set_shape")
+
+
+def kq_tune_get_shape(qtype: int, n_rows: int, k: int) -> tuple[int, int, int]:
+    a, b, c = C.c_int(), C.c_int(), C.c_int()
+    _check(lib().kq_tune_get_shape(int(qtype), int(n_rows), int(k), C.byref(a), C.byref(b),
+                                   C.byref(c)), "kq_tune_get_shape")
+    return a.value, b.value, c.value

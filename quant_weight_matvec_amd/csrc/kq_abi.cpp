@@ -1,0 +1,194 @@
+// kq_abi.cpp -- the C ABI of libkq: argument validation, status strings,
+// build identity.  Every check runs on the host before anything is enqueued,
+// so a call that fails leaves its outputs untouched and the stream unchanged
+// (the pages' engine fails closed in the same way rather than falling back:
+// Ch 4 "Pipeline state objects and the three kernel sources", section 4.7).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/kq.h"
+#include "../../include/kq_tune.h"
+#include "kq_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// [a, a+an) and [b, b+bn) overlap (byte ranges; empty ranges never overlap)
+bool overlap(const void *a, int64_t an, const void *b, int64_t bn)
+{
+    if (!a || !b || an <= 0 || bn <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+kq_status check_k(int64_t k)
+{
+    if (k < KQ_QK || k % KQ_QK) return KQ_ERR_SHAPE;
+    if (k > KQ_MAX_K) return KQ_ERR_UNSUPPORTED;
+    return KQ_OK;
+}
+
+kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH; }
+
+kq_status check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KQ_ERR_DEVICE;
+    return KQ_OK;
+}
+
+kq_status check_matvec(const void *W, int64_t wbytes_per_row, uintptr_t walign, const float *x,
+                       float *y, int64_t n_rows, int64_t k, const float *gate)
+{
+    if (!W || !x || !y) return KQ_ERR_NULL;
+    if (n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (!aligned(W, walign) || !aligned(x, 16) || !aligned(y, 4) || (gate && !aligned(gate, 4)))
+        return KQ_ERR_ALIGN;
+    const int64_t wbytes = n_rows * wbytes_per_row;
+    const int64_t ybytes = n_rows * 4;
+    if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, x, k * 4) ||
+        overlap(y, ybytes, gate, gate ? ybytes : 0))
+        return KQ_ERR_ALIAS;
+    return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        const float *silu_gate, void *stream)
+{
+    const int64_t rowb = (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    kq_status s = check_matvec(W, rowb, 16, x, y, n_rows, k, silu_gate);
+    if (s != KQ_OK) return s;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_matvec_q4k((const uint8_t *)W, x, y, (int)n_rows, (int)k,
+                                           silu_gate, (hipStream_t)stream));
+}
+
+kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        void *stream)
+{
+    const int64_t rowb = (k / KQ_QK) * KQ_Q6K_BLOCK_BYTES;
+    kq_status s = check_matvec(W, rowb, 4, x, y, n_rows, k, nullptr);
+    if (s != KQ_OK) return s;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_matvec_q6k((const uint8_t *)W, x, y, (int)n_rows, (int)k,
+                                           (hipStream_t)stream));
+}
+
+kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ldx, float *Y,
+                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *stream)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (!W || !X || !Y) return KQ_ERR_NULL;
+    if (m < 1 || n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    if (m > KQ_MAX_M) return KQ_ERR_UNSUPPORTED;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (ldx < k || ldx % 4 || ldy < n_rows || ldy < 1) return KQ_ERR_SHAPE;
+    const uintptr_t walign = qtype == KQ_QTYPE_Q4K ? 16 : 4;
+    if (!aligned(W, walign) || !aligned(X, 16) || !aligned(Y, 4)) return KQ_ERR_ALIGN;
+    const int64_t blk = qtype == KQ_QTYPE_Q4K ? KQ_Q4K_BLOCK_BYTES : KQ_Q6K_BLOCK_BYTES;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * blk;
+    const int64_t ybytes = ((int64_t)(m - 1) * ldy + n_rows) * 4;
+    const int64_t xbytes = ((int64_t)(m - 1) * ldx + k) * 4;
+    if (overlap(Y, ybytes, W, wbytes) || overlap(Y, ybytes, X, xbytes)) return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_small_m(qtype, (const uint8_t *)W, X, ldx, Y, ldy, (int)n_rows,
+                                        (int)k, m, (hipStream_t)stream));
+}
+
+kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,
+                                 const float *g_post, const float *g_next, int64_t rows,
+                                 int64_t n, float eps_post, float eps_next, void *stream)
+{
+    if (!residual || !projected || !next_in || !g_post || !g_next) return KQ_ERR_NULL;
+    if (rows < 0 || rows > INT32_MAX || n < 4 || n % 4) return KQ_ERR_SHAPE;
+    if (n > KQ_MAX_TAIL_N) return KQ_ERR_UNSUPPORTED;
+    if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
+        return KQ_ERR_SHAPE;
+    if (!aligned(residual, 16) || !aligned(projected, 16) || !aligned(next_in, 16) ||
+        !aligned(g_post, 16) || !aligned(g_next, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t b = rows * n * 4;
+    if (overlap(next_in, b, residual, b) || overlap(next_in, b, projected, b) ||
+        overlap(next_in, b, g_post, n * 4) || overlap(next_in, b, g_next, n * 4) ||
+        overlap(residual, b, projected, b) || overlap(residual, b, g_post, n * 4) ||
+        overlap(residual, b, g_next, n * 4))
+        return KQ_ERR_ALIAS;
+    if (rows == 0) return KQ_OK;
+    kq_status s = check_device();
+    if (s != KQ_OK) return s;
+    return from_hip(kqi::launch_tail(residual, projected, next_in, g_post, g_next, (int)rows,
+                                     (int)n, eps_post, eps_next, (hipStream_t)stream));
+}
+
+const char *kq_status_string(kq_status s)
+{
+    switch (s) {
+    case KQ_OK: return "KQ_OK";
+    case KQ_ERR_NULL: return "KQ_ERR_NULL: a required pointer is NULL";
+    case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE: a size is out of range or inconsistent";
+    case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN: a pointer is not aligned as required";
+    case KQ_ERR_ALIAS: return "KQ_ERR_ALIAS: an output overlaps an input";
+    case KQ_ERR_UNSUPPORTED: return "KQ_ERR_UNSUPPORTED: valid but unsupported arguments";
+    case KQ_ERR_LAUNCH: return "KQ_ERR_LAUNCH: the HIP runtime refused the launch";
+    case KQ_ERR_DEVICE: return "KQ_ERR_DEVICE: no usable current device";
+    default: return "KQ_ERR_UNKNOWN";
+    }
+}
+
+#ifndef KQ_GIT_SHA
+#define KQ_GIT_SHA "unknown"
+#endif
+
+const char *kq_build_info(void)
+{
+    static char buf[512];
+    static int done = 0;
+    if (!done) {
+        snprintf(buf, sizeof buf, "libkq target=gfx950 hip=%d.%d.%d git=%s variants: %s",
+                 HIP_VERSION_MAJOR, HIP_VERSION_MINOR, HIP_VERSION_PATCH, KQ_GIT_SHA,
+                 kqi::variant_names());
+        done = 1;
+    }
+    return buf;
+}
+
+kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (lanes && lanes != 4 && lanes != 8 && lanes != 16 && lanes != 32 && lanes != 64)
+        return KQ_ERR_SHAPE;
+    if (waves < 0 || waves > 16 || grid < 0) return KQ_ERR_SHAPE;
+    kqi::set_shape_override(qtype, kqi::MatvecShape{lanes, waves, grid});
+    return KQ_OK;
+}
+
+kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, int *waves,
+                            int *grid)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (!lanes || !waves || !grid) return KQ_ERR_NULL;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (n_rows < 1) return KQ_ERR_SHAPE;
+    if ((s = check_device()) != KQ_OK) return s;
+    const kqi::MatvecShape sh = kqi::auto_shape(qtype, n_rows, k, 1);
+    *lanes = sh.lanes;
+    *waves = sh.waves;
+    *grid = sh.grid;
+    return KQ_OK;
+}
+
+}  // extern "C"

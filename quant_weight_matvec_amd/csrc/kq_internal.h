@@ -1,0 +1,39 @@
+// kq_internal.h -- declarations shared by the C-ABI shim (kq_abi.cpp) and
+// the kernel launchers (kq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kqi {
+
+// Launch shape of a matvec: `lanes` lanes cooperate on one weight row, a
+// workgroup has `waves` wavefronts, and `grid` workgroups split the rows into
+// contiguous ranges.  Zero fields mean "choose automatically".
+struct MatvecShape {
+    int lanes;
+    int waves;
+    int grid;
+};
+
+// Tuning override, process-wide (used by sweeps; 0 = automatic).
+void set_shape_override(int qtype, MatvecShape s);
+MatvecShape get_shape_override(int qtype);
+
+// Each launcher assumes the arguments were validated by the ABI shim.
+hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
+                             const float *silu_gate, hipStream_t stream);
+hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
+                             hipStream_t stream);
+hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+                          int64_t ldy, int n_rows, int k, int m, hipStream_t stream);
+hipError_t launch_tail(float *residual, const float *projected, float *next_in,
+                       const float *g_post, const float *g_next, int rows, int n,
+                       float eps_post, float eps_next, hipStream_t stream);
+
+// The shape the automatic choice would use (for reports and tests).
+MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);
+
+const char *variant_names();
+
+}  // namespace kqi

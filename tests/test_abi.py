@@ -1,0 +1,131 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the public
+headers declare, and rejects bad arguments on the host before any device call.
+
+Runs without a GPU: every call here fails validation (or is the n_rows == 0
+no-op), and validation happens before the library touches the HIP runtime.
+Pointers are fake addresses that are never dereferenced.
+"""
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+import quant_weight_matvec_amd as kq
+from quant_weight_matvec_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kq.lib()
+    names = _declared_symbols()
+    assert "kq_matvec_q4k" in names and "kq_fused_residual_norm" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings_and_build_info():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        s = kq.kq_status_string(code)
+        assert s.startswith("KQ_")
+    assert kq.kq_status_string(-99) == "KQ_ERR_UNKNOWN"
+    info = kq.kq_build_info()
+    assert "gfx950" in info and "q4k_matvec" in info
+
+
+W, X, Y, G = 0x100000, 0x200000, 0x300000, 0x400000  # fake, aligned, never dereferenced
+
+
+def _q4(W=W, x=X, y=Y, n=8, k=1024, gate=None):
+    return kq.lib().kq_matvec_q4k(W, x, y, n, k, gate, None)
+
+
+def _q6(W=W, x=X, y=Y, n=8, k=1024):
+    return kq.lib().kq_matvec_q6k(W, x, y, n, k, None)
+
+
+def test_matvec_validation():
+    assert _q4(W=None) == B.KQ_ERR_NULL
+    assert _q4(x=None) == B.KQ_ERR_NULL
+    assert _q4(y=None) == B.KQ_ERR_NULL
+    assert _q4(k=300) == B.KQ_ERR_SHAPE
+    assert _q4(k=0) == B.KQ_ERR_SHAPE
+    assert _q4(k=128) == B.KQ_ERR_SHAPE
+    assert _q4(k=B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
+    assert _q4(n=-1) == B.KQ_ERR_SHAPE
+    assert _q4(n=2**31) == B.KQ_ERR_SHAPE
+    assert _q4(W=W + 4) == B.KQ_ERR_ALIGN          # Q4_K needs 16-byte weights
+    assert _q4(x=X + 4) == B.KQ_ERR_ALIGN
+    assert _q4(y=Y + 2) == B.KQ_ERR_ALIGN
+    assert _q4(gate=G + 1) == B.KQ_ERR_ALIGN
+    assert _q6(W=W + 2) == B.KQ_ERR_ALIGN            # Q6_K needs 4-byte weights
+    assert _q4(y=W + 64) == B.KQ_ERR_ALIAS           # output inside the weights
+    assert _q4(y=X + 16) == B.KQ_ERR_ALIAS           # output inside x
+    assert _q4(y=G, gate=G) == B.KQ_ERR_ALIAS        # output on the gate
+    assert _q6(y=W + 8 * 4 * 210 - 4) == B.KQ_ERR_ALIAS
+    assert _q4(n=0) == B.KQ_OK                       # empty: nothing enqueued
+    assert _q6(n=0) == B.KQ_OK
+
+
+def test_small_m_validation():
+    f = kq.lib().kq_matmul_small_m
+    assert f(3, W, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # qtype
+    assert f(1, W, X, 1024, Y, 8, 8, 1024, 0, None) == B.KQ_ERR_SHAPE      # m = 0
+    assert f(1, W, X, 1024, Y, 8, 8, 1024, 17, None) == B.KQ_ERR_UNSUPPORTED
+    assert f(1, W, X, 1000, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldx < k
+    assert f(1, W, X, 1026, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldx % 4
+    assert f(1, W, X, 1024, Y, 7, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldy < n_rows
+    assert f(1, None, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_NULL
+    assert f(2, W + 2, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_ALIGN
+    assert f(1, W, X, 1024, X + 4 * 1024, 8, 8, 1024, 4, None) == B.KQ_ERR_ALIAS
+    assert f(1, W, X, 1024, Y, 8, 0, 1024, 4, None) == B.KQ_OK             # empty
+
+
+def test_tail_validation():
+    f = kq.lib().kq_fused_residual_norm
+    R, P, O, GP, GN = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+    ok = (R, P, O, GP, GN, 2, 6656, C.c_float(1e-8), C.c_float(1e-5), None)
+    assert f(*ok[:5], 2, 6, *ok[7:]) == B.KQ_ERR_SHAPE
+    assert f(*ok[:5], 2, 0, *ok[7:]) == B.KQ_ERR_SHAPE
+    assert f(*ok[:5], 2, B.KQ_MAX_TAIL_N + 4, *ok[7:]) == B.KQ_ERR_UNSUPPORTED
+    assert f(*ok[:5], -1, 6656, *ok[7:]) == B.KQ_ERR_SHAPE
+    assert f(*ok[:7], C.c_float(float("nan")), ok[8], None) == B.KQ_ERR_SHAPE
+    assert f(*ok[:7], ok[7], C.c_float(-1.0), None) == B.KQ_ERR_SHAPE
+    assert f(None, *ok[1:]) == B.KQ_ERR_NULL
+    assert f(R + 4, *ok[1:]) == B.KQ_ERR_ALIGN
+    assert f(R, P, R + 16, *ok[3:]) == B.KQ_ERR_ALIAS                      # next_in on residual
+    assert f(R, R + 64, O, *ok[3:]) == B.KQ_ERR_ALIAS                      # projected on residual
+    assert f(*ok[:5], 0, 6656, *ok[7:]) == B.KQ_OK                          # empty
+
+
+def test_tune_validation():
+    with pytest.raises(kq.KQError):
+        kq.kq_tune_set_shape(1, lanes=12)
+    with pytest.raises(kq.KQError):
+        kq.kq_tune_set_shape(3, lanes=8)
+    with pytest.raises(kq.KQError):
+        kq.kq_tune_set_shape(1, waves=17)
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_matvec_q4k(W, X, Y, 8, 300, stream=0)
+    assert e.value.status == B.KQ_ERR_SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(kq.KQLibraryMissing):
+        kq.kq_matvec_q4k(W, X, Y, 8, 1024, stream=0)
