@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the k-quant decode hot path on one MI355X.
+
+A step is one decode token through the 52-layer FFN weight stream: per layer a
+Q4_K gate matvec (19968 x 6656), a Q4_K up matvec with the SiLU-gated epilogue,
+a Q6_K down matvec (6656 x 19968) and the fused dual-eps tail; the activation
+is chained layer to layer (the weight arena of Ch 19 "The down projection +
+residual", section 19.6, times 52 layers).  Weights are seeded synthetic
+(13.44 GB of distinct bytes, larger than the 256 MB Infinity Cache), resident
+in HBM before timing.  The pass is captured once as a HIP graph and replayed.
+
+Printed: one JSON line (rank 0) with the headline metric -- achieved HBM GB/s
+of the pass -- plus the roofline of the dominant kernel (timed with HIP events
+on the launch stream), per-kernel numbers, the measured read-stream ceiling,
+isolated matvec rates with weight rotation, and the CPU oracle's rate on a
+bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HIDDEN, FFN, LAYERS = 6656, 19968, 52
+PEAK_HBM_GBPS = 8000.0
+Q4K_BLOCK, Q6K_BLOCK = 144, 210
+FULL_MODEL_TOKEN_BYTES = 16_756_681_056  # pages' per-token weight bytes (Ch 1, section 1.3)
+
+
+def q4k_bytes(n, k):
+    return n * (k // 256) * Q4K_BLOCK
+
+
+def q6k_bytes(n, k):
+    return n * (k // 256) * Q6K_BLOCK
+
+
+# Algorithmic bytes per launch: every weight byte once, activations in and out.
+BYTES = {
+    "gate": q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN,
+    "up_silu": q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN + 4 * FFN,
+    "down": q6k_bytes(HIDDEN, FFN) + 4 * FFN + 4 * HIDDEN,
+    # tail: read projected, read+write residual, write next_in, read two gains
+    "tail": 4 * HIDDEN * 6,
+}
+PASS_BYTES = LAYERS * sum(BYTES.values()) + BYTES["tail"]  # + the entry norm
+WEIGHT_BYTES_PASS = LAYERS * (2 * q4k_bytes(FFN, HIDDEN) + q6k_bytes(HIDDEN, FFN))
+KERNEL_SYMBOL = {
+    "gate": "q4k_matvec_kernel<..., false>",
+    "up_silu": "q4k_matvec_kernel<..., true>",
+    "down": "q6k_matvec_kernel",
+    "tail": "tail_kernel",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kq_kernels.hip", "kq_abi.cpp", "kq_internal.h"):
+        with open(os.path.join(ROOT, "quant_weight_matvec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class FFNChain:
+    """Device buffers of the 52-layer chain and the launches of one pass."""
+
+    def __init__(self, torch, kq, I, layers=LAYERS):
+        self.torch, self.kq = torch, kq
+        dev = torch.device("cuda")
+        self.layers = layers
+        t0 = time.time()
+        self.Wg, self.Wu, self.Wd, self.gp, self.gn = [], [], [], [], []
+        for l in range(layers):
+            self.Wg.append(torch.from_numpy(I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, l, I.ROLE_W_GATE))).to(dev))
+            self.Wu.append(torch.from_numpy(I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, l, I.ROLE_W_UP))).to(dev))
+            self.Wd.append(torch.from_numpy(I.q6k_matrix(HIDDEN, FFN, stream=I.stream_id(4, l, I.ROLE_W_DOWN))).to(dev))
+            self.gp.append(torch.from_numpy(I.gains_f32(HIDDEN, stream=I.stream_id(4, l, I.ROLE_GPOST))).to(dev))
+            self.gn.append(torch.from_numpy(I.gains_f32(HIDDEN, stream=I.stream_id(4, l, I.ROLE_GNEXT))).to(dev))
+        torch.cuda.synchronize()
+        log(f"generated and uploaded {layers} layers ({WEIGHT_BYTES_PASS * layers / LAYERS / 1e9:.2f} GB) "
+            f"in {time.time() - t0:.1f}s")
+        self.res0 = torch.from_numpy(I.normal_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_RESID))).to(dev)
+        self.residual = self.res0.clone()
+        self.x = [torch.empty(HIDDEN, device=dev), torch.empty(HIDDEN, device=dev)]
+        self.g = torch.empty(FFN, device=dev)
+        self.mid = torch.empty(FFN, device=dev)
+        self.p = torch.empty(HIDDEN, device=dev)
+        self.zeros = torch.zeros(HIDDEN, device=dev)
+        self.ones = torch.ones(HIDDEN, device=dev)
+
+    def entry_norm(self):
+        # x_0 = rms_norm(residual, 1e-5) with unit gain: the tail with a zero
+        # projection leaves the residual unchanged and emits exactly that.
+        self.kq.kq_fused_residual_norm(self.residual, self.zeros, self.x[0], self.ones, self.ones,
+                                       1, HIDDEN, 1e-8, 1e-5)
+
+    def layer(self, l, ev=None):
+        kq = self.kq
+        x, xn = self.x[l % 2], self.x[(l + 1) % 2]
+        calls = (
+            ("gate", lambda: kq.kq_matvec_q4k(self.Wg[l], x, self.g, FFN, HIDDEN)),
+            ("up_silu", lambda: kq.kq_matvec_q4k(self.Wu[l], x, self.mid, FFN, HIDDEN, self.g)),
+            ("down", lambda: kq.kq_matvec_q6k(self.Wd[l], self.mid, self.p, HIDDEN, FFN)),
+            ("tail", lambda: kq.kq_fused_residual_norm(self.residual, self.p, xn, self.gp[l],
+                                                       self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
+        )
+        for name, fn in calls:
+            if ev is None:
+                fn()
+            else:
+                a, b = ev.pair()
+                a.record()
+                fn()
+                b.record()
+                ev.note(name, a, b)
+
+    def run_pass(self, ev=None):
+        self.entry_norm()
+        for l in range(self.layers):
+            self.layer(l, ev)
+
+
+class EventLog:
+    def __init__(self, torch):
+        self.torch = torch
+        self.items = []
+
+    def pair(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    def note(self, name, a, b):
+        self.items.append((name, a, b))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        out = {}
+        for name, a, b in self.items:
+            out.setdefault(name, []).append(a.elapsed_time(b) * 1e3)  # us
+        return {k: np.array(v) for k, v in out.items()}
+
+
+def read_ceiling(torch, kq, nbytes=4 << 30, reps=5):
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(7)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus * 8
+    out = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
+    kq.kq_probe_read_bw(buf, nbytes, out, grid)
+    E = torch.cuda.Event
+    times = []
+    for _ in range(reps):
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        kq.kq_probe_read_bw(buf, nbytes, out, grid)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    del buf
+    return nbytes / np.median(times) / 1e9
+
+
+def isolated_matvecs(torch, kq, I, reps=20):
+    """Single matvecs at the FFN shapes, rotating >= 1 GiB of weight copies so
+    the Infinity Cache cannot serve them; back-to-back launches timed per
+    launch with events on the launch stream."""
+    out = {}
+    cases = [("q4k_19968x6656", "q4k", FFN, HIDDEN), ("q4k_6656x19968", "q4k", HIDDEN, FFN),
+             ("q6k_6656x19968", "q6k", HIDDEN, FFN)]
+    for name, qt, n, k in cases:
+        W = torch.from_numpy(I.weight_matrix(qt, n, k, stream=777)).cuda()
+        ncopy = max(2, int(np.ceil((1 << 30) / W.numel())))
+        copies = [W] + [W.clone() for _ in range(ncopy - 1)]
+        x = torch.from_numpy(I.normal_f32(k, stream=778)).cuda()
+        y = torch.empty(n, device="cuda")
+        fn = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
+        for c in copies:
+            fn(c, x, y, n, k)
+        ev = EventLog(torch)
+        for r in range(reps):
+            c = copies[r % ncopy]
+            a, b = ev.pair()
+            a.record()
+            fn(c, x, y, n, k)
+            b.record()
+            ev.note(name, a, b)
+        us = ev.summary()[name]
+        nbytes = W.numel() + 4 * (n + k)
+        med = float(np.median(us))
+        out[name] = {"us_median": round(med, 3), "us_cv": round(float(np.std(us) / np.mean(us)), 4),
+                     "GBps": round(nbytes / med / 1e3, 1), "frac_peak": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
+                     "copies_rotated": ncopy, "bytes": nbytes,
+                     "shape": list(kq.kq_tune_get_shape(1 if qt == "q4k" else 2, n, k))}
+        del copies, W
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(I, budget_s=12.0):
+    """The oracle (plain C, binary64) on a bounded sample of the same pass:
+    layer 0's FFN (gate, up, silu, down, tail) at full size, repeated until
+    about budget_s seconds of CPU work."""
+    import oracle
+    o = oracle.get()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    Wg = I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, 0, I.ROLE_W_GATE))
+    Wu = I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, 0, I.ROLE_W_UP))
+    Wd = I.q6k_matrix(HIDDEN, FFN, stream=I.stream_id(4, 0, I.ROLE_W_DOWN))
+    gp, gn = I.gains_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_GPOST)), I.gains_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_GNEXT))
+    res = I.normal_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_RESID)).astype(np.float64)
+    x = o.rms_norm(res, 1e-5)
+    runs, t0 = 0, time.time()
+    while True:
+        o.ffn_layer(Wg, Wu, Wd, HIDDEN, FFN, x, res, gp, gn, nthreads=threads)
+        runs += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    layer_bytes = WEIGHT_BYTES_PASS / LAYERS
+    return {"value": round(layer_bytes * runs / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{runs} run(s) of layer 0 of the 52-layer FFN pass (gate, up, silu, down, tail; "
+                      f"{layer_bytes / 1e6:.1f} MB of weights each) in {dt:.1f}s; "
+                      f"pass-equivalent {dt / runs * LAYERS:.1f} s/token"}
+
+
+def load_pmc(symbol_key: str, src_hash: str):
+    """HBM traffic per launch from a committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{symbol_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=LAYERS, help=argparse.SUPPRESS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip read ceiling and isolated matvecs")
+    ap.add_argument("--eager", action="store_true", help="time uncaptured launches instead of a graph")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              "built and measured on a single MI355X. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quant_weight_matvec_amd as kq
+    from quant_weight_matvec_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kq.lib()
+    log(kq.kq_build_info())
+    src_hash = kernel_source_hash()
+
+    chain = FFNChain(torch, kq, I, args.layers)
+    stream = torch.cuda.current_stream()
+    # warm-up (eager), then capture the pass
+    for _ in range(max(1, args.warmup)):
+        chain.run_pass()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            chain.run_pass()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K passes
+    log(f"timing {args.steps} steps ({'graph replay' if graph else 'eager'})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            chain.run_pass()
+    eb.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ea.elapsed_time(eb) / args.steps
+    pass_bytes = LAYERS * sum(BYTES.values()) + BYTES["tail"] if args.layers == LAYERS else \
+        args.layers * sum(BYTES.values()) + BYTES["tail"]
+    value = pass_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- per-kernel durations: HIP events around every launch of eager passes
+    ev = EventLog(torch)
+    for _ in range(max(2, min(args.steps, 5))):
+        chain.run_pass(ev)
+    per = ev.summary()
+    kernels = {}
+    for name, us in per.items():
+        avg = float(np.mean(us))
+        gbps = BYTES[name] / (avg * 1e-6) / 1e9
+        kernels[name] = {"symbol": KERNEL_SYMBOL[name], "launches": int(us.size), "us_avg": round(avg, 3),
+                         "us_median": round(float(np.median(us)), 3), "bytes_per_launch": BYTES[name],
+                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                         "total_us_per_pass": round(avg * (args.layers + (1 if name == "tail" else 0)), 1)}
+    dom = max(kernels, key=lambda k: kernels[k]["total_us_per_pass"])
+    dk = kernels[dom]
+    traffic = load_pmc(dom, src_hash)
+    roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": dk["frac_peak"], "traffic": traffic,
+                "bytes_per_launch": dk["bytes_per_launch"], "us_avg": dk["us_avg"]}
+
+    extras = {}
+    if not args.no_extras:
+        log("read-stream ceiling probe")
+        ceil = read_ceiling(torch, kq)
+        extras["read_ceiling_GBps"] = round(ceil, 1)
+        roofline["frac_of_read_ceiling"] = round(dk["GBps"] / ceil, 4)
+        del chain  # free 13.4 GB before the isolated runs
+        torch.cuda.empty_cache()
+        log("isolated matvecs with weight rotation")
+        extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(I)
+
+    rec = {
+        "metric": "achieved HBM GB/s (% of peak) for Q4_K/Q6_K matvec; equiv. decode tokens/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8 quants x i8 limbs -> i32, f32",
+        "data": "synthetic (seeded Q4_K/Q6_K superblocks, N(0,1) activations, N(1,0.1) gains)",
+        "config": {"workload": "ffn52: one decode token through 52 FFN layers (Q4_K gate+up 19968x6656 "
+                               "with SiLU epilogue, Q6_K down 6656x19968, fused dual-eps tail)",
+                   "hidden": HIDDEN, "ffn": FFN, "layers": args.layers, "tokens_per_step": 1,
+                   "weight_bytes_per_step": WEIGHT_BYTES_PASS * args.layers // LAYERS,
+                   "algorithmic_bytes_per_step": pass_bytes, "timing": "graph replay" if graph else "eager"},
+        "frac_peak": round(value / PEAK_HBM_GBPS, 4),
+        "tokens_per_s": round(1e3 / ms_per_step, 2),
+        "full_model_equiv_tokens_per_s": round(value * 1e9 / FULL_MODEL_TOKEN_BYTES, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "kernel_source_hash": src_hash,
+        "build": kq.kq_build_info(),
+    }
+    rec.update(extras)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,12 +20,13 @@ extern "C" {
 /*
  * Process-wide override of the launch shape of the M = 1 matvec of `qtype`
  * (KQ_QTYPE_Q4K or KQ_QTYPE_Q6K): `lanes` lanes per weight row (4, 8, 16, 32
- * or 64), `waves` wavefronts per workgroup (1..16), `grid` workgroups.  A zero
- * field keeps the automatic choice for that field; all zeros restores it.
+ * or 64), `waves` wavefronts per workgroup (1..16), `grid` workgroups,
+ * `depth` half-superblock units kept in flight per lane (1..3).  A zero field
+ * keeps the automatic choice for that field; all zeros restores it.
  * Not thread-safe against concurrent matvec calls.
  * Errors: KQ_ERR_SHAPE for an unknown qtype or an out-of-range field.
  */
-kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid);
+kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth);
 
 /*
  * The launch shape the current settings give a matvec of n_rows x k on the
@@ -33,7 +34,19 @@ kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid);
  * Errors: KQ_ERR_SHAPE, KQ_ERR_NULL, KQ_ERR_UNSUPPORTED, KQ_ERR_DEVICE.
  */
 kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, int *waves,
-                            int *grid);
+                            int *grid, int *depth);
+
+/*
+ * Read-stream probe (benchmark only): reads every byte of the device buffer
+ * `buf` once with 16-byte loads over `grid` workgroups of 256 threads and
+ * writes grid*4 xor-folded words to the device buffer `out` (so the loads
+ * cannot be dropped).  Its duration gives the measured HBM read ceiling the
+ * matvec bandwidths are compared with.
+ *   bytes  multiple of 16; buf 16-byte aligned; out [grid*4] uint32.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS, KQ_ERR_LAUNCH,
+ * KQ_ERR_DEVICE.
+ */
+kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, void *stream);
 
 #ifdef __cplusplus
 }

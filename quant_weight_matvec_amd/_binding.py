@@ -65,10 +65,11 @@ def lib() -> C.CDLL:
     L.kq_status_string.restype = C.c_char_p
     L.kq_build_info.argtypes = []
     L.kq_build_info.restype = C.c_char_p
-    L.kq_tune_set_shape.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int]
+    L.kq_tune_set_shape.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int]
     L.kq_tune_get_shape.argtypes = [C.c_int, _i64, _i64, C.POINTER(C.c_int),
-                                    C.POINTER(C.c_int), C.POINTER(C.c_int)]
-    for fn in ("kq_matvec_q4k", "kq_matvec_q6k", "kq_matmul_small_m", "kq_fused_residual_norm",
+                                    C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]
+    L.kq_probe_read_bw.argtypes = [_vp, _i64, _vp, C.c_int, _vp]
+    for fn in ("kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
     _lib = L
@@ -131,13 +132,19 @@ def kq_fused_residual_norm(residual, projected, next_in, g_post, g_next, rows: i
     _check(rc, "kq_fused_residual_norm")
 
 
-def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0) -> None:
-    _check(lib().kq_tune_set_shape(int(qtype), int(lanes), int(waves), int(grid)),
+def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0,
+                      depth: int = 0) -> None:
+    _check(lib().kq_tune_set_shape(int(qtype), int(lanes), int(waves), int(grid), int(depth)),
            "kq_tune_set_shape")
 
 
-def kq_tune_get_shape(qtype: int, n_rows: int, k: int) -> tuple[int, int, int]:
-    a, b, c = C.c_int(), C.c_int(), C.c_int()
+def kq_tune_get_shape(qtype: int, n_rows: int, k: int) -> tuple[int, int, int, int]:
+    a, b, c, d = C.c_int(), C.c_int(), C.c_int(), C.c_int()
     _check(lib().kq_tune_get_shape(int(qtype), int(n_rows), int(k), C.byref(a), C.byref(b),
-                                   C.byref(c)), "kq_tune_get_shape")
-    return a.value, b.value, c.value
+                                   C.byref(c), C.byref(d)), "kq_tune_get_shape")
+    return a.value, b.value, c.value, d.value
+
+
+def kq_probe_read_bw(buf, nbytes: int, out, grid: int, stream=None) -> None:
+    _check(lib().kq_probe_read_bw(_ptr(buf), int(nbytes), _ptr(out), int(grid), _stream(stream)),
+           "kq_probe_read_bw")

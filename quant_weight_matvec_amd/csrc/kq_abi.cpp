@@ -8,8 +8,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "../../include/kq.h"
-#include "../../include/kq_tune.h"
+#include "kq.h"
+#include "kq_tune.h"
 #include "kq_internal.h"
 
 namespace {
@@ -165,21 +165,21 @@ const char *kq_build_info(void)
     return buf;
 }
 
-kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid)
+kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)
 {
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
     if (lanes && lanes != 4 && lanes != 8 && lanes != 16 && lanes != 32 && lanes != 64)
         return KQ_ERR_SHAPE;
-    if (waves < 0 || waves > 16 || grid < 0) return KQ_ERR_SHAPE;
-    kqi::set_shape_override(qtype, kqi::MatvecShape{lanes, waves, grid});
+    if (waves < 0 || waves > 16 || grid < 0 || depth < 0 || depth > 3) return KQ_ERR_SHAPE;
+    kqi::set_shape_override(qtype, kqi::MatvecShape{lanes, waves, grid, depth});
     return KQ_OK;
 }
 
 kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, int *waves,
-                            int *grid)
+                            int *grid, int *depth)
 {
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
-    if (!lanes || !waves || !grid) return KQ_ERR_NULL;
+    if (!lanes || !waves || !grid || !depth) return KQ_ERR_NULL;
     kq_status s = check_k(k);
     if (s != KQ_OK) return s;
     if (n_rows < 1) return KQ_ERR_SHAPE;
@@ -188,7 +188,19 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
     *lanes = sh.lanes;
     *waves = sh.waves;
     *grid = sh.grid;
+    *depth = sh.depth;
     return KQ_OK;
+}
+
+kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, void *stream)
+{
+    if (!buf || !out) return KQ_ERR_NULL;
+    if (bytes < 16 || bytes % 16 || grid < 1) return KQ_ERR_SHAPE;
+    if (!aligned(buf, 16) || !aligned(out, 4)) return KQ_ERR_ALIGN;
+    if (overlap(out, (int64_t)grid * 16, buf, bytes)) return KQ_ERR_ALIAS;
+    kq_status s = check_device();
+    if (s != KQ_OK) return s;
+    return from_hip(kqi::launch_read_probe(buf, bytes, out, grid, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,366 @@
+// kq_device.h -- device-side building blocks shared by the kernel files of
+// libkq: superblock unit loads and dot products, activation staging into LDS,
+// fixed-order reductions.  See kq_kernels.hip for the design notes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#define KQ_LIMBS 3
+
+namespace kqd {
+
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQ4Bytes = 144;
+constexpr int kQ6Bytes = 210;
+
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+
+__device__ __forceinline__ float half_hi(uint32_t v)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+template <int LIMBS>
+__device__ __forceinline__ constexpr int limb_bits()
+{
+    return LIMBS == 3 ? 22 : 14;
+}
+
+// ---------------------------------------------------------------------------
+// Activation staging into LDS.
+// Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
+// then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
+template <int GROUP, int LIMBS>
+__device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict__ plane, int n4,
+                                            float *__restrict__ tscale, float *__restrict__ tsum)
+{
+    constexpr int TPG = GROUP / 4;  // threads per group, one float4 each
+    constexpr int QB = limb_bits<LIMBS>();
+    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    float sm = (v.x + v.y) + (v.z + v.w);
+#pragma unroll
+    for (int o = 1; o < TPG; o <<= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+        sm = sm + __shfl_xor(sm, o);
+    }
+    const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
+    const int sh = QB - e;
+    int q[4];
+    q[0] = (int)rintf(ldexpf(v.x, sh));
+    q[1] = (int)rintf(ldexpf(v.y, sh));
+    q[2] = (int)rintf(ldexpf(v.z, sh));
+    q[3] = (int)rintf(ldexpf(v.w, sh));
+    uint32_t pk[LIMBS];
+#pragma unroll
+    for (int l = 0; l < LIMBS; ++l) pk[l] = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // balanced base-256 digits, each in [-128, 127]
+        const int c = (q[j] << 24) >> 24;
+        const int t = (q[j] - c) >> 8;
+        if constexpr (LIMBS == 3) {
+            const int b = (t << 24) >> 24;
+            const int a = (t - b) >> 8;
+            pk[0] |= (uint32_t)(a & 255) << (8 * j);
+            pk[1] |= (uint32_t)(b & 255) << (8 * j);
+            pk[2] |= (uint32_t)(c & 255) << (8 * j);
+        } else {
+            pk[0] |= (uint32_t)(t & 255) << (8 * j);
+            pk[1] |= (uint32_t)(c & 255) << (8 * j);
+        }
+    }
+#pragma unroll
+    for (int l = 0; l < LIMBS; ++l) plane[l * n4 + i] = pk[l];
+    if ((i & (TPG - 1)) == 0) {
+        const int g = i / TPG;
+        tscale[g] = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
+        tsum[g] = sm;
+    }
+}
+
+// Activation staging into LDS.
+// Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
+// then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
+// The x loads of a thread are issued in batches of four before any of them is
+// converted, so the staging costs one or two memory round trips, not one per
+// float4.
+template <int GROUP, int LIMBS>
+__device__ __forceinline__ void stage_activation(const float *__restrict__ x, int k,
+                                                 uint8_t *__restrict__ smem)
+{
+    constexpr int B = 4;
+    const int n4 = k >> 2;  // a multiple of 64: whole waves stay active
+    uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
+    float *tscale = reinterpret_cast<float *>(smem + LIMBS * k);
+    float *tsum = tscale + k / GROUP;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    const int stride = blockDim.x;
+    for (int i0 = threadIdx.x; i0 < n4; i0 += B * stride) {
+        f32x4 v[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int i = i0 + b * stride;
+            if (i < n4) v[b] = x4[i];
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int i = i0 + b * stride;
+            if (i < n4) stage_group<GROUP, LIMBS>(v[b], i, plane, n4, tscale, tsum);
+        }
+    }
+}
+
+template <int LIMBS>
+__device__ __forceinline__ float combine_limbs(const int *acc)
+{
+    if constexpr (LIMBS == 3)
+        return (float)acc[0] * 65536.0f + (float)(acc[1] * 256 + acc[2]);
+    else
+        return (float)(acc[0] * 256 + acc[1]);
+}
+
+template <int LANES>
+__device__ __forceinline__ float lane_group_sum(float v)
+{
+#pragma unroll
+    for (int o = LANES / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K unit = one half superblock (sub-blocks 4h..4h+3, 128 weights): the
+// 16-byte header and 64 contiguous bytes of nibbles.
+struct Q4Unit {
+    u32x4 hdr;
+    u32x4 q[4];
+};
+
+__device__ __forceinline__ Q4Unit q4_load(const uint8_t *__restrict__ sb, int h)
+{
+    Q4Unit u;
+    u.hdr = *reinterpret_cast<const u32x4 *>(sb);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(sb + 16 + 64 * h);
+    u.q[0] = p[0];
+    u.q[1] = p[1];
+    u.q[2] = p[2];
+    u.q[3] = p[3];
+    return u;
+}
+
+// Contribution of one unit to the row's dot product.  `base` is the input
+// position of the unit's first weight (256 b + 128 h).
+template <int LIMBS>
+__device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, int k,
+                                             const uint8_t *__restrict__ planes,
+                                             const float *__restrict__ tscale,
+                                             const float *__restrict__ tsum)
+{
+    // 6-bit scales and mins of sub-blocks 4h..4h+3, one per byte.
+    const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
+    uint32_t scb, mnb;
+    if (h == 0) {
+        scb = S0 & 0x3F3F3F3Fu;
+        mnb = S1 & 0x3F3F3F3Fu;
+    } else {
+        scb = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+        mnb = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+    }
+    const float d = half_lo(u.hdr.x), dmin = half_hi(u.hdr.x);
+
+    int acc[4][LIMBS];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) acc[s][l] = 0;
+
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        // 16 bytes = inputs j0..j0+15 of sub-block 2c (low nibbles) and of
+        // sub-block 2c+1 (high nibbles), c = 2h + p/2, j0 = 16 (p & 1).
+        const int plo = base + 64 * (p >> 1) + 16 * (p & 1);
+        const int slo = 2 * (p >> 1);
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            lo[w] = u.q[p][w] & 0x0F0F0F0Fu;
+            hi[w] = (u.q[p][w] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) {
+            const u32x4 xl = *reinterpret_cast<const u32x4 *>(planes + l * k + plo);
+            const u32x4 xh = *reinterpret_cast<const u32x4 *>(planes + l * k + plo + 32);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc[slo][l] = sdot4(lo[w], xl[w], acc[slo][l]);
+                acc[slo + 1][l] = sdot4(hi[w], xh[w], acc[slo + 1][l]);
+            }
+        }
+    }
+
+    const int g0 = base >> 5;  // first 32-input group of this unit
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(tscale + g0);
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(tsum + g0);
+    float out = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const float sc = (float)((scb >> (8 * s)) & 0xFFu);
+        const float mn = (float)((mnb >> (8 * s)) & 0xFFu);
+        const float v = combine_limbs<LIMBS>(acc[s]);
+        out += (d * sc) * (gs[s] * v) - (dmin * mn) * gm[s];
+    }
+    return out;
+}
+
+// ---------------------------------------------------------------------------
+// Q6_K unit = one half superblock h: ql bytes 64h..64h+63, qh bytes
+// 128+32h..128+32h+31, the 8 int8 scales 192+8h.., and d.  A superblock
+// starts 2-byte aligned when its index is odd, so each field is read with
+// 4-byte aligned loads that start up to 2 bytes early and is re-aligned in
+// registers (v_alignbyte).  No load reaches past the superblock's last byte.
+struct Q6Unit {
+    u32x4 ql[4];
+    uint32_t ql_x;
+    u32x4 qh[2];
+    uint32_t qh_x;
+    uint32_t sc[3];
+    uint32_t d;
+    int shift;
+};
+
+__device__ __forceinline__ Q6Unit q6_load(const uint8_t *__restrict__ sb, int h)
+{
+    Q6Unit u;
+    const int shift = (int)((uintptr_t)sb & 3u);
+    u.shift = shift;
+    const uint8_t *a = sb - shift;
+    const u32x4_a4 *pl = reinterpret_cast<const u32x4_a4 *>(a + 64 * h);
+    u.ql[0] = pl[0];
+    u.ql[1] = pl[1];
+    u.ql[2] = pl[2];
+    u.ql[3] = pl[3];
+    u.ql_x = *reinterpret_cast<const uint32_t *>(a + 64 * h + 64);
+    const u32x4_a4 *ph = reinterpret_cast<const u32x4_a4 *>(a + 128 + 32 * h);
+    u.qh[0] = ph[0];
+    u.qh[1] = ph[1];
+    u.qh_x = *reinterpret_cast<const uint32_t *>(a + 128 + 32 * h + 32);
+    const uint32_t *ps = reinterpret_cast<const uint32_t *>(a + 192 + 8 * h);
+    u.sc[0] = ps[0];
+    u.sc[1] = ps[1];
+    u.sc[2] = shift ? ps[2] : 0u;
+    u.d = *reinterpret_cast<const uint16_t *>(sb + 208);
+    return u;
+}
+
+__device__ __forceinline__ uint32_t realign(uint32_t hi, uint32_t lo, int shift)
+{
+    return __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)shift);
+}
+
+template <int LIMBS>
+__device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
+                                             const uint8_t *__restrict__ planes,
+                                             const float *__restrict__ tscale,
+                                             const float *__restrict__ tsum)
+{
+    const int sh = u.shift;
+    uint32_t ql[17], qh[9];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) ql[4 * i + w] = u.ql[i][w];
+    ql[16] = u.ql_x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qh[4 * i + w] = u.qh[i][w];
+    qh[8] = u.qh_x;
+    uint32_t L[16], H[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) L[i] = realign(ql[i + 1], ql[i], sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) H[i] = realign(qh[i + 1], qh[i], sh);
+    const uint32_t sc0 = realign(u.sc[1], u.sc[0], sh);
+    const uint32_t sc1 = realign(u.sc[2], u.sc[1], sh);
+    const float d = half_lo(u.d);
+
+    // base = 256 b + 128 h; 16-input groups of this unit: base/16 .. base/16+7
+    const int g0 = base >> 4;
+    const f32x4 gsA = *reinterpret_cast<const f32x4 *>(tscale + g0);
+    const f32x4 gsB = *reinterpret_cast<const f32x4 *>(tscale + g0 + 4);
+    const f32x4 gmA = *reinterpret_cast<const f32x4 *>(tsum + g0);
+    const f32x4 gmB = *reinterpret_cast<const f32x4 *>(tsum + g0 + 4);
+    float out = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        int acc[4][LIMBS];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int l = 0; l < LIMBS; ++l) acc[g][l] = 0;
+        uint32_t q[4][4];  // [g][t]: quants of inputs base + 32g + 16jj + 4t .. +3
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t l0 = L[4 * jj + t], l1 = L[8 + 4 * jj + t], hh = H[4 * jj + t];
+            q[0][t] = (l0 & 0x0F0F0F0Fu) | ((hh & 0x03030303u) << 4);
+            q[1][t] = (l1 & 0x0F0F0F0Fu) | ((hh & 0x0C0C0C0Cu) << 2);
+            q[2][t] = ((l0 >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
+            q[3][t] = ((l1 >> 4) & 0x0F0F0F0Fu) | ((hh >> 2) & 0x30303030u);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int pos = base + 32 * g + 16 * jj;
+#pragma unroll
+            for (int l = 0; l < LIMBS; ++l) {
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(planes + l * k + pos);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[g][l] = sdot4(q[g][t], xv[t], acc[g][l]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int li = 2 * g + jj;  // local sub-block (16 inputs) 0..7
+            const uint32_t sw = (li < 4) ? sc0 : sc1;
+            const int scv = ((int)(sw << (24 - 8 * (li & 3)))) >> 24;
+            const float gsc = (li < 4) ? gsA[li] : gsB[li - 4];
+            const float gsum = (li < 4) ? gmA[li] : gmB[li - 4];
+            const float v = combine_limbs<LIMBS>(acc[g]);
+            out += (d * (float)scv) * (gsc * v - 32.0f * gsum);
+        }
+    }
+    return out;
+}
+
+
+__device__ __forceinline__ float block_sum_fixed(float v, float *red)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();  // `red` may still be read from the previous reduction
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int w = 0; w < nw; ++w) t += red[w];
+    return t;
+}
+
+__device__ __forceinline__ float sumsq4(f32x4 v)
+{
+    return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+}
+
+}  // namespace kqd

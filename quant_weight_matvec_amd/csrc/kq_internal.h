@@ -10,10 +10,13 @@ namespace kqi {
 // Launch shape of a matvec: `lanes` lanes cooperate on one weight row, a
 // workgroup has `waves` wavefronts, and `grid` workgroups split the rows into
 // contiguous ranges.  Zero fields mean "choose automatically".
+// `depth` = units in flight per lane, 1..3 (the one being computed plus a
+// look-ahead of depth-1).
 struct MatvecShape {
     int lanes;
     int waves;
     int grid;
+    int depth;
 };
 
 // Tuning override, process-wide (used by sweeps; 0 = automatic).
@@ -30,6 +33,9 @@ hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t l
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
                        float eps_post, float eps_next, hipStream_t stream);
+
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
+                             hipStream_t stream);
 
 // The shape the automatic choice would use (for reports and tests).
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);

@@ -31,216 +31,26 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "kq_device.h"
 #include "kq_internal.h"
-
-#define KQ_LIMBS 3
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace kqd;
 
-constexpr int kQ4Bytes = 144;
-constexpr int kQ6Bytes = 210;
-
-__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
-{
-    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
-}
-
-__device__ __forceinline__ float half_lo(uint32_t v)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
-}
-
-__device__ __forceinline__ float half_hi(uint32_t v)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-}
-
-template <int LIMBS>
-__device__ __forceinline__ constexpr int limb_bits()
-{
-    return LIMBS == 3 ? 22 : 14;
-}
-
-// ---------------------------------------------------------------------------
-// Activation staging into LDS.
-// Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
-// then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
-template <int GROUP, int LIMBS>
-__device__ __forceinline__ void stage_activation(const float *__restrict__ x, int k,
-                                                 uint8_t *__restrict__ smem)
-{
-    constexpr int TPG = GROUP / 4;  // threads per group, one float4 each
-    constexpr int QB = limb_bits<LIMBS>();
-    const int n4 = k >> 2;          // a multiple of 64: whole waves stay active
-    uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
-    float *tscale = reinterpret_cast<float *>(smem + LIMBS * k);
-    float *tsum = tscale + k / GROUP;
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-        const f32x4 v = x4[i];
-        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-        float sm = (v.x + v.y) + (v.z + v.w);
-#pragma unroll
-        for (int o = 1; o < TPG; o <<= 1) {
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-            sm = sm + __shfl_xor(sm, o);
-        }
-        const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
-        const int sh = QB - e;
-        int q[4];
-        q[0] = (int)rintf(ldexpf(v.x, sh));
-        q[1] = (int)rintf(ldexpf(v.y, sh));
-        q[2] = (int)rintf(ldexpf(v.z, sh));
-        q[3] = (int)rintf(ldexpf(v.w, sh));
-        uint32_t pk[LIMBS];
-#pragma unroll
-        for (int l = 0; l < LIMBS; ++l) pk[l] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // balanced base-256 digits, each in [-128, 127]
-            const int c = (q[j] << 24) >> 24;
-            const int t = (q[j] - c) >> 8;
-            if constexpr (LIMBS == 3) {
-                const int b = (t << 24) >> 24;
-                const int a = (t - b) >> 8;
-                pk[0] |= (uint32_t)(a & 255) << (8 * j);
-                pk[1] |= (uint32_t)(b & 255) << (8 * j);
-                pk[2] |= (uint32_t)(c & 255) << (8 * j);
-            } else {
-                pk[0] |= (uint32_t)(t & 255) << (8 * j);
-                pk[1] |= (uint32_t)(c & 255) << (8 * j);
-            }
-        }
-#pragma unroll
-        for (int l = 0; l < LIMBS; ++l) plane[l * n4 + i] = pk[l];
-        if ((i & (TPG - 1)) == 0) {
-            const int g = i / TPG;
-            tscale[g] = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
-            tsum[g] = sm;
-        }
-    }
-}
-
-template <int LIMBS>
-__device__ __forceinline__ float combine_limbs(const int *acc)
-{
-    if constexpr (LIMBS == 3)
-        return (float)acc[0] * 65536.0f + (float)(acc[1] * 256 + acc[2]);
-    else
-        return (float)(acc[0] * 256 + acc[1]);
-}
-
-template <int LANES>
-__device__ __forceinline__ float lane_group_sum(float v)
-{
-#pragma unroll
-    for (int o = LANES / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-
-// ---------------------------------------------------------------------------
-// Q4_K unit = one half superblock (sub-blocks 4h..4h+3, 128 weights): the
-// 16-byte header and 64 contiguous bytes of nibbles.
-struct Q4Unit {
-    u32x4 hdr;
-    u32x4 q[4];
-};
-
-__device__ __forceinline__ Q4Unit q4_load(const uint8_t *__restrict__ sb, int h)
-{
-    Q4Unit u;
-    u.hdr = *reinterpret_cast<const u32x4 *>(sb);
-    const u32x4 *p = reinterpret_cast<const u32x4 *>(sb + 16 + 64 * h);
-    u.q[0] = p[0];
-    u.q[1] = p[1];
-    u.q[2] = p[2];
-    u.q[3] = p[3];
-    return u;
-}
-
-// Contribution of one unit to the row's dot product.  `base` is the input
-// position of the unit's first weight (256 b + 128 h).
-template <int LIMBS>
-__device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, int k,
-                                             const uint8_t *__restrict__ planes,
-                                             const float *__restrict__ tscale,
-                                             const float *__restrict__ tsum)
-{
-    // 6-bit scales and mins of sub-blocks 4h..4h+3, one per byte.
-    const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
-    uint32_t scb, mnb;
-    if (h == 0) {
-        scb = S0 & 0x3F3F3F3Fu;
-        mnb = S1 & 0x3F3F3F3Fu;
-    } else {
-        scb = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
-        mnb = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
-    }
-    const float d = half_lo(u.hdr.x), dmin = half_hi(u.hdr.x);
-
-    int acc[4][LIMBS];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int l = 0; l < LIMBS; ++l) acc[s][l] = 0;
-
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        // 16 bytes = inputs j0..j0+15 of sub-block 2c (low nibbles) and of
-        // sub-block 2c+1 (high nibbles), c = 2h + p/2, j0 = 16 (p & 1).
-        const int plo = base + 64 * (p >> 1) + 16 * (p & 1);
-        const int slo = 2 * (p >> 1);
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            lo[w] = u.q[p][w] & 0x0F0F0F0Fu;
-            hi[w] = (u.q[p][w] >> 4) & 0x0F0F0F0Fu;
-        }
-#pragma unroll
-        for (int l = 0; l < LIMBS; ++l) {
-            const u32x4 xl = *reinterpret_cast<const u32x4 *>(planes + l * k + plo);
-            const u32x4 xh = *reinterpret_cast<const u32x4 *>(planes + l * k + plo + 32);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                acc[slo][l] = sdot4(lo[w], xl[w], acc[slo][l]);
-                acc[slo + 1][l] = sdot4(hi[w], xh[w], acc[slo + 1][l]);
-            }
-        }
-    }
-
-    const int g0 = base >> 5;  // first 32-input group of this unit
-    const f32x4 gs = *reinterpret_cast<const f32x4 *>(tscale + g0);
-    const f32x4 gm = *reinterpret_cast<const f32x4 *>(tsum + g0);
-    float out = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const float sc = (float)((scb >> (8 * s)) & 0xFFu);
-        const float mn = (float)((mnb >> (8 * s)) & 0xFFu);
-        const float v = combine_limbs<LIMBS>(acc[s]);
-        out += (d * sc) * (gs[s] * v) - (dmin * mn) * gm[s];
-    }
-    return out;
-}
-
-template <int LANES, int LIMBS, bool SILU>
-__global__ __launch_bounds__(1024) void q4k_matvec_kernel(const uint8_t *__restrict__ W,
-                                                          const float *__restrict__ x,
-                                                          float *__restrict__ y,
-                                                          const float *__restrict__ gate,
-                                                          int n_rows, int k)
+// One wave holds RPT = 64/LANES rows; lane `sub` of a row takes units sub,
+// sub+LANES, ...  Each lane keeps DEPTH units of look-ahead in flight: the
+// first DEPTH loads are issued before the activation staging (so HBM is busy
+// while x is converted), and every step issues the load DEPTH units ahead
+// before computing the current one.  DEPTH = 0 loads and computes in turn.
+template <int LANES, int LIMBS, int DEPTH, int WMAX, bool SILU>
+__global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__restrict__ W,
+                                                               const float *__restrict__ x,
+                                                               float *__restrict__ y,
+                                                               const float *__restrict__ gate,
+                                                               int n_rows, int k)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    stage_activation<32, LIMBS>(x, k, smem);
-    __syncthreads();
-
-    const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
-    const float *tsum = tscale + (k >> 5);
-
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ4Bytes;
@@ -252,168 +62,72 @@ __global__ __launch_bounds__(1024) void q4k_matvec_kernel(const uint8_t *__restr
     constexpr int RPT = 64 / LANES;
     const int sub = lane % LANES;
     const int h = sub & 1;  // LANES is even: a lane always takes the same half
+    const int steps = (units + LANES - 1) / LANES;
 
-    for (int t0 = r_lo + wave * RPT; t0 < r_hi; t0 += nwaves * RPT) {
-        const int r = t0 + lane / LANES;
+    int t0 = r_lo + wave * RPT;
+    int r = t0 + lane / LANES;
+    bool rv = r < r_hi;
+    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    // ring[j] holds unit sub + LANES*j of the current row (loads in flight)
+    Q4Unit ring[DEPTH > 0 ? DEPTH : 1];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+        const int u = sub + LANES * j;
+        if (rv && u < units) ring[j] = q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
+    }
+
+
+    stage_activation<32, LIMBS>(x, k, smem);
+    __syncthreads();
+    const uint8_t *planes = smem;
+    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
+    const float *tsum = tscale + (k >> 5);
+
+    while (t0 < r_hi) {
         float acc = 0.0f;
-        if (r < r_hi) {
-            const uint8_t *rowp = W + (int64_t)r * row_bytes;
-            int u = sub;
-            Q4Unit cur;
-            if (u < units) cur = q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
-            for (; u < units; u += LANES) {
-                const int un = u + LANES;
-                Q4Unit nxt;
-                if (un < units) nxt = q4_load(rowp + (int64_t)(un >> 1) * kQ4Bytes, h);
-                acc += q4_unit_dot<LIMBS>(cur, h, 256 * (u >> 1) + 128 * h, k, planes, tscale,
-                                          tsum);
-                cur = nxt;
+        for (int st = 0; st < steps; ++st) {
+            const int u = sub + LANES * st;
+            const int un = u + LANES * DEPTH;
+            Q4Unit nxt;
+            if (rv && un < units) nxt = q4_load(rowp + (int64_t)(un >> 1) * kQ4Bytes, h);
+            if (rv && u < units) {
+                const Q4Unit &cur = DEPTH > 0 ? ring[0] : nxt;
+                acc += q4_unit_dot<LIMBS>(cur, h, 256 * (u >> 1) + 128 * h, k, planes,
+                                          tscale, tsum);
+            }
+            if constexpr (DEPTH > 0) {
+#pragma unroll
+                for (int j = 0; j + 1 < DEPTH; ++j) ring[j] = ring[j + 1];
+                ring[DEPTH - 1] = nxt;
             }
         }
         acc = lane_group_sum<LANES>(acc);
-        if (sub == 0 && r < r_hi) {
+        if (sub == 0 && rv) {
             if constexpr (SILU) {
                 const float g = gate[r];
                 acc = (g / (1.0f + __expf(-g))) * acc;
             }
             y[r] = acc;
         }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Q6_K unit = one half superblock h: ql bytes 64h..64h+63, qh bytes
-// 128+32h..128+32h+31, the 8 int8 scales 192+8h.., and d.  A superblock
-// starts 2-byte aligned when its index is odd, so each field is read with
-// 4-byte aligned loads that start up to 2 bytes early and is re-aligned in
-// registers (v_alignbyte).  No load reaches past the superblock's last byte.
-struct Q6Unit {
-    u32x4 ql[4];
-    uint32_t ql_x;
-    u32x4 qh[2];
-    uint32_t qh_x;
-    uint32_t sc[3];
-    uint32_t d;
-    int shift;
-};
-
-__device__ __forceinline__ Q6Unit q6_load(const uint8_t *__restrict__ sb, int h)
-{
-    Q6Unit u;
-    const int shift = (int)((uintptr_t)sb & 3u);
-    u.shift = shift;
-    const uint8_t *a = sb - shift;
-    const u32x4_a4 *pl = reinterpret_cast<const u32x4_a4 *>(a + 64 * h);
-    u.ql[0] = pl[0];
-    u.ql[1] = pl[1];
-    u.ql[2] = pl[2];
-    u.ql[3] = pl[3];
-    u.ql_x = *reinterpret_cast<const uint32_t *>(a + 64 * h + 64);
-    const u32x4_a4 *ph = reinterpret_cast<const u32x4_a4 *>(a + 128 + 32 * h);
-    u.qh[0] = ph[0];
-    u.qh[1] = ph[1];
-    u.qh_x = *reinterpret_cast<const uint32_t *>(a + 128 + 32 * h + 32);
-    const uint32_t *ps = reinterpret_cast<const uint32_t *>(a + 192 + 8 * h);
-    u.sc[0] = ps[0];
-    u.sc[1] = ps[1];
-    u.sc[2] = shift ? ps[2] : 0u;
-    u.d = *reinterpret_cast<const uint16_t *>(sb + 208);
-    return u;
-}
-
-__device__ __forceinline__ uint32_t realign(uint32_t hi, uint32_t lo, int shift)
-{
-    return __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)shift);
-}
-
-template <int LIMBS>
-__device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
-                                             const uint8_t *__restrict__ planes,
-                                             const float *__restrict__ tscale,
-                                             const float *__restrict__ tsum)
-{
-    const int sh = u.shift;
-    uint32_t ql[17], qh[9];
+        t0 += nwaves * RPT;
+        r = t0 + lane / LANES;
+        rv = r < r_hi;
+        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) ql[4 * i + w] = u.ql[i][w];
-    ql[16] = u.ql_x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) qh[4 * i + w] = u.qh[i][w];
-    qh[8] = u.qh_x;
-    uint32_t L[16], H[8];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) L[i] = realign(ql[i + 1], ql[i], sh);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) H[i] = realign(qh[i + 1], qh[i], sh);
-    const uint32_t sc0 = realign(u.sc[1], u.sc[0], sh);
-    const uint32_t sc1 = realign(u.sc[2], u.sc[1], sh);
-    const float d = half_lo(u.d);
-
-    // base = 256 b + 128 h; 16-input groups of this unit: base/16 .. base/16+7
-    const int g0 = base >> 4;
-    const f32x4 gsA = *reinterpret_cast<const f32x4 *>(tscale + g0);
-    const f32x4 gsB = *reinterpret_cast<const f32x4 *>(tscale + g0 + 4);
-    const f32x4 gmA = *reinterpret_cast<const f32x4 *>(tsum + g0);
-    const f32x4 gmB = *reinterpret_cast<const f32x4 *>(tsum + g0 + 4);
-    float out = 0.0f;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        int acc[4][LIMBS];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int l = 0; l < LIMBS; ++l) acc[g][l] = 0;
-        uint32_t q[4][4];  // [g][t]: quants of inputs base + 32g + 16jj + 4t .. +3
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t l0 = L[4 * jj + t], l1 = L[8 + 4 * jj + t], hh = H[4 * jj + t];
-            q[0][t] = (l0 & 0x0F0F0F0Fu) | ((hh & 0x03030303u) << 4);
-            q[1][t] = (l1 & 0x0F0F0F0Fu) | ((hh & 0x0C0C0C0Cu) << 2);
-            q[2][t] = ((l0 >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
-            q[3][t] = ((l1 >> 4) & 0x0F0F0F0Fu) | ((hh >> 2) & 0x30303030u);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int pos = base + 32 * g + 16 * jj;
-#pragma unroll
-            for (int l = 0; l < LIMBS; ++l) {
-                const u32x4 xv = *reinterpret_cast<const u32x4 *>(planes + l * k + pos);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) acc[g][l] = sdot4(q[g][t], xv[t], acc[g][l]);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int li = 2 * g + jj;  // local sub-block (16 inputs) 0..7
-            const uint32_t sw = (li < 4) ? sc0 : sc1;
-            const int scv = ((int)(sw << (24 - 8 * (li & 3)))) >> 24;
-            const float gsc = (li < 4) ? gsA[li] : gsB[li - 4];
-            const float gsum = (li < 4) ? gmA[li] : gmB[li - 4];
-            const float v = combine_limbs<LIMBS>(acc[g]);
-            out += (d * (float)scv) * (gsc * v - 32.0f * gsum);
+        for (int j = 0; j < DEPTH; ++j) {
+            const int u = sub + LANES * j;
+            if (rv && u < units) ring[j] = q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
         }
     }
-    return out;
 }
 
-template <int LANES, int LIMBS>
-__global__ __launch_bounds__(1024) void q6k_matvec_kernel(const uint8_t *__restrict__ W,
-                                                          const float *__restrict__ x,
-                                                          float *__restrict__ y, int n_rows,
-                                                          int k)
+template <int LANES, int LIMBS, int DEPTH, int WMAX>
+__global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__restrict__ W,
+                                                               const float *__restrict__ x,
+                                                               float *__restrict__ y, int n_rows,
+                                                               int k)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    stage_activation<16, LIMBS>(x, k, smem);
-    __syncthreads();
-
-    const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
-    const float *tsum = tscale + (k >> 4);
-
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ6Bytes;
@@ -425,22 +139,56 @@ __global__ __launch_bounds__(1024) void q6k_matvec_kernel(const uint8_t *__restr
     constexpr int RPT = 64 / LANES;
     const int sub = lane % LANES;
     const int h = sub & 1;
+    const int steps = (units + LANES - 1) / LANES;
 
-    for (int t0 = r_lo + wave * RPT; t0 < r_hi; t0 += nwaves * RPT) {
-        const int r = t0 + lane / LANES;
+    int t0 = r_lo + wave * RPT;
+    int r = t0 + lane / LANES;
+    bool rv = r < r_hi;
+    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    // ring[j] holds unit sub + LANES*j of the current row (loads in flight)
+    Q6Unit ring[DEPTH > 0 ? DEPTH : 1];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+        const int u = sub + LANES * j;
+        if (rv && u < units) ring[j] = q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+    }
+
+
+    stage_activation<16, LIMBS>(x, k, smem);
+    __syncthreads();
+    const uint8_t *planes = smem;
+    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
+    const float *tsum = tscale + (k >> 4);
+
+    while (t0 < r_hi) {
         float acc = 0.0f;
-        if (r < r_hi) {
-            const uint8_t *rowp = W + (int64_t)r * row_bytes;
-            // A Q6_K unit holds 30 registers of raw bytes, so it is not double
-            // buffered: the workgroup's many waves keep the loads in flight.
-            for (int u = sub; u < units; u += LANES) {
-                const Q6Unit cur = q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+        for (int st = 0; st < steps; ++st) {
+            const int u = sub + LANES * st;
+            const int un = u + LANES * DEPTH;
+            Q6Unit nxt;
+            if (rv && un < units) nxt = q6_load(rowp + (int64_t)(un >> 1) * kQ6Bytes, h);
+            if (rv && u < units) {
+                const Q6Unit &cur = DEPTH > 0 ? ring[0] : nxt;
                 acc += q6_unit_dot<LIMBS>(cur, 256 * (u >> 1) + 128 * h, k, planes, tscale,
                                           tsum);
             }
+            if constexpr (DEPTH > 0) {
+#pragma unroll
+                for (int j = 0; j + 1 < DEPTH; ++j) ring[j] = ring[j + 1];
+                ring[DEPTH - 1] = nxt;
+            }
         }
         acc = lane_group_sum<LANES>(acc);
-        if (sub == 0 && r < r_hi) y[r] = acc;
+        if (sub == 0 && rv) y[r] = acc;
+        t0 += nwaves * RPT;
+        r = t0 + lane / LANES;
+        rv = r < r_hi;
+        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+            const int u = sub + LANES * j;
+            if (rv && u < units) ring[j] = q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+        }
     }
 }
 
@@ -453,24 +201,6 @@ __global__ __launch_bounds__(1024) void q6k_matvec_kernel(const uint8_t *__restr
 // block reductions run in a fixed order (per thread in slot order, an
 // xor-butterfly within a wave, then the per-wave partials in wave order), so
 // the result is reproducible bit for bit.
-__device__ __forceinline__ float block_sum_fixed(float v, float *red)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    __syncthreads();  // `red` may still be read from the previous reduction
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
-    __syncthreads();
-    float t = 0.0f;
-    for (int w = 0; w < nw; ++w) t += red[w];
-    return t;
-}
-
-__device__ __forceinline__ float sumsq4(f32x4 v)
-{
-    return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-}
-
 __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual,
                                                     const float *__restrict__ projected,
                                                     float *__restrict__ next_in,
@@ -505,6 +235,91 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
     for (int i = threadIdx.x; i < n4; i += blockDim.x) o4[i] = (r4[i] * inv_r) * gn4[i];
 }
 
+// Register form of the tail for rows up to kTailRegMax wide: every operand is
+// loaded once, up front (one memory round trip instead of three); the post-add
+// residual is stored and the next norm uses the same f32 values that were
+// stored.  Same reduction order as tail_kernel.
+constexpr int kTailVec = 4;
+constexpr int kTailThreads = 512;
+constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
+
+__global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
+    float *__restrict__ residual, const float *__restrict__ projected, float *__restrict__ next_in,
+    const float *__restrict__ g_post, const float *__restrict__ g_next, int n, float eps_post,
+    float eps_next)
+{
+    __shared__ float red[kTailThreads / 64];
+    const int64_t off = (int64_t)blockIdx.x * n;
+    f32x4 *r4 = reinterpret_cast<f32x4 *>(residual + off);
+    const f32x4 *p4 = reinterpret_cast<const f32x4 *>(projected + off);
+    f32x4 *o4 = reinterpret_cast<f32x4 *>(next_in + off);
+    const f32x4 *gp4 = reinterpret_cast<const f32x4 *>(g_post);
+    const f32x4 *gn4 = reinterpret_cast<const f32x4 *>(g_next);
+    const int n4 = n >> 2;
+    const float inv_n = 1.0f / (float)n;
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    f32x4 pv[kTailVec], rv[kTailVec], gp[kTailVec], gn[kTailVec];
+#pragma unroll
+    for (int j = 0; j < kTailVec; ++j) {
+        const int i = threadIdx.x + j * blockDim.x;
+        const bool ok = i < n4;
+        pv[j] = ok ? p4[i] : z;
+        rv[j] = ok ? r4[i] : z;
+        gp[j] = ok ? gp4[i] : z;
+        gn[j] = ok ? gn4[i] : z;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTailVec; ++j) ss += sumsq4(pv[j]);
+    ss = block_sum_fixed(ss, red);
+    const float inv_p = rsqrtf(ss * inv_n + eps_post);
+
+    float sr = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTailVec; ++j) {
+        const int i = threadIdx.x + j * blockDim.x;
+        rv[j] = rv[j] + (pv[j] * inv_p) * gp[j];
+        if (i < n4) r4[i] = rv[j];
+        sr += sumsq4(rv[j]);
+    }
+    sr = block_sum_fixed(sr, red);
+    const float inv_r = rsqrtf(sr * inv_n + eps_next);
+#pragma unroll
+    for (int j = 0; j < kTailVec; ++j) {
+        const int i = threadIdx.x + j * blockDim.x;
+        if (i < n4) o4[i] = (rv[j] * inv_r) * gn[j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Read-stream probe: every byte of a buffer read once with 16-byte loads in
+// a grid-stride loop (each wave instruction covers 1 KB of consecutive
+// bytes), folded with xor so the loads stay live.  It measures the HBM read
+// ceiling that the matvecs are compared with; it is not on the decode path.
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict__ p, int64_t n16,
+                                                         uint32_t *__restrict__ out)
+{
+    constexpr int U = 8;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(p + i + j * stride);
+#pragma unroll
+        for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = acc;
+}
+
 // ---------------------------------------------------------------------------
 // Host side: launch shapes.
 struct DevInfo {
@@ -528,13 +343,20 @@ int device_cus()
     return g_dev[dev].cus;
 }
 
-// Pick lanes-per-row, waves per workgroup and grid for a matvec.  The score
-// favours: every lane busy in every unit step, every wave slot holding a
-// row, and at least 8 waves per CU for latency hiding.
-kqi::MatvecShape choose_shape(int64_t n_rows, int units, int cus)
+// Pick lanes-per-row, waves per workgroup, grid and depth for a matvec.  The
+// score favours every lane busy in every unit step and every wave slot holding
+// a row, then enough waves per CU.  Measured on MI355X at the FFN shapes: Q4_K
+// streams best with many waves (about 8+) and no look-ahead (depth 1); Q6_K,
+// whose 30-register units limit occupancy, streams best with a few waves per
+// CU each keeping 3 units in flight, which needs the 8-wave VGPR budget.
+kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus)
 {
     static const int kLanes[] = {4, 8, 16, 32, 64};
-    kqi::MatvecShape best{8, 1, 1};
+    const bool q6 = qtype == 2;
+    const int depth = q6 ? 3 : 1;
+    const int wmax = q6 ? 8 : 16;
+    const double want_waves = q6 ? 4.0 : 8.0;
+    kqi::MatvecShape best{8, 1, 1, depth};
     double best_score = -1.0;
     for (int L : kLanes) {
         const int rpt = 64 / L;
@@ -542,16 +364,20 @@ kqi::MatvecShape choose_shape(int64_t n_rows, int units, int cus)
         const int grid = (int)(tiles_total < cus ? (tiles_total > 0 ? tiles_total : 1) : cus);
         const int64_t rows_wg = (n_rows + grid - 1) / grid;
         const int64_t tiles = (rows_wg + rpt - 1) / rpt;
-        const int waves = (int)(tiles < 16 ? tiles : 16);
+        const int waves = (int)(tiles < wmax ? tiles : wmax);
         const int64_t rounds = (tiles + waves - 1) / waves;
         const int steps = (units + L - 1) / L;
         const double lane_eff = (double)units / (double)(L * steps);
         const double slot_eff = (double)rows_wg / (double)(rpt * waves * rounds);
-        const double occ = waves >= 8 ? 1.0 : (double)waves / 8.0;
-        const double score = lane_eff * slot_eff * occ;
+        const double occ = waves >= want_waves ? 1.0 : (double)waves / want_waves;
+        // Q6_K: 8 lanes per row measured best whenever a workgroup has rows
+        // for it; idle waves still share the activation staging, so the
+        // workgroup keeps all 8.
+        const double pref = (q6 && L == 8) ? 1.25 : 1.0;
+        const double score = lane_eff * slot_eff * occ * pref;
         if (score > best_score + 1e-9) {
             best_score = score;
-            best = kqi::MatvecShape{L, waves, grid};
+            best = kqi::MatvecShape{L, q6 ? wmax : waves, grid, depth};
         }
     }
     return best;
@@ -579,27 +405,28 @@ size_t staging_bytes(int k)
 
 kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k)
 {
-    kqi::MatvecShape s = choose_shape(n_rows, 2 * (k >> 8), device_cus());
+    kqi::MatvecShape s = choose_shape(qtype, n_rows, 2 * (k >> 8), device_cus());
     const kqi::MatvecShape o = g_override[qtype];
     if (o.lanes) s.lanes = o.lanes;
     if (o.waves) s.waves = o.waves;
     if (o.grid) s.grid = o.grid;
+    if (o.depth) s.depth = o.depth;
     return s;
 }
 
-template <int LANES>
-hipError_t launch_q4k_lanes(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                            const float *gate, kqi::MatvecShape s, hipStream_t stream)
+template <int LANES, int DEPTH, int WMAX>
+hipError_t launch_q4k_cfg(const uint8_t *W, const float *x, float *y, int n_rows, int k,
+                          const float *gate, kqi::MatvecShape s, hipStream_t stream)
 {
     const size_t lds = staging_bytes<32>(k);
     hipError_t e;
     if (gate) {
-        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, true>;
+        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, true>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, gate,
                            n_rows, k);
     } else {
-        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, false>;
+        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, false>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, gate,
                            n_rows, k);
@@ -607,17 +434,54 @@ hipError_t launch_q4k_lanes(const uint8_t *W, const float *x, float *y, int n_ro
     return hipGetLastError();
 }
 
-template <int LANES>
-hipError_t launch_q6k_lanes(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                            kqi::MatvecShape s, hipStream_t stream)
+template <int LANES, int DEPTH, int WMAX>
+hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, float *y, int n_rows, int k,
+                          const float *, kqi::MatvecShape s, hipStream_t stream)
 {
     const size_t lds = staging_bytes<16>(k);
-    constexpr auto kern = q6k_matvec_kernel<LANES, KQ_LIMBS>;
+    constexpr auto kern = q6k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX>;
     hipError_t e = allow_lds<kern>(lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, n_rows, k);
     return hipGetLastError();
 }
+
+// Dispatch a runtime shape to the kernel instantiation: lanes 4..64, units
+// in flight per lane 1..3 (look-ahead 0..2), and a workgroup-size class (up to 8 waves gets the 256-VGPR budget
+// of two waves per SIMD; up to 16 waves the 128-VGPR budget).
+template <template <int, int, int> class F>
+hipError_t dispatch_shape(kqi::MatvecShape s, const uint8_t *W, const float *x, float *y,
+                          int n_rows, int k, const float *gate, hipStream_t stream)
+{
+    const bool small = s.waves <= 8;
+#define KQ_CASE(L, D)                                                                        \
+    if (s.lanes == L && s.depth == D)                                                        \
+        return small ? F<L, D - 1, 8>::go(W, x, y, n_rows, k, gate, s, stream)               \
+                     : F<L, D - 1, 16>::go(W, x, y, n_rows, k, gate, s, stream);
+#define KQ_CASES(L) KQ_CASE(L, 1) KQ_CASE(L, 2) KQ_CASE(L, 3)
+    KQ_CASES(4) KQ_CASES(8) KQ_CASES(16) KQ_CASES(32) KQ_CASES(64)
+#undef KQ_CASES
+#undef KQ_CASE
+    return hipErrorInvalidValue;
+}
+
+template <int L, int D, int WM>
+struct Q4Launch {
+    static hipError_t go(const uint8_t *W, const float *x, float *y, int n, int k, const float *g,
+                         kqi::MatvecShape s, hipStream_t st)
+    {
+        return launch_q4k_cfg<L, D, WM>(W, x, y, n, k, g, s, st);
+    }
+};
+
+template <int L, int D, int WM>
+struct Q6Launch {
+    static hipError_t go(const uint8_t *W, const float *x, float *y, int n, int k, const float *g,
+                         kqi::MatvecShape s, hipStream_t st)
+    {
+        return launch_q6k_cfg<L, D, WM>(W, x, y, n, k, g, s, st);
+    }
+};
 
 }  // namespace
 
@@ -630,7 +494,7 @@ void set_shape_override(int qtype, MatvecShape s)
 
 MatvecShape get_shape_override(int qtype)
 {
-    return (qtype == 1 || qtype == 2) ? g_override[qtype] : MatvecShape{0, 0, 0};
+    return (qtype == 1 || qtype == 2) ? g_override[qtype] : MatvecShape{0, 0, 0, 0};
 }
 
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
@@ -642,29 +506,15 @@ MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              const float *silu_gate, hipStream_t stream)
 {
-    const MatvecShape s = resolve_shape(1, n_rows, k);
-    switch (s.lanes) {
-    case 4: return launch_q4k_lanes<4>(W, x, y, n_rows, k, silu_gate, s, stream);
-    case 8: return launch_q4k_lanes<8>(W, x, y, n_rows, k, silu_gate, s, stream);
-    case 16: return launch_q4k_lanes<16>(W, x, y, n_rows, k, silu_gate, s, stream);
-    case 32: return launch_q4k_lanes<32>(W, x, y, n_rows, k, silu_gate, s, stream);
-    case 64: return launch_q4k_lanes<64>(W, x, y, n_rows, k, silu_gate, s, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k), W, x, y, n_rows, k, silu_gate,
+                                    stream);
 }
 
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              hipStream_t stream)
 {
-    const MatvecShape s = resolve_shape(2, n_rows, k);
-    switch (s.lanes) {
-    case 4: return launch_q6k_lanes<4>(W, x, y, n_rows, k, s, stream);
-    case 8: return launch_q6k_lanes<8>(W, x, y, n_rows, k, s, stream);
-    case 16: return launch_q6k_lanes<16>(W, x, y, n_rows, k, s, stream);
-    case 32: return launch_q6k_lanes<32>(W, x, y, n_rows, k, s, stream);
-    case 64: return launch_q6k_lanes<64>(W, x, y, n_rows, k, s, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k), W, x, y, n_rows, k, nullptr,
+                                    stream);
 }
 
 hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
@@ -686,8 +536,16 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
                        float eps_post, float eps_next, hipStream_t stream)
 {
-    // about 4 float4 slots per thread, between 1 and 16 waves
     const int n4 = n >> 2;
+    if (n <= kTailRegMax) {
+        // up to kTailVec float4 slots per thread, whole waves
+        int threads = ((n4 + kTailVec * 64 - 1) / (kTailVec * 64)) * 64;
+        if (threads < 64) threads = 64;
+        hipLaunchKernelGGL(tail_reg_kernel, dim3(rows), dim3(threads), 0, stream, residual,
+                           projected, next_in, g_post, g_next, n, eps_post, eps_next);
+        return hipGetLastError();
+    }
+    // wider rows: about 4 float4 slots per thread, between 1 and 16 waves
     int threads = ((n4 + 4 * 64 - 1) / (4 * 64)) * 64;
     if (threads < 64) threads = 64;
     if (threads > 1024) threads = 1024;
@@ -696,10 +554,18 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
     return hipGetLastError();
 }
 
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
+                             hipStream_t stream)
+{
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4 *>(buf), bytes / 16, out);
+    return hipGetLastError();
+}
+
 const char *variant_names()
 {
-    return "q4k_matvec[lanes=4..64,limbs=3,silu=0/1,prefetch=1] q6k_matvec[lanes=4..64,limbs=3,prefetch=0] "
-           "small_m[per-row matvec] tail[rows x (64..1024) threads, 3 passes]";
+    return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1] q6k_matvec[lanes=4..64,limbs=3,depth=1..3] "
+           "small_m[per-row matvec] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

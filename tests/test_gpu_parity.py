@@ -104,12 +104,13 @@ def test_zero_and_nan_activation():
 
 
 @pytest.mark.parametrize("lanes", [4, 8, 16, 32, 64])
-@pytest.mark.parametrize("waves,grid", [(1, 0), (4, 7), (16, 1)])
-def test_every_launch_shape(lanes, waves, grid):
+@pytest.mark.parametrize("waves,grid", [(1, 0), (4, 7), (16, 1), (8, 300)])
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_every_launch_shape(lanes, waves, grid, depth):
     n = 301
     try:
         for qt, qti, k in (("q4k", kq.KQ_QTYPE_Q4K, 1792), ("q6k", kq.KQ_QTYPE_Q6K, 2816)):
-            kq.kq_tune_set_shape(qti, lanes, waves, grid)
+            kq.kq_tune_set_shape(qti, lanes, waves, grid, depth)
             _full_check(qt, n, k, 5000 + lanes)
     finally:
         kq.kq_tune_set_shape(kq.KQ_QTYPE_Q4K)
