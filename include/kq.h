@@ -79,6 +79,7 @@ typedef int kq_status;
 #define KQ_MAX_K 40960      /* largest k (inputs per row) any matvec accepts */
 #define KQ_MAX_M 16         /* largest activation batch of kq_matmul_small_m */
 #define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
+#define KQ_MAX_CHAIN_HIDDEN 16384 /* largest hidden size of kq_ffn_chain */
 
 /*
  * Q4_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows, with an
@@ -142,6 +143,60 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
 kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,
                                  const float *g_post, const float *g_next, int64_t rows,
                                  int64_t n, float eps_post, float eps_next, void *stream);
+
+/*
+ * One decode token through `layers` FFN layers in a single persistent launch:
+ * the FFN weight stream of the decode graph (Ch 10 "The forward pass at a
+ * glance", section 10.3, boxes 11-13, recorded once per token; Ch 19 "The down
+ * projection + residual", section 19.1).  With x_0 = x_in, for l = 0..layers-1:
+ *   mid      = silu(W_gate[l] x_l) * (W_up[l] x_l)
+ *   p        = W_down[l] mid
+ *   residual = residual + rms_norm(p, eps_post) * g_post[l]
+ *   x_{l+1}  = rms_norm(residual, eps_next) * g_next[l]
+ * and x_out = x_layers.  Each step meets the tolerance of the matching
+ * single-op call; results are deterministic but not bitwise equal to a chain
+ * of single-op calls (the lane splits differ).
+ *   w_gate, w_up    DEVICE array [layers] of device pointers, each to Q4_K
+ *                   weights [ffn x hidden], 16-byte aligned.
+ *   w_down          DEVICE array [layers] of device pointers to down_qtype
+ *                   weights [hidden x ffn] (Q6_K 4-byte, Q4_K 16-byte aligned).
+ *   down_qtype      KQ_QTYPE_Q6K or KQ_QTYPE_Q4K.
+ *   g_post, g_next  DEVICE arrays [layers] of device pointers to [hidden] f32
+ *                   gains, 16-byte aligned.
+ *   x_in [hidden] f32 in, residual [hidden] f32 in/out, x_out [hidden] f32 out;
+ *                   16-byte aligned and pairwise disjoint.
+ *   hidden, ffn     multiples of 256; hidden <= KQ_MAX_CHAIN_HIDDEN,
+ *                   ffn <= KQ_MAX_K; layers >= 1.
+ *   workspace       device buffer of at least kq_ffn_chain_workspace_bytes()
+ *                   bytes, 256-byte aligned, zeroed once before its first use;
+ *                   a completed call leaves its control words zero again.
+ *                   Calls sharing a workspace must not overlap in time.
+ * The launch is cooperative (one workgroup per CU, all co-resident) and returns
+ * KQ_ERR_LAUNCH if the device cannot host it.  The pointer tables live in
+ * device memory and are checked by the kernel: a NULL or misaligned entry
+ * makes it do nothing and record error 2 in the workspace; a grid barrier
+ * that does not complete within about a second records error 1 and ends the
+ * launch.  kq_ffn_chain_error() reads that word.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE (also: workspace too small), KQ_ERR_ALIGN,
+ * KQ_ERR_ALIAS, KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
+ */
+kq_status kq_ffn_chain(const void *const *w_gate, const void *const *w_up,
+                       const void *const *w_down, int down_qtype, const float *const *g_post,
+                       const float *const *g_next, int64_t layers, int64_t hidden, int64_t ffn,
+                       const float *x_in, float *residual, float *x_out, float eps_post,
+                       float eps_next, void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes kq_ffn_chain needs for these sizes (0 if they are invalid). */
+int64_t kq_ffn_chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype);
+
+/*
+ * Synchronous: copies the error word of a kq_ffn_chain workspace to *error
+ * (0 = none, 1 = barrier timeout, 2 = bad pointer table).  Waits for the
+ * device to finish the work already enqueued on the default stream's device
+ * memory (a blocking hipMemcpy).  Errors: KQ_ERR_NULL, KQ_ERR_ALIGN,
+ * KQ_ERR_LAUNCH.
+ */
+kq_status kq_ffn_chain_error(const void *workspace, int *error);
 
 /* Static text for a status code (never NULL). */
 const char *kq_status_string(kq_status s);

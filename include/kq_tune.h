@@ -37,6 +37,12 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
                             int *grid, int *depth);
 
 /*
+ * Lanes per weight row in the gate/up phase of kq_ffn_chain (2, 4 or 8;
+ * default 4), process-wide.  Errors: KQ_ERR_SHAPE.
+ */
+kq_status kq_tune_set_chain_lanes(int lanes);
+
+/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of 256 threads and
  * writes grid*4 xor-folded words to the device buffer `out` (so the loads

@@ -37,6 +37,17 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
                              hipStream_t stream);
 
+// Persistent FFN chain (kq_chain.hip).
+size_t chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype);
+size_t chain_lds_bytes(int64_t hidden, int64_t ffn, int down_qtype, int grid);
+int chain_grid();
+void set_chain_lanes(int lanes);
+hipError_t launch_ffn_chain(const uint8_t *const *wg, const uint8_t *const *wu,
+                            const uint8_t *const *wd, int down_qtype, const float *const *gpost,
+                            const float *const *gnext, int layers, int hidden, int ffn,
+                            const float *x_in, float *residual, float *x_out, float eps_post,
+                            float eps_next, void *workspace, hipStream_t stream);
+
 // The shape the automatic choice would use (for reports and tests).
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);
 

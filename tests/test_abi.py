@@ -129,3 +129,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(kq.KQLibraryMissing):
         kq.kq_matvec_q4k(W, X, Y, 8, 1024, stream=0)
+
+
+def test_chain_validation():
+    f = kq.lib().kq_ffn_chain
+    T = (0x100000, 0x101000, 0x102000)        # device pointer tables (fake)
+    G = (0x103000, 0x104000)
+    XI, R, XO, WS = 0x200000, 0x300000, 0x400000, 0x500000
+    need = kq.kq_ffn_chain_workspace_bytes(6656, 19968, B.KQ_QTYPE_Q6K)
+    assert need > 0
+    assert kq.kq_ffn_chain_workspace_bytes(6656, 1000, B.KQ_QTYPE_Q6K) == 0
+    ok = (*T, B.KQ_QTYPE_Q6K, *G, 52, 6656, 19968, XI, R, XO, C.c_float(1e-8), C.c_float(1e-5),
+          WS, need, None)
+    def call(**kw):
+        a = list(ok)
+        names = ["wg", "wu", "wd", "qt", "gp", "gn", "layers", "hidden", "ffn", "xi", "r", "xo",
+                 "ep", "en", "ws", "wsb", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    assert call(wg=None) == B.KQ_ERR_NULL
+    assert call(ws=None) == B.KQ_ERR_NULL
+    assert call(qt=3) == B.KQ_ERR_SHAPE
+    assert call(layers=0) == B.KQ_ERR_SHAPE
+    assert call(hidden=6600) == B.KQ_ERR_SHAPE
+    assert call(ffn=B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == B.KQ_ERR_SHAPE
+    assert call(ws=WS + 128) == B.KQ_ERR_ALIGN
+    assert call(xi=XI + 4) == B.KQ_ERR_ALIGN
+    assert call(wg=T[0] + 4) == B.KQ_ERR_ALIGN
+    assert call(xo=R) == B.KQ_ERR_ALIAS
+    assert call(xo=WS + 1024) == B.KQ_ERR_ALIAS
+    assert call(en=C.c_float(float("inf"))) == B.KQ_ERR_SHAPE
