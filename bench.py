@@ -60,7 +60,7 @@ KERNEL_SYMBOL = {
     "gate": "q4k_matvec_kernel<..., false>",
     "up_silu": "q4k_matvec_kernel<..., true>",
     "down": "q6k_matvec_kernel",
-    "tail": "tail_kernel",
+    "tail": "tail_reg_kernel",
 }
 
 
@@ -134,30 +134,48 @@ class FFNChain:
         self.kq.kq_fused_residual_norm(self.residual, self.zeros, self.x[0], self.ones, self.ones,
                                        1, HIDDEN, 1e-8, 1e-5)
 
-    def layer(self, l, ev=None):
+    def calls(self, l):
         kq = self.kq
         x, xn = self.x[l % 2], self.x[(l + 1) % 2]
-        calls = (
+        return (
             ("gate", lambda: kq.kq_matvec_q4k(self.Wg[l], x, self.g, FFN, HIDDEN)),
             ("up_silu", lambda: kq.kq_matvec_q4k(self.Wu[l], x, self.mid, FFN, HIDDEN, self.g)),
             ("down", lambda: kq.kq_matvec_q6k(self.Wd[l], self.mid, self.p, HIDDEN, FFN)),
             ("tail", lambda: kq.kq_fused_residual_norm(self.residual, self.p, xn, self.gp[l],
                                                        self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
         )
-        for name, fn in calls:
-            if ev is None:
-                fn()
-            else:
-                a, b = ev.pair()
-                a.record()
-                fn()
-                b.record()
-                ev.note(name, a, b)
 
-    def run_pass(self, ev=None):
+    def run_pass(self):
         self.entry_norm()
         for l in range(self.layers):
-            self.layer(l, ev)
+            for _, fn in self.calls(l):
+                fn()
+
+    def per_kernel_us(self, reps):
+        """Average duration of each per-op kernel: one graph per kernel holding
+        its launch for every layer (distinct weights, so no cache reuse),
+        replayed reps times; time / (reps * layers)."""
+        torch = self.torch
+        out = {}
+        for i, name in enumerate(("gate", "up_silu", "down", "tail")):
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for l in range(self.layers):
+                    self.calls(l)[i][1]()
+            torch.cuda.synchronize()
+            g.replay()
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ea.record()
+            for _ in range(reps):
+                g.replay()
+            eb.record()
+            torch.cuda.synchronize()
+            out[name] = ea.elapsed_time(eb) * 1e3 / (reps * self.layers)
+            del g
+        return out
 
 
 class EventLog:
@@ -348,9 +366,8 @@ def main():
             graph.replay()
     per_op_ms, _ = timed((lambda: graph.replay()) if graph is not None else chain.run_pass,
                          args.steps)
+    per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph is not None else {}
     ev = EventLog(torch)
-    for _ in range(max(2, min(args.steps, 5))):
-        chain.run_pass(ev)
 
     # ---- the hot path as timed: the persistent chain (one launch per token)
     for _ in range(max(1, args.warmup)):
@@ -366,13 +383,19 @@ def main():
 
     per = ev.summary()
     kernels = {}
-    for name, us in per.items():
+    for name, us in per.items():  # the chain: events around each launch
         avg = float(np.mean(us))
-        nb = bytes_chain_launch if name == "chain" else BYTES[name]
-        gbps = nb / (avg * 1e-6) / 1e9
+        gbps = bytes_chain_launch / (avg * 1e-6) / 1e9
         kernels[name] = {"symbol": KERNEL_SYMBOL[name], "launches": int(us.size), "us_avg": round(avg, 3),
-                         "us_median": round(float(np.median(us)), 3), "bytes_per_launch": nb,
-                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+                         "us_median": round(float(np.median(us)), 3), "bytes_per_launch": bytes_chain_launch,
+                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                         "timing": "HIP events around each launch"}
+    for name, avg in per_kernel.items():  # per-op kernels: graph of one launch per layer
+        gbps = BYTES[name] / (avg * 1e-6) / 1e9
+        kernels[name] = {"symbol": KERNEL_SYMBOL[name], "us_avg": round(avg, 3),
+                         "bytes_per_launch": BYTES[name], "GBps": round(gbps, 1),
+                         "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                         "timing": f"graph of {layers} back-to-back launches (one per layer)"}
     dk = kernels["chain"]
     traffic = load_pmc("chain", src_hash)
     roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS,
