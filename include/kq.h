@@ -111,19 +111,41 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
                         void *stream);
 
 /*
- * Small-M matmul for the speculative-verify batch: for m < M and r < n_rows,
+ * Small-M matmul for the speculative-verify batch (Ch 36 "Speculative
+ * decoding", section 36.4: the verify pass multiplies each weight row by T
+ * positions at once; Ch 19, section 19.4 times it at M = 16): for m < M and
+ * r < n_rows,
  *   Y[m * ldy + r] = sum_i w[r,i] * X[m * ldx + i].
- * Each weight is read from memory once and applied to all M rows.
+ * Each weight is read from memory once and applied to all M rows.  M = 1 runs
+ * the matvec of that qtype (identical results); M >= 2 runs the matrix-core
+ * kernel, whose partial sums over ranges of k may pass through `workspace`.
  *   qtype   KQ_QTYPE_Q4K or KQ_QTYPE_Q6K.
  *   W       weight bytes as for the matvec of that qtype (same alignment).
  *   X       [M][ldx] f32, ldx >= k and ldx % 4 == 0, 16-byte aligned.
  *   Y       [M][ldy] f32 output, ldy >= n_rows, 4-byte aligned; must not
- *           overlap W or X.
+ *           overlap W, X or the workspace.
  *   n_rows  >= 0; k as for the matvec; 1 <= m <= KQ_MAX_M.
- * Errors as kq_matvec_q4k.
+ *   workspace, workspace_bytes
+ *           caller-owned device memory of at least
+ *           kq_matmul_small_m_workspace_bytes(qtype, n_rows, k, m) bytes,
+ *           256-byte aligned and zero-filled before its first use; every call
+ *           leaves it zero-filled where it matters (its counters), so it can
+ *           be reused without clearing.  May be NULL when that size is 0.
+ *           Calls sharing a workspace must be ordered (same stream, or
+ *           synchronised); concurrent calls need separate workspaces.
+ * Results are deterministic for a given shape and device.
+ * Errors as kq_matvec_q4k; a workspace that is too small is KQ_ERR_SHAPE.
  */
 kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ldx, float *Y,
-                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *stream);
+                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *workspace,
+                            int64_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes kq_matmul_small_m needs for this shape on the current
+ * device (0 if none), or a negative kq_status for arguments it would reject
+ * (KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED, KQ_ERR_DEVICE).  Synchronous, no GPU work.
+ */
+int64_t kq_matmul_small_m_workspace_bytes(int qtype, int64_t n_rows, int64_t k, int m);
 
 /*
  * Fused dual-epsilon residual tail, rows independent:

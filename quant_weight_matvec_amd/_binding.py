@@ -58,7 +58,10 @@ def lib() -> C.CDLL:
     L = C.CDLL(LIB_PATH)
     L.kq_matvec_q4k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp]
     L.kq_matvec_q6k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
-    L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp]
+    L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp,
+                                    _i64, _vp]
+    L.kq_matmul_small_m_workspace_bytes.argtypes = [C.c_int, _i64, _i64, C.c_int]
+    L.kq_matmul_small_m_workspace_bytes.restype = _i64
     L.kq_fused_residual_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, C.c_float,
                                          C.c_float, _vp]
     L.kq_status_string.argtypes = [C.c_int]
@@ -125,10 +128,20 @@ def kq_matvec_q6k(W, x, y, n_rows: int, k: int, stream=None) -> None:
 
 
 def kq_matmul_small_m(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: int, m: int,
-                      stream=None) -> None:
+                      workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     rc = lib().kq_matmul_small_m(int(qtype), _ptr(W), _ptr(X), int(ldx), _ptr(Y), int(ldy),
-                                 int(n_rows), int(k), int(m), _stream(stream))
+                                 int(n_rows), int(k), int(m), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
     _check(rc, "kq_matmul_small_m")
+
+
+def kq_matmul_small_m_workspace_bytes(qtype: int, n_rows: int, k: int, m: int) -> int:
+    """Bytes of workspace kq_matmul_small_m needs (0 = none); raises KQError
+    for arguments the call would reject."""
+    n = int(lib().kq_matmul_small_m_workspace_bytes(int(qtype), int(n_rows), int(k), int(m)))
+    if n < 0:
+        _check(n, "kq_matmul_small_m_workspace_bytes")
+    return n
 
 
 def kq_fused_residual_norm(residual, projected, next_in, g_post, g_next, rows: int, n: int,

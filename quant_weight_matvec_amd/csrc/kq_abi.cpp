@@ -85,18 +85,35 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
                                            (hipStream_t)stream));
 }
 
+static kq_status check_small_m(int qtype, int64_t n_rows, int64_t k, int m)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (m < 1 || n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    if (m > KQ_MAX_M) return KQ_ERR_UNSUPPORTED;
+    return check_k(k);
+}
+
+int64_t kq_matmul_small_m_workspace_bytes(int qtype, int64_t n_rows, int64_t k, int m)
+{
+    kq_status s = check_small_m(qtype, n_rows, k, m);
+    if (s != KQ_OK) return s;
+    if (n_rows == 0 || m == 1) return 0;
+    if ((s = check_device()) != KQ_OK) return s;
+    return (int64_t)kqi::small_m_workspace_bytes(qtype, (int)n_rows, (int)k, m);
+}
+
 kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ldx, float *Y,
-                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *stream)
+                            int64_t ldy, int64_t n_rows, int64_t k, int m, void *workspace,
+                            int64_t workspace_bytes, void *stream)
 {
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
     if (!W || !X || !Y) return KQ_ERR_NULL;
-    if (m < 1 || n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
-    if (m > KQ_MAX_M) return KQ_ERR_UNSUPPORTED;
-    kq_status s = check_k(k);
+    kq_status s = check_small_m(qtype, n_rows, k, m);
     if (s != KQ_OK) return s;
-    if (ldx < k || ldx % 4 || ldy < n_rows || ldy < 1) return KQ_ERR_SHAPE;
+    if (ldx < k || ldx % 4 || ldy < n_rows || ldy < 1 || workspace_bytes < 0) return KQ_ERR_SHAPE;
     const uintptr_t walign = qtype == KQ_QTYPE_Q4K ? 16 : 4;
-    if (!aligned(W, walign) || !aligned(X, 16) || !aligned(Y, 4)) return KQ_ERR_ALIGN;
+    if (!aligned(W, walign) || !aligned(X, 16) || !aligned(Y, 4) || !aligned(workspace, 256))
+        return KQ_ERR_ALIGN;
     const int64_t blk = qtype == KQ_QTYPE_Q4K ? KQ_Q4K_BLOCK_BYTES : KQ_Q6K_BLOCK_BYTES;
     const int64_t wbytes = n_rows * (k / KQ_QK) * blk;
     const int64_t ybytes = ((int64_t)(m - 1) * ldy + n_rows) * 4;
@@ -104,8 +121,24 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
     if (overlap(Y, ybytes, W, wbytes) || overlap(Y, ybytes, X, xbytes)) return KQ_ERR_ALIAS;
     if (n_rows == 0) return KQ_OK;
     if ((s = check_device()) != KQ_OK) return s;
-    return from_hip(kqi::launch_small_m(qtype, (const uint8_t *)W, X, ldx, Y, ldy, (int)n_rows,
-                                        (int)k, m, (hipStream_t)stream));
+    if (m == 1)
+        return from_hip(qtype == KQ_QTYPE_Q4K
+                            ? kqi::launch_matvec_q4k((const uint8_t *)W, X, Y, (int)n_rows,
+                                                     (int)k, nullptr, (hipStream_t)stream)
+                            : kqi::launch_matvec_q6k((const uint8_t *)W, X, Y, (int)n_rows,
+                                                     (int)k, (hipStream_t)stream));
+    const int64_t need =
+        (int64_t)kqi::small_m_workspace_bytes(qtype, (int)n_rows, (int)k, m);
+    if (need > 0) {
+        if (!workspace) return KQ_ERR_NULL;
+        if (workspace_bytes < need) return KQ_ERR_SHAPE;
+        if (overlap(workspace, need, Y, ybytes) || overlap(workspace, need, X, xbytes) ||
+            overlap(workspace, need, W, wbytes))
+            return KQ_ERR_ALIAS;
+    }
+    return from_hip(kqi::launch_small_m_mfma(qtype, (const uint8_t *)W, X, ldx, Y, ldy,
+                                             (int)n_rows, (int)k, m, workspace, workspace_bytes,
+                                             (hipStream_t)stream));
 }
 
 kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,

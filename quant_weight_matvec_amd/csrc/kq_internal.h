@@ -28,8 +28,11 @@ hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_r
                              const float *silu_gate, hipStream_t stream);
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              hipStream_t stream);
-hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
-                          int64_t ldy, int n_rows, int k, int m, hipStream_t stream);
+// Batched small-m kernel (kq_small_m.hip), m = 2..16.
+size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
+hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+                               int64_t ldy, int n_rows, int k, int m, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream);
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
                        float eps_post, float eps_next, hipStream_t stream);

@@ -517,21 +517,6 @@ hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_r
                                     stream);
 }
 
-hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
-                          int64_t ldy, int n_rows, int k, int m, hipStream_t stream)
-{
-    // One matvec per activation row.  Correct, but reads the weights m times;
-    // the batched kernel replaces this path.
-    for (int i = 0; i < m; ++i) {
-        hipError_t e = (qtype == 1)
-                           ? launch_matvec_q4k(W, X + i * ldx, Y + i * ldy, n_rows, k, nullptr,
-                                               stream)
-                           : launch_matvec_q6k(W, X + i * ldx, Y + i * ldy, n_rows, k, stream);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-}
-
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
                        float eps_post, float eps_next, hipStream_t stream)
@@ -565,7 +550,7 @@ hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int 
 const char *variant_names()
 {
     return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1] q6k_matvec[lanes=4..64,limbs=3,depth=1..3] "
-           "small_m[per-row matvec] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
+           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 128-row groups] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

@@ -80,16 +80,25 @@ def test_matvec_validation():
 
 def test_small_m_validation():
     f = kq.lib().kq_matmul_small_m
-    assert f(3, W, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # qtype
-    assert f(1, W, X, 1024, Y, 8, 8, 1024, 0, None) == B.KQ_ERR_SHAPE      # m = 0
-    assert f(1, W, X, 1024, Y, 8, 8, 1024, 17, None) == B.KQ_ERR_UNSUPPORTED
-    assert f(1, W, X, 1000, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldx < k
-    assert f(1, W, X, 1026, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldx % 4
-    assert f(1, W, X, 1024, Y, 7, 8, 1024, 4, None) == B.KQ_ERR_SHAPE      # ldy < n_rows
-    assert f(1, None, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_NULL
-    assert f(2, W + 2, X, 1024, Y, 8, 8, 1024, 4, None) == B.KQ_ERR_ALIGN
-    assert f(1, W, X, 1024, X + 4 * 1024, 8, 8, 1024, 4, None) == B.KQ_ERR_ALIAS
-    assert f(1, W, X, 1024, Y, 8, 0, 1024, 4, None) == B.KQ_OK             # empty
+    WS = 0x600000
+    a = lambda *v, ws=WS, wsb=1 << 20: f(*v, ws, wsb, None)
+    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 0) == B.KQ_ERR_SHAPE      # m = 0
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
+    assert a(1, W, X, 1000, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldx < k
+    assert a(1, W, X, 1026, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldx % 4
+    assert a(1, W, X, 1024, Y, 7, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldy < n_rows
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 4, wsb=-1) == B.KQ_ERR_SHAPE
+    assert a(1, None, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_NULL
+    assert a(2, W + 2, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_ALIGN
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 4, ws=WS + 16) == B.KQ_ERR_ALIGN
+    assert a(1, W, X, 1024, X + 4 * 1024, 8, 8, 1024, 4) == B.KQ_ERR_ALIAS
+    assert a(1, W, X, 1024, Y, 8, 0, 1024, 4) == B.KQ_OK             # empty
+    q = kq.lib().kq_matmul_small_m_workspace_bytes
+    assert q(1, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
+    assert q(3, 8, 1024, 4) == B.KQ_ERR_SHAPE
+    assert q(1, 8, 300, 4) == B.KQ_ERR_SHAPE
+    assert q(1, 0, 1024, 4) == 0 and q(2, 8, 1024, 1) == 0        # empty, or m = 1 (matvec)
 
 
 def test_tail_validation():

@@ -215,27 +215,6 @@ def test_down_projection_then_tail():
     assert dr <= 2e-3 and do <= 2e-3
 
 
-# ---------------------------------------------------------------- small M
-@pytest.mark.parametrize("qt", ["q4k", "q6k"])
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
-def test_small_m(qt, m):
-    n, k = (2048, 6656) if qt == "q4k" else (1024, 19968)
-    W = weights(qt, n, k, 6000 + m)
-    X = I.normal_f32((16, k), stream=6100 + m)
-    ldy = n + 4
-    Y = nan_like((m, ldy))
-    qti = kq.KQ_QTYPE_Q4K if qt == "q4k" else kq.KQ_QTYPE_Q6K
-    kq.kq_matmul_small_m(qti, dev(W), dev(X), k, Y, ldy, n, k, m)
-    torch.cuda.synchronize()
-    Yg = Y.cpu().numpy().astype(np.float64)
-    rows = sample_rows(n, 96, seed=m)
-    sub = np.ascontiguousarray(W[rows])
-    Yr, S = O.matmul(qt, sub, X[:m], len(rows), k, nthreads=NTHREADS)
-    for i in range(m):
-        assert_matvec_close(Yg[i, rows], Yr[i], S[i], what=f"{qt} m={m} row {i}")
-    assert np.all(np.isnan(Yg[:, n:])), "wrote past n_rows inside the ldy padding"
-
-
 # ---------------------------------------------------------------- graph capture
 def test_graph_replay_matches_eager():
     """A captured matvec + tail replayed several times, with eager work and

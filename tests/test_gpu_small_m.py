@@ -1,0 +1,189 @@
+"""kq_matmul_small_m (the batched verify matmul) against the CPU oracle.
+
+Contract per output: |Y[m][r] - Y_ref[m][r]| <= 1e-3 * sum_i |w_ri X_mi|, as for
+the matvec.  M = 1 runs the matvec and must equal it bitwise.  M >= 2 runs the
+matrix-core kernel with its stream-K split; shapes below cover row counts
+that are not multiples of the 16-row tile or the 128-row group, k from one
+superblock up, workgroups whose range holds one tile, several row groups, or
+parts of two, and the full FFN shapes on sampled rows.  Every output starts
+as NaN, with NaN padding past n_rows inside ldy that must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quant_weight_matvec_amd as kq
+from quant_weight_matvec_amd import inputs as I
+from gpu_util import NTHREADS, assert_matvec_close, dev, nan_like, sample_rows, weights
+
+pytestmark = pytest.mark.gpu
+O = oracle.get()
+QT = {"q4k": kq.KQ_QTYPE_Q4K, "q6k": kq.KQ_QTYPE_Q6K}
+
+
+def workspace(qt, n, k, m):
+    nbytes = kq.kq_matmul_small_m_workspace_bytes(QT[qt], n, k, m)
+    ws = torch.zeros(max(nbytes, 256) // 4, dtype=torch.int32, device="cuda")
+    return ws, nbytes
+
+
+def run(qt, Wd, Xd, ldx, n, k, m, ldy=None, ws=None):
+    ldy = n + 3 if ldy is None else ldy
+    Y = nan_like((m, ldy))
+    if ws is None:
+        ws = workspace(qt, n, k, m)
+    kq.kq_matmul_small_m(QT[qt], Wd, Xd, ldx, Y, ldy, n, k, m, ws[0], ws[1])
+    torch.cuda.synchronize()
+    Yg = Y.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(Yg[:, n:])), "wrote past n_rows inside the ldy padding"
+    return Yg[:, :n]
+
+
+def check(qt, n, k, m, seed, rows=None, xscale=None, ldx=None):
+    W = weights(qt, n, k, seed)
+    ldx = k if ldx is None else ldx
+    X = np.zeros((m, ldx), np.float32)
+    X[:, :k] = I.normal_f32((m, k), stream=seed + 1)
+    if xscale is not None:
+        X[:, :k] *= np.asarray(xscale, np.float32).reshape(-1, 1)
+    Yg = run(qt, dev(W), dev(X), ldx, n, k, m)
+    rows = np.arange(n) if rows is None else rows
+    Yr, S = O.matmul(qt, np.ascontiguousarray(W[rows]), X[:, :k], len(rows), k, nthreads=NTHREADS)
+    worst = 0.0
+    for i in range(m):
+        worst = max(worst, assert_matvec_close(Yg[i, rows], Yr[i], S[i], what=f"{qt} {n}x{k} m={m} row {i}"))
+    return worst
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+@pytest.mark.parametrize("m", [2, 3, 4, 8, 16])
+def test_small_shapes_all_rows(qt, m):
+    """Several row groups with a ragged last group, k of 11 superblocks."""
+    print("worst |dy|/S", check(qt, 300, 2816, m, 7000 + m))
+
+
+@pytest.mark.parametrize("qt,n,k", [("q4k", 1, 256), ("q6k", 1, 256), ("q4k", 5, 512),
+                                    ("q6k", 17, 1280), ("q4k", 129, 768), ("q6k", 255, 2304),
+                                    ("q4k", 1000, 6656), ("q6k", 77, 19968), ("q4k", 4100, 1024),
+                                    ("q6k", 2049, 4096)])
+def test_ragged_shapes(qt, n, k):
+    print("worst |dy|/S", check(qt, n, k, 5, 7100 + n, rows=sample_rows(n, 160, seed=n)))
+
+
+@pytest.mark.parametrize("qt,n,k", [("q4k", 19968, 6656), ("q6k", 6656, 19968)])
+@pytest.mark.parametrize("m", [2, 4, 8, 16])
+def test_full_size_sampled_rows(qt, n, k, m):
+    """The verify shapes at M = 2..16 in the benchmark's launch configuration."""
+    print("worst |dy|/S", check(qt, n, k, m, 7200 + m, rows=sample_rows(n, 96, seed=m)))
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_m1_is_the_matvec(qt):
+    n, k = 1000, 6656
+    W, x = weights(qt, n, k, 7300), I.normal_f32(k, stream=7301)
+    Wd, xd = dev(W), dev(x)
+    Yg = run(qt, Wd, xd, k, n, k, 1)
+    y = nan_like(n)
+    (kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k)(Wd, xd, y, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(Yg[0], y.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_rows_are_independent_of_m(qt):
+    """Row m of the result does not depend on the other activation rows:
+    M = 16 and M = 3 agree bitwise on the first three rows (same launch plan
+    up to LDS chunking, same per-row arithmetic)."""
+    n, k = 700, 4096
+    W, X = weights(qt, n, k, 7400), I.normal_f32((16, k), stream=7401)
+    Wd, Xd = dev(W), dev(X)
+    a = run(qt, Wd, Xd, k, n, k, 16)
+    b = run(qt, Wd, Xd, k, n, k, 3)
+    Yr, S = O.matmul(qt, W, X[:3], n, k, nthreads=NTHREADS)
+    for i in range(3):
+        assert_matvec_close(a[i], Yr[i], S[i], what=f"m=16 row {i}")
+        assert_matvec_close(b[i], Yr[i], S[i], what=f"m=3 row {i}")
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_deterministic_and_workspace_reuse(qt):
+    n, k, m = 6656, 19968, 8
+    if qt == "q4k":
+        n, k = 19968, 6656
+    W, X = weights(qt, n, k, 7500), I.normal_f32((m, k), stream=7501)
+    Wd, Xd = dev(W), dev(X)
+    ws = workspace(qt, n, k, m)
+    a = run(qt, Wd, Xd, k, n, k, m, ws=ws)
+    b = run(qt, Wd, Xd, k, n, k, m, ws=ws)  # counters were left at zero
+    assert np.array_equal(a, b)
+    if ws[1] > 0:
+        cnt = ws[0][: (n + 127) // 128].cpu().numpy()
+        assert np.all(cnt == 0), "row-group counters not reset"
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_dynamic_range_per_row(qt):
+    """Activation rows scaled by 1e-30 .. 1e30: each output row stays within
+    its own tolerance (the power-of-two prescale is per row and superblock)."""
+    n, k, m = 520, 3072, 6
+    print("worst |dy|/S", check(qt, n, k, m, 7600, xscale=[1e-30, 1e-12, 1.0, 3e5, 1e18, 1e30]))
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_heavy_tailed_and_mixed_magnitudes(qt):
+    """One superblock group spanning 2^-20 .. 2^20 in magnitude."""
+    n, k, m = 256, 2048, 4
+    W = weights(qt, n, k, 7700)
+    rng = np.random.default_rng(7701)
+    X = (rng.standard_normal((m, k)) * np.exp2(rng.uniform(-20, 20, (m, k)))).astype(np.float32)
+    Yg = run(qt, dev(W), dev(X), k, n, k, m)
+    Yr, S = O.matmul(qt, W, X, n, k, nthreads=NTHREADS)
+    for i in range(m):
+        assert_matvec_close(Yg[i], Yr[i], S[i], what=f"row {i}")
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_nonfinite_activation_poisons_only_its_row(qt):
+    n, k, m = 400, 2048, 4
+    W = weights(qt, n, k, 7800)
+    X = I.normal_f32((m, k), stream=7801)
+    X[1, 1500] = np.nan
+    X[2, 37] = np.inf
+    Yg = run(qt, dev(W), dev(X), k, n, k, m)
+    assert np.all(np.isnan(Yg[1])), "NaN input did not propagate"
+    assert not np.any(np.isfinite(Yg[2])), "Inf input did not propagate"
+    Yr, S = O.matmul(qt, W, X[[0, 3]], n, k, nthreads=NTHREADS)
+    assert_matvec_close(Yg[0], Yr[0], S[0], what="row 0")
+    assert_matvec_close(Yg[3], Yr[1], S[1], what="row 3")
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_strided_x_and_y(qt):
+    n, k, m = 333, 1536, 7
+    print("worst |dy|/S", check(qt, n, k, m, 7900, ldx=k + 260))
+
+
+def test_zero_activations_give_zero():
+    n, k, m = 300, 1024, 5
+    for qt in ("q4k", "q6k"):
+        W = weights(qt, n, k, 8000)
+        Yg = run(qt, dev(W), dev(np.zeros((m, k), np.float32)), k, n, k, m)
+        assert np.all(Yg == 0.0)
+
+
+def test_workspace_errors():
+    qt, n, k, m = "q6k", 6656, 19968, 8
+    need = kq.kq_matmul_small_m_workspace_bytes(QT[qt], n, k, m)
+    assert need > 0
+    W, X = dev(weights(qt, n, k, 8100)), dev(I.normal_f32((m, k), stream=8101))
+    Y = nan_like((m, n))
+    ws = torch.zeros(need // 4, dtype=torch.int32, device="cuda")
+    with pytest.raises(kq.KQError):
+        kq.kq_matmul_small_m(QT[qt], W, X, k, Y, n, n, k, m, ws, need - 256)
+    with pytest.raises(kq.KQError):
+        kq.kq_matmul_small_m(QT[qt], W, X, k, Y, n, n, k, m, None, 0)
+    with pytest.raises(kq.KQError):  # output inside the workspace
+        kq.kq_matmul_small_m(QT[qt], W, X, k, ws, n, n, k, 2, ws, need)
+    torch.cuda.synchronize()
+    assert torch.isnan(Y).all(), "a rejected call wrote its output"
