@@ -69,8 +69,10 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the chain kernel's machine code is built from; the
+    committed counter summary is used only while it matches."""
     h = hashlib.sha256()
-    for f in ("kq_kernels.hip", "kq_chain.hip", "kq_device.h", "kq_abi.cpp", "kq_internal.h"):
+    for f in ("kq_chain.hip", "kq_device.h"):
         with open(os.path.join(ROOT, "quant_weight_matvec_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -254,6 +256,53 @@ def isolated_matvecs(torch, kq, I, reps=20):
     return out
 
 
+def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
+    """kq_matmul_small_m at the verify shapes, M = 1..16: per-launch time from a
+    graph of launches over >= 1 GiB of rotated weight copies (so the Infinity
+    Cache cannot serve them), with GB/s (weights once + X + Y) and GFLOP/s."""
+    out = {}
+    cases = [("q4k_19968x6656", kq.KQ_QTYPE_Q4K, "q4k", FFN, HIDDEN),
+             ("q6k_6656x19968", kq.KQ_QTYPE_Q6K, "q6k", HIDDEN, FFN)]
+    for name, qti, qt, n, k in cases:
+        W = torch.from_numpy(I.weight_matrix(qt, n, k, stream=779)).cuda()
+        ncopy = max(2, int(np.ceil((1 << 30) / W.numel())))
+        copies = [W] + [W.clone() for _ in range(ncopy - 1)]
+        X = torch.from_numpy(I.normal_f32((16, k), stream=780)).cuda()
+        Y = torch.empty((16, n), device="cuda")
+        res = {}
+        for m in ms:
+            nbytes = kq.kq_matmul_small_m_workspace_bytes(qti, n, k, m)
+            ws = torch.zeros(max(nbytes, 256) // 4, dtype=torch.int32, device="cuda")
+            call = lambda c: kq.kq_matmul_small_m(qti, c, X, k, Y, n, n, k, m, ws, nbytes)
+            for c in copies:
+                call(c)
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for c in copies:
+                    call(c)
+            torch.cuda.synchronize()
+            g.replay()
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ea.record()
+            for _ in range(reps):
+                g.replay()
+            eb.record()
+            torch.cuda.synchronize()
+            us = ea.elapsed_time(eb) * 1e3 / (reps * ncopy)
+            b = W.numel() + 4 * m * (n + k)
+            res[f"m{m}"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                            "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4),
+                            "GFLOPs": round(2.0 * m * n * k / us / 1e3, 1), "bytes": b}
+            del g, ws
+        out[name] = {"copies_rotated": ncopy, **res}
+        del copies, W
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(I, budget_s=12.0):
     """The oracle (plain C, binary64) on a bounded sample of the same pass:
     layer 0's FFN (gate, up, silu, down, tail) at full size, repeated until
@@ -416,6 +465,8 @@ def main():
         torch.cuda.empty_cache()
         log("isolated matvecs with weight rotation")
         extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
+        log("small-M verify matmul sweep")
+        extras["small_m"] = small_m_sweep(torch, kq, I)
 
     cpu = None
     if not args.no_cpu_baseline:

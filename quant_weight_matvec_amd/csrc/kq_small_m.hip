@@ -41,6 +41,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kq_device.h"
 #include "kq_internal.h"
 
@@ -54,11 +56,26 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSmWaves = 8;
+// Launch shape: waves per workgroup (one 16-row tile each), weight superblocks
+// in flight per wave, and workgroups per CU the grid is sized for.
+#ifndef KQ_SM_WAVES
+#define KQ_SM_WAVES 8
+#endif
+#ifndef KQ_SM_Q4_DEPTH
+#define KQ_SM_Q4_DEPTH 4
+#endif
+#ifndef KQ_SM_Q6_DEPTH
+#define KQ_SM_Q6_DEPTH 3
+#endif
+#ifndef KQ_SM_OCC
+#define KQ_SM_OCC 1
+#endif
+constexpr int kSmWaves = KQ_SM_WAVES;
 constexpr int kSmThreads = 64 * kSmWaves;
 constexpr int kSmRows = 16 * kSmWaves;  // rows per row group
 constexpr uint32_t kBias = 0x64006400u;  // f16 1024.0 in both halves
 constexpr int kSmLdsMax = 160 * 1024;
+constexpr int kSmLdsBudget = kSmLdsMax / KQ_SM_OCC;  // per workgroup
 
 struct SmArgs {
     const uint8_t *W;
@@ -74,6 +91,7 @@ struct SmArgs {
     int part_off;       // byte offset of the partial tiles in the workspace
     int ws_bytes;
     int flag_off;       // LDS byte offset of the last-arrival flag
+    int xs_off;         // LDS byte offset of the staged activations
 };
 
 __device__ __forceinline__ int first_tile(int g, int T, int G)
@@ -98,69 +116,197 @@ __device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
 }
 
 // ---------------------------------------------------------------------------
-// Per-lane weight data of one superblock of the lane's row.
-// Lane l: kb = l >> 4 selects which quarter of every sub-block the lane
-// supplies, r = l & 15 the row of the tile.
+// Weight tiles.  A wave's tile is one superblock of each of its 16 rows.  It is
+// read from HBM with coalesced 16-byte loads (consecutive lanes take
+// consecutive 16-byte pieces of a row), written to the wave's own LDS slot, and
+// every lane then reads the bytes its MFMA operands need from there.  (Reading
+// those bytes straight from memory would cost one L1 tag lookup per lane per
+// few bytes.)  Slot s of the tile is handled by lane s % 64 in load i = s / 64.
 
+// Q4_K: 16 rows x 9 pieces of 16 bytes (rows are 16-byte aligned).
+constexpr int kQ4Pieces = 9;
+constexpr int kQ4Slots = 16 * kQ4Pieces;   // 144
+constexpr int kQ4Loads = 3;                // ceil(144 / 64)
+constexpr int kQ4RowLds = 144;             // LDS bytes per row of a tile
+constexpr int kQ4TileLds = 16 * kQ4RowLds;
+
+struct Q4Tile {
+    u32x4 c[kQ4Loads];
+};
+
+// Q6_K: a superblock starts 2-byte aligned when its global index is odd.  A row
+// of the tile is read from the 4-byte aligned address a at or below it: 13
+// pieces of 16 bytes cover [a, a + 208) and a tail covers [a + 208, sb + 210)
+// (a dword when a = sb - 2, a 16-bit load when a = sb).  Every access stays in
+// [sb - 2, sb + 210), and sb - 2 is used only when sb is not the first byte of
+// W.  Rows sit 240 bytes apart in LDS so the lanes of different rows hit
+// different banks.
+constexpr int kQ6Pieces = 13;
+constexpr int kQ6Slots = 16 * kQ6Pieces;   // 208
+constexpr int kQ6Loads = 4;                // ceil(208 / 64)
+constexpr int kQ6RowLds = 240;
+constexpr int kQ6TileLds = 16 * kQ6RowLds;
+
+struct Q6Tile {
+    u32x4 c[kQ6Loads];
+    uint32_t tail;
+};
+
+template <typename U> struct TileTraits;
+template <> struct TileTraits<Q4Tile> {
+    static constexpr int kPieces = kQ4Pieces, kLoads = kQ4Loads,
+                         kRowLds = kQ4RowLds, kTileLds = kQ4TileLds, kBlk = kQ4Bytes;
+};
+template <> struct TileTraits<Q6Tile> {
+    static constexpr int kPieces = kQ6Pieces, kLoads = kQ6Loads,
+                         kRowLds = kQ6RowLds, kTileLds = kQ6TileLds, kBlk = kQ6Bytes;
+};
+
+// Per-lane addressing of a tile: for each load i, the byte offset in W of the
+// row this lane's slot belongs to (row clamped to the matrix), and the piece.
+template <typename U>
+struct TileAddr {
+    int64_t row_off[TileTraits<U>::kLoads];
+    int64_t tail_off;  // Q6_K: the row of the tail this lane loads (lanes 0..15)
+};
+
+template <typename U>
+__device__ __forceinline__ void tile_rows(TileAddr<U> &ta, int rg, int wave, int lane, int n_rows,
+                                          int64_t row_bytes, int rows_per_group)
+{
+    using T = TileTraits<U>;
+#pragma unroll
+    for (int i = 0; i < T::kLoads; ++i) {
+        const int slot = 64 * i + lane;
+        const int tr = min(slot / T::kPieces, 15);
+        const int row = min(rg * rows_per_group + 16 * wave + tr, n_rows - 1);
+        ta.row_off[i] = (int64_t)row * row_bytes;
+    }
+    const int row = min(rg * rows_per_group + 16 * wave + (lane & 15), n_rows - 1);
+    ta.tail_off = (int64_t)row * row_bytes;
+}
+
+__device__ __forceinline__ Q4Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q4Tile> &ta,
+                                            int b, int lane)
+{
+    Q4Tile u;
+#pragma unroll
+    for (int i = 0; i < kQ4Loads; ++i) {
+        const int slot = 64 * i + lane;
+        if (slot < kQ4Slots)
+            u.c[i] = *reinterpret_cast<const u32x4 *>(W + ta.row_off[i] + (int64_t)b * kQ4Bytes +
+                                                      16 * (slot % kQ4Pieces));
+    }
+    return u;
+}
+
+__device__ __forceinline__ Q6Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q6Tile> &ta,
+                                            int b, int lane)
+{
+    Q6Tile u;
+#pragma unroll
+    for (int i = 0; i < kQ6Loads; ++i) {
+        const int slot = 64 * i + lane;
+        if (slot < kQ6Slots) {
+            const int64_t a = (ta.row_off[i] + (int64_t)b * kQ6Bytes) & ~(int64_t)3;
+            u.c[i] = *reinterpret_cast<const u32x4_a4 *>(W + a + 16 * (slot % kQ6Pieces));
+        }
+    }
+    if (lane < 16) {
+        const int64_t sb = ta.tail_off + (int64_t)b * kQ6Bytes;
+        const int64_t a = sb & ~(int64_t)3;
+        u.tail = (sb & 3) ? *reinterpret_cast<const uint32_t *>(W + a + 208)
+                          : (uint32_t) * reinterpret_cast<const uint16_t *>(W + a + 208);
+    }
+    return u;
+}
+
+__device__ __forceinline__ void store_tile(const Q4Tile &u, uint8_t *tile, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < kQ4Loads; ++i) {
+        const int slot = 64 * i + lane;
+        if (slot < kQ4Slots) *reinterpret_cast<u32x4 *>(tile + 16 * slot) = u.c[i];
+    }
+}
+
+__device__ __forceinline__ void store_tile(const Q6Tile &u, uint8_t *tile, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < kQ6Loads; ++i) {
+        const int slot = 64 * i + lane;
+        if (slot < kQ6Slots)
+            *reinterpret_cast<u32x4 *>(tile + kQ6RowLds * (slot / kQ6Pieces) +
+                                       16 * (slot % kQ6Pieces)) = u.c[i];
+    }
+    if (lane < 16) *reinterpret_cast<uint32_t *>(tile + kQ6RowLds * lane + 208) = u.tail;
+}
+
+// What one lane needs of its row's superblock, read back from the LDS tile.
 struct Q4Sb {
     u32x4 hdr;      // d, dmin, 12 bytes of packed 6-bit scales and mins
     uint32_t q[8];  // chunk c: bytes 16 + 32c + 8kb .. +7 as q[2c], q[2c+1]
 };
 
-__device__ __forceinline__ Q4Sb load_sb(const uint8_t *__restrict__ sb, int kb, Q4Sb *)
+__device__ __forceinline__ Q4Sb read_sb(const uint8_t *__restrict__ row, int kb, int, Q4Sb *)
 {
     Q4Sb u;
-    u.hdr = *reinterpret_cast<const u32x4 *>(sb);
+    u.hdr = *reinterpret_cast<const u32x4 *>(row);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(sb + 16 + 32 * c + 8 * kb);
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(row + 16 + 32 * c + 8 * kb);
         u.q[2 * c] = v.x;
         u.q[2 * c + 1] = v.y;
     }
     return u;
 }
 
-// Q6_K: a superblock starts 2-byte aligned when its global index is odd.  Each
-// needed dword is read as an 8-byte window starting at the 4-byte aligned
-// address at or below it and re-aligned in registers; every window stays in
-// [sb - 2, sb + 210) and sb - 2 is only used when sb is not the first byte of W.
 struct Q6Sb {
     uint32_t w[24];  // ql windows u = 0..7 (w[2u], w[2u+1]); qh windows v = 0..3 (w[16+2v], ..)
     u32x4 hs;        // scale bytes, aligned window
     uint32_t tail;   // shift 2: scales 14, 15 and d; shift 0: d
+    int sh;          // byte offset of the superblock from 4-byte alignment (0 or 2)
 };
 
-__device__ __forceinline__ Q6Sb load_sb(const uint8_t *__restrict__ sb, int kb, Q6Sb *)
+__device__ __forceinline__ Q6Sb read_sb(const uint8_t *__restrict__ row, int kb, int sh, Q6Sb *)
 {
     Q6Sb u;
-    const int sh = (int)((uintptr_t)sb & 3u);
-    const uint8_t *a = sb - sh;
+    const uint32_t *rw = reinterpret_cast<const uint32_t *>(row);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(a + 16 * i + 4 * kb);
-        u.w[2 * i] = v.x;
-        u.w[2 * i + 1] = v.y;
+        u.w[2 * i] = rw[4 * i + kb];
+        u.w[2 * i + 1] = rw[4 * i + kb + 1];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4 *>(a + 128 + 16 * i + 4 * kb);
-        u.w[16 + 2 * i] = v.x;
-        u.w[17 + 2 * i] = v.y;
+        u.w[16 + 2 * i] = rw[32 + 4 * i + kb];
+        u.w[17 + 2 * i] = rw[32 + 4 * i + kb + 1];
     }
-    u.hs = *reinterpret_cast<const u32x4_a4 *>(a + 192);
-    u.tail = sh ? *reinterpret_cast<const uint32_t *>(a + 208)
-                : (uint32_t) * reinterpret_cast<const uint16_t *>(a + 208);
+    u.hs = *reinterpret_cast<const u32x4 *>(row + 192);
+    u.tail = rw[52];
+    u.sh = sh;
     return u;
 }
 
 __device__ __forceinline__ h8 as_h8(u32x4 v) { return __builtin_bit_cast(h8, v); }
 __device__ __forceinline__ h4 as_h4(u32x2 v) { return __builtin_bit_cast(h4, v); }
 
-// f16 pairs (1024 + byte0 nibble, 1024 + byte2 nibble) etc. from one dword of
-// packed nibbles; `s` selects the nibble (0 low, 4 high) and byte pair (0 or 8).
-__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s)
+// (x & mask) | bias in one VALU instruction.  gfx9 VOP3 encodings read at
+// most one scalar or literal operand, so the mask is passed in a VGPR (set once
+// per lane) and the bias as the one scalar operand.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t vmask, uint32_t bias)
 {
-    return ((w >> s) & 0x000F000Fu) | kBias;
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(vmask), "s"(bias));
+    return r;
+}
+
+// f16 pairs (1024 + nibble of byte 0, 1024 + nibble of byte 2) etc. from one
+// dword of packed nibbles; `s` selects the nibble (0 low, 4 high) and the byte
+// pair (0: bytes 0 and 2, 8: bytes 1 and 3).
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s, uint32_t vmask)
+{
+    return and_or(w >> s, vmask, kBias);
 }
 
 // Contribution of one Q4_K superblock to the lane's 4 outputs, in units of the
@@ -168,7 +314,7 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s)
 // hi plane at this superblock's first input + 8 kb; the lo plane is `lo_off`
 // bytes further.  `st` = group sums of the superblock at [s][m0..m0+3].
 __device__ __forceinline__ f32x4 sb_mma(const Q4Sb &u, const uint8_t *__restrict__ ah,
-                                        int lo_off, const float *__restrict__ st)
+                                        int lo_off, const float *__restrict__ st, uint32_t vmask)
 {
     const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
     const uint32_t scA = S0 & 0x3F3F3F3Fu, mnA = S1 & 0x3F3F3F3Fu;
@@ -178,24 +324,35 @@ __device__ __forceinline__ f32x4 sb_mma(const Q4Sb &u, const uint8_t *__restrict
     const h8 off = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
     f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t w0 = u.q[2 * c], w1 = u.q[2 * c + 1];
+    for (int c0 = 0; c0 < 4; c0 += 2) {
+        // sub-blocks 2c0 .. 2c0+3: all hi MFMAs, then all lo MFMAs
+        h8 B[4];
+        f32x4 acc[4];
 #pragma unroll
-        for (int hn = 0; hn < 2; ++hn) {  // hn 0: low nibbles (sub-block 2c), 1: high (2c+1)
-            const int s = 2 * c + hn;
-            const u32x4 bq = {nib_pair(w0, 4 * hn), nib_pair(w0, 4 * hn + 8), nib_pair(w1, 4 * hn),
-                              nib_pair(w1, 4 * hn + 8)};
-            const h8 B = as_h8(bq) - off;
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + (j >> 1), hn = j & 1, s = 2 * c + hn;
+            const uint32_t w0 = u.q[2 * c], w1 = u.q[2 * c + 1];
+            const u32x4 bq = {nib_pair(w0, 4 * hn, vmask), nib_pair(w0, 4 * hn + 8, vmask),
+                              nib_pair(w1, 4 * hn, vmask), nib_pair(w1, 4 * hn + 8, vmask)};
+            B[j] = as_h8(bq) - off;
             const h8 Ahi = *reinterpret_cast<const h8 *>(ah + 64 * s);
-            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * s);
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, acc, 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                Ahi, B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * (4 * (c0 >> 1) + j));
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B[j], acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = 2 * c0 + j;
             const uint32_t scw = s < 4 ? scA : scB, mnw = s < 4 ? mnA : mnB;
             const float c1 = d * (float)((scw >> (8 * (s & 3))) & 0xFFu);
             const float c2 = dmin * (float)((mnw >> (8 * (s & 3))) & 0xFFu);
             const f32x4 sm = *reinterpret_cast<const f32x4 *>(st + 16 * s);
-            ys += c1 * acc - c2 * sm;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ys[i] = fmaf(c1, acc[j][i], fmaf(-c2, sm[i], ys[i]));
         }
     }
     return ys;
@@ -204,8 +361,9 @@ __device__ __forceinline__ f32x4 sb_mma(const Q4Sb &u, const uint8_t *__restrict
 // One Q6_K superblock; `ah` = the lane's activation row at the superblock's
 // first input + 4 kb.
 __device__ __forceinline__ f32x4 sb_mma(const Q6Sb &u, const uint8_t *__restrict__ ah,
-                                        int lo_off, const float *__restrict__, int sh)
+                                        int lo_off, const float *__restrict__, uint32_t vmask)
 {
+    const int sh = u.sh;
     uint32_t L[8], H[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) L[i] = __builtin_amdgcn_alignbyte(u.w[2 * i + 1], u.w[2 * i], sh);
@@ -221,20 +379,37 @@ __device__ __forceinline__ f32x4 sb_mma(const Q6Sb &u, const uint8_t *__restrict
     const h4 off = {1056, 1056, 1056, 1056};
     f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const int h = s >> 3, g = (s >> 1) & 3, hf = s & 1;
-        const uint32_t l = L[4 * h + 2 * (g & 1) + hf], hh = H[2 * h + hf];
-        const uint32_t lo4 = (g < 2 ? l : (l >> 4)) & 0x0F0F0F0Fu;
-        const uint32_t q = lo4 | (((hh >> (2 * g)) & 0x03030303u) << 4);
-        const u32x2 bq = {(q & 0x00FF00FFu) | kBias, ((q >> 8) & 0x00FF00FFu) | kBias};
-        const h4 B = as_h4(bq) - off;
-        const h4 Ahi = *reinterpret_cast<const h4 *>(ah + 32 * s);
-        const h4 Alo = *reinterpret_cast<const h4 *>(ah + lo_off + 32 * s);
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(Ahi, B, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(Alo, B, acc, 0, 0, 0);
-        const int scv = ((int)(sc[s >> 2] << (24 - 8 * (s & 3)))) >> 24;
-        ys += (d * (float)scv) * acc;
+    for (int s0 = 0; s0 < 16; s0 += 4) {
+        // four sub-blocks at a time: all hi MFMAs, then all lo MFMAs, so no
+        // MFMA waits on the one just issued
+        h4 B[4];
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = s0 + j;
+            const int h = s >> 3, g = (s >> 1) & 3, hf = s & 1;
+            const uint32_t l = L[4 * h + 2 * (g & 1) + hf], hh = H[2 * h + hf];
+            const uint32_t lo4 = (g < 2 ? l : (l >> 4)) & 0x0F0F0F0Fu;
+            const uint32_t q = lo4 | (((hh >> (2 * g)) & 0x03030303u) << 4);
+            const u32x2 bq = {and_or(q, vmask, kBias), and_or(q >> 8, vmask, kBias)};
+            B[j] = as_h4(bq) - off;
+            const h4 Ahi = *reinterpret_cast<const h4 *>(ah + 32 * s);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ahi, B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
+                                                           0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const h4 Alo = *reinterpret_cast<const h4 *>(ah + lo_off + 32 * (s0 + j));
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Alo, B[j], acc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = s0 + j;
+            const int scv = ((int)(sc[s >> 2] << (24 - 8 * (s & 3)))) >> 24;
+            const float c1 = d * (float)scv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ys[i] = fmaf(c1, acc[j][i], ys[i]);
+        }
     }
     return ys;
 }
@@ -242,7 +417,7 @@ __device__ __forceinline__ f32x4 sb_mma(const Q6Sb &u, const uint8_t *__restrict
 template <typename U>
 __device__ __forceinline__ constexpr bool is_q4()
 {
-    return sizeof(U) == sizeof(Q4Sb);
+    return TileTraits<U>::kBlk == kQ4Bytes;
 }
 
 // ---------------------------------------------------------------------------
@@ -313,117 +488,167 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
     }
 }
 
+// This workgroup's share of row group rg is complete: store it, or publish it
+// as a partial tile and, if it is the last contributor, sum all of them.
+__device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, int gh, int g,
+                                               f32x4 yacc, int wave, int r, int m0, int &last_flag)
+{
+    const int nb = a.nb, M = a.m;
+    const int row0 = rg * kSmRows;
+    if (gl == gh) {
+        const int row = row0 + 16 * wave + r;
+        if (row < a.n_rows) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (m0 + i < M) a.Y[(int64_t)(m0 + i) * a.ldy + row] = yacc[i];
+        }
+        return;
+    }
+    float *part = reinterpret_cast<float *>(a.ws + a.part_off);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(a.ws);
+    const int slot = (first_tile(g, a.T, a.G) / nb == rg) ? 0 : 1;
+    float *pp = part + (int64_t)(2 * g + slot) * (16 * kSmRows);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_agent(pp + (m0 + i) * kSmRows + 16 * wave + r, yacc[i]);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt + rg, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (old + 1 == (uint32_t)(gh - gl + 1));
+    }
+    __syncthreads();
+    if (last_flag) {
+        // sum the contributors' partial tiles in workgroup order
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(a.ws, (short)0, a.ws_bytes, 0x00020000);
+        for (int e = threadIdx.x; e < M * (kSmRows / 4); e += kSmThreads) {
+            const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
+            f32x4 s;
+            for (int c = gl; c <= gh; ++c) {
+                const int sl = (first_tile(c, a.T, a.G) / nb == rg) ? 0 : 1;
+                const uint32_t off = (uint32_t)a.part_off +
+                                     4u * (uint32_t)((2 * c + sl) * (16 * kSmRows) +
+                                                     m * kSmRows + 4 * q);
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16 /* sc1 */));
+                s = (c == gl) ? v : s + v;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row0 + 4 * q + i;
+                if (row < a.n_rows) a.Y[(int64_t)m * a.ldy + row] = s[i];
+            }
+        }
+        if (threadIdx.x == 0) st_agent(cnt + rg, 0u);
+    }
+}
+
 template <typename U, int DEPTH>
-__global__ void __launch_bounds__(kSmThreads) small_m_kernel(SmArgs a)
+__global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_kernel(SmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using TT = TileTraits<U>;
+    using Sb = std::conditional_t<is_q4<U>(), Q4Sb, Q6Sb>;
     constexpr bool Q4 = is_q4<U>();
-    constexpr int BLK = Q4 ? kQ4Bytes : kQ6Bytes;
+    constexpr int BLK = TT::kBlk;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kb = lane >> 4, r = lane & 15, m0 = 4 * kb;
     const int g = blockIdx.x, nb = a.nb, M = a.m;
     const int t0 = first_tile(g, a.T, a.G), t1 = first_tile(g + 1, a.T, a.G);
     const int64_t row_bytes = (int64_t)nb * BLK;
     const int ma = min(r, M - 1);  // activation row this lane feeds into A
+    uint8_t *xs = smem + a.xs_off;  // staged activations and their tables
+    uint8_t *tile = smem + wave * TT::kTileLds;  // this wave's weight tile
     const int lo_off = M * a.RS;
-    const int *etab = reinterpret_cast<const int *>(smem + 2 * M * a.RS);
+    const int *etab = reinterpret_cast<const int *>(xs + 2 * M * a.RS);
     const float *stab = reinterpret_cast<const float *>(etab + 16 * a.CH);
     int &last_flag = *reinterpret_cast<int *>(smem + a.flag_off);
+    uint32_t vmask;  // kept in a VGPR for v_and_or_b32
+    asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(Q4 ? 0x000F000Fu : 0x00FF00FFu));
 
-    auto tile_ptr = [&](int t) {
-        const int rg = t / nb, b = t - rg * nb;
-        const int row = min(rg * kSmRows + 16 * wave + r, a.n_rows - 1);
-        return a.W + row * row_bytes + (int64_t)b * BLK;
+    // next tile to load: row group rl, superblock bl
+    int rl = t0 / nb, bl = t0 - rl * nb;
+    TileAddr<U> ta;
+    tile_rows<U>(ta, rl, wave, lane, a.n_rows, row_bytes, kSmRows);
+    auto load_next = [&]() {
+        const U u = load_tile(a.W, ta, bl, lane);
+        if (++bl == nb) {
+            bl = 0;
+            tile_rows<U>(ta, ++rl, wave, lane, a.n_rows, row_bytes, kSmRows);
+        }
+        return u;
     };
 
     U ring[DEPTH];
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i)
-        if (t0 + i < t1) ring[i] = load_sb(tile_ptr(t0 + i), kb, (U *)nullptr);
+        if (t0 + i < t1) ring[i] = load_next();
 
-    int t = t0;
-    while (t < t1) {
-        const int rg = t / nb, bs = t - rg * nb;
-        const int be = min(nb, bs + (t1 - t));
-        f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int cb = bs; cb < be; cb += a.CH) {
-            const int n = min(a.CH, be - cb);
-            __syncthreads();  // the previous chunk's LDS reads are done
-            stage_chunk<Q4>(a, cb, n, smem);
-            __syncthreads();
-            for (int bb = 0; bb < n; ++bb, ++t) {
-                const U cur = ring[0];
+    // tile being computed: row group rg, superblock b; `left` tiles remain in
+    // the staged chunk that starts at superblock cb
+    int t = t0, rg = t0 / nb, b = t0 - rg * nb, left = 0, cb = b;
+    // byte offset in W of this lane's own row (for the Q6_K alignment shift)
+    int64_t own_row = (int64_t)min(rg * kSmRows + 16 * wave + r, a.n_rows - 1) * row_bytes;
+    f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool more = t0 < t1;
+    // Contributors of the first and last row group this workgroup touches;
+    // every row group in between lies wholly inside [t0, t1).
+    const int rg_first = t0 / nb, rg_last = (t1 - 1) / nb;
+    const int gl_first = owner(rg_first * nb, a.T, a.G);
+    const int gh_first = owner(rg_first * nb + nb - 1, a.T, a.G);
+    const int gl_last = owner(rg_last * nb, a.T, a.G);
+    const int gh_last = owner(rg_last * nb + nb - 1, a.T, a.G);
+    while (more) {
 #pragma unroll
-                for (int i = 0; i + 1 < DEPTH; ++i) ring[i] = ring[i + 1];
-                if (t + DEPTH < t1) ring[DEPTH - 1] = load_sb(tile_ptr(t + DEPTH), kb, (U *)nullptr);
-                const uint8_t *ah = smem + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
-                f32x4 ys;
-                if constexpr (Q4)
-                    ys = sb_mma(cur, ah, lo_off, stab + 128 * bb + m0);
-                else
-                    ys = sb_mma(cur, ah, lo_off, nullptr,
-                                (int)((uintptr_t)tile_ptr(t) & 3u));
-                const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) yacc[i] += ldexpf(ys[i], ex[i]);
+        for (int j = 0; j < DEPTH; ++j) {
+            if (left == 0) {
+                cb = b;
+                left = min(a.CH, min(nb - b, t1 - t));
+                __syncthreads();  // the previous chunk's LDS reads are done
+                stage_chunk<Q4>(a, cb, left, xs);
+                __syncthreads();
             }
-        }
-
-        // ---- this workgroup's share of row group rg is complete
-        const int gl = owner(rg * nb, a.T, a.G), gh = owner(rg * nb + nb - 1, a.T, a.G);
-        const int row0 = rg * kSmRows;
-        if (gl == gh) {
-            const int row = row0 + 16 * wave + r;
-            if (row < a.n_rows) {
+            const U cur = ring[j];
+            if (t + DEPTH < t1) ring[j] = load_next();
+            // The tile slot is private to this wave and LDS executes a wave's
+            // accesses in order, so the previous tile's reads are done and
+            // this tile's writes are visible to the reads below.
+            __builtin_amdgcn_wave_barrier();
+            store_tile(cur, tile, lane);
+            __builtin_amdgcn_wave_barrier();
+            const int sh = (int)((own_row + (int64_t)b * BLK) & 3);
+            const Sb sb = read_sb(tile + TT::kRowLds * r, kb, sh, (Sb *)nullptr);
+            const int bb = b - cb;
+            const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
+            const f32x4 ys = sb_mma(sb, ah, lo_off, stab + 128 * bb + m0, vmask);
+            const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (m0 + i < M) a.Y[(int64_t)(m0 + i) * a.ldy + row] = yacc[i];
-            }
-            continue;
-        }
-        float *part = reinterpret_cast<float *>(a.ws + a.part_off);
-        uint32_t *cnt = reinterpret_cast<uint32_t *>(a.ws);
-        const int slot = (first_tile(g, a.T, a.G) / nb == rg) ? 0 : 1;
-        float *pp = part + (int64_t)(2 * g + slot) * (16 * kSmRows);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_agent(pp + (m0 + i) * kSmRows + 16 * wave + r, yacc[i]);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's stores have completed
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(cnt + rg, 1u, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-            last_flag = (old + 1 == (uint32_t)(gh - gl + 1));
-        }
-        __syncthreads();
-        if (last_flag) {
-            // sum the contributors' partial tiles in workgroup order
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc(a.ws, (short)0, a.ws_bytes, 0x00020000);
-            for (int e = threadIdx.x; e < M * (kSmRows / 4); e += kSmThreads) {
-                const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
-                f32x4 s;
-                for (int c = gl; c <= gh; ++c) {
-                    const int sl = (first_tile(c, a.T, a.G) / nb == rg) ? 0 : 1;
-                    const uint32_t off = (uint32_t)a.part_off +
-                                         4u * (uint32_t)((2 * c + sl) * (16 * kSmRows) +
-                                                         m * kSmRows + 4 * q);
-                    const f32x4 v = __builtin_bit_cast(
-                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16 /* sc1 */));
-                    s = (c == gl) ? v : s + v;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = row0 + 4 * q + i;
-                    if (row < a.n_rows) a.Y[(int64_t)m * a.ldy + row] = s[i];
+            for (int i = 0; i < 4; ++i) yacc[i] += ldexpf(ys[i], ex[i]);
+            ++t;
+            ++b;
+            --left;
+            if (b == nb || t == t1) {
+                const int gl = rg == rg_first ? gl_first : (rg == rg_last ? gl_last : g);
+                const int gh = rg == rg_first ? gh_first : (rg == rg_last ? gh_last : g);
+                finish_segment(a, rg, gl, gh, g, yacc, wave, r, m0, last_flag);
+                yacc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                if (b == nb) {
+                    b = 0;
+                    ++rg;
+                    own_row = (int64_t)min(rg * kSmRows + 16 * wave + r, a.n_rows - 1) * row_bytes;
                 }
             }
-            if (threadIdx.x == 0) st_agent(cnt + rg, 0u);
+            if (t == t1) {
+                more = false;
+                break;
+            }
         }
     }
 }
 
 struct SmPlan {
-    int nb, T, G, CH, RS, part_off, flag_off;
+    int nb, T, G, CH, RS, part_off, flag_off, xs_off;
     size_t lds, ws;
 };
 
@@ -448,16 +673,17 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
-    p.G = p.T < sm_cus() ? p.T : sm_cus();
+    p.G = p.T < KQ_SM_OCC * sm_cus() ? p.T : KQ_SM_OCC * sm_cus();
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 512 : 0);  // LDS bytes per staged superblock
-    int ch = (kSmLdsMax - 16 - 32 * m) / per_sb;
+    p.xs_off = kSmWaves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
+    int ch = (kSmLdsBudget - p.xs_off - 16 - 32 * m) / per_sb;
     const int seg = (p.T + p.G - 1) / p.G;  // longest range of a workgroup
     if (ch > seg) ch = seg;
     if (ch > p.nb) ch = p.nb;
     if (ch < 1) ch = 1;
     p.CH = ch;
     p.RS = 512 * ch + 16;
-    p.flag_off = 2 * m * p.RS + 64 * ch + (qtype == 1 ? 512 * ch : 0);
+    p.flag_off = p.xs_off + 2 * m * p.RS + 64 * ch + (qtype == 1 ? 512 * ch : 0);
     p.lds = (size_t)p.flag_off + 16;
     // workspace: one counter per row group, then two partial tiles per workgroup
     p.part_off = ((rgs * 4 + 255) / 256) * 256;
@@ -513,13 +739,14 @@ hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int6
     a.part_off = p.part_off;
     a.ws_bytes = (int)p.ws;
     a.flag_off = p.flag_off;
+    a.xs_off = p.xs_off;
     hipError_t e;
     if (qtype == 1) {
-        constexpr auto K = small_m_kernel<Q4Sb, 4>;
+        constexpr auto K = small_m_kernel<Q4Tile, KQ_SM_Q4_DEPTH>;
         if ((e = allow_lds<K>()) != hipSuccess) return e;
         hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);
     } else {
-        constexpr auto K = small_m_kernel<Q6Sb, 3>;
+        constexpr auto K = small_m_kernel<Q6Tile, KQ_SM_Q6_DEPTH>;
         if ((e = allow_lds<K>()) != hipSuccess) return e;
         hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);
     }
