@@ -43,6 +43,14 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
 kq_status kq_tune_set_chain_lanes(int lanes);
 
 /*
+ * Matvec implementation for qtype, process-wide: 0 = register-ring kernels
+ * (each lane group streams its own rows), 1 = in-order LDS stream (each
+ * workgroup reads its contiguous run of superblocks in address order through
+ * an LDS ring; Q4_K only).  Errors: KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED.
+ */
+kq_status kq_tune_set_matvec_impl(int qtype, int impl);
+
+/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of 256 threads and
  * writes grid*4 xor-folded words to the device buffer `out` (so the loads

@@ -78,7 +78,8 @@ def lib() -> C.CDLL:
     L.kq_ffn_chain_workspace_bytes.restype = _i64
     L.kq_ffn_chain_error.argtypes = [_vp, C.POINTER(C.c_int)]
     L.kq_tune_set_chain_lanes.argtypes = [C.c_int]
-    for fn in ("kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes",
+    L.kq_tune_set_matvec_impl.argtypes = [C.c_int, C.c_int]
+    for fn in ("kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
                "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
@@ -195,3 +196,7 @@ def kq_ffn_chain_error(workspace) -> int:
 
 def kq_tune_set_chain_lanes(lanes: int) -> None:
     _check(lib().kq_tune_set_chain_lanes(int(lanes)), "kq_tune_set_chain_lanes")
+
+
+def kq_tune_set_matvec_impl(qtype: int, impl: int) -> None:
+    _check(lib().kq_tune_set_matvec_impl(int(qtype), int(impl)), "kq_tune_set_matvec_impl")

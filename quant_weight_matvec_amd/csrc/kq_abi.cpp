@@ -283,6 +283,14 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
     return KQ_OK;
 }
 
+kq_status kq_tune_set_matvec_impl(int qtype, int impl)
+{
+    if ((qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) || impl < 0 || impl > 1) return KQ_ERR_SHAPE;
+    if (impl == 1 && qtype != KQ_QTYPE_Q4K) return KQ_ERR_UNSUPPORTED;
+    kqi::set_matvec_impl(qtype, impl);
+    return KQ_OK;
+}
+
 kq_status kq_tune_set_chain_lanes(int lanes)
 {
     if (lanes != 2 && lanes != 4 && lanes != 8) return KQ_ERR_SHAPE;

@@ -160,13 +160,8 @@ __device__ __forceinline__ void encode_group_global(f32x4 v, int i, uint32_t *en
     constexpr int TPG = GROUP / 4;
     constexpr int QB = limb_bits<KQ_LIMBS>();
     const int n4 = ffn >> 2;
-    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    float sm = (v.x + v.y) + (v.z + v.w);
-#pragma unroll
-    for (int o = 1; o < TPG; o <<= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-        sm = sm + __shfl_xor(sm, o);
-    }
+    const float mx = group_max<TPG>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float sm = group_sum<TPG>((v.x + v.y) + (v.z + v.w));
     const int e = __builtin_amdgcn_frexp_expf(mx);
     const int sh = QB - e;
     int q[4];

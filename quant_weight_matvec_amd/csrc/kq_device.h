@@ -41,6 +41,45 @@ __device__ __forceinline__ constexpr int limb_bits()
 }
 
 // ---------------------------------------------------------------------------
+// Reductions over aligned groups of 2, 4 or 8 consecutive lanes with DPP moves
+// (VALU operations; no LDS round trip).  Steps: swap neighbours, swap pairs
+// within a quad, then mirror within the 8-lane half row.  After step s every
+// lane holds the reduction over its aligned 2^s-lane group, the same value in
+// all of them (each step combines two group values that are uniform within
+// their groups, and max and + are commutative).  Every lane of a group must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+
+template <int N>
+__device__ __forceinline__ float group_max(float v)
+{
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+    if constexpr (N >= 2) v = fmaxf(v, dpp_mov<kDppXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_mov<kDppXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+    if constexpr (N >= 2) v = v + dpp_mov<kDppXor1>(v);
+    if constexpr (N >= 4) v = v + dpp_mov<kDppXor2>(v);
+    if constexpr (N >= 8) v = v + dpp_mov<kDppHalfMirror>(v);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
 // Activation staging into LDS.
 // Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
 // then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
@@ -50,13 +89,8 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
 {
     constexpr int TPG = GROUP / 4;  // threads per group, one float4 each
     constexpr int QB = limb_bits<LIMBS>();
-    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    float sm = (v.x + v.y) + (v.z + v.w);
-#pragma unroll
-    for (int o = 1; o < TPG; o <<= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-        sm = sm + __shfl_xor(sm, o);
-    }
+    const float mx = group_max<TPG>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float sm = group_sum<TPG>((v.x + v.y) + (v.z + v.w));
     const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
     const int sh = QB - e;
     int q[4];
@@ -133,12 +167,18 @@ __device__ __forceinline__ float combine_limbs(const int *acc)
         return (float)(acc[0] * 256 + acc[1]);
 }
 
+// Sum over the LANES lanes that share a row (aligned groups): DPP for up to 8
+// lanes, cross-lane shuffles for the wider steps.
 template <int LANES>
 __device__ __forceinline__ float lane_group_sum(float v)
 {
+    if constexpr (LANES <= 8) {
+        return group_sum<LANES>(v);
+    } else {
 #pragma unroll
-    for (int o = LANES / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+        for (int o = LANES / 2; o >= 8; o >>= 1) v += __shfl_xor(v, o);
+        return group_sum<8>(v);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -277,22 +317,18 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
                                              const float *__restrict__ tsum)
 {
     const int sh = u.shift;
-    uint32_t ql[17], qh[9];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) ql[4 * i + w] = u.ql[i][w];
-    ql[16] = u.ql_x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) qh[4 * i + w] = u.qh[i][w];
-    qh[8] = u.qh_x;
-    uint32_t L[16], H[8];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) L[i] = realign(ql[i + 1], ql[i], sh);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) H[i] = realign(qh[i + 1], qh[i], sh);
+    // ql word i (i = 0..15) and qh word i (i = 0..7) of the unit, re-aligned
+    // on use so that only the words of one half are live at a time
+    auto qlw = [&](int i) -> uint32_t {
+        const uint32_t lo = u.ql[i >> 2][i & 3];
+        const uint32_t hi = i == 15 ? u.ql_x : u.ql[(i + 1) >> 2][(i + 1) & 3];
+        return realign(hi, lo, sh);
+    };
+    auto qhw = [&](int i) -> uint32_t {
+        const uint32_t lo = u.qh[i >> 2][i & 3];
+        const uint32_t hi = i == 7 ? u.qh_x : u.qh[(i + 1) >> 2][(i + 1) & 3];
+        return realign(hi, lo, sh);
+    };
     const uint32_t sc0 = realign(u.sc[1], u.sc[0], sh);
     const uint32_t sc1 = realign(u.sc[2], u.sc[1], sh);
     const float d = half_lo(u.d);
@@ -314,7 +350,7 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
         uint32_t q[4][4];  // [g][t]: quants of inputs base + 32g + 16jj + 4t .. +3
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t l0 = L[4 * jj + t], l1 = L[8 + 4 * jj + t], hh = H[4 * jj + t];
+            const uint32_t l0 = qlw(4 * jj + t), l1 = qlw(8 + 4 * jj + t), hh = qhw(4 * jj + t);
             q[0][t] = (l0 & 0x0F0F0F0Fu) | ((hh & 0x03030303u) << 4);
             q[1][t] = (l1 & 0x0F0F0F0Fu) | ((hh & 0x0C0C0C0Cu) << 2);
             q[2][t] = ((l0 >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
@@ -345,10 +381,33 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
 }
 
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(lds_void *)p;
+}
+
+// One direct-to-LDS 16-byte load per lane: lane i's 16 bytes from `src` land
+// at LDS byte lds + 16 i.  Written as inline assembly on purpose: the compiler
+// then does not track these loads as LDS writes, so it does not drain every
+// load in flight at each workgroup barrier; the kernel waits for exactly the
+// chunk it needs (s_waitcnt vmcnt) before the barrier that publishes it.  The
+// compiler's own counter waits can only become more conservative.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory");
+}
+
 __device__ __forceinline__ float block_sum_fixed(float v, float *red)
 {
+    v = group_sum<8>(v);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = 32; o >= 8; o >>= 1) v += __shfl_xor(v, o);
     const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     __syncthreads();  // `red` may still be read from the previous reduction
     if ((threadIdx.x & 63) == 0) red[wave] = v;

@@ -28,6 +28,15 @@ hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_r
                              const float *silu_gate, hipStream_t stream);
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              hipStream_t stream);
+// In-order LDS-streaming matvec (kq_stream.hip).  matvec_impl(qtype): 0 =
+// register-ring kernels of kq_kernels.hip, 1 = LDS stream (Q4_K).
+int matvec_impl(int qtype);
+void set_matvec_impl(int qtype, int impl);
+size_t q4k_stream_lds(int n_rows, int k, int grid, int nbuf, int *rows_per_wg, int *x_bytes,
+                      int *part_off, int *ring_off);
+hipError_t launch_matvec_q4k_stream(const uint8_t *W, const float *x, float *y, int n_rows, int k,
+                                    const float *silu_gate, int grid, int nbuf, hipStream_t stream);
+
 // Batched small-m kernel (kq_small_m.hip), m = 2..16.
 size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,

@@ -506,6 +506,13 @@ MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              const float *silu_gate, hipStream_t stream)
 {
+    if (matvec_impl(1) == 1) {
+        const int grid = device_cus();
+        for (int nbuf = 7; nbuf >= 2; --nbuf)
+            if (q4k_stream_lds(n_rows, k, grid, nbuf, nullptr, nullptr, nullptr, nullptr) <=
+                160 * 1024)
+                return launch_matvec_q4k_stream(W, x, y, n_rows, k, silu_gate, grid, nbuf, stream);
+    }
     return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k), W, x, y, n_rows, k, silu_gate,
                                     stream);
 }

@@ -452,8 +452,9 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
             if (gi >= ngroups) break;  // wave-uniform
             const int m = gi / n, bb = gi - m * n;
             float mx = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+            mx = group_max<8>(mx);
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            for (int o = 8; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
             const bool fin = mx <= FLT_MAX;  // false for Inf and NaN
             const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
             const int sh = 15 - e;
@@ -479,9 +480,7 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
             *reinterpret_cast<u32x2 *>(lo + boff) = pl;
             if (lane == 0) etab[16 * bb + m] = e - 15;
             if constexpr (Q4) {
-                float sm = (s.x + s.y) + (s.z + s.w);
-#pragma unroll
-                for (int o = 1; o < 8; o <<= 1) sm += __shfl_xor(sm, o);
+                const float sm = group_sum<8>((s.x + s.y) + (s.z + s.w));
                 if ((lane & 7) == 0) stab[128 * bb + 16 * (lane >> 3) + m] = fin ? sm : __builtin_nanf("");
             }
         }
