@@ -111,10 +111,10 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
                         void *stream);
 
 /*
- * Small-M matmul for the speculative-verify batch (Ch 36 "Speculative
- * decoding", section 36.4: the verify pass multiplies each weight row by T
- * positions at once; Ch 19, section 19.4 times it at M = 16): for m < M and
- * r < n_rows,
+ * Small-M matmul for the verify batch (Ch 36 "Prefill vs decode: the two
+ * graphs", section 36.4 "Projections: from matvec to GEMM": each weight row is
+ * read once and used for every input column; Ch 19 "The down projection +
+ * residual", section 19.7, times M = 16): for m < M and r < n_rows,
  *   Y[m * ldy + r] = sum_i w[r,i] * X[m * ldx + i].
  * Each weight is read from memory once and applied to all M rows.  M = 1 runs
  * the matvec of that qtype (identical results); M >= 2 runs the matrix-core

@@ -1,7 +1,8 @@
 // kq_small_m.hip -- Y[m] = W X[m] for up to 16 activation rows over Q4_K /
-// Q6_K weights (the pages' verify / small-batch case: Ch 36 "Speculative
-// decoding", section 36.4, where one read of each weight row serves every
-// verified position; the M = 16 timings of Ch 19, section 19.4).
+// Q6_K weights: the pages' matvec-to-GEMM step (Ch 36 "Prefill vs decode: the
+// two graphs", section 36.4 "Projections: from matvec to GEMM": one read of a
+// weight row serves every input column), at the verify batch sizes whose M = 16
+// timings Ch 19 "The down projection + residual" gives in section 19.7.
 //
 // Design for gfx950 (the pages' kernels use scalar f32 MACs on another GPU):
 //

@@ -1,9 +1,10 @@
 // kq_stream.hip -- the M = 1 matvec as an in-order byte stream through LDS.
 //
 // A workgroup owns a contiguous range of weight rows, i.e. one contiguous run
-// of superblocks in memory (rows are stored back to back, Appendix A of the
-// pages' k-quant description; Ch 19 "The down projection + residual", section
-// 19.1, for the decode matvec itself).  It reads that run in address order,
+// of superblocks in memory (each row is its k/256 superblocks back to back and
+// rows follow one another; Ch 19 "The down projection + residual", section
+// 19.3, gives the 78 superblocks per 19,968-wide row, and section 19.1 the
+// decode matvec itself).  It reads that run in address order,
 // chunk after chunk, with direct-to-LDS 16-byte loads (global_load_lds_dwordx4:
 // no registers held while in flight), keeping NBUF chunks in flight.  Every
 // DRAM page is thus read whole while it is open, and the number of bytes in
