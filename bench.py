@@ -53,6 +53,8 @@ BYTES = {
     # tail: read projected, read+write residual, write next_in, read two gains
     "tail": 4 * HIDDEN * 6,
 }
+# gate and up in one launch: both matrices, x in, mid out
+GATE_UP_BYTES = 2 * q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN
 PASS_BYTES = LAYERS * sum(BYTES.values()) + BYTES["tail"]  # + the entry norm
 WEIGHT_BYTES_PASS = LAYERS * (2 * q4k_bytes(FFN, HIDDEN) + q6k_bytes(HIDDEN, FFN))
 KERNEL_SYMBOL = {
@@ -61,6 +63,7 @@ KERNEL_SYMBOL = {
     "up_silu": "q4k_matvec_kernel<..., true>",
     "down": "q6k_matvec_kernel",
     "tail": "tail_reg_kernel",
+    "gate_up": "q4k_gate_up_kernel",
 }
 
 
@@ -68,11 +71,15 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the chain kernel's machine code is built from; the
-    committed counter summary is used only while it matches."""
+CHAIN_SOURCES = ("kq_chain.hip", "kq_device.h")
+GATE_UP_SOURCES = ("kq_kernels.hip", "kq_device.h")
+
+
+def kernel_source_hash(files=CHAIN_SOURCES) -> str:
+    """Hash of the sources a kernel's machine code is built from; a committed
+    counter summary is used only while it matches."""
     h = hashlib.sha256()
-    for f in ("kq_chain.hip", "kq_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "quant_weight_matvec_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -147,10 +154,21 @@ class FFNChain:
                                                        self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
         )
 
-    def run_pass(self):
+    def calls_fused(self, l):
+        """The layer as three launches: gate+up+SiLU, down, tail."""
+        kq = self.kq
+        x, xn = self.x[l % 2], self.x[(l + 1) % 2]
+        return (
+            ("gate_up", lambda: kq.kq_ffn_gate_up_q4k(self.Wg[l], self.Wu[l], x, self.mid, FFN, HIDDEN)),
+            ("down", lambda: kq.kq_matvec_q6k(self.Wd[l], self.mid, self.p, HIDDEN, FFN)),
+            ("tail", lambda: kq.kq_fused_residual_norm(self.residual, self.p, xn, self.gp[l],
+                                                       self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
+        )
+
+    def run_pass(self, fused=False):
         self.entry_norm()
         for l in range(self.layers):
-            for _, fn in self.calls(l):
+            for _, fn in (self.calls_fused(l) if fused else self.calls(l)):
                 fn()
 
     def per_kernel_us(self, reps):
@@ -159,15 +177,18 @@ class FFNChain:
         replayed reps times; time / (reps * layers)."""
         torch = self.torch
         out = {}
-        for i, name in enumerate(("gate", "up_silu", "down", "tail")):
+        for name in ("gate", "up_silu", "down", "tail", "gate_up"):
+            pick = (lambda l: self.calls_fused(l)[0][1]) if name == "gate_up" else \
+                (lambda l, i=("gate", "up_silu", "down", "tail").index(name): self.calls(l)[i][1])
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 for l in range(self.layers):
-                    self.calls(l)[i][1]()
+                    pick(l)()
             torch.cuda.synchronize()
-            g.replay()
+            for _ in range(3):  # steady clocks before timing
+                g.replay()
             ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             ea.record()
@@ -283,7 +304,8 @@ def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
                 for c in copies:
                     call(c)
             torch.cuda.synchronize()
-            g.replay()
+            for _ in range(3):  # steady clocks before timing
+                g.replay()
             ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             ea.record()
@@ -368,7 +390,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kq.lib()
     log(kq.kq_build_info())
-    src_hash = kernel_source_hash()
+    src_hash = {"gate_up": kernel_source_hash(GATE_UP_SOURCES), "chain": kernel_source_hash(CHAIN_SOURCES)}
 
     if args.calibration_copy:
         # a plain copy kernel of known size: 1 GiB read, 1 GiB written
@@ -399,69 +421,90 @@ def main():
         torch.cuda.synchronize()
         return ea.elapsed_time(eb) / steps, time.perf_counter() - t0
 
-    # ---- per-op path: 4 launches per layer, captured once as a graph
-    for _ in range(max(1, args.warmup)):
-        chain.run_pass()
-    torch.cuda.synchronize()
-    graph = None
-    if not args.eager:
+    def capture(fn):
+        """fn's launches captured once as a graph (None with --eager)."""
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        if args.eager:
+            return None
         s = torch.cuda.Stream()
         s.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=s):
-            chain.run_pass()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
         torch.cuda.synchronize()
         for _ in range(args.warmup):
-            graph.replay()
-    per_op_ms, _ = timed((lambda: graph.replay()) if graph is not None else chain.run_pass,
-                         args.steps)
-    per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph is not None else {}
-    ev = EventLog(torch)
+            g.replay()
+        return g
 
-    # ---- the hot path as timed: the persistent chain (one launch per token)
+    # ---- the step as timed: one graph replay of the whole pass, the entry norm
+    # then per layer gate+up+SiLU (one launch), down, tail
+    fused_pass = lambda: chain.run_pass(fused=True)
+    graph_f = capture(fused_pass)
+    log(f"timing {args.steps} steps (graph: 3 launches per layer)")
+    ms_per_step, wall = timed((lambda: graph_f.replay()) if graph_f is not None else fused_pass,
+                              args.steps)
+    value = pass_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- the same pass two other ways, reported beside it
+    graph4 = capture(chain.run_pass)
+    per_op4_ms, _ = timed((lambda: graph4.replay()) if graph4 is not None else chain.run_pass,
+                          args.steps)
     for _ in range(max(1, args.warmup)):
         chain.run_chain()
     torch.cuda.synchronize()
     assert kq.kq_ffn_chain_error(chain.ws) == 0, "chain kernel reported an error"
-    log(f"timing {args.steps} steps (persistent chain)")
-    ms_per_step, wall = timed(chain.run_chain, args.steps)
+    chain_ms, _ = timed(chain.run_chain, args.steps)
     assert kq.kq_ffn_chain_error(chain.ws) == 0, "chain kernel reported an error"
-    value = pass_bytes / (ms_per_step * 1e-3) / 1e9
+    ev = EventLog(torch)
     for _ in range(max(2, min(args.steps, 5))):
         chain.run_chain(ev)
 
+    per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph_f is not None else {}
     per = ev.summary()
     kernels = {}
-    for name, us in per.items():  # the chain: events around each launch
+    for name, avg in per_kernel.items():  # per-op kernels: graph of one launch per layer
+        nb = GATE_UP_BYTES if name == "gate_up" else BYTES[name]
+        gbps = nb / (avg * 1e-6) / 1e9
+        kernels[name] = {"symbol": KERNEL_SYMBOL[name], "us_avg": round(avg, 3),
+                         "bytes_per_launch": nb, "GBps": round(gbps, 1),
+                         "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                         "timing": f"graph of {layers} back-to-back launches (one per layer), "
+                                   "HIP events on the replay stream"}
+    for name, us in per.items():  # the persistent chain: events around each launch
         avg = float(np.mean(us))
         gbps = bytes_chain_launch / (avg * 1e-6) / 1e9
         kernels[name] = {"symbol": KERNEL_SYMBOL[name], "launches": int(us.size), "us_avg": round(avg, 3),
                          "us_median": round(float(np.median(us)), 3), "bytes_per_launch": bytes_chain_launch,
                          "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                          "timing": "HIP events around each launch"}
-    for name, avg in per_kernel.items():  # per-op kernels: graph of one launch per layer
-        gbps = BYTES[name] / (avg * 1e-6) / 1e9
-        kernels[name] = {"symbol": KERNEL_SYMBOL[name], "us_avg": round(avg, 3),
-                         "bytes_per_launch": BYTES[name], "GBps": round(gbps, 1),
-                         "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                         "timing": f"graph of {layers} back-to-back launches (one per layer)"}
-    dk = kernels["chain"]
-    traffic = load_pmc("chain", src_hash)
-    roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": dk["frac_peak"], "traffic": traffic,
-                "bytes_per_launch": dk["bytes_per_launch"], "us_avg": dk["us_avg"]}
-    per_op = {"ms_per_step": round(per_op_ms, 4),
-              "GBps": round(pass_bytes / (per_op_ms * 1e-3) / 1e9, 1),
-              "timing": "graph replay" if graph is not None else "eager",
-              "launches_per_step": 4 * layers + 1}
+    # the dominant kernel of the timed step: gate+up+SiLU (150 MB of its ~260 MB per layer)
+    dk = kernels.get("gate_up")
+    roofline = None
+    if dk is not None:
+        roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"],
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dk["frac_peak"],
+                    "traffic": load_pmc("gate_up", kernel_source_hash(GATE_UP_SOURCES)),
+                    "bytes_per_launch": dk["bytes_per_launch"], "us_avg": dk["us_avg"]}
+    alternatives = {
+        "graph_4_launches_per_layer": {"ms_per_step": round(per_op4_ms, 4),
+                                       "GBps": round(pass_bytes / (per_op4_ms * 1e-3) / 1e9, 1),
+                                       "launches_per_step": 4 * layers + 1},
+        "persistent_chain": {"ms_per_step": round(chain_ms, 4),
+                             "GBps": round(pass_bytes / (chain_ms * 1e-3) / 1e9, 1),
+                             "launches_per_step": 2,
+                             "traffic_per_launch": load_pmc("chain", kernel_source_hash(CHAIN_SOURCES))},
+    }
 
     extras = {}
     if not args.no_extras:
         log("read-stream ceiling probe")
         ceil = read_ceiling(torch, kq)
         extras["read_ceiling_GBps"] = round(ceil, 1)
-        roofline["frac_of_read_ceiling"] = round(dk["GBps"] / ceil, 4)
-        del chain, graph  # free 13.4 GB before the isolated runs
+        if roofline is not None:
+            roofline["frac_of_read_ceiling"] = round(dk["GBps"] / ceil, 4)
+        del chain, graph_f, graph4  # free 13.4 GB before the isolated runs
         torch.cuda.empty_cache()
         log("isolated matvecs with weight rotation")
         extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
@@ -484,8 +527,9 @@ def main():
                    "hidden": HIDDEN, "ffn": FFN, "layers": args.layers, "tokens_per_step": 1,
                    "weight_bytes_per_step": WEIGHT_BYTES_PASS * args.layers // LAYERS,
                    "algorithmic_bytes_per_step": pass_bytes,
-                   "timing": "entry norm + one kq_ffn_chain launch per step, back to back"},
-        "per_op_pass": per_op,
+                   "timing": "one graph replay per step: entry norm, then per layer "
+                             "kq_ffn_gate_up_q4k, kq_matvec_q6k, kq_fused_residual_norm"},
+        "alternatives": alternatives,
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "tokens_per_s": round(1e3 / ms_per_step, 2),
         "full_model_equiv_tokens_per_s": round(value * 1e9 / FULL_MODEL_TOKEN_BYTES, 2),

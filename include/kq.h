@@ -99,6 +99,18 @@ kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows,
                         const float *silu_gate, void *stream);
 
 /*
+ * FFN entry in one launch (Ch 10 "The forward pass at a glance", section 10.3:
+ * gate and up read the same normed input and meet in the SiLU product):
+ *   mid[r] = silu((W_gate x)[r]) * (W_up x)[r],  silu(z) = z / (1 + exp(-z)),
+ * for r < n_rows.  Both matrices are Q4_K with the layout and alignment of
+ * kq_matvec_q4k, n_rows x k each; x is read and staged once.
+ *   mid [n_rows] f32 output, 4-byte aligned; must not overlap W_gate, W_up or x.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_ffn_gate_up_q4k(const void *W_gate, const void *W_up, const float *x, float *mid,
+                             int64_t n_rows, int64_t k, void *stream);
+
+/*
  * Q6_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows.
  *   W   [n_rows * (k/256) * 210] bytes, 4-byte aligned (a 210-byte superblock
  *       keeps only 2-byte alignment, and rows keep 4-byte alignment).

@@ -58,6 +58,7 @@ def lib() -> C.CDLL:
     L = C.CDLL(LIB_PATH)
     L.kq_matvec_q4k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp]
     L.kq_matvec_q6k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
+    L.kq_ffn_gate_up_q4k.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
     L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp,
                                     _i64, _vp]
     L.kq_matmul_small_m_workspace_bytes.argtypes = [C.c_int, _i64, _i64, C.c_int]
@@ -80,7 +81,7 @@ def lib() -> C.CDLL:
     L.kq_tune_set_chain_lanes.argtypes = [C.c_int]
     L.kq_tune_set_matvec_impl.argtypes = [C.c_int, C.c_int]
     for fn in ("kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
-               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_matmul_small_m", "kq_fused_residual_norm",
+               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
     _lib = L
@@ -121,6 +122,12 @@ def kq_matvec_q4k(W, x, y, n_rows: int, k: int, silu_gate=None, stream=None) -> 
     rc = lib().kq_matvec_q4k(_ptr(W), _ptr(x), _ptr(y), int(n_rows), int(k), _ptr(silu_gate),
                              _stream(stream))
     _check(rc, "kq_matvec_q4k")
+
+
+def kq_ffn_gate_up_q4k(W_gate, W_up, x, mid, n_rows: int, k: int, stream=None) -> None:
+    rc = lib().kq_ffn_gate_up_q4k(_ptr(W_gate), _ptr(W_up), _ptr(x), _ptr(mid), int(n_rows),
+                                  int(k), _stream(stream))
+    _check(rc, "kq_ffn_gate_up_q4k")
 
 
 def kq_matvec_q6k(W, x, y, n_rows: int, k: int, stream=None) -> None:

@@ -73,6 +73,25 @@ kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows,
                                            silu_gate, (hipStream_t)stream));
 }
 
+kq_status kq_ffn_gate_up_q4k(const void *W_gate, const void *W_up, const float *x, float *mid,
+                             int64_t n_rows, int64_t k, void *stream)
+{
+    if (!W_gate || !W_up || !x || !mid) return KQ_ERR_NULL;
+    if (n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(x, 16) || !aligned(mid, 4))
+        return KQ_ERR_ALIGN;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    if (overlap(mid, n_rows * 4, W_gate, wbytes) || overlap(mid, n_rows * 4, W_up, wbytes) ||
+        overlap(mid, n_rows * 4, x, k * 4))
+        return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_gate_up_q4k((const uint8_t *)W_gate, (const uint8_t *)W_up, x, mid,
+                                            (int)n_rows, (int)k, (hipStream_t)stream));
+}
+
 kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
                         void *stream)
 {

@@ -26,6 +26,8 @@ MatvecShape get_shape_override(int qtype);
 // Each launcher assumes the arguments were validated by the ABI shim.
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              const float *silu_gate, hipStream_t stream);
+hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *mid,
+                              int n_rows, int k, hipStream_t stream);
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
                              hipStream_t stream);
 // In-order LDS-streaming matvec (kq_stream.hip).  matvec_impl(qtype): 0 =

@@ -78,6 +78,22 @@ def test_matvec_validation():
     assert _q6(n=0) == B.KQ_OK
 
 
+def test_gate_up_validation():
+    f = kq.lib().kq_ffn_gate_up_q4k
+    U, M = 0x500000, 0x300000
+    assert f(None, U, X, M, 8, 1024, None) == B.KQ_ERR_NULL
+    assert f(W, U, X, None, 8, 1024, None) == B.KQ_ERR_NULL
+    assert f(W, U, X, M, 8, 1000, None) == B.KQ_ERR_SHAPE
+    assert f(W, U, X, M, -1, 1024, None) == B.KQ_ERR_SHAPE
+    assert f(W, U, X, M, 8, B.KQ_MAX_K + 256, None) == B.KQ_ERR_UNSUPPORTED
+    assert f(W, U + 8, X, M, 8, 1024, None) == B.KQ_ERR_ALIGN   # Q4_K weights 16-byte aligned
+    assert f(W, U, X + 4, M, 8, 1024, None) == B.KQ_ERR_ALIGN
+    assert f(W, U, X, M + 2, 8, 1024, None) == B.KQ_ERR_ALIGN
+    assert f(W, U, X, U + 64, 8, 1024, None) == B.KQ_ERR_ALIAS  # mid inside W_up
+    assert f(W, U, X, X + 16, 8, 1024, None) == B.KQ_ERR_ALIAS  # mid inside x
+    assert f(W, U, X, M, 0, 1024, None) == B.KQ_OK
+
+
 def test_small_m_validation():
     f = kq.lib().kq_matmul_small_m
     WS = 0x600000

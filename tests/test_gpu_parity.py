@@ -274,3 +274,40 @@ def test_q4k_lds_stream_impl(n, k):
     gg = g.astype(np.float64)
     silu = gg / (1.0 + np.exp(-gg))
     assert np.allclose(ys, silu * y, rtol=1e-6, atol=1e-30), "SiLU epilogue"
+
+
+# ---------------------------------------------------------------- gate + up in one launch
+def _mid_bound(gr, Sg, ur, Su):
+    dg, du = 1e-3 * Sg, 1e-3 * Su
+    sil = np.abs(gr / (1 + np.exp(-gr)))
+    return 1.1 * dg * (np.abs(ur) + du) + sil * du
+
+
+@pytest.mark.parametrize("n,k", [(1, 256), (5, 512), (129, 768), (1000, 6656), (4100, 1024),
+                                 (19968, 6656), (6656, 19968)])
+def test_ffn_gate_up_one_launch(n, k):
+    """mid = silu(W_gate x) * (W_up x) from kq_ffn_gate_up_q4k against the
+    oracle's gate and up rows (sampled at the large shapes), within the bound
+    derived from the two matvec contracts; and equal to the two-launch path
+    within the same bound."""
+    Wg = weights("q4k", n, k, 9300 + n)
+    Wu = weights("q4k", n, k, 9400 + n)
+    x = I.normal_f32(k, stream=9500 + n)
+    Wgd, Wud, xd = dev(Wg), dev(Wu), dev(x)
+    mid = nan_like(n)
+    kq.kq_ffn_gate_up_q4k(Wgd, Wud, xd, mid, n, k)
+    g2, mid2 = nan_like(n), nan_like(n)
+    kq.kq_matvec_q4k(Wgd, xd, g2, n, k)
+    kq.kq_matvec_q4k(Wud, xd, mid2, n, k, g2)
+    torch.cuda.synchronize()
+    got = mid.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), "unwritten rows"
+    rows = sample_rows(n, 384, seed=n)
+    gr, Sg = oracle_rows("q4k", Wg, x, rows, k)
+    ur, Su = oracle_rows("q4k", Wu, x, rows, k)
+    bound = _mid_bound(gr, Sg, ur, Su)
+    err = np.abs(got[rows] - O.silu_mul(gr, ur))
+    print(f"worst |dmid|/bound {np.max(err / bound):.2e}")
+    assert np.all(err <= bound), "mid outside the derived bound"
+    two = mid2.cpu().numpy().astype(np.float64)[rows]
+    assert np.all(np.abs(got[rows] - two) <= 2 * bound), "one-launch and two-launch paths disagree"
