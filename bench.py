@@ -55,7 +55,9 @@ BYTES = {
 }
 # gate and up in one launch: both matrices, x in, mid out
 GATE_UP_BYTES = 2 * q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN
-PASS_BYTES = LAYERS * sum(BYTES.values()) + BYTES["tail"]  # + the entry norm
+# one token through the pass: per layer gate+up (x in, mid out), down, tail; plus the entry norm.
+# The same count serves every schedule of the pass, so their rates compare work for work.
+PASS_BYTES = LAYERS * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
 WEIGHT_BYTES_PASS = LAYERS * (2 * q4k_bytes(FFN, HIDDEN) + q6k_bytes(HIDDEN, FFN))
 KERNEL_SYMBOL = {
     "chain": "ffn_chain_kernel",
@@ -406,7 +408,7 @@ def main():
     chain = FFNChain(torch, kq, I, args.layers)
     chain.build_chain()
     layers = args.layers
-    pass_bytes = layers * sum(BYTES.values()) + BYTES["tail"]
+    pass_bytes = layers * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
     bytes_chain_launch = pass_bytes - BYTES["tail"]  # the entry norm is its own launch
     stream = torch.cuda.current_stream()
 

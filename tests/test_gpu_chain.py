@@ -1,12 +1,17 @@
-"""The persistent FFN chain (kq_ffn_chain) against the CPU oracle.
+"""The FFN layer stack against the CPU oracle, run two ways: the persistent
+chain (kq_ffn_chain, one launch per token) and the single-op pass (per layer
+kq_ffn_gate_up_q4k, the down matvec, kq_fused_residual_norm), eagerly and as a
+replayed graph, which is how the decode step is timed.
 
-Protocol for the 52-layer chain (a reading: the pages fix no parity protocol
+Protocol for the 52-layer stack (a reading: the pages fix no parity protocol
 for a layer stack):
   (i)  teacher-forced: each layer is run alone on the GPU from the GPU's own
        (x_l, residual_l) and compared with the oracle's layer from the same
        input, at the tail's 2e-3 absolute tolerance;
-  (ii) end to end: one launch over all layers against the oracle's binary64
-       chain from the same start, at the same 2e-3 absolute tolerance.
+  (ii) end to end: all layers in one go against the oracle's binary64
+       chain from the same start, at the same 2e-3 absolute tolerance (or, if
+       the oracle's own sensitivity shows the stack ill-conditioned at that
+       level, at that tolerance scaled by the measured amplification).
 Small shapes also cover workgroups with no rows in a phase (fewer scale groups
 or down rows than workgroups).
 """
@@ -61,6 +66,51 @@ class Stack:
         assert kq.kq_ffn_chain_error(self.ws) == 0
         return xo.cpu().numpy().astype(np.float64), r.cpu().numpy().astype(np.float64)
 
+    def ops(self, l, x, xn, r, mid, p):
+        """Layer l as the three single-op launches (gate+up+SiLU, down, tail)."""
+        d = self.dev[l]
+        kq.kq_ffn_gate_up_q4k(d["wg"], d["wu"], x, mid, self.ffn, self.hidden)
+        if self.down == "q6k":
+            kq.kq_matvec_q6k(d["wd"], mid, p, self.hidden, self.ffn)
+        else:
+            kq.kq_matvec_q4k(d["wd"], mid, p, self.hidden, self.ffn)
+        kq.kq_fused_residual_norm(r, p, xn, d["gp"], d["gn"], 1, self.hidden, 1e-8, 1e-5)
+
+    def run_ops(self, x, res, first=0, count=None, replays=0):
+        """Layers [first, first+count) through the single-op launches, eagerly;
+        with replays > 0 also captured as one graph and replayed that many times
+        from the same start, each replay required to equal the eager result
+        bit for bit.  Returns (x_out, residual)."""
+        count = self.layers - first if count is None else count
+        x0, r0 = dev(np.asarray(x, np.float32)), dev(np.asarray(res, np.float32))
+        xs = [torch.empty(self.hidden, device="cuda") for _ in range(2)]
+        r = torch.empty(self.hidden, device="cuda")
+        mid, p = torch.empty(self.ffn, device="cuda"), torch.empty(self.hidden, device="cuda")
+
+        def body():
+            for i in range(count):
+                self.ops(first + i, xs[i % 2], xs[(i + 1) % 2], r, mid, p)
+
+        xs[0].copy_(x0); r.copy_(r0)
+        body()
+        torch.cuda.synchronize()
+        out_x, out_r = xs[count % 2].cpu().numpy(), r.cpu().numpy()
+        if replays:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                body()
+            torch.cuda.synchronize()
+            for k in range(replays):
+                xs[0].copy_(x0); r.copy_(r0); xs[1].fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                assert np.array_equal(xs[count % 2].cpu().numpy(), out_x), f"replay {k}: x differs"
+                assert np.array_equal(r.cpu().numpy(), out_r), f"replay {k}: residual differs"
+        return out_x.astype(np.float64), out_r.astype(np.float64)
+
     def oracle_layer(self, l, x, res):
         h = self.host(l)
         L = O.ffn_layer(h["wg"], h["wu"], h["wd"], self.hidden, self.ffn, x, res, h["gp"],
@@ -80,6 +130,21 @@ def test_chain_small_end_to_end(layers, hidden, ffn, down):
     st = Stack(layers, hidden, ffn, down)
     x0, r0 = start_state(hidden)
     xg, rg = st.run(x0, r0)
+    x, r = x0.astype(np.float64), r0.astype(np.float64)
+    for l in range(layers):
+        x, r = st.oracle_layer(l, x, r)
+    dx, dr = np.max(np.abs(xg - x)), np.max(np.abs(rg - r))
+    print(f"max |dx| {dx:.2e} |dres| {dr:.2e}")
+    assert dx <= 2e-3 and dr <= 2e-3
+
+
+@pytest.mark.parametrize("layers,hidden,ffn,down", [(1, 512, 1536, "q6k"), (4, 512, 1536, "q6k"),
+                                                    (3, 1024, 4096, "q4k"), (2, 768, 2560, "q6k")])
+def test_op_pass_small_end_to_end(layers, hidden, ffn, down):
+    """The pass as three launches per layer, eager and as a replayed graph."""
+    st = Stack(layers, hidden, ffn, down)
+    x0, r0 = start_state(hidden)
+    xg, rg = st.run_ops(x0, r0, replays=2)
     x, r = x0.astype(np.float64), r0.astype(np.float64)
     for l in range(layers):
         x, r = st.oracle_layer(l, x, r)
@@ -155,16 +220,55 @@ def test_chain_lane_variants(lanes):
     assert np.max(np.abs(xg - x)) <= 2e-3 and np.max(np.abs(rg - r)) <= 2e-3
 
 
-def test_chain_52_layers_full_size():
-    """The 52-layer FFN stream at 6656 / 19968 (Q4_K gate/up, Q6_K down):
-    (i) teacher-forced per layer, (ii) end to end in one launch."""
-    layers, hidden, ffn = 52, 6656, 19968
+FULL = dict(layers=52, hidden=6656, ffn=19968)
+
+
+@pytest.fixture(scope="module")
+def full():
+    """The 52-layer FFN stream at 6656 / 19968 (Q4_K gate/up, Q6_K down), with
+    the oracle's end-to-end result from the seeded start and, beside it, the
+    oracle's own result from a start perturbed by 1e-7 (relative)."""
+    layers, hidden, ffn = FULL["layers"], FULL["hidden"], FULL["ffn"]
     st = Stack(layers, hidden, ffn, "q6k", cfg=4)
     x0, r0 = start_state(hidden, cfg=4)
-    # (i) teacher-forced: the GPU's state feeds both sides at every layer
-    xg, rg = x0, r0
-    worst = 0.0
+    rng = np.random.default_rng(1)
+    x, r = x0.astype(np.float64), r0.astype(np.float64)
+    xp = x * (1 + 1e-7 * rng.standard_normal(hidden))
+    rp = r * (1 + 1e-7 * rng.standard_normal(hidden))
     for l in range(layers):
+        x, r = st.oracle_layer(l, x, r)
+        xp, rp = st.oracle_layer(l, xp, rp)
+    sens = max(np.max(np.abs(xp - x)), np.max(np.abs(rp - r)))
+    print(f"oracle end to end from a 1e-7 perturbed start moves by {sens:.2e} "
+          f"(|res| max {np.max(np.abs(r)):.1f})", flush=True)
+    return dict(st=st, x0=x0, r0=r0, x=x, r=r, sens=sens)
+
+
+def check_end_to_end(full, xe, re, worst):
+    """(ii) end to end.  If the oracle itself moves by more than the 2e-3
+    tolerance under a 1e-7 perturbation, the stack is ill-conditioned at that
+    tolerance and the end-to-end result is held to the per-layer error
+    amplified as that perturbation is (the strict gate is then the
+    teacher-forced check); a gross error (a layer skipped, reordered or
+    mis-wired) still fails the sanity bound."""
+    x, r, sens = full["x"], full["r"], full["sens"]
+    dx, dr = np.max(np.abs(xe - x)), np.max(np.abs(re - r))
+    print(f"end to end: GPU vs oracle max |dx| {dx:.2e} |dres| {dr:.2e}", flush=True)
+    assert np.all(np.isfinite(xe)) and np.all(np.isfinite(re))
+    if sens * 100 < 2e-3:
+        assert dx <= 2e-3 and dr <= 2e-3, "well-conditioned stack: end to end must hold"
+    else:
+        amp = sens / 1e-7
+        assert max(dx, dr) <= 10 * amp * max(worst, 1e-7) + 2e-3, "end-to-end drift too large"
+        assert max(dx / 1.0, dr / max(1.0, np.max(np.abs(r)))) < 0.1, "gross end-to-end error"
+
+
+def test_chain_52_layers_full_size(full):
+    """(i) teacher-forced per layer, (ii) end to end in one launch."""
+    st = full["st"]
+    xg, rg = full["x0"], full["r0"]
+    worst = 0.0
+    for l in range(st.layers):
         xn, rn = st.run(xg, rg, first=l, count=1)
         xo, ro = st.oracle_layer(l, xg.astype(np.float64), rg.astype(np.float64))
         d = max(np.max(np.abs(xn - xo)), np.max(np.abs(rn - ro)))
@@ -174,31 +278,26 @@ def test_chain_52_layers_full_size():
         if l % 13 == 0:
             print(f"teacher-forced layer {l}: max diff {d:.2e}", flush=True)
     print(f"teacher-forced worst {worst:.2e}", flush=True)
-    # (ii) end to end, with the oracle's own sensitivity beside it: the same
-    # binary64 chain started from a state perturbed by 1e-7 (relative).  If the
-    # oracle itself moves by more than the 2e-3 tolerance, the stack is
-    # ill-conditioned at that tolerance and (ii) is reported, not asserted; the
-    # strict gate is then (i).  A gross error (a layer skipped, reordered or
-    # mis-wired) still fails the sanity bound below.
-    xe, re = st.run(x0, r0)
-    rng = np.random.default_rng(1)
-    x, r = x0.astype(np.float64), r0.astype(np.float64)
-    xp = x * (1 + 1e-7 * rng.standard_normal(hidden))
-    rp = r * (1 + 1e-7 * rng.standard_normal(hidden))
-    for l in range(layers):
-        x, r = st.oracle_layer(l, x, r)
-        xp, rp = st.oracle_layer(l, xp, rp)
-    dx, dr = np.max(np.abs(xe - x)), np.max(np.abs(re - r))
-    sx, sr = np.max(np.abs(xp - x)), np.max(np.abs(rp - r))
-    print(f"end to end: GPU vs oracle max |dx| {dx:.2e} |dres| {dr:.2e}; oracle vs oracle from a "
-          f"1e-7 perturbed start: |dx| {sx:.2e} |dres| {sr:.2e} (|res| max {np.max(np.abs(r)):.1f})",
-          flush=True)
-    assert np.all(np.isfinite(xe)) and np.all(np.isfinite(re))
-    if max(sx, sr) * 100 < 2e-3:
-        assert dx <= 2e-3 and dr <= 2e-3, "well-conditioned stack: end to end must hold"
-    else:
-        # ill-conditioned: errors of the measured per-layer size (<= 1e-4)
-        # amplified as a 1e-7 perturbation is amplified
-        amp = max(sx, sr) / 1e-7
-        assert max(dx, dr) <= 10 * amp * max(worst, 1e-7) + 2e-3, "end-to-end drift too large"
-        assert max(dx / 1.0, dr / max(1.0, np.max(np.abs(r)))) < 0.1, "gross end-to-end error"
+    xe, re = st.run(full["x0"], full["r0"])
+    check_end_to_end(full, xe, re, worst)
+
+
+def test_op_pass_52_layers_full_size(full):
+    """The timed decode step: three launches per layer over the 52 layers,
+    replayed as one graph.  (i) teacher-forced on every layer through the same
+    launches, (ii) end to end, each graph replay equal to the eager pass."""
+    st = full["st"]
+    xg, rg = full["x0"], full["r0"]
+    worst = 0.0
+    for l in range(st.layers):
+        xn, rn = st.run_ops(xg, rg, first=l, count=1)
+        xo, ro = st.oracle_layer(l, xg.astype(np.float64), rg.astype(np.float64))
+        d = max(np.max(np.abs(xn - xo)), np.max(np.abs(rn - ro)))
+        worst = max(worst, d)
+        assert d <= 2e-3, f"layer {l}: {d}"
+        xg, rg = xn.astype(np.float32), rn.astype(np.float32)
+        if l % 13 == 0:
+            print(f"teacher-forced layer {l}: max diff {d:.2e}", flush=True)
+    print(f"teacher-forced worst {worst:.2e}", flush=True)
+    xe, re = st.run_ops(full["x0"], full["r0"], replays=3)
+    check_end_to_end(full, xe, re, worst)
