@@ -93,29 +93,33 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
     const float sm = group_sum<TPG>((v.x + v.y) + (v.z + v.w));
     const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
     const int sh = QB - e;
-    int q[4];
-    q[0] = (int)rintf(ldexpf(v.x, sh));
-    q[1] = (int)rintf(ldexpf(v.y, sh));
-    q[2] = (int)rintf(ldexpf(v.z, sh));
-    q[3] = (int)rintf(ldexpf(v.w, sh));
+    // q = x * 2^sh rounded to nearest even, |q| <= 2^QB.  Adding 1.5 * 2^23
+    // rounds once and leaves q in the low mantissa bits of a float in
+    // [2^23, 2^24], so the float's bit pattern minus 0x4B400000 is q.  The
+    // same subtraction adds 0x80 to every limb byte: the bytes of
+    // u = q + 0x80...80 are the balanced base-256 digits of q (each in
+    // [-128, 127]) with their top bit flipped, carries included.
+    constexpr uint32_t kOff = LIMBS == 3 ? 0x808080u : 0x8080u;
+    constexpr uint32_t kBias = 0x4B400000u - kOff;
+    const float magic = 12582912.0f;  // 1.5 * 2^23
+    const uint32_t u0 = __builtin_bit_cast(uint32_t, ldexpf(v.x, sh) + magic) - kBias;
+    const uint32_t u1 = __builtin_bit_cast(uint32_t, ldexpf(v.y, sh) + magic) - kBias;
+    const uint32_t u2 = __builtin_bit_cast(uint32_t, ldexpf(v.z, sh) + magic) - kBias;
+    const uint32_t u3 = __builtin_bit_cast(uint32_t, ldexpf(v.w, sh) + magic) - kBias;
+    // byte transpose (v_perm_b32): plane word l holds limb l of the four
+    // inputs, input j in byte j; then flip the top bits back
+    const uint32_t lo01 = __builtin_amdgcn_perm(u1, u0, 0x05010400u);  // u0.b0 u1.b0 u0.b1 u1.b1
+    const uint32_t lo23 = __builtin_amdgcn_perm(u3, u2, 0x05010400u);
     uint32_t pk[LIMBS];
-#pragma unroll
-    for (int l = 0; l < LIMBS; ++l) pk[l] = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // balanced base-256 digits, each in [-128, 127]
-        const int c = (q[j] << 24) >> 24;
-        const int t = (q[j] - c) >> 8;
-        if constexpr (LIMBS == 3) {
-            const int b = (t << 24) >> 24;
-            const int a = (t - b) >> 8;
-            pk[0] |= (uint32_t)(a & 255) << (8 * j);
-            pk[1] |= (uint32_t)(b & 255) << (8 * j);
-            pk[2] |= (uint32_t)(c & 255) << (8 * j);
-        } else {
-            pk[0] |= (uint32_t)(t & 255) << (8 * j);
-            pk[1] |= (uint32_t)(c & 255) << (8 * j);
-        }
+    if constexpr (LIMBS == 3) {
+        const uint32_t hi01 = __builtin_amdgcn_perm(u1, u0, 0x07030602u);  // u0.b2 u1.b2 - -
+        const uint32_t hi23 = __builtin_amdgcn_perm(u3, u2, 0x07030602u);
+        pk[0] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u;
+        pk[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
+        pk[2] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
+    } else {
+        pk[0] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
+        pk[1] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
     }
 #pragma unroll
     for (int l = 0; l < LIMBS; ++l) plane[l * n4 + i] = pk[l];
@@ -129,33 +133,69 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
 // Activation staging into LDS.
 // Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
 // then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
-// The x loads of a thread are issued in batches of four before any of them is
-// converted, so the staging costs one or two memory round trips, not one per
-// float4.
-template <int GROUP, int LIMBS>
-__device__ __forceinline__ void stage_activation(const float *__restrict__ x, int k,
-                                                 uint8_t *__restrict__ smem)
+//
+// A kernel issues the first B float4 of each thread's share of x
+// (x_preload) before any weight load: vector loads of a wave complete in
+// issue order, so x then arrives after one memory round trip instead of
+// queueing behind the weights' look-ahead loads.  stage_activation encodes
+// the preloaded part and loads the rest (if k exceeds B float4 per thread)
+// in batches of four, each batch one round trip.
+template <int B>
+struct XPre {
+    f32x4 v[B];
+};
+
+template <int B>
+__device__ __forceinline__ XPre<B> x_preload(const float *__restrict__ x, int k)
 {
-    constexpr int B = 4;
+    XPre<B> p;
+    const int n4 = k >> 2;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const int i = threadIdx.x + b * blockDim.x;
+        if (i < n4) p.v[b] = x4[i];
+    }
+    return p;
+}
+
+template <int GROUP, int LIMBS, int B>
+__device__ __forceinline__ void stage_activation(const XPre<B> &pre, const float *__restrict__ x,
+                                                 int k, uint8_t *__restrict__ smem)
+{
+    constexpr int BR = 4;
     const int n4 = k >> 2;  // a multiple of 64: whole waves stay active
     uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
     float *tscale = reinterpret_cast<float *>(smem + LIMBS * k);
     float *tsum = tscale + k / GROUP;
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
     const int stride = blockDim.x;
-    for (int i0 = threadIdx.x; i0 < n4; i0 += B * stride) {
-        f32x4 v[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B; ++b) {
+        const int i = threadIdx.x + b * stride;
+        if (i < n4) stage_group<GROUP, LIMBS>(pre.v[b], i, plane, n4, tscale, tsum);
+    }
+    for (int i0 = threadIdx.x + B * stride; i0 < n4; i0 += BR * stride) {
+        f32x4 v[BR];
+#pragma unroll
+        for (int b = 0; b < BR; ++b) {
             const int i = i0 + b * stride;
             if (i < n4) v[b] = x4[i];
         }
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
+        for (int b = 0; b < BR; ++b) {
             const int i = i0 + b * stride;
             if (i < n4) stage_group<GROUP, LIMBS>(v[b], i, plane, n4, tscale, tsum);
         }
     }
+}
+
+// Staging without a preload: x loaded in batches of four float4 per thread.
+template <int GROUP, int LIMBS>
+__device__ __forceinline__ void stage_activation(const float *__restrict__ x, int k,
+                                                 uint8_t *__restrict__ smem)
+{
+    stage_activation<GROUP, LIMBS, 4>(x_preload<4>(x, k), x, k, smem);
 }
 
 template <int LIMBS>
@@ -211,14 +251,13 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
 {
     // 6-bit scales and mins of sub-blocks 4h..4h+3, one per byte.
     const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
-    uint32_t scb, mnb;
-    if (h == 0) {
-        scb = S0 & 0x3F3F3F3Fu;
-        mnb = S1 & 0x3F3F3F3Fu;
-    } else {
-        scb = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
-        mnb = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
-    }
+    // both halves' forms, then a per-lane select: a branch on h would split
+    // the wave (neighbouring lanes take different halves)
+    const uint32_t sc_lo = S0 & 0x3F3F3F3Fu, mn_lo = S1 & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+    const uint32_t scb = h ? sc_hi : sc_lo;
+    const uint32_t mnb = h ? mn_hi : mn_lo;
     const float d = half_lo(u.hdr.x), dmin = half_hi(u.hdr.x);
 
     int acc[4][LIMBS];
@@ -300,7 +339,9 @@ __device__ __forceinline__ Q6Unit q6_load(const uint8_t *__restrict__ sb, int h)
     const uint32_t *ps = reinterpret_cast<const uint32_t *>(a + 192 + 8 * h);
     u.sc[0] = ps[0];
     u.sc[1] = ps[1];
-    u.sc[2] = shift ? ps[2] : 0u;
+    // third word only needed when shifted; otherwise re-read the second, so
+    // the load stays inside the superblock and is not a branch
+    u.sc[2] = ps[shift ? 2 : 1];
     u.d = *reinterpret_cast<const uint16_t *>(sb + 208);
     return u;
 }

@@ -38,6 +38,10 @@ namespace {
 
 using namespace kqd;
 
+// float4 of x per thread loaded ahead of the weights, times the waves per
+// workgroup: 80 / WMAX float4 per thread cover k = 20480 in one round trip.
+constexpr int kXPre = 80;
+
 // One wave holds RPT = 64/LANES rows; lane `sub` of a row takes units sub,
 // sub+LANES, ...  Each lane keeps DEPTH units of look-ahead in flight: the
 // first DEPTH loads are issued before the activation staging (so HBM is busy
@@ -63,21 +67,29 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     const int sub = lane % LANES;
     const int h = sub & 1;  // LANES is even: a lane always takes the same half
     const int steps = (units + LANES - 1) / LANES;
+    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
     const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
-    // ring[j] holds unit sub + LANES*j of the current row (loads in flight)
-    Q4Unit ring[DEPTH > 0 ? DEPTH : 1];
+    // Loads are unconditional: a lane past the row's last unit re-reads that
+    // unit, a lane without a row reads the workgroup's first row (its result
+    // is dropped), so every wave issues the same loads in the same order and
+    // waits only for the unit it is about to use.
+    auto load = [&](int st) {
+        const int u = min(sub + LANES * st, units - 1);
+        return q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
+    };
+    constexpr int R = DEPTH + 1;
+    Q4Unit ring[R];
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        const int u = sub + LANES * j;
-        if (rv && u < units) ring[j] = q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
+    for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
+        ring[j] = load(j);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-
-    stage_activation<32, LIMBS>(x, k, smem);
+    stage_activation<32, LIMBS>(xpre, x, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -85,22 +97,31 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
 
     while (t0 < r_hi) {
         float acc = 0.0f;
-        for (int st = 0; st < steps; ++st) {
+        // step st computes ring slot st % R and first refills the slot freed
+        // by the previous step with unit st + DEPTH
+        auto step = [&](int j, int st, bool prefetch) __attribute__((always_inline)) {
+            // keep each step's arithmetic inside the step: hoisted into an
+            // earlier step it would wait there for loads still in flight
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch) ring[(j + DEPTH) % R] = load(st + DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
             const int u = sub + LANES * st;
-            const int un = u + LANES * DEPTH;
-            Q4Unit nxt;
-            if (rv && un < units) nxt = q4_load(rowp + (int64_t)(un >> 1) * kQ4Bytes, h);
-            if (rv && u < units) {
-                const Q4Unit &cur = DEPTH > 0 ? ring[0] : nxt;
-                acc += q4_unit_dot<LIMBS>(cur, h, 256 * (u >> 1) + 128 * h, k, planes,
-                                          tscale, tsum);
-            }
-            if constexpr (DEPTH > 0) {
+            const int uc = min(u, units - 1);  // the unit that was loaded
+            const float d = q4_unit_dot<LIMBS>(ring[j], h, 256 * (uc >> 1) + 128 * h, k, planes,
+                                               tscale, tsum);
+            acc += (rv && u < units) ? d : 0.0f;
+        };
+        // whole passes of R steps: constant slot indices and no branch between
+        // a load and its use, so each wait covers exactly the unit needed
+        int s0 = 0;
+        for (; s0 + R <= steps; s0 += R) {
 #pragma unroll
-                for (int j = 0; j + 1 < DEPTH; ++j) ring[j] = ring[j + 1];
-                ring[DEPTH - 1] = nxt;
-            }
+            for (int j = 0; j < R; ++j) step(j, s0 + j, true);
         }
+        // the last steps - s0 < R steps: their units are already in flight
+#pragma unroll
+        for (int j = 0; j + 1 < R; ++j)
+            if (s0 + j < steps) step(j, s0 + j, false);
         acc = lane_group_sum<LANES>(acc);
         if (sub == 0 && rv) {
             if constexpr (SILU) {
@@ -113,10 +134,12 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
         r = t0 + lane / LANES;
         rv = r < r_hi;
         rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        if (t0 < r_hi) {
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            const int u = sub + LANES * j;
-            if (rv && u < units) ring[j] = q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
+            for (int j = 0; j < DEPTH; ++j) {
+                ring[j] = load(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }
@@ -147,24 +170,29 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
     const int sub = lane % LANES;
     const int h = sub & 1;  // LANES and units are even: a lane always takes the same half
     const int steps = (units2 + LANES - 1) / LANES;
+    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
     const uint8_t *gp = Wg + (int64_t)(rv ? r : r_lo) * row_bytes;
     const uint8_t *up = Wu + (int64_t)(rv ? r : r_lo) * row_bytes;
-    auto load = [&](int u) {
-        return u < units ? q4_load(gp + (int64_t)(u >> 1) * kQ4Bytes, h)
-                         : q4_load(up + (int64_t)((u - units) >> 1) * kQ4Bytes, h);
+    // unconditional loads, as in q4k_matvec_kernel
+    auto load = [&](int st) {
+        const int u = min(sub + LANES * st, units2 - 1);
+        const uint8_t *p = u < units ? gp + (int64_t)(u >> 1) * kQ4Bytes
+                                     : up + (int64_t)((u - units) >> 1) * kQ4Bytes;
+        return q4_load(p, h);
     };
-    Q4Unit ring[DEPTH > 0 ? DEPTH : 1];
+    constexpr int R = DEPTH + 1;
+    Q4Unit ring[R];
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        const int u = sub + LANES * j;
-        if (rv && u < units2) ring[j] = load(u);
+    for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
+        ring[j] = load(j);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    stage_activation<32, LIMBS>(x, k, smem);
+    stage_activation<32, LIMBS>(xpre, x, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -172,27 +200,28 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
 
     while (t0 < r_hi) {
         float acc_g = 0.0f, acc_u = 0.0f;
-        for (int st = 0; st < steps; ++st) {
+        auto step = [&](int j, int st, bool prefetch) __attribute__((always_inline)) {
+            // keep each step's arithmetic inside the step: hoisted into an
+            // earlier step it would wait there for loads still in flight
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch) ring[(j + DEPTH) % R] = load(st + DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
             const int u = sub + LANES * st;
-            const int un = u + LANES * DEPTH;
-            Q4Unit nxt;
-            if (rv && un < units2) nxt = load(un);
-            if (rv && u < units2) {
-                const Q4Unit &cur = DEPTH > 0 ? ring[0] : nxt;
-                const int uu = u < units ? u : u - units;
-                const float d = q4_unit_dot<LIMBS>(cur, h, 256 * (uu >> 1) + 128 * h, k, planes,
-                                                   tscale, tsum);
-                if (u < units)
-                    acc_g += d;
-                else
-                    acc_u += d;
-            }
-            if constexpr (DEPTH > 0) {
+            const int uc = min(u, units2 - 1);  // the unit that was loaded
+            const int uu = uc < units ? uc : uc - units;
+            const float d = q4_unit_dot<LIMBS>(ring[j], h, 256 * (uu >> 1) + 128 * h, k, planes,
+                                               tscale, tsum);
+            acc_g += (rv && u < units) ? d : 0.0f;
+            acc_u += (rv && u >= units && u < units2) ? d : 0.0f;
+        };
+        int s0 = 0;
+        for (; s0 + R <= steps; s0 += R) {
 #pragma unroll
-                for (int j = 0; j + 1 < DEPTH; ++j) ring[j] = ring[j + 1];
-                ring[DEPTH - 1] = nxt;
-            }
+            for (int j = 0; j < R; ++j) step(j, s0 + j, true);
         }
+#pragma unroll
+        for (int j = 0; j + 1 < R; ++j)
+            if (s0 + j < steps) step(j, s0 + j, false);
         acc_g = lane_group_sum<LANES>(acc_g);
         acc_u = lane_group_sum<LANES>(acc_u);
         if (sub == 0 && rv) mid[r] = (acc_g / (1.0f + __expf(-acc_g))) * acc_u;
@@ -201,10 +230,12 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         rv = r < r_hi;
         gp = Wg + (int64_t)(rv ? r : r_lo) * row_bytes;
         up = Wu + (int64_t)(rv ? r : r_lo) * row_bytes;
+        if (t0 < r_hi) {
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            const int u = sub + LANES * j;
-            if (rv && u < units2) ring[j] = load(u);
+            for (int j = 0; j < DEPTH; ++j) {
+                ring[j] = load(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }
@@ -228,21 +259,26 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     const int sub = lane % LANES;
     const int h = sub & 1;
     const int steps = (units + LANES - 1) / LANES;
+    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
     const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
-    // ring[j] holds unit sub + LANES*j of the current row (loads in flight)
-    Q6Unit ring[DEPTH > 0 ? DEPTH : 1];
+    // unconditional loads, as in q4k_matvec_kernel
+    auto load = [&](int st) {
+        const int u = min(sub + LANES * st, units - 1);
+        return q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+    };
+    constexpr int R = DEPTH + 1;
+    Q6Unit ring[R];
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-        const int u = sub + LANES * j;
-        if (rv && u < units) ring[j] = q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+    for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
+        ring[j] = load(j);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-
-    stage_activation<16, LIMBS>(x, k, smem);
+    stage_activation<16, LIMBS>(xpre, x, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -250,32 +286,38 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
 
     while (t0 < r_hi) {
         float acc = 0.0f;
-        for (int st = 0; st < steps; ++st) {
+        auto step = [&](int j, int st, bool prefetch) __attribute__((always_inline)) {
+            // keep each step's arithmetic inside the step: hoisted into an
+            // earlier step it would wait there for loads still in flight
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch) ring[(j + DEPTH) % R] = load(st + DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
             const int u = sub + LANES * st;
-            const int un = u + LANES * DEPTH;
-            Q6Unit nxt;
-            if (rv && un < units) nxt = q6_load(rowp + (int64_t)(un >> 1) * kQ6Bytes, h);
-            if (rv && u < units) {
-                const Q6Unit &cur = DEPTH > 0 ? ring[0] : nxt;
-                acc += q6_unit_dot<LIMBS>(cur, 256 * (u >> 1) + 128 * h, k, planes, tscale,
-                                          tsum);
-            }
-            if constexpr (DEPTH > 0) {
+            const int uc = min(u, units - 1);  // the unit that was loaded
+            const float d = q6_unit_dot<LIMBS>(ring[j], 256 * (uc >> 1) + 128 * h, k, planes,
+                                               tscale, tsum);
+            acc += (rv && u < units) ? d : 0.0f;
+        };
+        int s0 = 0;
+        for (; s0 + R <= steps; s0 += R) {
 #pragma unroll
-                for (int j = 0; j + 1 < DEPTH; ++j) ring[j] = ring[j + 1];
-                ring[DEPTH - 1] = nxt;
-            }
+            for (int j = 0; j < R; ++j) step(j, s0 + j, true);
         }
+#pragma unroll
+        for (int j = 0; j + 1 < R; ++j)
+            if (s0 + j < steps) step(j, s0 + j, false);
         acc = lane_group_sum<LANES>(acc);
         if (sub == 0 && rv) y[r] = acc;
         t0 += nwaves * RPT;
         r = t0 + lane / LANES;
         rv = r < r_hi;
         rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        if (t0 < r_hi) {
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            const int u = sub + LANES * j;
-            if (rv && u < units) ring[j] = q6_load(rowp + (int64_t)(u >> 1) * kQ6Bytes, h);
+            for (int j = 0; j < DEPTH; ++j) {
+                ring[j] = load(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }
@@ -439,36 +481,23 @@ int device_cus()
 // CU each keeping 3 units in flight, which needs the 8-wave VGPR budget.
 kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus)
 {
-    static const int kLanes[] = {4, 8, 16, 32, 64};
+    // Measured on MI355X (sweeps of lanes 8..32, waves 4..16, one or two
+    // workgroups per CU, look-ahead 0..2 units):
+    //   Q4_K 19968 x 6656: 8 lanes, 8 waves, 2 workgroups per CU, 1 unit ahead
+    //   Q4_K 6656 x 19968: 8 lanes, 16 waves, 1 workgroup per CU, 1 unit ahead
+    //   Q6_K 6656 x 19968: 8 lanes, 8 waves, 1 workgroup per CU, 1 unit ahead
+    // 8 lanes per row keep a row's loads contiguous and the lane reduction to
+    // DPP moves.  Waves without rows still share the activation staging, so a
+    // long k takes the widest workgroup the registers allow (Q6_K's ring
+    // needs more than 128 VGPRs, which caps it at 8 waves).
     const bool q6 = qtype == 2;
-    const int depth = q6 ? 3 : 1;
-    const int wmax = q6 ? 8 : 16;
-    const double want_waves = q6 ? 4.0 : 8.0;
-    kqi::MatvecShape best{8, 1, 1, depth};
-    double best_score = -1.0;
-    for (int L : kLanes) {
-        const int rpt = 64 / L;
-        const int64_t tiles_total = (n_rows + rpt - 1) / rpt;
-        const int grid = (int)(tiles_total < cus ? (tiles_total > 0 ? tiles_total : 1) : cus);
-        const int64_t rows_wg = (n_rows + grid - 1) / grid;
-        const int64_t tiles = (rows_wg + rpt - 1) / rpt;
-        const int waves = (int)(tiles < wmax ? tiles : wmax);
-        const int64_t rounds = (tiles + waves - 1) / waves;
-        const int steps = (units + L - 1) / L;
-        const double lane_eff = (double)units / (double)(L * steps);
-        const double slot_eff = (double)rows_wg / (double)(rpt * waves * rounds);
-        const double occ = waves >= want_waves ? 1.0 : (double)waves / want_waves;
-        // Q6_K: 8 lanes per row measured best whenever a workgroup has rows
-        // for it; idle waves still share the activation staging, so the
-        // workgroup keeps all 8.
-        const double pref = (q6 && L == 8) ? 1.25 : 1.0;
-        const double score = lane_eff * slot_eff * occ * pref;
-        if (score > best_score + 1e-9) {
-            best_score = score;
-            best = kqi::MatvecShape{L, q6 ? wmax : waves, grid, depth};
-        }
-    }
-    return best;
+    const int64_t tiles = (n_rows + 7) / 8;
+    const int64_t k = 128 * (int64_t)units;
+    const bool two_per_cu = !q6 && k <= 8192 && n_rows >= 32 * 2 * (int64_t)cus;
+    const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
+    const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
+    const int waves = q6 ? 8 : (two_per_cu ? 8 : 16);
+    return kqi::MatvecShape{8, waves, grid, 2};
 }
 
 // Raise a kernel's dynamic-LDS limit once to the largest staging size any
@@ -621,11 +650,11 @@ hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_r
 hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *mid,
                               int n_rows, int k, hipStream_t stream)
 {
-    // Measured on MI355X at 19968 x 6656 (sweep of lanes 4/8/16, waves 4..16,
-    // grid 1-4 per CU, depth 1-3): 8 lanes per row, 8-wave workgroups, two
-    // workgroups per CU and no look-ahead stream best (33.0 us, 4.5 TB/s).
+    // Measured on MI355X at 19968 x 6656 (sweep of lanes 8/16, waves 8..16,
+    // grid 1-2 per CU, depth 1-3): 8 lanes per row, one 12-wave workgroup per
+    // CU and one unit of look-ahead best (32.4 us, 4.6 TB/s).
     const int tiles = (n_rows + 7) / 8;
-    MatvecShape s{8, 8, tiles < 2 * device_cus() ? tiles : 2 * device_cus(), 1};
+    MatvecShape s{8, 12, tiles < device_cus() ? tiles : device_cus(), 2};
     const MatvecShape o = g_override[1];
     if (o.lanes) s.lanes = o.lanes;
     if (o.waves) s.waves = o.waves;
