@@ -55,6 +55,24 @@ BYTES = {
 }
 # gate and up in one launch: both matrices, x in, mid out
 GATE_UP_BYTES = 2 * q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN
+
+
+def staged_bytes(group, k):
+    """Bytes of a staged activation: 3 byte limbs per input, a scale and a sum per group."""
+    return 3 * k + 8 * (k // group)
+
+
+# the staged pass: activations cross launches in the consumer's staged form
+# (groups of 32 inputs for Q4_K, 16 for Q6_K); mid is also written as f32
+STAGED_BYTES = {
+    "gate_up_staged": 2 * q4k_bytes(FFN, HIDDEN) + staged_bytes(32, HIDDEN) + 4 * FFN
+                      + staged_bytes(16, FFN),
+    "down_staged": q6k_bytes(HIDDEN, FFN) + staged_bytes(16, FFN) + 4 * HIDDEN,
+    "tail_staged": 4 * HIDDEN * 6 + staged_bytes(32, HIDDEN),
+    # the previous layer's tail fused into gate+up: the tail's four inputs and
+    # the residual it writes, both matrices, mid f32 and staged
+    "tail_gate_up": 2 * q4k_bytes(FFN, HIDDEN) + 5 * 4 * HIDDEN + 4 * FFN + staged_bytes(16, FFN),
+}
 # one token through the pass: per layer gate+up (x in, mid out), down, tail; plus the entry norm.
 # The same count serves every schedule of the pass, so their rates compare work for work.
 PASS_BYTES = LAYERS * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
@@ -66,6 +84,10 @@ KERNEL_SYMBOL = {
     "down": "q6k_matvec_kernel",
     "tail": "tail_reg_kernel",
     "gate_up": "q4k_gate_up_kernel",
+    "gate_up_staged": "q4k_gate_up_kernel (staged x in, staged mid out)",
+    "down_staged": "q6k_matvec_kernel (staged x in)",
+    "tail_staged": "tail_reg_kernel (staged next_in out)",
+    "tail_gate_up": "q4k_gate_up_kernel<..., true> (previous tail fused in, staged mid out)",
 }
 
 
@@ -113,6 +135,11 @@ class FFNChain:
         self.p = torch.empty(HIDDEN, device=dev)
         self.zeros = torch.zeros(HIDDEN, device=dev)
         self.ones = torch.ones(HIDDEN, device=dev)
+        u8 = torch.uint8
+        self.xst = [torch.empty(kq.kq_staged_bytes(kq.KQ_QTYPE_Q4K, HIDDEN), dtype=u8, device=dev)
+                    for _ in range(2)]
+        self.mid_s = torch.empty(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, FFN), dtype=u8, device=dev)
+        self.R = [self.residual, torch.empty(HIDDEN, device=dev)]  # residual ping-pong
 
     def build_chain(self):
         """Device pointer tables and workspace for kq_ffn_chain."""
@@ -145,6 +172,52 @@ class FFNChain:
         self.kq.kq_fused_residual_norm(self.residual, self.zeros, self.x[0], self.ones, self.ones,
                                        1, HIDDEN, 1e-8, 1e-5)
 
+    def entry_norm_staged(self):
+        self.kq.kq_fused_residual_norm_staged(self.residual, self.zeros, self.x[0], self.xst[0],
+                                              self.kq.KQ_QTYPE_Q4K, self.ones, self.ones, 1,
+                                              HIDDEN, 1e-8, 1e-5)
+
+    def calls_staged(self, l):
+        """The layer as three launches with staged activations: gate+up+SiLU
+        reads x staged and writes mid staged, down reads it, the tail writes
+        the next x staged."""
+        kq = self.kq
+        xs, xn, xsn = self.xst[l % 2], self.x[(l + 1) % 2], self.xst[(l + 1) % 2]
+        Q4, Q6 = kq.KQ_QTYPE_Q4K, kq.KQ_QTYPE_Q6K
+        return (
+            ("gate_up_staged", lambda: kq.kq_ffn_gate_up_q4k_staged(
+                self.Wg[l], self.Wu[l], xs, self.mid, self.mid_s, Q6, FFN, HIDDEN)),
+            ("down_staged", lambda: kq.kq_matvec_staged(Q6, self.Wd[l], self.mid_s, self.p,
+                                                        HIDDEN, FFN)),
+            ("tail_staged", lambda: kq.kq_fused_residual_norm_staged(
+                self.residual, self.p, xn, xsn, Q4, self.gp[l], self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
+        )
+
+    def calls_fusedtail(self, l):
+        """The layer as two launches: the previous layer's tail fused into
+        this layer's gate+up+SiLU (layer 0: the entry norm, i.e. the tail with
+        a zero projection and unit gains), then the down matvec on staged mid.
+        The residual alternates between two buffers: every workgroup of the
+        fused launch reads the old one while one of them writes the new one."""
+        kq = self.kq
+        Q6 = kq.KQ_QTYPE_Q6K
+        pp, gp, gn = (self.zeros, self.ones, self.ones) if l == 0 else \
+            (self.p, self.gp[l - 1], self.gn[l - 1])
+        R = self.R
+        return (
+            ("tail_gate_up", lambda: kq.kq_ffn_tail_gate_up_q4k(
+                R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, self.Wg[l], self.Wu[l], self.mid,
+                self.mid_s, Q6, FFN, HIDDEN, 1e-8, 1e-5)),
+            ("down_staged", lambda: kq.kq_matvec_staged(Q6, self.Wd[l], self.mid_s, self.p,
+                                                        HIDDEN, FFN)),
+        )
+
+    def final_tail(self):
+        """The last layer's tail (after the fused pass): residual and x_out."""
+        L = self.layers
+        self.kq.kq_fused_residual_norm(self.R[L % 2], self.p, self.x[0], self.gp[L - 1],
+                                       self.gn[L - 1], 1, HIDDEN, 1e-8, 1e-5)
+
     def calls(self, l):
         kq = self.kq
         x, xn = self.x[l % 2], self.x[(l + 1) % 2]
@@ -167,10 +240,24 @@ class FFNChain:
                                                        self.gn[l], 1, HIDDEN, 1e-8, 1e-5)),
         )
 
-    def run_pass(self, fused=False):
-        self.entry_norm()
+    def run_pass(self, mode="4launch"):
+        """One token: the entry norm, then every layer as 4 launches ("4launch"),
+        3 with gate and up fused ("fused"), 3 with staged activations
+        ("staged"); or every layer as 2 launches with each tail fused into the
+        next gate+up, then the last tail ("fusedtail")."""
+        if mode == "fusedtail":
+            for l in range(self.layers):
+                for _, fn in self.calls_fusedtail(l):
+                    fn()
+            self.final_tail()
+            return
+        if mode == "staged":
+            self.entry_norm_staged()
+        else:
+            self.entry_norm()
+        calls = {"4launch": self.calls, "fused": self.calls_fused, "staged": self.calls_staged}[mode]
         for l in range(self.layers):
-            for _, fn in (self.calls_fused(l) if fused else self.calls(l)):
+            for _, fn in calls(l):
                 fn()
 
     def per_kernel_us(self, reps):
@@ -179,9 +266,17 @@ class FFNChain:
         replayed reps times; time / (reps * layers)."""
         torch = self.torch
         out = {}
-        for name in ("gate", "up_silu", "down", "tail", "gate_up"):
-            pick = (lambda l: self.calls_fused(l)[0][1]) if name == "gate_up" else \
-                (lambda l, i=("gate", "up_silu", "down", "tail").index(name): self.calls(l)[i][1])
+        four = ("gate", "up_silu", "down", "tail")
+        st = ("gate_up_staged", "down_staged", "tail_staged")
+        for name in four + ("gate_up",) + st + ("tail_gate_up",):
+            if name == "tail_gate_up":
+                pick = lambda l: self.calls_fusedtail(l)[0][1]
+            elif name == "gate_up":
+                pick = lambda l: self.calls_fused(l)[0][1]
+            elif name in st:
+                pick = lambda l, i=st.index(name): self.calls_staged(l)[i][1]
+            else:
+                pick = lambda l, i=four.index(name): self.calls(l)[i][1]
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
             g = torch.cuda.CUDAGraph()
@@ -440,18 +535,28 @@ def main():
             g.replay()
         return g
 
-    # ---- the step as timed: one graph replay of the whole pass, the entry norm
-    # then per layer gate+up+SiLU (one launch), down, tail
-    fused_pass = lambda: chain.run_pass(fused=True)
-    graph_f = capture(fused_pass)
-    log(f"timing {args.steps} steps (graph: 3 launches per layer)")
-    ms_per_step, wall = timed((lambda: graph_f.replay()) if graph_f is not None else fused_pass,
+    # ---- the step as timed: one graph replay of the whole pass: per layer the
+    # previous tail (the entry norm for layer 0) fused with gate+up+SiLU, then
+    # the down matvec on staged mid; then the last tail
+    ft_pass = lambda: chain.run_pass("fusedtail")
+    graph_t = capture(ft_pass)
+    log(f"timing {args.steps} steps (graph: 2 launches per layer, tail fused into gate+up)")
+    ms_per_step, wall = timed((lambda: graph_t.replay()) if graph_t is not None else ft_pass,
                               args.steps)
     value = pass_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # ---- the same pass two other ways, reported beside it
-    graph4 = capture(chain.run_pass)
-    per_op4_ms, _ = timed((lambda: graph4.replay()) if graph4 is not None else chain.run_pass,
+    # ---- the same pass other ways, reported beside it
+    staged_pass = lambda: chain.run_pass("staged")
+    graph_s = capture(staged_pass)
+    staged_ms, _ = timed((lambda: graph_s.replay()) if graph_s is not None else staged_pass,
+                         args.steps)
+    fused_pass = lambda: chain.run_pass("fused")
+    graph_f = capture(fused_pass)
+    fused_ms, _ = timed((lambda: graph_f.replay()) if graph_f is not None else fused_pass,
+                        args.steps)
+    four_pass = lambda: chain.run_pass("4launch")
+    graph4 = capture(four_pass)
+    per_op4_ms, _ = timed((lambda: graph4.replay()) if graph4 is not None else four_pass,
                           args.steps)
     for _ in range(max(1, args.warmup)):
         chain.run_chain()
@@ -463,11 +568,11 @@ def main():
     for _ in range(max(2, min(args.steps, 5))):
         chain.run_chain(ev)
 
-    per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph_f is not None else {}
+    per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph_t is not None else {}
     per = ev.summary()
     kernels = {}
     for name, avg in per_kernel.items():  # per-op kernels: graph of one launch per layer
-        nb = GATE_UP_BYTES if name == "gate_up" else BYTES[name]
+        nb = GATE_UP_BYTES if name == "gate_up" else (STAGED_BYTES.get(name) or BYTES[name])
         gbps = nb / (avg * 1e-6) / 1e9
         kernels[name] = {"symbol": KERNEL_SYMBOL[name], "us_avg": round(avg, 3),
                          "bytes_per_launch": nb, "GBps": round(gbps, 1),
@@ -482,7 +587,7 @@ def main():
                          "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                          "timing": "HIP events around each launch"}
     # the dominant kernel of the timed step: gate+up+SiLU (150 MB of its ~260 MB per layer)
-    dk = kernels.get("gate_up")
+    dk = kernels.get("tail_gate_up")
     roofline = None
     if dk is not None:
         roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"],
@@ -490,6 +595,13 @@ def main():
                     "traffic": load_pmc("gate_up", kernel_source_hash(GATE_UP_SOURCES)),
                     "bytes_per_launch": dk["bytes_per_launch"], "us_avg": dk["us_avg"]}
     alternatives = {
+        "graph_3_launches_per_layer_staged_activations": {
+            "ms_per_step": round(staged_ms, 4),
+            "GBps": round(pass_bytes / (staged_ms * 1e-3) / 1e9, 1),
+            "launches_per_step": 3 * layers + 1},
+        "graph_3_launches_per_layer_f32_activations": {
+            "ms_per_step": round(fused_ms, 4), "GBps": round(pass_bytes / (fused_ms * 1e-3) / 1e9, 1),
+            "launches_per_step": 3 * layers + 1},
         "graph_4_launches_per_layer": {"ms_per_step": round(per_op4_ms, 4),
                                        "GBps": round(pass_bytes / (per_op4_ms * 1e-3) / 1e9, 1),
                                        "launches_per_step": 4 * layers + 1},
@@ -506,7 +618,7 @@ def main():
         extras["read_ceiling_GBps"] = round(ceil, 1)
         if roofline is not None:
             roofline["frac_of_read_ceiling"] = round(dk["GBps"] / ceil, 4)
-        del chain, graph_f, graph4  # free 13.4 GB before the isolated runs
+        del chain, graph_t, graph_s, graph_f, graph4  # free 13.4 GB before the isolated runs
         torch.cuda.empty_cache()
         log("isolated matvecs with weight rotation")
         extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
@@ -529,8 +641,10 @@ def main():
                    "hidden": HIDDEN, "ffn": FFN, "layers": args.layers, "tokens_per_step": 1,
                    "weight_bytes_per_step": WEIGHT_BYTES_PASS * args.layers // LAYERS,
                    "algorithmic_bytes_per_step": pass_bytes,
-                   "timing": "one graph replay per step: entry norm, then per layer "
-                             "kq_ffn_gate_up_q4k, kq_matvec_q6k, kq_fused_residual_norm"},
+                   "timing": "one graph replay per step: per layer kq_ffn_tail_gate_up_q4k "
+                             "(the previous layer's tail, or the entry norm, fused with gate, "
+                             "up and SiLU) and kq_matvec_staged (Q6_K down), then the last "
+                             "kq_fused_residual_norm; 105 launches"},
         "alternatives": alternatives,
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "tokens_per_s": round(1e3 / ms_per_step, 2),

@@ -80,6 +80,8 @@ typedef int kq_status;
 #define KQ_MAX_M 16         /* largest activation batch of kq_matmul_small_m */
 #define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
 #define KQ_MAX_CHAIN_HIDDEN 16384 /* largest hidden size of kq_ffn_chain */
+#define KQ_STAGED_LIMBS 3   /* byte limbs per input in a staged activation */
+#define KQ_MAX_FUSED_TAIL_K 8192 /* largest k of kq_ffn_tail_gate_up_q4k */
 
 /*
  * Q4_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows, with an
@@ -177,6 +179,109 @@ int64_t kq_matmul_small_m_workspace_bytes(int qtype, int64_t n_rows, int64_t k, 
 kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,
                                  const float *g_post, const float *g_next, int64_t rows,
                                  int64_t n, float eps_post, float eps_next, void *stream);
+
+/*
+ * Staged activations.  Every matvec workgroup converts its f32 input into a
+ * block-floating-point form in on-chip memory before the weight stream: per
+ * scale group (32 inputs for a Q4_K consumer, 16 for Q6_K) a power-of-two
+ * scale and the group sum, and each input as KQ_STAGED_LIMBS signed byte
+ * limbs.  A producer that already holds the values can write that form once
+ * (a "staged" vector), and every consumer workgroup then copies it instead of
+ * converting x again.  This fuses dispatches without moving a rounding point
+ * (Ch 19 "The down projection + residual", section 19.7): a matvec on a
+ * staged vector returns bit for bit what it returns on the f32 vector the
+ * stage was made from.  The layout is internal to this library: KQ_STAGED_LIMBS
+ * byte planes of k bytes, then k/G f32 scales, then k/G f32 group sums.
+ *
+ * kq_staged_bytes: bytes of the staged form of a k-vector for a consumer of
+ * weight type qtype (KQ_QTYPE_Q4K or KQ_QTYPE_Q6K); k as for the matvecs.
+ * Returns the size (> 0), or a negative kq_status for a bad qtype or k.
+ */
+int64_t kq_staged_bytes(int qtype, int64_t k);
+
+/*
+ * Staged form of x for a consumer of type qtype.
+ *   x   [k] f32, 16-byte aligned; k as for the matvecs.
+ *   xs  kq_staged_bytes(qtype, k) bytes output, 16-byte aligned, must not
+ *       overlap x.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS,
+ * KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
+ */
+kq_status kq_stage_activation(int qtype, const float *x, void *xs, int64_t k, void *stream);
+
+/*
+ * kq_matvec_q4k / kq_matvec_q6k on a staged input (same results, bit for bit,
+ * as on the f32 vector the stage was made from).
+ *   qtype      weight type of W; xs must have been staged for that type.
+ *   W, y, n_rows, k, silu_gate  as for the matvec of that type (silu_gate
+ *              only for Q4_K: KQ_ERR_UNSUPPORTED otherwise).
+ *   xs         kq_staged_bytes(qtype, k) bytes, 16-byte aligned; y must not
+ *              overlap it.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_matvec_staged(int qtype, const void *W, const void *xs, float *y, int64_t n_rows,
+                           int64_t k, const float *silu_gate, void *stream);
+
+/*
+ * kq_ffn_gate_up_q4k on a staged input (xs, staged for Q4_K), optionally also
+ * writing mid in staged form for the next matvec (the down projection,
+ * Ch 10 section 10.3, weight type mid_qtype).
+ *   xs     kq_staged_bytes(KQ_QTYPE_Q4K, k) bytes, 16-byte aligned.
+ *   mid    [n_rows] f32 output, as for kq_ffn_gate_up_q4k.
+ *   mid_s  NULL, or kq_staged_bytes(mid_qtype, n_rows) bytes output, 16-byte
+ *          aligned; then n_rows must be a multiple of 256 (it is the next
+ *          matvec's k).  No output may overlap an input or the other output.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_ffn_gate_up_q4k_staged(const void *W_gate, const void *W_up, const void *xs,
+                                    float *mid, void *mid_s, int mid_qtype, int64_t n_rows,
+                                    int64_t k, void *stream);
+
+/*
+ * One layer boundary in one launch: the previous layer's dual-eps tail
+ * (Ch 19 "The down projection + residual", section 19.3) followed by this
+ * layer's gate, up and SiLU product (Ch 10 "The forward pass at a glance",
+ * section 10.3: the tail's second output is the next layer's input):
+ *   residual_out = residual_in + rms_norm(projected, eps_post) * g_post
+ *   x            = rms_norm(residual_out, eps_next) * g_next
+ *   next_in      = x                                  (if next_in != NULL)
+ *   mid[r]       = silu((W_gate x)[r]) * (W_up x)[r]  for r < n_rows
+ *   mid_s        = staged form of mid for a consumer of mid_qtype (if non-NULL)
+ * x has k elements (the tail's row width is the gate and up matrices' k).
+ * Every workgroup runs the tail itself, in the order of kq_fused_residual_norm,
+ * so residual_out, next_in and mid equal, bit for bit, kq_fused_residual_norm
+ * followed by kq_ffn_gate_up_q4k.
+ *   residual_in, projected, g_post, g_next  [k] f32, 16-byte aligned.
+ *   residual_out  [k] f32 output, 16-byte aligned; must not overlap
+ *                 residual_in (every workgroup reads it while one writes).
+ *   next_in       NULL or [k] f32 output, 16-byte aligned.
+ *   W_gate, W_up, mid, mid_s, mid_qtype  as for kq_ffn_gate_up_q4k_staged.
+ *   n_rows        >= 1 (the tail's outputs need a launch), < 2^31.
+ *   k             multiple of 256, <= KQ_MAX_FUSED_TAIL_K.
+ *   eps_post, eps_next  >= 0 and finite.
+ * No output may overlap an input or another output.
+ * Errors as kq_matvec_q4k.
+ */
+kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *projected,
+                                  const float *g_post, const float *g_next, float *residual_out,
+                                  float *next_in, const void *W_gate, const void *W_up, float *mid,
+                                  void *mid_s, int mid_qtype, int64_t n_rows, int64_t k,
+                                  float eps_post, float eps_next, void *stream);
+
+/*
+ * kq_fused_residual_norm that also writes next_in in staged form, for a
+ * consumer of type next_qtype (the next layer's gate and up: Q4_K).
+ *   next_in_s  rows * kq_staged_bytes(next_qtype, n) bytes output (row r at
+ *              r * kq_staged_bytes(next_qtype, n)), 16-byte aligned, must not
+ *              overlap any other argument.
+ *   n          multiple of 256 (it is the next matvec's k), <= KQ_MAX_TAIL_N.
+ *   The other arguments and the f32 outputs as for kq_fused_residual_norm.
+ * Errors as kq_fused_residual_norm.
+ */
+kq_status kq_fused_residual_norm_staged(float *residual, const float *projected, float *next_in,
+                                        void *next_in_s, int next_qtype, const float *g_post,
+                                        const float *g_next, int64_t rows, int64_t n,
+                                        float eps_post, float eps_next, void *stream);
 
 /*
  * One decode token through `layers` FFN layers in a single persistent launch:

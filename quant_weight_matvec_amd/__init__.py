@@ -11,4 +11,6 @@ from ._binding import (  # noqa: F401
     KQError, KQLibraryMissing, kq_build_info, kq_ffn_chain, kq_ffn_chain_error,
     kq_ffn_chain_workspace_bytes, kq_tune_set_chain_lanes, kq_tune_set_matvec_impl, kq_fused_residual_norm, kq_matmul_small_m, kq_matmul_small_m_workspace_bytes,
     kq_matvec_q4k, kq_matvec_q6k, kq_ffn_gate_up_q4k, kq_probe_read_bw, kq_status_string, kq_tune_get_shape, kq_tune_set_shape, lib,
+    kq_staged_bytes, kq_stage_activation, kq_matvec_staged, kq_ffn_gate_up_q4k_staged,
+    kq_fused_residual_norm_staged, kq_ffn_tail_gate_up_q4k,
 )

@@ -80,7 +80,19 @@ def lib() -> C.CDLL:
     L.kq_ffn_chain_error.argtypes = [_vp, C.POINTER(C.c_int)]
     L.kq_tune_set_chain_lanes.argtypes = [C.c_int]
     L.kq_tune_set_matvec_impl.argtypes = [C.c_int, C.c_int]
-    for fn in ("kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
+    L.kq_staged_bytes.argtypes = [C.c_int, _i64]
+    L.kq_staged_bytes.restype = _i64
+    L.kq_stage_activation.argtypes = [C.c_int, _vp, _vp, _i64, _vp]
+    L.kq_matvec_staged.argtypes = [C.c_int, _vp, _vp, _vp, _i64, _i64, _vp, _vp]
+    L.kq_ffn_gate_up_q4k_staged.argtypes = [_vp, _vp, _vp, _vp, _vp, C.c_int, _i64, _i64, _vp]
+    L.kq_fused_residual_norm_staged.argtypes = [_vp, _vp, _vp, _vp, C.c_int, _vp, _vp, _i64, _i64,
+                                                C.c_float, C.c_float, _vp]
+    L.kq_ffn_tail_gate_up_q4k.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          C.c_int, _i64, _i64, C.c_float, C.c_float, _vp]
+    for fn in ("kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
+               "kq_ffn_tail_gate_up_q4k",
+               "kq_fused_residual_norm_staged",
+               "kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
                "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
@@ -158,6 +170,54 @@ def kq_fused_residual_norm(residual, projected, next_in, g_post, g_next, rows: i
                                       _ptr(g_post), _ptr(g_next), int(rows), int(n),
                                       float(eps_post), float(eps_next), _stream(stream))
     _check(rc, "kq_fused_residual_norm")
+
+
+def kq_staged_bytes(qtype: int, k: int) -> int:
+    n = int(lib().kq_staged_bytes(int(qtype), int(k)))
+    if n < 0:
+        _check(n, "kq_staged_bytes")
+    return n
+
+
+def kq_stage_activation(qtype: int, x, xs, k: int, stream=None) -> None:
+    rc = lib().kq_stage_activation(int(qtype), _ptr(x), _ptr(xs), int(k), _stream(stream))
+    _check(rc, "kq_stage_activation")
+
+
+def kq_matvec_staged(qtype: int, W, xs, y, n_rows: int, k: int, silu_gate=None,
+                     stream=None) -> None:
+    rc = lib().kq_matvec_staged(int(qtype), _ptr(W), _ptr(xs), _ptr(y), int(n_rows), int(k),
+                                _ptr(silu_gate), _stream(stream))
+    _check(rc, "kq_matvec_staged")
+
+
+def kq_ffn_gate_up_q4k_staged(W_gate, W_up, xs, mid, mid_s, mid_qtype: int, n_rows: int, k: int,
+                              stream=None) -> None:
+    rc = lib().kq_ffn_gate_up_q4k_staged(_ptr(W_gate), _ptr(W_up), _ptr(xs), _ptr(mid),
+                                         _ptr(mid_s), int(mid_qtype), int(n_rows), int(k),
+                                         _stream(stream))
+    _check(rc, "kq_ffn_gate_up_q4k_staged")
+
+
+def kq_fused_residual_norm_staged(residual, projected, next_in, next_in_s, next_qtype: int,
+                                  g_post, g_next, rows: int, n: int, eps_post: float = 1e-8,
+                                  eps_next: float = 1e-5, stream=None) -> None:
+    rc = lib().kq_fused_residual_norm_staged(_ptr(residual), _ptr(projected), _ptr(next_in),
+                                             _ptr(next_in_s), int(next_qtype), _ptr(g_post),
+                                             _ptr(g_next), int(rows), int(n), float(eps_post),
+                                             float(eps_next), _stream(stream))
+    _check(rc, "kq_fused_residual_norm_staged")
+
+
+def kq_ffn_tail_gate_up_q4k(residual_in, projected, g_post, g_next, residual_out, next_in,
+                            W_gate, W_up, mid, mid_s, mid_qtype: int, n_rows: int, k: int,
+                            eps_post: float = 1e-8, eps_next: float = 1e-5, stream=None) -> None:
+    rc = lib().kq_ffn_tail_gate_up_q4k(_ptr(residual_in), _ptr(projected), _ptr(g_post),
+                                       _ptr(g_next), _ptr(residual_out), _ptr(next_in),
+                                       _ptr(W_gate), _ptr(W_up), _ptr(mid), _ptr(mid_s),
+                                       int(mid_qtype), int(n_rows), int(k), float(eps_post),
+                                       float(eps_next), _stream(stream))
+    _check(rc, "kq_ffn_tail_gate_up_q4k")
 
 
 def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0,

@@ -69,7 +69,7 @@ kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows,
     if (s != KQ_OK) return s;
     if (n_rows == 0) return KQ_OK;
     if ((s = check_device()) != KQ_OK) return s;
-    return from_hip(kqi::launch_matvec_q4k((const uint8_t *)W, x, y, (int)n_rows, (int)k,
+    return from_hip(kqi::launch_matvec_q4k((const uint8_t *)W, x, nullptr, y, (int)n_rows, (int)k,
                                            silu_gate, (hipStream_t)stream));
 }
 
@@ -88,8 +88,9 @@ kq_status kq_ffn_gate_up_q4k(const void *W_gate, const void *W_up, const float *
         return KQ_ERR_ALIAS;
     if (n_rows == 0) return KQ_OK;
     if ((s = check_device()) != KQ_OK) return s;
-    return from_hip(kqi::launch_gate_up_q4k((const uint8_t *)W_gate, (const uint8_t *)W_up, x, mid,
-                                            (int)n_rows, (int)k, (hipStream_t)stream));
+    return from_hip(kqi::launch_gate_up_q4k((const uint8_t *)W_gate, (const uint8_t *)W_up, x,
+                                            nullptr, mid, nullptr, 0, (int)n_rows, (int)k,
+                                            nullptr, (hipStream_t)stream));
 }
 
 kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
@@ -100,7 +101,7 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
     if (s != KQ_OK) return s;
     if (n_rows == 0) return KQ_OK;
     if ((s = check_device()) != KQ_OK) return s;
-    return from_hip(kqi::launch_matvec_q6k((const uint8_t *)W, x, y, (int)n_rows, (int)k,
+    return from_hip(kqi::launch_matvec_q6k((const uint8_t *)W, x, nullptr, y, (int)n_rows, (int)k,
                                            (hipStream_t)stream));
 }
 
@@ -142,10 +143,11 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
     if ((s = check_device()) != KQ_OK) return s;
     if (m == 1)
         return from_hip(qtype == KQ_QTYPE_Q4K
-                            ? kqi::launch_matvec_q4k((const uint8_t *)W, X, Y, (int)n_rows,
-                                                     (int)k, nullptr, (hipStream_t)stream)
-                            : kqi::launch_matvec_q6k((const uint8_t *)W, X, Y, (int)n_rows,
-                                                     (int)k, (hipStream_t)stream));
+                            ? kqi::launch_matvec_q4k((const uint8_t *)W, X, nullptr, Y,
+                                                     (int)n_rows, (int)k, nullptr,
+                                                     (hipStream_t)stream)
+                            : kqi::launch_matvec_q6k((const uint8_t *)W, X, nullptr, Y,
+                                                     (int)n_rows, (int)k, (hipStream_t)stream));
     const int64_t need =
         (int64_t)kqi::small_m_workspace_bytes(qtype, (int)n_rows, (int)k, m);
     if (need > 0) {
@@ -182,7 +184,173 @@ kq_status kq_fused_residual_norm(float *residual, const float *projected, float 
     kq_status s = check_device();
     if (s != KQ_OK) return s;
     return from_hip(kqi::launch_tail(residual, projected, next_in, g_post, g_next, (int)rows,
-                                     (int)n, eps_post, eps_next, (hipStream_t)stream));
+                                     (int)n, eps_post, eps_next, nullptr, 0,
+                                     (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Staged activations.  The group size follows the consuming weight type:
+// 32 inputs for Q4_K, 16 for Q6_K.
+static int staged_group(int qtype)
+{
+    return qtype == KQ_QTYPE_Q4K ? 32 : (qtype == KQ_QTYPE_Q6K ? 16 : 0);
+}
+
+static int64_t staged_size(int qtype, int64_t k)
+{
+    return KQ_STAGED_LIMBS * k + 8 * (k / staged_group(qtype));
+}
+
+int64_t kq_staged_bytes(int qtype, int64_t k)
+{
+    if (!staged_group(qtype)) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    return staged_size(qtype, k);
+}
+
+kq_status kq_stage_activation(int qtype, const float *x, void *xs, int64_t k, void *stream)
+{
+    if (!staged_group(qtype)) return KQ_ERR_SHAPE;
+    if (!x || !xs) return KQ_ERR_NULL;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (!aligned(x, 16) || !aligned(xs, 16)) return KQ_ERR_ALIGN;
+    if (overlap(xs, staged_size(qtype, k), x, k * 4)) return KQ_ERR_ALIAS;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_stage(x, (uint8_t *)xs, (int)k, staged_group(qtype),
+                                      (hipStream_t)stream));
+}
+
+kq_status kq_matvec_staged(int qtype, const void *W, const void *xs, float *y, int64_t n_rows,
+                           int64_t k, const float *silu_gate, void *stream)
+{
+    if (!staged_group(qtype)) return KQ_ERR_SHAPE;
+    if (!W || !xs || !y) return KQ_ERR_NULL;
+    if (qtype == KQ_QTYPE_Q6K && silu_gate) return KQ_ERR_UNSUPPORTED;
+    if (n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    const bool q4 = qtype == KQ_QTYPE_Q4K;
+    if (!aligned(W, q4 ? 16 : 4) || !aligned(xs, 16) || !aligned(y, 4) ||
+        (silu_gate && !aligned(silu_gate, 4)))
+        return KQ_ERR_ALIGN;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * (q4 ? KQ_Q4K_BLOCK_BYTES : KQ_Q6K_BLOCK_BYTES);
+    const int64_t ybytes = n_rows * 4;
+    if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, xs, staged_size(qtype, k)) ||
+        overlap(y, ybytes, silu_gate, silu_gate ? ybytes : 0))
+        return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(q4 ? kqi::launch_matvec_q4k((const uint8_t *)W, nullptr, (const uint8_t *)xs, y,
+                                                (int)n_rows, (int)k, silu_gate,
+                                                (hipStream_t)stream)
+                       : kqi::launch_matvec_q6k((const uint8_t *)W, nullptr, (const uint8_t *)xs, y,
+                                                (int)n_rows, (int)k, (hipStream_t)stream));
+}
+
+kq_status kq_ffn_gate_up_q4k_staged(const void *W_gate, const void *W_up, const void *xs,
+                                    float *mid, void *mid_s, int mid_qtype, int64_t n_rows,
+                                    int64_t k, void *stream)
+{
+    if (!W_gate || !W_up || !xs || !mid) return KQ_ERR_NULL;
+    if (mid_s && !staged_group(mid_qtype)) return KQ_ERR_SHAPE;
+    if (n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
+    if (mid_s && n_rows % KQ_QK) return KQ_ERR_SHAPE;  // mid is the next matvec's input
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(xs, 16) || !aligned(mid, 4) ||
+        !aligned(mid_s, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    const int64_t xsb = staged_size(KQ_QTYPE_Q4K, k);
+    const int64_t mb = n_rows * 4, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
+    if (overlap(mid, mb, W_gate, wbytes) || overlap(mid, mb, W_up, wbytes) ||
+        overlap(mid, mb, xs, xsb) || overlap(mid_s, msb, W_gate, wbytes) ||
+        overlap(mid_s, msb, W_up, wbytes) || overlap(mid_s, msb, xs, xsb) ||
+        overlap(mid_s, msb, mid, mb))
+        return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_gate_up_q4k(
+        (const uint8_t *)W_gate, (const uint8_t *)W_up, nullptr, (const uint8_t *)xs, mid,
+        (uint8_t *)mid_s, mid_s ? staged_group(mid_qtype) : 0, (int)n_rows, (int)k, nullptr,
+        (hipStream_t)stream));
+}
+
+kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *projected,
+                                  const float *g_post, const float *g_next, float *residual_out,
+                                  float *next_in, const void *W_gate, const void *W_up, float *mid,
+                                  void *mid_s, int mid_qtype, int64_t n_rows, int64_t k,
+                                  float eps_post, float eps_next, void *stream)
+{
+    if (!residual_in || !projected || !g_post || !g_next || !residual_out || !W_gate || !W_up ||
+        !mid)
+        return KQ_ERR_NULL;
+    if (mid_s && !staged_group(mid_qtype)) return KQ_ERR_SHAPE;
+    if (n_rows < 1 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;  // the tail needs a launch
+    if (mid_s && n_rows % KQ_QK) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (k > KQ_MAX_FUSED_TAIL_K) return KQ_ERR_UNSUPPORTED;
+    if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
+        return KQ_ERR_SHAPE;
+    if (!aligned(residual_in, 16) || !aligned(projected, 16) || !aligned(g_post, 16) ||
+        !aligned(g_next, 16) || !aligned(residual_out, 16) || !aligned(next_in, 16) ||
+        !aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(mid, 4) || !aligned(mid_s, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t vb = k * 4, wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    const int64_t mb = n_rows * 4, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
+    const void *ins[] = {residual_in, projected, g_post, g_next, W_gate, W_up};
+    const int64_t inb[] = {vb, vb, vb, vb, wbytes, wbytes};
+    void *outs[] = {residual_out, next_in, mid, mid_s};
+    const int64_t outb[] = {vb, next_in ? vb : 0, mb, msb};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[o], outb[o], ins[i], inb[i])) return KQ_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return KQ_ERR_ALIAS;
+    }
+    if ((s = check_device()) != KQ_OK) return s;
+    const kqi::TailArgs tail{residual_in, projected, g_post, g_next, residual_out, next_in,
+                             eps_post, eps_next};
+    return from_hip(kqi::launch_gate_up_q4k(
+        (const uint8_t *)W_gate, (const uint8_t *)W_up, nullptr, nullptr, mid, (uint8_t *)mid_s,
+        mid_s ? staged_group(mid_qtype) : 0, (int)n_rows, (int)k, &tail, (hipStream_t)stream));
+}
+
+kq_status kq_fused_residual_norm_staged(float *residual, const float *projected, float *next_in,
+                                        void *next_in_s, int next_qtype, const float *g_post,
+                                        const float *g_next, int64_t rows, int64_t n,
+                                        float eps_post, float eps_next, void *stream)
+{
+    if (!next_in_s) return KQ_ERR_NULL;
+    if (!staged_group(next_qtype)) return KQ_ERR_SHAPE;
+    if (n % KQ_QK) return KQ_ERR_SHAPE;  // next_in is a matvec input
+    if (!aligned(next_in_s, 16)) return KQ_ERR_ALIGN;
+    if (!residual || !projected || !next_in || !g_post || !g_next) return KQ_ERR_NULL;
+    if (rows < 0 || rows > INT32_MAX || n < 4) return KQ_ERR_SHAPE;
+    if (n > KQ_MAX_TAIL_N) return KQ_ERR_UNSUPPORTED;
+    if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
+        return KQ_ERR_SHAPE;
+    if (!aligned(residual, 16) || !aligned(projected, 16) || !aligned(next_in, 16) ||
+        !aligned(g_post, 16) || !aligned(g_next, 16))
+        return KQ_ERR_ALIGN;
+    const int64_t b = rows * n * 4;
+    const int64_t sb = rows * staged_size(next_qtype, n);
+    if (overlap(next_in, b, residual, b) || overlap(next_in, b, projected, b) ||
+        overlap(next_in, b, g_post, n * 4) || overlap(next_in, b, g_next, n * 4) ||
+        overlap(residual, b, projected, b) || overlap(residual, b, g_post, n * 4) ||
+        overlap(residual, b, g_next, n * 4) || overlap(next_in_s, sb, residual, b) ||
+        overlap(next_in_s, sb, projected, b) || overlap(next_in_s, sb, next_in, b) ||
+        overlap(next_in_s, sb, g_post, n * 4) || overlap(next_in_s, sb, g_next, n * 4))
+        return KQ_ERR_ALIAS;
+    if (rows == 0) return KQ_OK;
+    kq_status s = check_device();
+    if (s != KQ_OK) return s;
+    return from_hip(kqi::launch_tail(residual, projected, next_in, g_post, g_next, (int)rows,
+                                     (int)n, eps_post, eps_next, (uint8_t *)next_in_s,
+                                     staged_group(next_qtype), (hipStream_t)stream));
 }
 
 int64_t kq_ffn_chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype)

@@ -133,47 +133,89 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
 // Activation staging into LDS.
 // Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
 // then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
-//
-// A kernel issues the first B float4 of each thread's share of x
-// (x_preload) before any weight load: vector loads of a wave complete in
-// issue order, so x then arrives after one memory round trip instead of
-// queueing behind the weights' look-ahead loads.  stage_activation encodes
-// the preloaded part and loads the rest (if k exceeds B float4 per thread)
-// in batches of four, each batch one round trip.
+// The same bytes in global memory are a "staged" activation: a producer
+// kernel that already holds the values writes them in this form once, and
+// every consumer workgroup copies them into LDS instead of encoding x again.
+template <int GROUP, int LIMBS>
+__host__ __device__ constexpr int64_t staged_bytes(int64_t k)
+{
+    return LIMBS * k + 2 * 4 * (k / GROUP);
+}
+
+// A kernel issues the first B 16-byte pieces of each thread's share of its
+// activation (float4 of x, or pieces of the staged form) before any weight
+// load: vector loads of a wave complete in issue order, so the activation
+// then arrives after one memory round trip instead of queueing behind the
+// weights' look-ahead loads.  stage_activation encodes (or copies) the
+// preloaded part and loads the rest in batches of four, each batch one round
+// trip.
 template <int B>
 struct XPre {
-    f32x4 v[B];
+    u32x4 v[B];
 };
 
 template <int B>
-__device__ __forceinline__ XPre<B> x_preload(const float *__restrict__ x, int k)
+__device__ __forceinline__ XPre<B> x_preload(const void *__restrict__ src, int n16)
 {
     XPre<B> p;
-    const int n4 = k >> 2;
-    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const int i = threadIdx.x + b * blockDim.x;
-        if (i < n4) p.v[b] = x4[i];
+        if (i < n16) p.v[b] = s4[i];
     }
     return p;
 }
 
+// Number of 16-byte pieces x_preload reads: float4 of x, or pieces of xs.
+template <int GROUP, int LIMBS>
+__device__ __forceinline__ int x_pieces(const uint8_t *xs, int k)
+{
+    return xs ? (int)(staged_bytes<GROUP, LIMBS>(k) >> 4) : (k >> 2);
+}
+
 template <int GROUP, int LIMBS, int B>
 __device__ __forceinline__ void stage_activation(const XPre<B> &pre, const float *__restrict__ x,
-                                                 int k, uint8_t *__restrict__ smem)
+                                                 const uint8_t *__restrict__ xs, int k,
+                                                 uint8_t *__restrict__ smem)
 {
     constexpr int BR = 4;
+    const int stride = blockDim.x;
+    if (xs) {  // staged by the producer: a plain copy
+        const int n16 = (int)(staged_bytes<GROUP, LIMBS>(k) >> 4);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(smem);
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(xs);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int i = threadIdx.x + b * stride;
+            if (i < n16) dst[i] = pre.v[b];
+        }
+        for (int i0 = threadIdx.x + B * stride; i0 < n16; i0 += BR * stride) {
+            u32x4 v[BR];
+#pragma unroll
+            for (int b = 0; b < BR; ++b) {
+                const int i = i0 + b * stride;
+                if (i < n16) v[b] = s4[i];
+            }
+#pragma unroll
+            for (int b = 0; b < BR; ++b) {
+                const int i = i0 + b * stride;
+                if (i < n16) dst[i] = v[b];
+            }
+        }
+        return;
+    }
     const int n4 = k >> 2;  // a multiple of 64: whole waves stay active
     uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
     float *tscale = reinterpret_cast<float *>(smem + LIMBS * k);
     float *tsum = tscale + k / GROUP;
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
-    const int stride = blockDim.x;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         const int i = threadIdx.x + b * stride;
-        if (i < n4) stage_group<GROUP, LIMBS>(pre.v[b], i, plane, n4, tscale, tsum);
+        if (i < n4)
+            stage_group<GROUP, LIMBS>(__builtin_bit_cast(f32x4, pre.v[b]), i, plane, n4, tscale,
+                                      tsum);
     }
     for (int i0 = threadIdx.x + B * stride; i0 < n4; i0 += BR * stride) {
         f32x4 v[BR];
@@ -190,12 +232,25 @@ __device__ __forceinline__ void stage_activation(const XPre<B> &pre, const float
     }
 }
 
-// Staging without a preload: x loaded in batches of four float4 per thread.
+// Staging of a plain x without a preload: loaded in batches of four float4.
 template <int GROUP, int LIMBS>
 __device__ __forceinline__ void stage_activation(const float *__restrict__ x, int k,
                                                  uint8_t *__restrict__ smem)
 {
-    stage_activation<GROUP, LIMBS, 4>(x_preload<4>(x, k), x, k, smem);
+    stage_activation<GROUP, LIMBS, 4>(x_preload<4>(x, k >> 2), x, nullptr, k, smem);
+}
+
+// Writes the staged form of values the calling threads hold: thread t of a
+// run of consecutive lanes holds float4 number i = i0 + t of the vector (k
+// values), and whole scale groups of lanes take part.  Output layout as in
+// LDS, at `out` in global memory.
+template <int GROUP, int LIMBS>
+__device__ __forceinline__ void stage_group_global(f32x4 v, int i, uint8_t *__restrict__ out, int k)
+{
+    uint32_t *plane = reinterpret_cast<uint32_t *>(out);
+    float *tscale = reinterpret_cast<float *>(out + LIMBS * (int64_t)k);
+    float *tsum = tscale + k / GROUP;
+    stage_group<GROUP, LIMBS>(v, i, plane, k >> 2, tscale, tsum);
 }
 
 template <int LIMBS>

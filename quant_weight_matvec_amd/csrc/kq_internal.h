@@ -24,12 +24,26 @@ void set_shape_override(int qtype, MatvecShape s);
 MatvecShape get_shape_override(int qtype);
 
 // Each launcher assumes the arguments were validated by the ABI shim.
-hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                             const float *silu_gate, hipStream_t stream);
-hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *mid,
-                              int n_rows, int k, hipStream_t stream);
-hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                             hipStream_t stream);
+// The matvec launchers take the activation either as f32 (x) or in the staged
+// form (xs, non-null: copied into LDS instead of encoded).
+hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, const float *silu_gate, hipStream_t stream);
+// The previous layer's dual-eps tail, run in the gate+up kernel's prologue in
+// place of a given input (k = the tail's row width).
+struct TailArgs {
+    const float *res_in, *proj, *g_post, *g_next;
+    float *res_out, *x_out;  // x_out nullable
+    float eps_post, eps_next;
+};
+// mid_s (nullable): also write mid staged with scale groups of mid_group (16 or 32).
+// tail (nullable): compute x as that tail (x and xs are then unused).
+hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x,
+                              const uint8_t *xs, float *mid, uint8_t *mid_s, int mid_group,
+                              int n_rows, int k, const TailArgs *tail, hipStream_t stream);
+hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, hipStream_t stream);
+// staged form of x with scale groups of `group` (16 or 32)
+hipError_t launch_stage(const float *x, uint8_t *xs, int k, int group, hipStream_t stream);
 // In-order LDS-streaming matvec (kq_stream.hip).  matvec_impl(qtype): 0 =
 // register-ring kernels of kq_kernels.hip, 1 = LDS stream (Q4_K).
 int matvec_impl(int qtype);
@@ -44,9 +58,11 @@ size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream);
+// xs_out (nullable): also write next_in staged, groups of xs_group, per row
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
-                       float eps_post, float eps_next, hipStream_t stream);
+                       float eps_post, float eps_next, uint8_t *xs_out, int xs_group,
+                       hipStream_t stream);
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
                              hipStream_t stream);

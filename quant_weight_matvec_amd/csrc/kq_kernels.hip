@@ -38,9 +38,55 @@ namespace {
 
 using namespace kqd;
 
+// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
+// b mod 8).  Row ranges follow the logical index this returns, so that each
+// XCD owns one contiguous eighth of the ranges: when the ranges differ in size
+// (whole scale groups per workgroup), every XCD gets the same mix of large
+// and small ones instead of one XCD getting all the small ones.
+__device__ __forceinline__ int xcd_block()
+{
+    const int g = gridDim.x, b = blockIdx.x;
+    return (g & 7) ? b : (b & 7) * (g >> 3) + (b >> 3);
+}
+
 // float4 of x per thread loaded ahead of the weights, times the waves per
 // workgroup: 80 / WMAX float4 per thread cover k = 20480 in one round trip.
 constexpr int kXPre = 80;
+
+// The dual-eps tail in registers: up to kTailVec float4 per thread, whole
+// waves, rows up to kTailRegMax wide.  tail_threads(n) is the block size of
+// the standalone tail; the fused form (q4k_gate_up_kernel with TAIL) lays its
+// threads out the same way so that both sum in the same order.
+constexpr int kTailVec = 4;
+constexpr int kTailThreads = 512;
+constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
+
+__host__ __device__ constexpr int tail_threads(int n)
+{
+    return (((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64)) * 64 > 64
+               ? (((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64)) * 64
+               : 64;
+}
+
+// r + rms-normed p times the post gain, and the next input, one float4 each
+__device__ __forceinline__ f32x4 tail_add(f32x4 r, f32x4 p, float inv_p, f32x4 g)
+{
+    return r + (p * inv_p) * g;
+}
+
+__device__ __forceinline__ f32x4 tail_next(f32x4 r, float inv_r, f32x4 g)
+{
+    return (r * inv_r) * g;
+}
+
+// The previous layer's tail, fused into the gate+up kernel's prologue
+// (Ch 10 "The forward pass at a glance", section 10.3: the tail's second
+// output is the next layer's input).
+struct TailIn {
+    const float *res_in, *proj, *g_post, *g_next;
+    float *res_out, *x_out;  // written by workgroup 0; x_out may be null
+    float eps_post, eps_next;
+};
 
 // One wave holds RPT = 64/LANES rows; lane `sub` of a row takes units sub,
 // sub+LANES, ...  Each lane keeps DEPTH units of look-ahead in flight: the
@@ -50,6 +96,7 @@ constexpr int kXPre = 80;
 template <int LANES, int LIMBS, int DEPTH, int WMAX, bool SILU>
 __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__restrict__ W,
                                                                const float *__restrict__ x,
+                                                               const uint8_t *__restrict__ xs,
                                                                float *__restrict__ y,
                                                                const float *__restrict__ gate,
                                                                int n_rows, int k)
@@ -58,8 +105,9 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ4Bytes;
-    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
-    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
+    const int bl = xcd_block();
+    const int r_lo = (int)((int64_t)bl * n_rows / gridDim.x);
+    const int r_hi = (int)((int64_t)(bl + 1) * n_rows / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -67,7 +115,8 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     const int sub = lane % LANES;
     const int h = sub & 1;  // LANES is even: a lane always takes the same half
     const int steps = (units + LANES - 1) / LANES;
-    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
+    const XPre<kXPre / WMAX> xpre =  // ahead of any weight load
+        x_preload<kXPre / WMAX>(xs ? (const void *)xs : (const void *)x, x_pieces<32, LIMBS>(xs, k));
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
@@ -89,7 +138,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    stage_activation<32, LIMBS>(xpre, x, k, smem);
+    stage_activation<32, LIMBS>(xpre, x, xs, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -149,28 +198,75 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
 // activation staging, one launch) and store mid = silu(gate x) * (up x)
 // (Ch 10 "The forward pass at a glance", section 10.3: gate and up read the
 // same normed input; the SiLU product follows them).
-template <int LANES, int LIMBS, int DEPTH, int WMAX>
+//
+// With TAIL the input is not given: every workgroup first runs the previous
+// layer's dual-eps tail on (tl.res_in, tl.proj) itself, in the thread layout
+// and summation order of the standalone tail (so its values are bit for bit
+// the standalone tail's), and encodes the result straight into LDS; workgroup
+// 0 also stores the post-add residual (tl.res_out) and next_in (tl.x_out).
+template <int LANES, int LIMBS, int DEPTH, int WMAX, bool TAIL>
 __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *__restrict__ Wg,
                                                                 const uint8_t *__restrict__ Wu,
                                                                 const float *__restrict__ x,
+                                                                const uint8_t *__restrict__ xs,
                                                                 float *__restrict__ mid,
-                                                                int n_rows, int k)
+                                                                uint8_t *__restrict__ mid_s,
+                                                                int mid_group, int n_rows, int k,
+                                                                TailIn tl)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ float red[16];
     const int nsb = k >> 8;
     const int units = 2 * nsb;      // half-superblock units per row
     const int units2 = 2 * units;   // gate units, then up units
     const int64_t row_bytes = (int64_t)nsb * kQ4Bytes;
-    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
-    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
+    // With a staged mid output every workgroup owns whole scale groups of
+    // mid_group rows (it encodes them itself); otherwise an even row split.
+    const int rg = mid_s ? mid_group : 1;
+    const int ngr = n_rows / rg;
+    const int bl = xcd_block();
+    const int r_lo = rg * (int)((int64_t)bl * ngr / gridDim.x);
+    const int r_hi = rg * (int)((int64_t)(bl + 1) * ngr / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     constexpr int RPT = 64 / LANES;
     const int sub = lane % LANES;
     const int h = sub & 1;  // LANES and units are even: a lane always takes the same half
+    float *midl = reinterpret_cast<float *>(smem + staged_bytes<32, LIMBS>(k));  // this group's mid
     const int steps = (units2 + LANES - 1) / LANES;
-    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
+    // the activation (or the tail's operands) ahead of any weight load
+    XPre<TAIL ? 1 : kXPre / WMAX> xpre;
+    const int tt = tail_threads(k), n4 = k >> 2;
+    const int tid = threadIdx.x;
+    f32x4 tp[kTailVec], tr[kTailVec], tg[kTailVec], tn[kTailVec];
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (TAIL) {
+        // Only the waves of the standalone tail's layout load (a wave-uniform
+        // branch); within them the loads are unconditional (index clamped into
+        // the row; slots outside the layout are zeroed at first use), p first:
+        // the first sum needs only p.
+        if (tid < tt) {
+#pragma unroll
+            for (int j = 0; j < kTailVec; ++j)
+                tp[j] = reinterpret_cast<const f32x4 *>(tl.proj)[min(tid + j * tt, n4 - 1)];
+#pragma unroll
+            for (int j = 0; j < kTailVec; ++j)
+                tr[j] = reinterpret_cast<const f32x4 *>(tl.res_in)[min(tid + j * tt, n4 - 1)];
+#pragma unroll
+            for (int j = 0; j < kTailVec; ++j)
+                tg[j] = reinterpret_cast<const f32x4 *>(tl.g_post)[min(tid + j * tt, n4 - 1)];
+#pragma unroll
+            for (int j = 0; j < kTailVec; ++j)
+                tn[j] = reinterpret_cast<const f32x4 *>(tl.g_next)[min(tid + j * tt, n4 - 1)];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kTailVec; ++j) tp[j] = tr[j] = tg[j] = tn[j] = z;
+        }
+    } else {
+        xpre = x_preload<kXPre / WMAX>(xs ? (const void *)xs : (const void *)x,
+                                       x_pieces<32, LIMBS>(xs, k));
+    }
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
@@ -186,13 +282,61 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
     };
     constexpr int R = DEPTH + 1;
     Q4Unit ring[R];
+    auto ring_prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
-        ring[j] = load(j);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
+            ring[j] = load(j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // the first weight loads go out before the activation staging; with TAIL
+    // once the tail's operands are in (issued earlier, they delay the tail's
+    // first-touch reads behind the whole chip's weight requests)
+    if constexpr (!TAIL) ring_prologue();
 
-    stage_activation<32, LIMBS>(xpre, x, k, smem);
+    if constexpr (TAIL) {
+        // the standalone tail's arithmetic, in its order; threads past its
+        // block add exact zeros to the (non-negative) sums
+        const float inv_n = 1.0f / (float)k;
+#pragma unroll
+        for (int j = 0; j < kTailVec; ++j) {
+            const bool ok = tid < tt && tid + j * tt < n4;
+            tp[j] = ok ? tp[j] : z;
+            tr[j] = ok ? tr[j] : z;
+            tg[j] = ok ? tg[j] : z;
+            tn[j] = ok ? tn[j] : z;
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kTailVec; ++j) ss += sumsq4(tp[j]);
+        ss = block_sum_fixed(ss, red);
+        const float inv_p = rsqrtf(ss * inv_n + tl.eps_post);
+        float sr = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kTailVec; ++j) {
+            const int i = tid + j * tt;
+            tr[j] = tail_add(tr[j], tp[j], inv_p, tg[j]);
+            if (blockIdx.x == 0 && tid < tt && i < n4)
+                reinterpret_cast<f32x4 *>(tl.res_out)[i] = tr[j];
+            sr += sumsq4(tr[j]);
+        }
+        sr = block_sum_fixed(sr, red);
+        ring_prologue();
+        const float inv_r = rsqrtf(sr * inv_n + tl.eps_next);
+        uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
+        float *tsc = reinterpret_cast<float *>(smem + LIMBS * k);
+#pragma unroll
+        for (int j = 0; j < kTailVec; ++j) {
+            const int i = tid + j * tt;
+            if (tid < tt && i < n4) {  // whole scale groups of lanes
+                const f32x4 o = tail_next(tr[j], inv_r, tn[j]);
+                if (blockIdx.x == 0 && tl.x_out) reinterpret_cast<f32x4 *>(tl.x_out)[i] = o;
+                stage_group<32, LIMBS>(o, i, plane, n4, tsc, tsc + (k >> 5));
+            }
+        }
+    } else {
+        stage_activation<32, LIMBS>(xpre, x, xs, k, smem);
+    }
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -224,7 +368,11 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
             if (s0 + j < steps) step(j, s0 + j, false);
         acc_g = lane_group_sum<LANES>(acc_g);
         acc_u = lane_group_sum<LANES>(acc_u);
-        if (sub == 0 && rv) mid[r] = (acc_g / (1.0f + __expf(-acc_g))) * acc_u;
+        if (sub == 0 && rv) {
+            const float m = (acc_g / (1.0f + __expf(-acc_g))) * acc_u;
+            mid[r] = m;
+            if (mid_s) midl[r - r_lo] = m;
+        }
         t0 += nwaves * RPT;
         r = t0 + lane / LANES;
         rv = r < r_hi;
@@ -238,11 +386,26 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
             }
         }
     }
+    if (mid_s) {
+        // staged form of this workgroup's rows of mid for the next matvec:
+        // consecutive lanes hold consecutive float4, whole groups of lanes
+        __syncthreads();
+        const int n4w = (r_hi - r_lo) >> 2;
+        for (int t = threadIdx.x; t < n4w; t += blockDim.x) {
+            const f32x4 v = reinterpret_cast<const f32x4 *>(midl)[t];
+            const int i = (r_lo >> 2) + t;
+            if (mid_group == 16)
+                stage_group_global<16, LIMBS>(v, i, mid_s, n_rows);
+            else
+                stage_group_global<32, LIMBS>(v, i, mid_s, n_rows);
+        }
+    }
 }
 
 template <int LANES, int LIMBS, int DEPTH, int WMAX>
 __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__restrict__ W,
                                                                const float *__restrict__ x,
+                                                               const uint8_t *__restrict__ xs,
                                                                float *__restrict__ y, int n_rows,
                                                                int k)
 {
@@ -250,8 +413,9 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ6Bytes;
-    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
-    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
+    const int bl = xcd_block();
+    const int r_lo = (int)((int64_t)bl * n_rows / gridDim.x);
+    const int r_hi = (int)((int64_t)(bl + 1) * n_rows / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -259,7 +423,8 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     const int sub = lane % LANES;
     const int h = sub & 1;
     const int steps = (units + LANES - 1) / LANES;
-    const XPre<kXPre / WMAX> xpre = x_preload<kXPre / WMAX>(x, k);  // ahead of any weight load
+    const XPre<kXPre / WMAX> xpre =  // ahead of any weight load
+        x_preload<kXPre / WMAX>(xs ? (const void *)xs : (const void *)x, x_pieces<16, LIMBS>(xs, k));
 
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
@@ -278,7 +443,7 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    stage_activation<16, LIMBS>(xpre, x, k, smem);
+    stage_activation<16, LIMBS>(xpre, x, xs, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
     const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
@@ -322,6 +487,36 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     }
 }
 
+// Staged form of a plain activation vector (the encoding the matvec kernels
+// otherwise apply per workgroup), for callers that hand the same x to several
+// matvecs.  One float4 per thread; k is a multiple of 256, so the blocks hold
+// whole scale groups.
+template <int GROUP>
+__global__ __launch_bounds__(256) void stage_kernel(const float *__restrict__ x,
+                                                    uint8_t *__restrict__ xs, int k)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < (k >> 2))
+        stage_group_global<GROUP, KQ_LIMBS>(reinterpret_cast<const f32x4 *>(x)[i], i, xs, k);
+}
+
+// Staged output of the tail (the next layer's input in the form its matvec
+// consumes; groups of 32 for Q4_K, 16 for Q6_K).  Callers pass whole groups
+// of consecutive lanes: n is a multiple of the group, the block a multiple of
+// 64 threads.
+__device__ __forceinline__ int64_t tail_staged_bytes(int n, int group)
+{
+    return group == 16 ? staged_bytes<16, KQ_LIMBS>(n) : staged_bytes<32, KQ_LIMBS>(n);
+}
+
+__device__ __forceinline__ void stage_tail_out(f32x4 o, int i, uint8_t *xs, int n, int group)
+{
+    if (group == 16)
+        stage_group_global<16, KQ_LIMBS>(o, i, xs, n);
+    else
+        stage_group_global<32, KQ_LIMBS>(o, i, xs, n);
+}
+
 // ---------------------------------------------------------------------------
 // Fused dual-epsilon tail: one workgroup per row, float4 slots strided over
 // the threads.  Three passes as the operation is defined: the sum of squares
@@ -336,7 +531,8 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
                                                     float *__restrict__ next_in,
                                                     const float *__restrict__ g_post,
                                                     const float *__restrict__ g_next, int n,
-                                                    float eps_post, float eps_next)
+                                                    float eps_post, float eps_next,
+                                                    uint8_t *__restrict__ xs_out, int xs_group)
 {
     __shared__ float red[16];
     const int64_t off = (int64_t)blockIdx.x * n;
@@ -362,21 +558,23 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
     sr = block_sum_fixed(sr, red);
     const float inv_r = rsqrtf(sr * inv_n + eps_next);
 
-    for (int i = threadIdx.x; i < n4; i += blockDim.x) o4[i] = (r4[i] * inv_r) * gn4[i];
+    uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+        const f32x4 o = (r4[i] * inv_r) * gn4[i];
+        o4[i] = o;
+        if (xs) stage_tail_out(o, i, xs, n, xs_group);
+    }
 }
 
 // Register form of the tail for rows up to kTailRegMax wide: every operand is
 // loaded once, up front (one memory round trip instead of three); the post-add
 // residual is stored and the next norm uses the same f32 values that were
 // stored.  Same reduction order as tail_kernel.
-constexpr int kTailVec = 4;
-constexpr int kTailThreads = 512;
-constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
 
 __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
     float *__restrict__ residual, const float *__restrict__ projected, float *__restrict__ next_in,
     const float *__restrict__ g_post, const float *__restrict__ g_next, int n, float eps_post,
-    float eps_next)
+    float eps_next, uint8_t *__restrict__ xs_out, int xs_group)
 {
     __shared__ float red[kTailThreads / 64];
     const int64_t off = (int64_t)blockIdx.x * n;
@@ -409,16 +607,21 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
 #pragma unroll
     for (int j = 0; j < kTailVec; ++j) {
         const int i = threadIdx.x + j * blockDim.x;
-        rv[j] = rv[j] + (pv[j] * inv_p) * gp[j];
+        rv[j] = tail_add(rv[j], pv[j], inv_p, gp[j]);
         if (i < n4) r4[i] = rv[j];
         sr += sumsq4(rv[j]);
     }
     sr = block_sum_fixed(sr, red);
     const float inv_r = rsqrtf(sr * inv_n + eps_next);
+    uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
 #pragma unroll
     for (int j = 0; j < kTailVec; ++j) {
         const int i = threadIdx.x + j * blockDim.x;
-        if (i < n4) o4[i] = (rv[j] * inv_r) * gn[j];
+        if (i < n4) {
+            const f32x4 o = tail_next(rv[j], inv_r, gn[j]);
+            o4[i] = o;
+            if (xs) stage_tail_out(o, i, xs, n, xs_group);
+        }
     }
 }
 
@@ -532,34 +735,37 @@ kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k)
 }
 
 template <int LANES, int DEPTH, int WMAX>
-hipError_t launch_q4k_cfg(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                          const float *gate, kqi::MatvecShape s, hipStream_t stream)
+hipError_t launch_q4k_cfg(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                          int n_rows, int k, const float *gate, kqi::MatvecShape s,
+                          hipStream_t stream)
 {
     const size_t lds = staging_bytes<32>(k);
     hipError_t e;
     if (gate) {
         constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, true>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, gate,
-                           n_rows, k);
+        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y,
+                           gate, n_rows, k);
     } else {
         constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, false>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, gate,
-                           n_rows, k);
+        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y,
+                           gate, n_rows, k);
     }
     return hipGetLastError();
 }
 
 template <int LANES, int DEPTH, int WMAX>
-hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                          const float *, kqi::MatvecShape s, hipStream_t stream)
+hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                          int n_rows, int k, const float *, kqi::MatvecShape s,
+                          hipStream_t stream)
 {
     const size_t lds = staging_bytes<16>(k);
     constexpr auto kern = q6k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX>;
     hipError_t e = allow_lds<kern>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, y, n_rows, k);
+    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y, n_rows,
+                       k);
     return hipGetLastError();
 }
 
@@ -567,14 +773,15 @@ hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, float *y, int n_rows
 // in flight per lane 1..3 (look-ahead 0..2), and a workgroup-size class (up to 8 waves gets the 256-VGPR budget
 // of two waves per SIMD; up to 16 waves the 128-VGPR budget).
 template <template <int, int, int> class F>
-hipError_t dispatch_shape(kqi::MatvecShape s, const uint8_t *W, const float *x, float *y,
-                          int n_rows, int k, const float *gate, hipStream_t stream)
+hipError_t dispatch_shape(kqi::MatvecShape s, const uint8_t *W, const float *x,
+                          const uint8_t *xs, float *y, int n_rows, int k, const float *gate,
+                          hipStream_t stream)
 {
     const bool small = s.waves <= 8;
 #define KQ_CASE(L, D)                                                                        \
     if (s.lanes == L && s.depth == D)                                                        \
-        return small ? F<L, D - 1, 8>::go(W, x, y, n_rows, k, gate, s, stream)               \
-                     : F<L, D - 1, 16>::go(W, x, y, n_rows, k, gate, s, stream);
+        return small ? F<L, D - 1, 8>::go(W, x, xs, y, n_rows, k, gate, s, stream)           \
+                     : F<L, D - 1, 16>::go(W, x, xs, y, n_rows, k, gate, s, stream);
 #define KQ_CASES(L) KQ_CASE(L, 1) KQ_CASE(L, 2) KQ_CASE(L, 3)
     KQ_CASES(4) KQ_CASES(8) KQ_CASES(16) KQ_CASES(32) KQ_CASES(64)
 #undef KQ_CASES
@@ -582,34 +789,41 @@ hipError_t dispatch_shape(kqi::MatvecShape s, const uint8_t *W, const float *x, 
     return hipErrorInvalidValue;
 }
 
-template <int LANES, int DEPTH, int WMAX>
-hipError_t launch_gate_up_cfg(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *mid,
-                              int n_rows, int k, kqi::MatvecShape s, hipStream_t stream)
+template <int LANES, int DEPTH, int WMAX, bool TAIL>
+hipError_t launch_gate_up_cfg(const uint8_t *Wg, const uint8_t *Wu, const float *x,
+                              const uint8_t *xs, float *mid, uint8_t *mid_s, int mid_group,
+                              int n_rows, int k, const TailIn &tl, kqi::MatvecShape s,
+                              hipStream_t stream)
 {
-    const size_t lds = staging_bytes<32>(k);
-    constexpr auto kern = q4k_gate_up_kernel<LANES, KQ_LIMBS, DEPTH, WMAX>;
+    // staging, then (with a staged mid) the workgroup's rows of mid
+    size_t lds = staging_bytes<32>(k);
+    if (mid_s) {
+        const int ngr = n_rows / mid_group;
+        lds += sizeof(float) * (size_t)mid_group * (size_t)((ngr + s.grid - 1) / s.grid);
+    }
+    constexpr auto kern = q4k_gate_up_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, TAIL>;
     hipError_t e = allow_lds<kern>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, Wg, Wu, x, mid,
-                       n_rows, k);
+    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, Wg, Wu, x, xs, mid,
+                       mid_s, mid_group, n_rows, k, tl);
     return hipGetLastError();
 }
 
 template <int L, int D, int WM>
 struct Q4Launch {
-    static hipError_t go(const uint8_t *W, const float *x, float *y, int n, int k, const float *g,
-                         kqi::MatvecShape s, hipStream_t st)
+    static hipError_t go(const uint8_t *W, const float *x, const uint8_t *xs, float *y, int n,
+                         int k, const float *g, kqi::MatvecShape s, hipStream_t st)
     {
-        return launch_q4k_cfg<L, D, WM>(W, x, y, n, k, g, s, st);
+        return launch_q4k_cfg<L, D, WM>(W, x, xs, y, n, k, g, s, st);
     }
 };
 
 template <int L, int D, int WM>
 struct Q6Launch {
-    static hipError_t go(const uint8_t *W, const float *x, float *y, int n, int k, const float *g,
-                         kqi::MatvecShape s, hipStream_t st)
+    static hipError_t go(const uint8_t *W, const float *x, const uint8_t *xs, float *y, int n,
+                         int k, const float *g, kqi::MatvecShape s, hipStream_t st)
     {
-        return launch_q6k_cfg<L, D, WM>(W, x, y, n, k, g, s, st);
+        return launch_q6k_cfg<L, D, WM>(W, x, xs, y, n, k, g, s, st);
     }
 };
 
@@ -633,22 +847,23 @@ MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
     return resolve_shape(qtype, n_rows, (int)k);
 }
 
-hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                             const float *silu_gate, hipStream_t stream)
+hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, const float *silu_gate, hipStream_t stream)
 {
-    if (matvec_impl(1) == 1) {
+    if (matvec_impl(1) == 1 && !xs) {
         const int grid = device_cus();
         for (int nbuf = 7; nbuf >= 2; --nbuf)
             if (q4k_stream_lds(n_rows, k, grid, nbuf, nullptr, nullptr, nullptr, nullptr) <=
                 160 * 1024)
                 return launch_matvec_q4k_stream(W, x, y, n_rows, k, silu_gate, grid, nbuf, stream);
     }
-    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k), W, x, y, n_rows, k, silu_gate,
-                                    stream);
+    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k), W, x, xs, y, n_rows, k,
+                                    silu_gate, stream);
 }
 
-hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x, float *mid,
-                              int n_rows, int k, hipStream_t stream)
+hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x,
+                              const uint8_t *xs, float *mid, uint8_t *mid_s, int mid_group,
+                              int n_rows, int k, const TailArgs *tail, hipStream_t stream)
 {
     // Measured on MI355X at 19968 x 6656 (sweep of lanes 8/16, waves 8..16,
     // grid 1-2 per CU, depth 1-3): 8 lanes per row, one 12-wave workgroup per
@@ -660,11 +875,35 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
     if (o.waves) s.waves = o.waves;
     if (o.grid) s.grid = o.grid;
     if (o.depth) s.depth = o.depth;
+    if (mid_s && s.grid > n_rows / mid_group) s.grid = n_rows / mid_group;  // whole groups each
     const bool small = s.waves <= 8;
+    if (tail) {
+        // the fused tail runs on the first tail_threads(k) threads: 8 lanes per
+        // row (the measured best) and a workgroup at least that wide
+        if (s.lanes != 8 || 64 * s.waves < tail_threads(k)) return hipErrorInvalidValue;
+        const TailIn tl{tail->res_in, tail->proj, tail->g_post, tail->g_next,
+                        tail->res_out, tail->x_out, tail->eps_post, tail->eps_next};
+#define KQ_GT(D)                                                                              \
+        if (s.depth == D)                                                                     \
+            return small ? launch_gate_up_cfg<8, D - 1, 8, true>(Wg, Wu, x, xs, mid, mid_s,   \
+                                                                 mid_group, n_rows, k, tl, s, \
+                                                                 stream)                      \
+                         : launch_gate_up_cfg<8, D - 1, 16, true>(Wg, Wu, x, xs, mid, mid_s,  \
+                                                                  mid_group, n_rows, k, tl,   \
+                                                                  s, stream);
+        KQ_GT(1) KQ_GT(2) KQ_GT(3)
+#undef KQ_GT
+        return hipErrorInvalidValue;
+    }
+    const TailIn none{};
 #define KQ_GU(L, D)                                                                           \
     if (s.lanes == L && s.depth == D)                                                         \
-        return small ? launch_gate_up_cfg<L, D - 1, 8>(Wg, Wu, x, mid, n_rows, k, s, stream)  \
-                     : launch_gate_up_cfg<L, D - 1, 16>(Wg, Wu, x, mid, n_rows, k, s, stream);
+        return small ? launch_gate_up_cfg<L, D - 1, 8, false>(Wg, Wu, x, xs, mid, mid_s,      \
+                                                              mid_group, n_rows, k, none, s,  \
+                                                              stream)                         \
+                     : launch_gate_up_cfg<L, D - 1, 16, false>(Wg, Wu, x, xs, mid, mid_s,     \
+                                                               mid_group, n_rows, k, none, s, \
+                                                               stream);
 #define KQ_GUS(L) KQ_GU(L, 1) KQ_GU(L, 2) KQ_GU(L, 3)
     KQ_GUS(4) KQ_GUS(8) KQ_GUS(16) KQ_GUS(32) KQ_GUS(64)
 #undef KQ_GUS
@@ -672,24 +911,25 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                             hipStream_t stream)
+hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, hipStream_t stream)
 {
-    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k), W, x, y, n_rows, k, nullptr,
+    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k), W, x, xs, y, n_rows, k, nullptr,
                                     stream);
 }
 
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
-                       float eps_post, float eps_next, hipStream_t stream)
+                       float eps_post, float eps_next, uint8_t *xs_out, int xs_group,
+                       hipStream_t stream)
 {
     const int n4 = n >> 2;
     if (n <= kTailRegMax) {
         // up to kTailVec float4 slots per thread, whole waves
-        int threads = ((n4 + kTailVec * 64 - 1) / (kTailVec * 64)) * 64;
-        if (threads < 64) threads = 64;
+        const int threads = tail_threads(n);
         hipLaunchKernelGGL(tail_reg_kernel, dim3(rows), dim3(threads), 0, stream, residual,
-                           projected, next_in, g_post, g_next, n, eps_post, eps_next);
+                           projected, next_in, g_post, g_next, n, eps_post, eps_next, xs_out,
+                           xs_group);
         return hipGetLastError();
     }
     // wider rows: about 4 float4 slots per thread, between 1 and 16 waves
@@ -697,7 +937,18 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
     if (threads < 64) threads = 64;
     if (threads > 1024) threads = 1024;
     hipLaunchKernelGGL(tail_kernel, dim3(rows), dim3(threads), 0, stream, residual, projected,
-                       next_in, g_post, g_next, n, eps_post, eps_next);
+                       next_in, g_post, g_next, n, eps_post, eps_next, xs_out, xs_group);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage(const float *x, uint8_t *xs, int k, int group, hipStream_t stream)
+{
+    const int n4 = k >> 2;
+    const int grid = (n4 + 255) / 256;
+    if (group == 16)
+        hipLaunchKernelGGL(stage_kernel<16>, dim3(grid), dim3(256), 0, stream, x, xs, k);
+    else
+        hipLaunchKernelGGL(stage_kernel<32>, dim3(grid), dim3(256), 0, stream, x, xs, k);
     return hipGetLastError();
 }
 
@@ -711,7 +962,8 @@ hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int 
 
 const char *variant_names()
 {
-    return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1] q6k_matvec[lanes=4..64,limbs=3,depth=1..3] "
+    return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged] "
+           "gate_up[q4k, mid staged out: 0/16/32] "
            "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 128-row groups] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 

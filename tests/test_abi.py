@@ -134,6 +134,73 @@ def test_tail_validation():
     assert f(*ok[:5], 0, 6656, *ok[7:]) == B.KQ_OK                          # empty
 
 
+def test_staged_validation():
+    L = kq.lib()
+    # sizes: 3 byte limbs per input, then a scale and a sum per group (32 for Q4_K, 16 for Q6_K)
+    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q4K, 6656) == 3 * 6656 + 8 * 6656 // 32
+    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q6K, 19968) == 3 * 19968 + 8 * 19968 // 16
+    assert L.kq_staged_bytes(3, 1024) == B.KQ_ERR_SHAPE
+    assert L.kq_staged_bytes(1, 1000) == B.KQ_ERR_SHAPE
+    assert L.kq_staged_bytes(1, B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
+    XS = 0x600000
+    st = L.kq_stage_activation
+    assert st(3, X, XS, 1024, None) == B.KQ_ERR_SHAPE
+    assert st(1, None, XS, 1024, None) == B.KQ_ERR_NULL
+    assert st(1, X, XS, 1000, None) == B.KQ_ERR_SHAPE
+    assert st(1, X, XS + 8, 1024, None) == B.KQ_ERR_ALIGN
+    assert st(1, X, X + 1024, 1024, None) == B.KQ_ERR_ALIAS
+    mv = L.kq_matvec_staged
+    assert mv(3, W, XS, Y, 8, 1024, None, None) == B.KQ_ERR_SHAPE
+    assert mv(1, W, None, Y, 8, 1024, None, None) == B.KQ_ERR_NULL
+    assert mv(2, W, XS, Y, 8, 1024, G, None) == B.KQ_ERR_UNSUPPORTED    # no SiLU epilogue for Q6_K
+    assert mv(1, W + 4, XS, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN
+    assert mv(2, W + 2, XS, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN
+    assert mv(1, W, XS + 4, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN
+    assert mv(1, W, XS, XS + 64, 8, 1024, None, None) == B.KQ_ERR_ALIAS  # y inside xs
+    assert mv(1, W, XS, Y, 0, 1024, None, None) == B.KQ_OK
+    gu = L.kq_ffn_gate_up_q4k_staged
+    U, M, MS = 0x500000, 0x700000, 0x800000
+    assert gu(W, U, None, M, MS, 2, 512, 1024, None) == B.KQ_ERR_NULL
+    assert gu(W, U, XS, M, MS, 3, 512, 1024, None) == B.KQ_ERR_SHAPE     # mid_qtype
+    assert gu(W, U, XS, M, MS, 2, 500, 1024, None) == B.KQ_ERR_SHAPE     # staged mid: n_rows % 256
+    assert gu(W, U, XS, M, MS + 8, 2, 512, 1024, None) == B.KQ_ERR_ALIGN
+    assert gu(W, U, XS, M, M + 16, 2, 512, 1024, None) == B.KQ_ERR_ALIAS  # mid_s on mid
+    assert gu(W, U, XS, XS + 16, None, 0, 8, 1024, None) == B.KQ_ERR_ALIAS  # mid inside xs
+    assert gu(W, U, XS, M, None, 0, 0, 1024, None) == B.KQ_OK
+    tl = L.kq_fused_residual_norm_staged
+    R, P, O, GP, GN, OS = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x900000
+    e = (C.c_float(1e-8), C.c_float(1e-5), None)
+    assert tl(R, P, O, None, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_NULL
+    assert tl(R, P, O, OS, 3, GP, GN, 1, 6656, *e) == B.KQ_ERR_SHAPE
+    assert tl(R, P, O, OS, 1, GP, GN, 1, 6660, *e) == B.KQ_ERR_SHAPE      # n % 256
+    assert tl(R, P, O, OS + 4, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_ALIGN
+    assert tl(R, P, O, O + 64, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_ALIAS  # staged on next_in
+    assert tl(R, P, O, OS, 1, GP, GN, 0, 6656, *e) == B.KQ_OK
+
+
+def test_tail_gate_up_validation():
+    f = kq.lib().kq_ffn_tail_gate_up_q4k
+    R, P, GP, GN, RO, XO = 0x100000, 0x110000, 0x120000, 0x130000, 0x140000, 0x150000
+    WG, WU, M, MS = 0x1000000, 0x2000000, 0x3000000, 0x3100000
+    e = (C.c_float(1e-8), C.c_float(1e-5), None)
+    ok = (R, P, GP, GN, RO, XO, WG, WU, M, MS, 2, 512, 1024)
+    a = lambda *v: f(*v, *e)
+    assert a(None, *ok[1:]) == B.KQ_ERR_NULL
+    assert a(*ok[:4], None, *ok[5:]) == B.KQ_ERR_NULL                  # residual_out
+    assert a(*ok[:11], 0, 1024) == B.KQ_ERR_SHAPE                      # n_rows 0
+    assert a(*ok[:11], 500, 1024) == B.KQ_ERR_SHAPE                    # staged mid: n_rows % 256
+    assert a(*ok[:10], 3, 512, 1024) == B.KQ_ERR_SHAPE                 # mid_qtype
+    assert a(*ok[:12], 1000) == B.KQ_ERR_SHAPE
+    assert a(*ok[:12], 8448) == B.KQ_ERR_UNSUPPORTED                   # k > KQ_MAX_FUSED_TAIL_K
+    assert f(*ok, C.c_float(-1.0), C.c_float(1e-5), None) == B.KQ_ERR_SHAPE
+    assert a(R + 4, *ok[1:]) == B.KQ_ERR_ALIGN
+    assert a(*ok[:5], XO + 8, *ok[6:]) == B.KQ_ERR_ALIGN               # next_in
+    assert a(*ok[:4], R, *ok[5:]) == B.KQ_ERR_ALIAS                    # residual_out on residual_in
+    assert a(*ok[:5], RO + 16, *ok[6:]) == B.KQ_ERR_ALIAS              # next_in on residual_out
+    assert a(*ok[:8], WG + 64, *ok[9:]) == B.KQ_ERR_ALIAS              # mid inside W_gate
+    assert a(*ok[:9], M + 16, *ok[10:]) == B.KQ_ERR_ALIAS              # mid_s on mid
+
+
 def test_tune_validation():
     with pytest.raises(kq.KQError):
         kq.kq_tune_set_shape(1, lanes=12)
