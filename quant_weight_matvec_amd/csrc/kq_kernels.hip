@@ -38,17 +38,6 @@ namespace {
 
 using namespace kqd;
 
-// Workgroups are dealt round-robin to the 8 XCDs (workgroup b runs on XCD
-// b mod 8).  Row ranges follow the logical index this returns, so that each
-// XCD owns one contiguous eighth of the ranges: when the ranges differ in size
-// (whole scale groups per workgroup), every XCD gets the same mix of large
-// and small ones instead of one XCD getting all the small ones.
-__device__ __forceinline__ int xcd_block()
-{
-    const int g = gridDim.x, b = blockIdx.x;
-    return (g & 7) ? b : (b & 7) * (g >> 3) + (b >> 3);
-}
-
 // float4 of x per thread loaded ahead of the weights, times the waves per
 // workgroup: 80 / WMAX float4 per thread cover k = 20480 in one round trip.
 constexpr int kXPre = 80;
@@ -105,9 +94,8 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ4Bytes;
-    const int bl = xcd_block();
-    const int r_lo = (int)((int64_t)bl * n_rows / gridDim.x);
-    const int r_hi = (int)((int64_t)(bl + 1) * n_rows / gridDim.x);
+    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
+    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -224,9 +212,8 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
     // mid_group rows (it encodes them itself); otherwise an even row split.
     const int rg = mid_s ? mid_group : 1;
     const int ngr = n_rows / rg;
-    const int bl = xcd_block();
-    const int r_lo = rg * (int)((int64_t)bl * ngr / gridDim.x);
-    const int r_hi = rg * (int)((int64_t)(bl + 1) * ngr / gridDim.x);
+    const int r_lo = rg * (int)((int64_t)blockIdx.x * ngr / gridDim.x);
+    const int r_hi = rg * (int)((int64_t)(blockIdx.x + 1) * ngr / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
@@ -413,9 +400,8 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     const int nsb = k >> 8;
     const int units = 2 * nsb;
     const int64_t row_bytes = (int64_t)nsb * kQ6Bytes;
-    const int bl = xcd_block();
-    const int r_lo = (int)((int64_t)bl * n_rows / gridDim.x);
-    const int r_hi = (int)((int64_t)(bl + 1) * n_rows / gridDim.x);
+    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
+    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
