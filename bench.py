@@ -338,37 +338,56 @@ def read_ceiling(torch, kq, nbytes=4 << 30, reps=5):
     return nbytes / np.median(times) / 1e9
 
 
-def isolated_matvecs(torch, kq, I, reps=20):
-    """Single matvecs at the FFN shapes, rotating >= 1 GiB of weight copies so
-    the Infinity Cache cannot serve them; back-to-back launches timed per
-    launch with events on the launch stream."""
+def isolated_matvecs(torch, kq, I, reps=5):
+    """Single matvecs at the FFN shapes, each launch on a different one of
+    >= 1 GiB of weight copies so the Infinity Cache cannot serve them: a graph
+    of two launches per copy, replayed `reps` times between HIP events on the
+    replay stream; time per launch = elapsed / launches.  Each shape with x
+    in f32 (every workgroup encodes it) and with x staged beforehand (the form
+    the pass hands between launches)."""
     out = {}
     cases = [("q4k_19968x6656", "q4k", FFN, HIDDEN), ("q4k_6656x19968", "q4k", HIDDEN, FFN),
              ("q6k_6656x19968", "q6k", HIDDEN, FFN)]
     for name, qt, n, k in cases:
+        qtype = kq.KQ_QTYPE_Q4K if qt == "q4k" else kq.KQ_QTYPE_Q6K
         W = torch.from_numpy(I.weight_matrix(qt, n, k, stream=777)).cuda()
         ncopy = max(2, int(np.ceil((1 << 30) / W.numel())))
         copies = [W] + [W.clone() for _ in range(ncopy - 1)]
         x = torch.from_numpy(I.normal_f32(k, stream=778)).cuda()
+        xs = torch.empty(kq.kq_staged_bytes(qtype, k), dtype=torch.uint8, device="cuda")
+        kq.kq_stage_activation(qtype, x, xs, k)
         y = torch.empty(n, device="cuda")
         fn = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
-        for c in copies:
-            fn(c, x, y, n, k)
-        ev = EventLog(torch)
-        for r in range(reps):
-            c = copies[r % ncopy]
-            a, b = ev.pair()
-            a.record()
-            fn(c, x, y, n, k)
-            b.record()
-            ev.note(name, a, b)
-        us = ev.summary()[name]
-        nbytes = W.numel() + 4 * (n + k)
-        med = float(np.median(us))
-        out[name] = {"us_median": round(med, 3), "us_cv": round(float(np.std(us) / np.mean(us)), 4),
-                     "GBps": round(nbytes / med / 1e3, 1), "frac_peak": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
-                     "copies_rotated": ncopy, "bytes": nbytes,
-                     "shape": list(kq.kq_tune_get_shape(1 if qt == "q4k" else 2, n, k))}
+        for form, call, xbytes in (
+                ("", lambda c: fn(c, x, y, n, k), 4 * k),
+                ("_staged", lambda c: kq.kq_matvec_staged(qtype, c, xs, y, n, k), xs.numel())):
+            launches = 2 * ncopy
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s_):
+                for i in range(launches):
+                    call(copies[i % ncopy])
+            torch.cuda.synchronize()
+            g.replay()
+            times = []
+            for _ in range(reps):
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                ea.record()
+                g.replay()
+                eb.record()
+                torch.cuda.synchronize()
+                times.append(ea.elapsed_time(eb) * 1e3 / launches)
+            del g
+            us = float(np.mean(times))
+            nbytes = W.numel() + xbytes + 4 * n
+            out[name + form] = {"us_avg": round(us, 3), "us_cv": round(float(np.std(times) / us), 4),
+                                "GBps": round(nbytes / us / 1e3, 1),
+                                "frac_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                "copies_rotated": ncopy, "bytes": nbytes}
+            if not form:  # the automatic shape of the f32 form (the staged form may differ)
+                out[name]["shape"] = list(kq.kq_tune_get_shape(qtype, n, k))
         del copies, W
         torch.cuda.empty_cache()
     return out

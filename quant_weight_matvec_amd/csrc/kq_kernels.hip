@@ -668,24 +668,26 @@ int device_cus()
 // streams best with many waves (about 8+) and no look-ahead (depth 1); Q6_K,
 // whose 30-register units limit occupancy, streams best with a few waves per
 // CU each keeping 3 units in flight, which needs the 8-wave VGPR budget.
-kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus)
+kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, bool staged)
 {
     // Measured on MI355X (sweeps of lanes 8..32, waves 4..16, one or two
     // workgroups per CU, look-ahead 0..2 units):
     //   Q4_K 19968 x 6656: 8 lanes, 8 waves, 2 workgroups per CU, 1 unit ahead
-    //   Q4_K 6656 x 19968: 8 lanes, 16 waves, 1 workgroup per CU, 1 unit ahead
+    //   Q4_K 6656 x 19968: 8 lanes, 16 waves (x staged: 8), 1 workgroup per CU,
+    //                      1 unit ahead
     //   Q6_K 6656 x 19968: 8 lanes, 8 waves, 1 workgroup per CU, 1 unit ahead
     // 8 lanes per row keep a row's loads contiguous and the lane reduction to
-    // DPP moves.  Waves without rows still share the activation staging, so a
-    // long k takes the widest workgroup the registers allow (Q6_K's ring
-    // needs more than 128 VGPRs, which caps it at 8 waves).
+    // DPP moves.  Waves without rows still share the conversion of an f32 x,
+    // so a long k takes the widest workgroup the registers allow (Q6_K's ring
+    // needs more than 128 VGPRs, which caps it at 8 waves); a staged x is only
+    // copied, and then 8 waves are best.
     const bool q6 = qtype == 2;
     const int64_t tiles = (n_rows + 7) / 8;
     const int64_t k = 128 * (int64_t)units;
     const bool two_per_cu = !q6 && k <= 8192 && n_rows >= 32 * 2 * (int64_t)cus;
     const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
     const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
-    const int waves = q6 ? 8 : (two_per_cu ? 8 : 16);
+    const int waves = (q6 || two_per_cu || staged) ? 8 : 16;
     return kqi::MatvecShape{8, waves, grid, 2};
 }
 
@@ -709,9 +711,9 @@ size_t staging_bytes(int k)
     return (size_t)KQ_LIMBS * k + 2 * sizeof(float) * (size_t)(k / GROUP);
 }
 
-kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k)
+kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k, bool staged = false)
 {
-    kqi::MatvecShape s = choose_shape(qtype, n_rows, 2 * (k >> 8), device_cus());
+    kqi::MatvecShape s = choose_shape(qtype, n_rows, 2 * (k >> 8), device_cus(), staged);
     const kqi::MatvecShape o = g_override[qtype];
     if (o.lanes) s.lanes = o.lanes;
     if (o.waves) s.waves = o.waves;
@@ -843,7 +845,8 @@ hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs
                 160 * 1024)
                 return launch_matvec_q4k_stream(W, x, y, n_rows, k, silu_gate, grid, nbuf, stream);
     }
-    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k), W, x, xs, y, n_rows, k,
+    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k, xs != nullptr), W, x, xs, y,
+                                    n_rows, k,
                                     silu_gate, stream);
 }
 
@@ -900,7 +903,8 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
                              int n_rows, int k, hipStream_t stream)
 {
-    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k), W, x, xs, y, n_rows, k, nullptr,
+    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k, xs != nullptr), W, x, xs, y, n_rows,
+                                    k, nullptr,
                                     stream);
 }
 
@@ -950,7 +954,7 @@ const char *variant_names()
 {
     return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged] "
            "gate_up[q4k, mid staged out: 0/16/32] "
-           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 128-row groups] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
+           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups, 2 16-row tiles per wave] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

@@ -31,11 +31,11 @@
 //   itself in with an agent-scope atomic; the last to arrive sums the partials
 //   in workgroup order (deterministic for a given grid) and resets the counter.
 //   Nothing ever waits on another workgroup, so a launch always terminates.
-// * Activation staging.  The inputs of the superblocks a workgroup is about to
-//   use are staged in chunks into LDS (hi and lo planes, each 4-group of
-//   inputs stored in the order 0,2,1,3 to match how the quant bytes unpack into
-//   f16 pairs).  The weight loads of the next tiles are issued before a chunk
-//   is staged, so HBM keeps streaming.
+// * Activation staging.  A workgroup stages the inputs of every superblock its
+//   range touches into LDS once, before its loop (hi and lo planes, each
+//   4-group of inputs stored in the order 0,2,1,3 to match how the quant bytes
+//   unpack into f16 pairs); the grid is sized so that every range fits.  The
+//   first weight loads are issued before the staging, so HBM keeps streaming.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -55,6 +55,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Launch shape: waves per workgroup (one 16-row tile each), weight superblocks
@@ -63,17 +64,18 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define KQ_SM_WAVES 8
 #endif
 #ifndef KQ_SM_Q4_DEPTH
-#define KQ_SM_Q4_DEPTH 4
+#define KQ_SM_Q4_DEPTH 2
 #endif
 #ifndef KQ_SM_Q6_DEPTH
-#define KQ_SM_Q6_DEPTH 3
+#define KQ_SM_Q6_DEPTH 1
 #endif
 #ifndef KQ_SM_OCC
 #define KQ_SM_OCC 1
 #endif
 constexpr int kSmWaves = KQ_SM_WAVES;
 constexpr int kSmThreads = 64 * kSmWaves;
-constexpr int kSmRows = 16 * kSmWaves;  // rows per row group
+constexpr int kSub = 2;                        // 16-row sub-tiles per wave
+constexpr int kSmRows = 16 * kSub * kSmWaves;  // rows per row group
 constexpr uint32_t kBias = 0x64006400u;  // f16 1024.0 in both halves
 constexpr int kSmLdsMax = 160 * 1024;
 constexpr int kSmLdsBudget = kSmLdsMax / KQ_SM_OCC;  // per workgroup
@@ -150,7 +152,8 @@ constexpr int kQ6TileLds = 16 * kQ6RowLds;
 
 struct Q6Tile {
     u32x4 c[kQ6Loads];
-    uint32_t tail;
+    uint32_t t;  // bytes sb+206..209: the last two scales, then d
+    bool sh2;    // the superblock starts 2 bytes past a 4-byte boundary
 };
 
 template <typename U> struct TileTraits;
@@ -172,31 +175,32 @@ struct TileAddr {
 };
 
 template <typename U>
-__device__ __forceinline__ void tile_rows(TileAddr<U> &ta, int rg, int wave, int lane, int n_rows,
-                                          int64_t row_bytes, int rows_per_group)
+__device__ __forceinline__ void tile_rows(TileAddr<U> &ta, int rg, int slice, int lane, int n_rows,
+                                          int64_t row_bytes)
 {
     using T = TileTraits<U>;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
         const int slot = 64 * i + lane;
         const int tr = min(slot / T::kPieces, 15);
-        const int row = min(rg * rows_per_group + 16 * wave + tr, n_rows - 1);
+        const int row = min(rg * kSmRows + 16 * slice + tr, n_rows - 1);
         ta.row_off[i] = (int64_t)row * row_bytes;
     }
-    const int row = min(rg * rows_per_group + 16 * wave + (lane & 15), n_rows - 1);
+    const int row = min(rg * kSmRows + 16 * slice + (lane & 15), n_rows - 1);
     ta.tail_off = (int64_t)row * row_bytes;
 }
 
 __device__ __forceinline__ Q4Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q4Tile> &ta,
                                             int b, int lane)
 {
+    // Every lane loads (a lane past the tile's last piece re-reads that
+    // piece; store_tile drops it): no branch between the loads and their use.
     Q4Tile u;
 #pragma unroll
     for (int i = 0; i < kQ4Loads; ++i) {
-        const int slot = 64 * i + lane;
-        if (slot < kQ4Slots)
-            u.c[i] = *reinterpret_cast<const u32x4 *>(W + ta.row_off[i] + (int64_t)b * kQ4Bytes +
-                                                      16 * (slot % kQ4Pieces));
+        const int slot = min(64 * i + lane, kQ4Slots - 1);
+        u.c[i] = *reinterpret_cast<const u32x4 *>(W + ta.row_off[i] + (int64_t)b * kQ4Bytes +
+                                                  16 * (slot % kQ4Pieces));
     }
     return u;
 }
@@ -204,21 +208,22 @@ __device__ __forceinline__ Q4Tile load_tile(const uint8_t *__restrict__ W, const
 __device__ __forceinline__ Q6Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q6Tile> &ta,
                                             int b, int lane)
 {
+    // Unconditional loads, as for Q4_K.  The tail is one dword at sb+206
+    // (2-byte aligned, inside the superblock): the last two scales, needed
+    // when a = sb - 2 and already in the pieces when a = sb, then d.
+    // store_tile picks the word [a + 208, a + 212) the pieces would have
+    // continued with (not here: touching loaded data at load time would wait
+    // for the load at once).
     Q6Tile u;
 #pragma unroll
     for (int i = 0; i < kQ6Loads; ++i) {
-        const int slot = 64 * i + lane;
-        if (slot < kQ6Slots) {
-            const int64_t a = (ta.row_off[i] + (int64_t)b * kQ6Bytes) & ~(int64_t)3;
-            u.c[i] = *reinterpret_cast<const u32x4_a4 *>(W + a + 16 * (slot % kQ6Pieces));
-        }
+        const int slot = min(64 * i + lane, kQ6Slots - 1);
+        const int64_t a = (ta.row_off[i] + (int64_t)b * kQ6Bytes) & ~(int64_t)3;
+        u.c[i] = *reinterpret_cast<const u32x4_a4 *>(W + a + 16 * (slot % kQ6Pieces));
     }
-    if (lane < 16) {
-        const int64_t sb = ta.tail_off + (int64_t)b * kQ6Bytes;
-        const int64_t a = sb & ~(int64_t)3;
-        u.tail = (sb & 3) ? *reinterpret_cast<const uint32_t *>(W + a + 208)
-                          : (uint32_t) * reinterpret_cast<const uint16_t *>(W + a + 208);
-    }
+    const int64_t sb = ta.tail_off + (int64_t)b * kQ6Bytes;
+    u.t = *reinterpret_cast<const u32_a2 *>(W + sb + 206);
+    u.sh2 = (sb & 3) != 0;  // combined in store_tile, where the data is needed anyway
     return u;
 }
 
@@ -240,7 +245,9 @@ __device__ __forceinline__ void store_tile(const Q6Tile &u, uint8_t *tile, int l
             *reinterpret_cast<u32x4 *>(tile + kQ6RowLds * (slot / kQ6Pieces) +
                                        16 * (slot % kQ6Pieces)) = u.c[i];
     }
-    if (lane < 16) *reinterpret_cast<uint32_t *>(tile + kQ6RowLds * lane + 208) = u.tail;
+    if (lane < 16)
+        *reinterpret_cast<uint32_t *>(tile + kQ6RowLds * lane + 208) =
+            u.sh2 ? u.t : (u.t >> 16);
 }
 
 // What one lane needs of its row's superblock, read back from the LDS tile.
@@ -310,109 +317,141 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s, uint32_t vmask)
     return and_or(w >> s, vmask, kBias);
 }
 
-// Contribution of one Q4_K superblock to the lane's 4 outputs, in units of the
-// staged (scaled) activations.  `ah` points at the lane's activation row in the
-// hi plane at this superblock's first input + 8 kb; the lo plane is `lo_off`
-// bytes further.  `st` = group sums of the superblock at [s][m0..m0+3].
-__device__ __forceinline__ f32x4 sb_mma(const Q4Sb &u, const uint8_t *__restrict__ ah,
-                                        int lo_off, const float *__restrict__ st, uint32_t vmask)
+// Contribution of one Q4_K superblock of each of the wave's NS sub-tiles to the
+// lane's 4 outputs per sub-tile, in units of the staged (scaled) activations.
+// `ah` points at the lane's activation row in the hi plane at this
+// superblock's first input + 8 kb; the lo plane is `lo_off` bytes further.
+// `st` = group sums of the superblock at [s][m0..m0+3].  Every activation
+// operand and group sum read from LDS serves all NS sub-tiles.
+template <int NS>
+__device__ __forceinline__ void sb_mma(const Q4Sb (&u)[NS], const uint8_t *__restrict__ ah,
+                                       int lo_off, const float *__restrict__ st, uint32_t vmask,
+                                       f32x4 (&ys)[NS])
 {
-    const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
-    const uint32_t scA = S0 & 0x3F3F3F3Fu, mnA = S1 & 0x3F3F3F3Fu;
-    const uint32_t scB = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
-    const uint32_t mnB = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
-    const float d = half_lo(u.hdr.x), dmin = half_hi(u.hdr.x);
+    uint32_t scA[NS], mnA[NS], scB[NS], mnB[NS];
+    float d[NS], dmin[NS];
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+        const uint32_t S0 = u[h].hdr.y, S1 = u[h].hdr.z, S2 = u[h].hdr.w;
+        scA[h] = S0 & 0x3F3F3F3Fu;
+        mnA[h] = S1 & 0x3F3F3F3Fu;
+        scB[h] = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+        mnB[h] = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+        d[h] = half_lo(u[h].hdr.x);
+        dmin[h] = half_hi(u[h].hdr.x);
+        ys[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
     const h8 off = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
-    f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c0 = 0; c0 < 4; c0 += 2) {
         // sub-blocks 2c0 .. 2c0+3: all hi MFMAs, then all lo MFMAs
-        h8 B[4];
-        f32x4 acc[4];
+        h8 B[NS][4];
+        f32x4 acc[NS][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = c0 + (j >> 1), hn = j & 1, s = 2 * c + hn;
-            const uint32_t w0 = u.q[2 * c], w1 = u.q[2 * c + 1];
-            const u32x4 bq = {nib_pair(w0, 4 * hn, vmask), nib_pair(w0, 4 * hn + 8, vmask),
-                              nib_pair(w1, 4 * hn, vmask), nib_pair(w1, 4 * hn + 8, vmask)};
-            B[j] = as_h8(bq) - off;
             const h8 Ahi = *reinterpret_cast<const h8 *>(ah + 64 * s);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                Ahi, B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                const uint32_t w0 = u[h].q[2 * c], w1 = u[h].q[2 * c + 1];
+                const u32x4 bq = {nib_pair(w0, 4 * hn, vmask), nib_pair(w0, 4 * hn + 8, vmask),
+                                  nib_pair(w1, 4 * hn, vmask), nib_pair(w1, 4 * hn + 8, vmask)};
+                B[h][j] = as_h8(bq) - off;
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    Ahi, B[h][j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * (4 * (c0 >> 1) + j));
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B[j], acc[j], 0, 0, 0);
+            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * (2 * c0 + j));
+#pragma unroll
+            for (int h = 0; h < NS; ++h)
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B[h][j], acc[h][j], 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = 2 * c0 + j;
-            const uint32_t scw = s < 4 ? scA : scB, mnw = s < 4 ? mnA : mnB;
-            const float c1 = d * (float)((scw >> (8 * (s & 3))) & 0xFFu);
-            const float c2 = dmin * (float)((mnw >> (8 * (s & 3))) & 0xFFu);
             const f32x4 sm = *reinterpret_cast<const f32x4 *>(st + 16 * s);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ys[i] = fmaf(c1, acc[j][i], fmaf(-c2, sm[i], ys[i]));
+            for (int h = 0; h < NS; ++h) {
+                const uint32_t scw = s < 4 ? scA[h] : scB[h], mnw = s < 4 ? mnA[h] : mnB[h];
+                const float c1 = d[h] * (float)((scw >> (8 * (s & 3))) & 0xFFu);
+                const float c2 = dmin[h] * (float)((mnw >> (8 * (s & 3))) & 0xFFu);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ys[h][i] = fmaf(c1, acc[h][j][i], fmaf(-c2, sm[i], ys[h][i]));
+            }
         }
     }
-    return ys;
 }
 
-// One Q6_K superblock; `ah` = the lane's activation row at the superblock's
-// first input + 4 kb.
-__device__ __forceinline__ f32x4 sb_mma(const Q6Sb &u, const uint8_t *__restrict__ ah,
-                                        int lo_off, const float *__restrict__, uint32_t vmask)
+// The same for Q6_K superblocks; `ah` = the lane's activation row at the
+// superblock's first input + 4 kb.
+template <int NS>
+__device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__restrict__ ah,
+                                       int lo_off, const float *__restrict__, uint32_t vmask,
+                                       f32x4 (&ys)[NS])
 {
-    const int sh = u.sh;
-    uint32_t L[8], H[4];
+    uint32_t L[NS][8], H[NS][4], sc[NS][4];
+    float d[NS];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) L[i] = __builtin_amdgcn_alignbyte(u.w[2 * i + 1], u.w[2 * i], sh);
+    for (int h = 0; h < NS; ++h) {
+        const int sh = u[h].sh;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        H[i] = __builtin_amdgcn_alignbyte(u.w[17 + 2 * i], u.w[16 + 2 * i], sh);
-    uint32_t sc[4];
-    sc[0] = __builtin_amdgcn_alignbyte(u.hs.y, u.hs.x, sh);
-    sc[1] = __builtin_amdgcn_alignbyte(u.hs.z, u.hs.y, sh);
-    sc[2] = __builtin_amdgcn_alignbyte(u.hs.w, u.hs.z, sh);
-    sc[3] = __builtin_amdgcn_alignbyte(u.tail, u.hs.w, sh);
-    const float d = half_lo(sh ? (u.tail >> 16) : u.tail);
+        for (int i = 0; i < 8; ++i)
+            L[h][i] = __builtin_amdgcn_alignbyte(u[h].w[2 * i + 1], u[h].w[2 * i], sh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            H[h][i] = __builtin_amdgcn_alignbyte(u[h].w[17 + 2 * i], u[h].w[16 + 2 * i], sh);
+        sc[h][0] = __builtin_amdgcn_alignbyte(u[h].hs.y, u[h].hs.x, sh);
+        sc[h][1] = __builtin_amdgcn_alignbyte(u[h].hs.z, u[h].hs.y, sh);
+        sc[h][2] = __builtin_amdgcn_alignbyte(u[h].hs.w, u[h].hs.z, sh);
+        sc[h][3] = __builtin_amdgcn_alignbyte(u[h].tail, u[h].hs.w, sh);
+        d[h] = half_lo(sh ? (u[h].tail >> 16) : u[h].tail);
+        ys[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
     const h4 off = {1056, 1056, 1056, 1056};
-    f32x4 ys = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s0 = 0; s0 < 16; s0 += 4) {
         // four sub-blocks at a time: all hi MFMAs, then all lo MFMAs, so no
         // MFMA waits on the one just issued
-        h4 B[4];
-        f32x4 acc[4];
+        h4 B[NS][4];
+        f32x4 acc[NS][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = s0 + j;
-            const int h = s >> 3, g = (s >> 1) & 3, hf = s & 1;
-            const uint32_t l = L[4 * h + 2 * (g & 1) + hf], hh = H[2 * h + hf];
-            const uint32_t lo4 = (g < 2 ? l : (l >> 4)) & 0x0F0F0F0Fu;
-            const uint32_t q = lo4 | (((hh >> (2 * g)) & 0x03030303u) << 4);
-            const u32x2 bq = {and_or(q, vmask, kBias), and_or(q >> 8, vmask, kBias)};
-            B[j] = as_h4(bq) - off;
+            const int hv = s >> 3, g = (s >> 1) & 3, hf = s & 1;
             const h4 Ahi = *reinterpret_cast<const h4 *>(ah + 32 * s);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ahi, B[j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f},
-                                                           0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                const uint32_t l = L[h][4 * hv + 2 * (g & 1) + hf], hh = H[h][2 * hv + hf];
+                const uint32_t lo4 = (g < 2 ? l : (l >> 4)) & 0x0F0F0F0Fu;
+                const uint32_t q = lo4 | (((hh >> (2 * g)) & 0x03030303u) << 4);
+                const u32x2 bq = {and_or(q, vmask, kBias), and_or(q >> 8, vmask, kBias)};
+                B[h][j] = as_h4(bq) - off;
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                    Ahi, B[h][j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const h4 Alo = *reinterpret_cast<const h4 *>(ah + lo_off + 32 * (s0 + j));
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Alo, B[j], acc[j], 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NS; ++h)
+                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(Alo, B[h][j], acc[h][j], 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = s0 + j;
-            const int scv = ((int)(sc[s >> 2] << (24 - 8 * (s & 3)))) >> 24;
-            const float c1 = d * (float)scv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ys[i] = fmaf(c1, acc[j][i], ys[i]);
+            for (int h = 0; h < NS; ++h) {
+                const int scv = ((int)(sc[h][s >> 2] << (24 - 8 * (s & 3)))) >> 24;
+                const float c1 = d[h] * (float)scv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ys[h][i] = fmaf(c1, acc[h][j][i], ys[h][i]);
+            }
         }
     }
-    return ys;
 }
 
 template <typename U>
@@ -422,12 +461,13 @@ __device__ __forceinline__ constexpr bool is_q4()
 }
 
 // ---------------------------------------------------------------------------
-// Staging of the activations of superblocks [cb, cb + n) into LDS.
+// Staging of the activations of superblocks [cb, cb + n) into LDS slots so, so + 1, ...
 // LDS: hi plane [M][RS bytes], lo plane [M][RS bytes], etab [CH][16] int
 // (back-scale exponents), stab [CH][8][16] f32 (Q4_K: sums of 32-input groups,
 // scaled).  One wave converts one (row, superblock) group of 256 inputs.
 template <bool Q4>
-__device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem)
+__device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem,
+                                            int so = 0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int M = a.m, RS = a.RS;
@@ -472,17 +512,18 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
                 }
             }
             // inputs 4 lane .. 4 lane + 3 stored in the order 0, 2, 1, 3
-            const int boff = m * RS + 2 * (256 * bb + 4 * lane);
+            const int sbb = so + bb;  // LDS slot of this superblock
+            const int boff = m * RS + 2 * (256 * sbb + 4 * lane);
             const u32x2 ph = {__builtin_bit_cast(uint32_t, (h4){h[0], h[2], h[1], h[3]}.xy),
                               __builtin_bit_cast(uint32_t, (h4){h[0], h[2], h[1], h[3]}.zw)};
             const u32x2 pl = {__builtin_bit_cast(uint32_t, (h4){l[0], l[2], l[1], l[3]}.xy),
                               __builtin_bit_cast(uint32_t, (h4){l[0], l[2], l[1], l[3]}.zw)};
             *reinterpret_cast<u32x2 *>(hi + boff) = ph;
             *reinterpret_cast<u32x2 *>(lo + boff) = pl;
-            if (lane == 0) etab[16 * bb + m] = e - 15;
+            if (lane == 0) etab[16 * sbb + m] = e - 15;
             if constexpr (Q4) {
                 const float sm = group_sum<8>((s.x + s.y) + (s.z + s.w));
-                if ((lane & 7) == 0) stab[128 * bb + 16 * (lane >> 3) + m] = fin ? sm : __builtin_nanf("");
+                if ((lane & 7) == 0) stab[128 * sbb + 16 * (lane >> 3) + m] = fin ? sm : __builtin_nanf("");
             }
         }
     }
@@ -490,17 +531,23 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
 
 // This workgroup's share of row group rg is complete: store it, or publish it
 // as a partial tile and, if it is the last contributor, sum all of them.
+// The lane's outputs of sub-tile h are rows 16 (kSub wave + h) + r of the row
+// group, activation rows m0 .. m0 + 3.
 __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, int gh, int g,
-                                               f32x4 yacc, int wave, int r, int m0, int &last_flag)
+                                               const f32x4 (&yacc)[kSub], int wave, int r, int m0,
+                                               int &last_flag)
 {
     const int nb = a.nb, M = a.m;
     const int row0 = rg * kSmRows;
     if (gl == gh) {
-        const int row = row0 + 16 * wave + r;
-        if (row < a.n_rows) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (m0 + i < M) a.Y[(int64_t)(m0 + i) * a.ldy + row] = yacc[i];
+        for (int h = 0; h < kSub; ++h) {
+            const int row = row0 + 16 * (kSub * wave + h) + r;
+            if (row < a.n_rows) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (m0 + i < M) a.Y[(int64_t)(m0 + i) * a.ldy + row] = yacc[h][i];
+            }
         }
         return;
     }
@@ -509,7 +556,10 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
     const int slot = (first_tile(g, a.T, a.G) / nb == rg) ? 0 : 1;
     float *pp = part + (int64_t)(2 * g + slot) * (16 * kSmRows);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st_agent(pp + (m0 + i) * kSmRows + 16 * wave + r, yacc[i]);
+    for (int h = 0; h < kSub; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st_agent(pp + (m0 + i) * kSmRows + 16 * (kSub * wave + h) + r, yacc[h][i]);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -544,6 +594,17 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
     }
 }
 
+// A workgroup's range is at most one row of superblocks long, so it touches at
+// most two row groups (segments).
+constexpr int kMaxSegs = 2;
+
+// The workgroup stages the activations of every superblock its range touches
+// once, up front (the host sizes the grid so that they fit in LDS), and keeps
+// each segment's sums in registers until after the loop.  The steady-state
+// step then holds no memory operation besides the ring's own load, and the
+// compiler's waits count only the ring (a load, store or barrier under a
+// branch in the loop would make it wait for every load in flight at the next
+// merge).
 template <typename U, int DEPTH>
 __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_kernel(SmArgs a)
 {
@@ -567,31 +628,59 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
     uint32_t vmask;  // kept in a VGPR for v_and_or_b32
     asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(Q4 ? 0x000F000Fu : 0x00FF00FFu));
 
-    // next tile to load: row group rl, superblock bl
+    // next tile to load: row group rl, superblock bl; the wave's sub-tile h
+    // is slice kSub wave + h of the row group
     int rl = t0 / nb, bl = t0 - rl * nb;
-    TileAddr<U> ta;
-    tile_rows<U>(ta, rl, wave, lane, a.n_rows, row_bytes, kSmRows);
+    TileAddr<U> ta[kSub];
+#pragma unroll
+    for (int h = 0; h < kSub; ++h) tile_rows<U>(ta[h], rl, kSub * wave + h, lane, a.n_rows, row_bytes);
+    struct Tiles {
+        U t[kSub];
+    };
     auto load_next = [&]() {
-        const U u = load_tile(a.W, ta, bl, lane);
+        Tiles u;
+#pragma unroll
+        for (int h = 0; h < kSub; ++h) u.t[h] = load_tile(a.W, ta[h], bl, lane);
         if (++bl == nb) {
             bl = 0;
-            tile_rows<U>(ta, ++rl, wave, lane, a.n_rows, row_bytes, kSmRows);
+            ++rl;
+#pragma unroll
+            for (int h = 0; h < kSub; ++h)
+                tile_rows<U>(ta[h], rl, kSub * wave + h, lane, a.n_rows, row_bytes);
         }
         return u;
     };
 
-    U ring[DEPTH];
+    // ring of R = DEPTH + 1 tile sets, steps unrolled R times so every slot
+    // index is a constant: step j issues the loads DEPTH steps ahead into the
+    // slot freed by the previous step, then uses slot j.  Loads past the
+    // workgroup's last tile read clamped rows (tile_rows) and are never used.
+    constexpr int R = DEPTH + 1;
+    Tiles ring[R];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-        if (t0 + i < t1) ring[i] = load_next();
+    for (int i = 0; i < DEPTH; ++i) {
+        ring[i] = load_next();
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // tile being computed: row group rg, superblock b; `left` tiles remain in
-    // the staged chunk that starts at superblock cb
-    int t = t0, rg = t0 / nb, b = t0 - rg * nb, left = 0, cb = b;
-    // byte offset in W of this lane's own row (for the Q6_K alignment shift)
-    int64_t own_row = (int64_t)min(rg * kSmRows + 16 * wave + r, a.n_rows - 1) * row_bytes;
-    f32x4 yacc = {0.0f, 0.0f, 0.0f, 0.0f};
-    bool more = t0 < t1;
+    // tile being computed: row group rg, superblock b; the staged window
+    // starts at superblock cb
+    int t = t0, rg = t0 / nb, b = t0 - rg * nb;
+    const int cb = b;
+    // byte offsets in W of this lane's own rows (for the Q6_K alignment shift)
+    int64_t own_row[kSub];
+    auto set_rows = [&]() {
+#pragma unroll
+        for (int h = 0; h < kSub; ++h)
+            own_row[h] = (int64_t)min(rg * kSmRows + 16 * (kSub * wave + h) + r, a.n_rows - 1) *
+                         row_bytes;
+    };
+    set_rows();
+    f32x4 yacc[kSub];
+#pragma unroll
+    for (int h = 0; h < kSub; ++h) yacc[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 sy[kMaxSegs][kSub];  // finished segments' sums
+    int seg = 0;
     // Contributors of the first and last row group this workgroup touches;
     // every row group in between lies wholly inside [t0, t1).
     const int rg_first = t0 / nb, rg_last = (t1 - 1) / nb;
@@ -599,50 +688,82 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
     const int gh_first = owner(rg_first * nb + nb - 1, a.T, a.G);
     const int gl_last = owner(rg_last * nb, a.T, a.G);
     const int gh_last = owner(rg_last * nb + nb - 1, a.T, a.G);
-    while (more) {
+    // the window of superblocks cb, cb + 1, ... (mod nb) the range touches
+    if (t0 < t1) {
+        const int w = t1 - t0;  // at most nb
+        const int n1 = min(w, nb - cb);
+        stage_chunk<Q4>(a, cb, n1, xs);
+        if (w > n1) stage_chunk<Q4>(a, 0, w - n1, xs, n1);
+        __syncthreads();
+    }
+    // One step: compute the tiles in ring slot u.
+    auto step = [&](const Tiles &u) __attribute__((always_inline)) {
+        Sb sb[kSub];
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) {
-            if (left == 0) {
-                cb = b;
-                left = min(a.CH, min(nb - b, t1 - t));
-                __syncthreads();  // the previous chunk's LDS reads are done
-                stage_chunk<Q4>(a, cb, left, xs);
-                __syncthreads();
-            }
-            const U cur = ring[j];
-            if (t + DEPTH < t1) ring[j] = load_next();
+        for (int h = 0; h < kSub; ++h) {
             // The tile slot is private to this wave and LDS executes a wave's
             // accesses in order, so the previous tile's reads are done and
             // this tile's writes are visible to the reads below.
             __builtin_amdgcn_wave_barrier();
-            store_tile(cur, tile, lane);
+            store_tile(u.t[h], tile, lane);
             __builtin_amdgcn_wave_barrier();
-            const int sh = (int)((own_row + (int64_t)b * BLK) & 3);
-            const Sb sb = read_sb(tile + TT::kRowLds * r, kb, sh, (Sb *)nullptr);
-            const int bb = b - cb;
-            const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
-            const f32x4 ys = sb_mma(sb, ah, lo_off, stab + 128 * bb + m0, vmask);
-            const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
+            const int sh = (int)((own_row[h] + (int64_t)b * BLK) & 3);
+            sb[h] = read_sb(tile + TT::kRowLds * r, kb, sh, (Sb *)nullptr);
+        }
+        const int bb = b >= cb ? b - cb : b + nb - cb;  // LDS slot of superblock b
+        const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
+        f32x4 ys[kSub];
+        sb_mma<kSub>(sb, ah, lo_off, stab + 128 * bb + m0, vmask, ys);
+        const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) yacc[i] += ldexpf(ys[i], ex[i]);
-            ++t;
-            ++b;
-            --left;
-            if (b == nb || t == t1) {
-                const int gl = rg == rg_first ? gl_first : (rg == rg_last ? gl_last : g);
-                const int gh = rg == rg_first ? gh_first : (rg == rg_last ? gh_last : g);
-                finish_segment(a, rg, gl, gh, g, yacc, wave, r, m0, last_flag);
-                yacc = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-                if (b == nb) {
-                    b = 0;
-                    ++rg;
-                    own_row = (int64_t)min(rg * kSmRows + 16 * wave + r, a.n_rows - 1) * row_bytes;
-                }
+        for (int h = 0; h < kSub; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[h][i] += ldexpf(ys[h][i], ex[i]);
+        ++t;
+        ++b;
+        if (b == nb || t == t1) {
+            // registers only: a select per finished segment
+#pragma unroll
+            for (int q = 0; q < kMaxSegs; ++q)
+#pragma unroll
+                for (int h = 0; h < kSub; ++h) sy[q][h] = (q == seg) ? yacc[h] : sy[q][h];
+            ++seg;
+#pragma unroll
+            for (int h = 0; h < kSub; ++h) yacc[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            if (b == nb) {
+                b = 0;
+                ++rg;
+                set_rows();
             }
-            if (t == t1) {
-                more = false;
-                break;
-            }
+        }
+    };
+    // Whole rounds of R steps, with no exit inside a round: the loop's only
+    // way out is its latch, so the loads in flight there are the ring's own
+    // and the compiler waits in each step only for that step's tile.  The
+    // remaining rem < R tiles already sit in ring slots 0 .. rem - 1 (a step
+    // loads DEPTH = R - 1 tiles ahead), so the tail steps load nothing.
+    const int rounds = (t1 - t0) / R, rem = (t1 - t0) - R * rounds;
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            ring[(j + DEPTH) % R] = load_next();
+            __builtin_amdgcn_sched_barrier(0);
+            step(ring[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j)
+        if (j < rem) step(ring[j]);
+    // finish the segments in order (seg and the row groups are the same in
+    // every wave, so the barriers inside are reached by all)
+#pragma unroll
+    for (int q = 0; q < kMaxSegs; ++q) {
+        if (q < seg) {
+            const int rq = rg_first + q;
+            const int gl = rq == rg_first ? gl_first : gl_last;
+            const int gh = rq == rg_first ? gh_first : gh_last;
+            finish_segment(a, rq, gl, gh, g, sy[q], wave, r, m0, last_flag);
         }
     }
 }
@@ -673,14 +794,16 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
-    p.G = p.T < KQ_SM_OCC * sm_cus() ? p.T : KQ_SM_OCC * sm_cus();
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 512 : 0);  // LDS bytes per staged superblock
     p.xs_off = kSmWaves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
-    int ch = (kSmLdsBudget - p.xs_off - 16 - 32 * m) / per_sb;
-    const int seg = (p.T + p.G - 1) / p.G;  // longest range of a workgroup
-    if (ch > seg) ch = seg;
+    int ch = (kSmLdsBudget - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
     if (ch > p.nb) ch = p.nb;
     if (ch < 1) ch = 1;
+    // one workgroup per CU (times the occupancy), more when a range would
+    // not fit in LDS at once: every range is then at most ch <= nb tiles long
+    p.G = p.T < KQ_SM_OCC * sm_cus() ? p.T : KQ_SM_OCC * sm_cus();
+    if ((p.T + p.G - 1) / p.G > ch) p.G = (p.T + ch - 1) / ch;
+    ch = (p.T + p.G - 1) / p.G;  // the longest range
     p.CH = ch;
     p.RS = 512 * ch + 16;
     p.flag_off = p.xs_off + 2 * m * p.RS + 64 * ch + (qtype == 1 ? 512 * ch : 0);
@@ -741,16 +864,16 @@ hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int6
     a.flag_off = p.flag_off;
     a.xs_off = p.xs_off;
     hipError_t e;
-    if (qtype == 1) {
-        constexpr auto K = small_m_kernel<Q4Tile, KQ_SM_Q4_DEPTH>;
-        if ((e = allow_lds<K>()) != hipSuccess) return e;
-        hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);
-    } else {
-        constexpr auto K = small_m_kernel<Q6Tile, KQ_SM_Q6_DEPTH>;
-        if ((e = allow_lds<K>()) != hipSuccess) return e;
-        hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);
+#define KQ_SM_GO(U, D)                                                                         \
+    {                                                                                         \
+        constexpr auto K = small_m_kernel<U, D>;                                              \
+        if ((e = allow_lds<K>()) != hipSuccess) return e;                                     \
+        hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);                  \
+        return hipGetLastError();                                                             \
     }
-    return hipGetLastError();
+    if (qtype == 1) KQ_SM_GO(Q4Tile, KQ_SM_Q4_DEPTH)
+    KQ_SM_GO(Q6Tile, KQ_SM_Q6_DEPTH)
+#undef KQ_SM_GO
 }
 
 }  // namespace kqi
