@@ -58,7 +58,9 @@ GATE_UP_BYTES = 2 * q4k_bytes(FFN, HIDDEN) + 4 * HIDDEN + 4 * FFN
 
 
 def staged_bytes(group, k):
-    """Bytes of a staged activation: 3 byte limbs per input, a scale and a sum per group."""
+    """Algorithmic bytes of a staged activation: 3 byte limbs per input, a scale
+    and a sum per group (the 16 bytes of padding per 128 inputs in the stored
+    form are layout, not counted)."""
     return 3 * k + 8 * (k // group)
 
 

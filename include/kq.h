@@ -191,7 +191,9 @@ kq_status kq_fused_residual_norm(float *residual, const float *projected, float 
  * (Ch 19 "The down projection + residual", section 19.7): a matvec on a
  * staged vector returns bit for bit what it returns on the f32 vector the
  * stage was made from.  The layout is internal to this library: KQ_STAGED_LIMBS
- * byte planes of k bytes, then k/G f32 scales, then k/G f32 group sums.
+ * byte planes of k + k/8 bytes (the inputs in order, 16 bytes of padding after
+ * every 128, so that lanes reading units 128 inputs apart use different LDS
+ * banks), then k/G f32 scales, then k/G f32 group sums.
  *
  * kq_staged_bytes: bytes of the staged form of a k-vector for a consumer of
  * weight type qtype (KQ_QTYPE_Q4K or KQ_QTYPE_Q6K); k as for the matvecs.

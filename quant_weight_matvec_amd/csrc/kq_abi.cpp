@@ -198,7 +198,9 @@ static int staged_group(int qtype)
 
 static int64_t staged_size(int qtype, int64_t k)
 {
-    return KQ_STAGED_LIMBS * k + 8 * (k / staged_group(qtype));
+    // limb planes of k + k/8 bytes (16 bytes of padding per 128 inputs), then
+    // a scale and a sum per group
+    return KQ_STAGED_LIMBS * (k + k / 8) + 8 * (k / staged_group(qtype));
 }
 
 int64_t kq_staged_bytes(int qtype, int64_t k)

@@ -152,8 +152,9 @@ __device__ bool grid_barrier(uint32_t *ctl, uint32_t epoch, int *ok_lds)
 
 // Encode 4 consecutive values of a scale group (GROUP inputs) into the
 // down projection's staging format, in global memory: LIMBS byte planes of
-// ffn bytes, then ffn/GROUP back-scales, then ffn/GROUP group sums (the same
-// layout the matvec kernels build in LDS).
+// plane_bytes(ffn) bytes (16 bytes of padding after every 128 inputs), then
+// ffn/GROUP back-scales, then ffn/GROUP group sums (the same layout the
+// matvec kernels build in LDS).
 template <int GROUP>
 __device__ __forceinline__ void encode_group_global(f32x4 v, int i, uint32_t *enc, int ffn)
 {
@@ -182,10 +183,11 @@ __device__ __forceinline__ void encode_group_global(f32x4 v, int i, uint32_t *en
         pk[1] |= (uint32_t)(b & 255) << (8 * j);
         pk[2] |= (uint32_t)(c & 255) << (8 * j);
     }
+    const int pw = n4 + (n4 >> 3), wi = i + ((i >> 5) << 2);  // padded plane words
 #pragma unroll
-    for (int l = 0; l < KQ_LIMBS; ++l) st_agent(enc + l * n4 + i, pk[l]);
+    for (int l = 0; l < KQ_LIMBS; ++l) st_agent(enc + l * pw + wi, pk[l]);
     if ((i & (TPG - 1)) == 0) {
-        float *tscale = reinterpret_cast<float *>(enc + KQ_LIMBS * n4);
+        float *tscale = reinterpret_cast<float *>(enc + KQ_LIMBS * pw);
         float *tsum = tscale + ffn / GROUP;
         const int g = i / TPG;
         st_agent(tscale + g, isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf(""));
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(kChainThreads) void ffn_chain_kernel(ChainArgs a, i
         // ---------------- phase A: gate and up rows, mid for [ra, rb)
         {
             const uint8_t *planes = L.stage;
-            const float *tscale = reinterpret_cast<const float *>(L.stage + KQ_LIMBS * H);
+            const float *tscale = reinterpret_cast<const float *>(L.stage + KQ_LIMBS * plane_bytes(H));
             const float *tsum = tscale + (H >> 5);
             for (int tile = wave; tile < tiles_a; tile += kChainWaves) {
                 if (tile != wave) loadA_for(l, tile);
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(kChainThreads) void ffn_chain_kernel(ChainArgs a, i
         }
         // ---------------- phase B: copy the encoded mid, rows [pa, pb) of p
         {
-            const int enc16 = (KQ_LIMBS * F + 8 * (F / GD)) >> 4;
+            const int enc16 = (int)((KQ_LIMBS * plane_bytes(F) + 8 * (F / GD)) >> 4);
             const uint32_t enc_off = (uint32_t)((uint8_t *)a.enc - a.ws);
             u32x4 *dst = reinterpret_cast<u32x4 *>(L.stage);
             for (int i0 = threadIdx.x; i0 < enc16; i0 += 4 * kChainThreads) {
@@ -403,7 +405,7 @@ __global__ __launch_bounds__(kChainThreads) void ffn_chain_kernel(ChainArgs a, i
             }
             __syncthreads();
             const uint8_t *planes = L.stage;
-            const float *tscale = reinterpret_cast<const float *>(L.stage + KQ_LIMBS * F);
+            const float *tscale = reinterpret_cast<const float *>(L.stage + KQ_LIMBS * plane_bytes(F));
             const float *tsum = tscale + F / GD;
             for (int tile = wave; tile < tiles_b; tile += kChainWaves) {
                 if (tile != wave) loadB_for(l, tile);
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(kChainThreads) void ffn_chain_kernel(ChainArgs a, i
             sr = block_sum_fixed(sr, L.red);
             const float inv_r = rsqrtf(sr * inv_n + a.eps_next);
             uint32_t *plane = reinterpret_cast<uint32_t *>(L.stage);
-            float *tscale = reinterpret_cast<float *>(L.stage + KQ_LIMBS * H);
+            float *tscale = reinterpret_cast<float *>(L.stage + KQ_LIMBS * plane_bytes(H));
             float *tsum = tscale + (H >> 5);
             const bool last = l + 1 == a.layers;
             for (int i = threadIdx.x; i < h4; i += blockDim.x) {
@@ -503,8 +505,8 @@ __global__ __launch_bounds__(kChainThreads) void ffn_chain_kernel(ChainArgs a, i
 size_t chain_stage_bytes(int hidden, int ffn, int down_qt)
 {
     const int gd = down_qt == 2 ? 16 : 32;
-    const size_t sa = (size_t)KQ_LIMBS * hidden + 8 * (size_t)(hidden / 32);
-    const size_t sb = (size_t)KQ_LIMBS * ffn + 8 * (size_t)(ffn / gd);
+    const size_t sa = (size_t)KQ_LIMBS * plane_bytes(hidden) + 8 * (size_t)(hidden / 32);
+    const size_t sb = (size_t)KQ_LIMBS * plane_bytes(ffn) + 8 * (size_t)(ffn / gd);
     return ((sa > sb ? sa : sb) + 15) & ~(size_t)15;
 }
 
@@ -537,7 +539,7 @@ constexpr size_t kCtlBytes = ((size_t)4 * kCtlWords + 255) & ~(size_t)255;
 size_t chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype)
 {
     const int gd = down_qtype == 2 ? 16 : 32;
-    const size_t enc = (size_t)KQ_LIMBS * ffn + 8 * (size_t)(ffn / gd);
+    const size_t enc = (size_t)KQ_LIMBS * plane_bytes(ffn) + 8 * (size_t)(ffn / gd);
     return kCtlBytes + ((enc + 255) & ~(size_t)255) + (((size_t)hidden * 4 + 255) & ~(size_t)255);
 }
 
@@ -575,7 +577,7 @@ hipError_t launch_ffn_chain(const uint8_t *const *wg, const uint8_t *const *wu,
     const int stage = (int)chain_stage_bytes(hidden, ffn, down_qtype);
     const size_t lds = chain_lds_bytes(hidden, ffn, down_qtype, grid);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    const size_t enc = (size_t)KQ_LIMBS * ffn + 8 * (size_t)(ffn / gd);
+    const size_t enc = (size_t)KQ_LIMBS * plane_bytes(ffn) + 8 * (size_t)(ffn / gd);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     ChainArgs a;
     a.wg = wg;

@@ -81,8 +81,16 @@ __device__ __forceinline__ float group_sum(float v)
 
 // ---------------------------------------------------------------------------
 // Activation staging into LDS.
-// Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
-// then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
+// Layout: LIMBS byte planes (plane 0 = most significant limb) of plane_bytes(k)
+// bytes each, then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32
+// group sums.  A plane holds the inputs in order with 16 bytes of padding
+// after every 128: the lanes of a row read units 128 inputs apart, which
+// without the padding fall on the same LDS banks.
+__host__ __device__ constexpr int64_t plane_bytes(int64_t k) { return k + (k >> 3); }
+
+// Byte offset of input j within a plane.
+__host__ __device__ constexpr int plane_off(int j) { return j + ((j >> 7) << 4); }
+
 template <int GROUP, int LIMBS>
 __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict__ plane, int n4,
                                             float *__restrict__ tscale, float *__restrict__ tsum)
@@ -121,8 +129,10 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
         pk[0] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
         pk[1] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
     }
+    // word i holds inputs 4i..4i+3; a plane is n4 + n4/8 words
+    const int pw = n4 + (n4 >> 3), wi = i + ((i >> 5) << 2);
 #pragma unroll
-    for (int l = 0; l < LIMBS; ++l) plane[l * n4 + i] = pk[l];
+    for (int l = 0; l < LIMBS; ++l) plane[l * pw + wi] = pk[l];
     if ((i & (TPG - 1)) == 0) {
         const int g = i / TPG;
         tscale[g] = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
@@ -130,16 +140,14 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
     }
 }
 
-// Activation staging into LDS.
-// Layout: LIMBS byte planes of k bytes each (plane 0 = most significant limb),
-// then k/GROUP f32 back-scale factors 2^(e - QB), then k/GROUP f32 group sums.
+// Activation staging into LDS, in the layout above.
 // The same bytes in global memory are a "staged" activation: a producer
 // kernel that already holds the values writes them in this form once, and
 // every consumer workgroup copies them into LDS instead of encoding x again.
 template <int GROUP, int LIMBS>
 __host__ __device__ constexpr int64_t staged_bytes(int64_t k)
 {
-    return LIMBS * k + 2 * 4 * (k / GROUP);
+    return LIMBS * plane_bytes(k) + 2 * 4 * (k / GROUP);
 }
 
 // A kernel issues the first B 16-byte pieces of each thread's share of its
@@ -207,7 +215,7 @@ __device__ __forceinline__ void stage_activation(const XPre<B> &pre, const float
     }
     const int n4 = k >> 2;  // a multiple of 64: whole waves stay active
     uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
-    float *tscale = reinterpret_cast<float *>(smem + LIMBS * k);
+    float *tscale = reinterpret_cast<float *>(smem + LIMBS * plane_bytes(k));
     float *tsum = tscale + k / GROUP;
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(x);
 #pragma unroll
@@ -248,7 +256,7 @@ template <int GROUP, int LIMBS>
 __device__ __forceinline__ void stage_group_global(f32x4 v, int i, uint8_t *__restrict__ out, int k)
 {
     uint32_t *plane = reinterpret_cast<uint32_t *>(out);
-    float *tscale = reinterpret_cast<float *>(out + LIMBS * (int64_t)k);
+    float *tscale = reinterpret_cast<float *>(out + LIMBS * plane_bytes(k));
     float *tsum = tscale + k / GROUP;
     stage_group<GROUP, LIMBS>(v, i, plane, k >> 2, tscale, tsum);
 }
@@ -320,6 +328,9 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int l = 0; l < LIMBS; ++l) acc[s][l] = 0;
+    // the unit's 128 inputs lie inside one padded 128-input run of each plane
+    const int P = (int)plane_bytes(k);
+    const uint8_t *xp = planes + (base >> 3);
 
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -335,8 +346,8 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
         }
 #pragma unroll
         for (int l = 0; l < LIMBS; ++l) {
-            const u32x4 xl = *reinterpret_cast<const u32x4 *>(planes + l * k + plo);
-            const u32x4 xh = *reinterpret_cast<const u32x4 *>(planes + l * k + plo + 32);
+            const u32x4 xl = *reinterpret_cast<const u32x4 *>(xp + l * P + plo);
+            const u32x4 xh = *reinterpret_cast<const u32x4 *>(xp + l * P + plo + 32);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 acc[slo][l] = sdot4(lo[w], xl[w], acc[slo][l]);
@@ -413,6 +424,9 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
                                              const float *__restrict__ tsum)
 {
     const int sh = u.shift;
+    // the unit's 128 inputs lie inside one padded 128-input run of each plane
+    const int P = (int)plane_bytes(k);
+    const uint8_t *xp = planes + (base >> 3);
     // ql word i (i = 0..15) and qh word i (i = 0..7) of the unit, re-aligned
     // on use so that only the words of one half are live at a time
     auto qlw = [&](int i) -> uint32_t {
@@ -457,7 +471,7 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
             const int pos = base + 32 * g + 16 * jj;
 #pragma unroll
             for (int l = 0; l < LIMBS; ++l) {
-                const u32x4 xv = *reinterpret_cast<const u32x4 *>(planes + l * k + pos);
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(xp + l * P + pos);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) acc[g][l] = sdot4(q[g][t], xv[t], acc[g][l]);
             }

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     stage_activation<32, LIMBS>(xpre, x, xs, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
+    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * plane_bytes(k));
     const float *tsum = tscale + (k >> 5);
 
     while (t0 < r_hi) {
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         ring_prologue();
         const float inv_r = rsqrtf(sr * inv_n + tl.eps_next);
         uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
-        float *tsc = reinterpret_cast<float *>(smem + LIMBS * k);
+        float *tsc = reinterpret_cast<float *>(smem + LIMBS * plane_bytes(k));
 #pragma unroll
         for (int j = 0; j < kTailVec; ++j) {
             const int i = tid + j * tt;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
     }
     __syncthreads();
     const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
+    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * plane_bytes(k));
     const float *tsum = tscale + (k >> 5);
 
     while (t0 < r_hi) {
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     stage_activation<16, LIMBS>(xpre, x, xs, k, smem);
     __syncthreads();
     const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * k);
+    const float *tscale = reinterpret_cast<const float *>(smem + LIMBS * plane_bytes(k));
     const float *tsum = tscale + (k >> 4);
 
     while (t0 < r_hi) {
@@ -708,7 +708,7 @@ hipError_t allow_lds(size_t bytes)
 template <int GROUP>
 size_t staging_bytes(int k)
 {
-    return (size_t)KQ_LIMBS * k + 2 * sizeof(float) * (size_t)(k / GROUP);
+    return (size_t)staged_bytes<GROUP, KQ_LIMBS>(k);
 }
 
 kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k, bool staged = false)

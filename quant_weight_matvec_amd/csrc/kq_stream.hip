@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(kStThreads) q4k_stream_kernel(StArgs a)
 
     stage_activation<32, KQ_LIMBS>(a.x, a.k, smem);
     const uint8_t *planes = smem;
-    const float *tscale = reinterpret_cast<const float *>(smem + KQ_LIMBS * a.k);
+    const float *tscale = reinterpret_cast<const float *>(smem + KQ_LIMBS * plane_bytes(a.k));
     const float *tsum = tscale + (a.k >> 5);
 
     const int sbl = threadIdx.x >> 2;  // superblock of this lane within a chunk
@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(kStThreads) q4k_stream_kernel(StArgs a)
             const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
             for (int l = 0; l < KQ_LIMBS; ++l) {
-                const uint8_t *pl = planes + l * a.k + base;
+                const uint8_t *pl = planes + l * (int)plane_bytes(a.k) + plane_off(base);
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
                     const u32x4 xl = *reinterpret_cast<const u32x4 *>(pl + 16 * p);
@@ -204,7 +204,7 @@ size_t q4k_stream_lds(int n_rows, int k, int grid, int nbuf, int *rows_per_wg, i
 {
     const int nb = k / 256;
     const int rpw = (n_rows + grid - 1) / grid;
-    const int xb = KQ_LIMBS * k + 8 * (k / 32);
+    const int xb = (int)staged_bytes<32, KQ_LIMBS>(k);
     const int po = (xb + 15) & ~15;
     const int ro = (po + 4 * rpw * nb + 1023) & ~1023;
     if (rows_per_wg) *rows_per_wg = rpw;

@@ -136,9 +136,10 @@ def test_tail_validation():
 
 def test_staged_validation():
     L = kq.lib()
-    # sizes: 3 byte limbs per input, then a scale and a sum per group (32 for Q4_K, 16 for Q6_K)
-    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q4K, 6656) == 3 * 6656 + 8 * 6656 // 32
-    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q6K, 19968) == 3 * 19968 + 8 * 19968 // 16
+    # sizes: 3 byte-limb planes of k + k/8 bytes (16 bytes of padding per 128
+    # inputs), then a scale and a sum per group (32 for Q4_K, 16 for Q6_K)
+    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q4K, 6656) == 3 * (6656 + 832) + 8 * 6656 // 32
+    assert kq.kq_staged_bytes(B.KQ_QTYPE_Q6K, 19968) == 3 * (19968 + 2496) + 8 * 19968 // 16
     assert L.kq_staged_bytes(3, 1024) == B.KQ_ERR_SHAPE
     assert L.kq_staged_bytes(1, 1000) == B.KQ_ERR_SHAPE
     assert L.kq_staged_bytes(1, B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED

@@ -26,6 +26,14 @@ def staged(qt, x, k):
     return xs
 
 
+def payload(xs, k):
+    """The bytes of a staged k-vector that carry data: its three limb planes
+    hold 144 bytes per 128 inputs (16 of them padding, never written or read),
+    then come the scales and sums."""
+    planes = xs[: 3 * (k + k // 8)].reshape(3, k // 128, 144)[:, :, :128]
+    return torch.cat([planes.reshape(-1), xs[3 * (k + k // 8):]])
+
+
 def plain(qt, W, x, n, k, gate=None):
     y = nan_like(n)
     if qt == "q4k":
@@ -81,7 +89,7 @@ def test_gate_up_staged(n, k, mq):
     kq.kq_ffn_gate_up_q4k_staged(Wg, Wu, xs, m2, None, 0, n, k)  # no staged output
     torch.cuda.synchronize()
     assert torch.equal(m0, m1) and torch.equal(m0, m2)
-    assert torch.equal(ms, staged(mq, m0, n))
+    assert torch.equal(payload(ms, n), payload(staged(mq, m0, n), n))
 
 
 @pytest.mark.parametrize("rows,n,nq", [(1, 6656, "q4k"), (2, 1024, "q6k"), (1, 16384, "q4k"),
@@ -100,7 +108,8 @@ def test_tail_staged(rows, n, nq):
     torch.cuda.synchronize()
     assert torch.equal(r0, r1) and torch.equal(o0, o1)
     for r in range(rows):
-        assert torch.equal(xs[r * sb:(r + 1) * sb], staged(nq, o0[r * n:(r + 1) * n], n)), r
+        assert torch.equal(payload(xs[r * sb:(r + 1) * sb], n),
+                           payload(staged(nq, o0[r * n:(r + 1) * n], n), n)), r
     # the f32 outputs against the oracle's tail
     ref_r, ref_o = oracle.get().dual_eps_tail(res.reshape(rows, n), proj.reshape(rows, n),
                                               gp.cpu().numpy(), gn.cpu().numpy())
@@ -129,6 +138,7 @@ def test_tail_gate_up_fused(n, k, mq, with_x):
     ms = torch.full((kq.kq_staged_bytes(QT[mq], n),), 0x77, dtype=torch.uint8, device="cuda")
     kq.kq_ffn_tail_gate_up_q4k(res, p, gp, gn, r_out, x_out, Wg, Wu, m, ms, QT[mq], n, k)
     torch.cuda.synchronize()
-    assert torch.equal(r_out, r_ref) and torch.equal(m, m_ref) and torch.equal(ms, ms_ref)
+    assert torch.equal(r_out, r_ref) and torch.equal(m, m_ref)
+    assert torch.equal(payload(ms, n), payload(ms_ref, n))
     if with_x:
         assert torch.equal(x_out, x_ref)
