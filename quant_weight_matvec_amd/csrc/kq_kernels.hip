@@ -673,22 +673,26 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
     // Measured on MI355X (sweeps of lanes 8..32, waves 4..16, one or two
     // workgroups per CU, look-ahead 0..2 units):
     //   Q4_K 19968 x 6656: 8 lanes, 8 waves, 2 workgroups per CU, 1 unit ahead
-    //   Q4_K 6656 x 19968: 8 lanes, 16 waves (x staged: 8), 1 workgroup per CU,
-    //                      1 unit ahead
+    //   Q4_K 6656 x 19968: 32 lanes, 16 waves, 1 workgroup per CU (staged x:
+    //                      8 waves, 2 workgroups per CU), 1 unit ahead
     //   Q6_K 6656 x 19968: 8 lanes, 8 waves, 1 workgroup per CU, 1 unit ahead
     // 8 lanes per row keep a row's loads contiguous and the lane reduction to
-    // DPP moves.  Waves without rows still share the conversion of an f32 x,
-    // so a long k takes the widest workgroup the registers allow (Q6_K's ring
-    // needs more than 128 VGPRs, which caps it at 8 waves); a staged x is only
-    // copied, and then 8 waves are best.
+    // DPP moves; a long Q4_K row (k > 8192) is better split 32 ways (9-13 %
+    // faster at k = 19968).  Waves without rows still share the conversion of
+    // an f32 x, so a long k takes the widest workgroup the registers allow
+    // (Q6_K's ring needs more than 128 VGPRs, which caps it at 8 waves); a
+    // staged x is only copied, and then 8 waves are best.
     const bool q6 = qtype == 2;
     const int64_t tiles = (n_rows + 7) / 8;
     const int64_t k = 128 * (int64_t)units;
-    const bool two_per_cu = !q6 && k <= 8192 && n_rows >= 32 * 2 * (int64_t)cus;
+    const bool long_q4 = !q6 && k > 8192;
+    // two workgroups per CU only where both stagings fit in the CU's LDS
+    const bool two_per_cu = !q6 && n_rows >= 32 * 2 * (int64_t)cus &&
+                            (k <= 8192 || (staged && 2 * staged_bytes<32, KQ_LIMBS>(k) <= 160 * 1024));
     const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
     const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
     const int waves = (q6 || two_per_cu || staged) ? 8 : 16;
-    return kqi::MatvecShape{8, waves, grid, 2};
+    return kqi::MatvecShape{long_q4 ? 32 : 8, waves, grid, 2};
 }
 
 // Raise a kernel's dynamic-LDS limit once to the largest staging size any
