@@ -74,7 +74,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kSmWaves = KQ_SM_WAVES;
 constexpr int kSmThreads = 64 * kSmWaves;
-constexpr int kSub = 2;                        // 16-row sub-tiles per wave
+#ifndef KQ_SM_SUB
+#define KQ_SM_SUB 2
+#endif
+constexpr int kSub = KQ_SM_SUB;                // 16-row sub-tiles per wave
 constexpr int kSmRows = 16 * kSub * kSmWaves;  // rows per row group
 constexpr uint32_t kBias = 0x64006400u;  // f16 1024.0 in both halves
 constexpr int kSmLdsMax = 160 * 1024;
@@ -89,7 +92,7 @@ struct SmArgs {
     int n_rows, k, m;
     int nb;             // superblocks per row
     int T, G;           // tiles, workgroups
-    int CH;             // superblocks per staged chunk
+    int CH;             // superblocks of the staged window (the longest range)
     int RS;             // bytes per activation row in one LDS plane
     int part_off;       // byte offset of the partial tiles in the workspace
     int ws_bytes;
@@ -321,11 +324,16 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s, uint32_t vmask)
 // lane's 4 outputs per sub-tile, in units of the staged (scaled) activations.
 // `ah` points at the lane's activation row in the hi plane at this
 // superblock's first input + 8 kb; the lo plane is `lo_off` bytes further.
-// `st` = group sums of the superblock at [s][m0..m0+3].  Every activation
-// operand and group sum read from LDS serves all NS sub-tiles.
+// `sf` = the lane's A fragment of the superblock's min-term table (see
+// stage_chunk).  Every activation operand read from LDS serves all NS
+// sub-tiles.
+//
+// The min term sum_s dmin m_s (sum of x over sub-block s) is one more MFMA per
+// tile: A = the 8 group sums of each activation row (hi and lo halves in K),
+// B = the row's 8 six-bit mins as exact f16 integers.
 template <int NS>
 __device__ __forceinline__ void sb_mma(const Q4Sb (&u)[NS], const uint8_t *__restrict__ ah,
-                                       int lo_off, const float *__restrict__ st, uint32_t vmask,
+                                       int lo_off, const uint8_t *__restrict__ sf, uint32_t vmask,
                                        f32x4 (&ys)[NS])
 {
     uint32_t scA[NS], mnA[NS], scB[NS], mnB[NS];
@@ -342,6 +350,19 @@ __device__ __forceinline__ void sb_mma(const Q4Sb (&u)[NS], const uint8_t *__res
         ys[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
     const h8 off = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
+    f32x4 dm[NS];
+    {
+        // mins of sub-blocks 0,2 | 1,3 | 4,6 | 5,7 as f16 pairs (the table's
+        // order within a row)
+        const h8 As = *reinterpret_cast<const h8 *>(sf);
+#pragma unroll
+        for (int h = 0; h < NS; ++h) {
+            const u32x4 bq = {(mnA[h] & 0x00FF00FFu) | kBias, ((mnA[h] >> 8) & 0x00FF00FFu) | kBias,
+                              (mnB[h] & 0x00FF00FFu) | kBias, ((mnB[h] >> 8) & 0x00FF00FFu) | kBias};
+            dm[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(As, as_h8(bq) - off,
+                                                           (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int c0 = 0; c0 < 4; c0 += 2) {
         // sub-blocks 2c0 .. 2c0+3: all hi MFMAs, then all lo MFMAs
@@ -371,25 +392,27 @@ __device__ __forceinline__ void sb_mma(const Q4Sb (&u)[NS], const uint8_t *__res
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s = 2 * c0 + j;
-            const f32x4 sm = *reinterpret_cast<const f32x4 *>(st + 16 * s);
 #pragma unroll
             for (int h = 0; h < NS; ++h) {
-                const uint32_t scw = s < 4 ? scA[h] : scB[h], mnw = s < 4 ? mnA[h] : mnB[h];
+                const uint32_t scw = s < 4 ? scA[h] : scB[h];
                 const float c1 = d[h] * (float)((scw >> (8 * (s & 3))) & 0xFFu);
-                const float c2 = dmin[h] * (float)((mnw >> (8 * (s & 3))) & 0xFFu);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ys[h][i] = fmaf(c1, acc[h][j][i], fmaf(-c2, sm[i], ys[h][i]));
+                for (int i = 0; i < 4; ++i) ys[h][i] = fmaf(c1, acc[h][j][i], ys[h][i]);
             }
         }
     }
+    // the table holds the group sums times 2^-5
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ys[h][i] = fmaf(-32.0f * dmin[h], dm[h][i], ys[h][i]);
 }
 
 // The same for Q6_K superblocks; `ah` = the lane's activation row at the
 // superblock's first input + 4 kb.
 template <int NS>
 __device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__restrict__ ah,
-                                       int lo_off, const float *__restrict__, uint32_t vmask,
+                                       int lo_off, const uint8_t *__restrict__, uint32_t vmask,
                                        f32x4 (&ys)[NS])
 {
     uint32_t L[NS][8], H[NS][4], sc[NS][4];
@@ -463,8 +486,12 @@ __device__ __forceinline__ constexpr bool is_q4()
 // ---------------------------------------------------------------------------
 // Staging of the activations of superblocks [cb, cb + n) into LDS slots so, so + 1, ...
 // LDS: hi plane [M][RS bytes], lo plane [M][RS bytes], etab [CH][16] int
-// (back-scale exponents), stab [CH][8][16] f32 (Q4_K: sums of 32-input groups,
-// scaled).  One wave converts one (row, superblock) group of 256 inputs.
+// (back-scale exponents), then for Q4_K the min-term table [CH][4][16][8] f16:
+// for slot c and row m, [c][0][m] and [c][1][m] are the hi and lo f16 halves
+// of 2^-5 times the sums of the row's 8 scaled 32-input groups (below 2^15 in
+// magnitude), groups in the order 0,2,1,3,4,6,5,7, and [c][2..3][m] are zero:
+// lane (r, kb) of the min-term MFMA reads [c][kb][r] as its A fragment.  One
+// wave converts one (row, superblock) group of 256 inputs.
 template <bool Q4>
 __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem,
                                             int so = 0)
@@ -473,7 +500,7 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
     const int M = a.m, RS = a.RS;
     uint8_t *hi = smem, *lo = smem + M * RS;
     int *etab = reinterpret_cast<int *>(smem + 2 * M * RS);
-    float *stab = reinterpret_cast<float *>(etab + 16 * a.CH);
+    uint8_t *sfrag = reinterpret_cast<uint8_t *>(etab + 16 * a.CH);
     const int ngroups = M * n;
     constexpr int B = 4;
     for (int g0 = wave; g0 < ngroups; g0 += B * kSmWaves) {
@@ -522,8 +549,20 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
             *reinterpret_cast<u32x2 *>(lo + boff) = pl;
             if (lane == 0) etab[16 * sbb + m] = e - 15;
             if constexpr (Q4) {
-                const float sm = group_sum<8>((s.x + s.y) + (s.z + s.w));
-                if ((lane & 7) == 0) stab[128 * sbb + 16 * (lane >> 3) + m] = fin ? sm : __builtin_nanf("");
+                const float sm = 0.03125f * group_sum<8>((s.x + s.y) + (s.z + s.w));
+                _Float16 *sf = reinterpret_cast<_Float16 *>(sfrag + 1024 * sbb) + 8 * m;
+                if ((lane & 7) == 0) {
+                    const int g = lane >> 3;
+                    const int pos = (g & 4) | ((g & 1) << 1) | ((g >> 1) & 1);  // 0,2,1,3,4,6,5,7
+                    const _Float16 hs = fin ? (_Float16)sm : (_Float16)__builtin_nanf("");
+                    sf[pos] = hs;
+                    sf[128 + pos] = fin ? (_Float16)(sm - (float)hs) : hs;
+                }
+                if (lane == 1) {
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(sf + 256) = z;
+                    *reinterpret_cast<u32x4 *>(sf + 384) = z;
+                }
             }
         }
     }
@@ -623,7 +662,7 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
     uint8_t *tile = smem + wave * TT::kTileLds;  // this wave's weight tile
     const int lo_off = M * a.RS;
     const int *etab = reinterpret_cast<const int *>(xs + 2 * M * a.RS);
-    const float *stab = reinterpret_cast<const float *>(etab + 16 * a.CH);
+    const uint8_t *sfrag = reinterpret_cast<const uint8_t *>(etab + 16 * a.CH);  // Q4_K min term
     int &last_flag = *reinterpret_cast<int *>(smem + a.flag_off);
     uint32_t vmask;  // kept in a VGPR for v_and_or_b32
     asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(Q4 ? 0x000F000Fu : 0x00FF00FFu));
@@ -713,7 +752,7 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
         const int bb = b >= cb ? b - cb : b + nb - cb;  // LDS slot of superblock b
         const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
         f32x4 ys[kSub];
-        sb_mma<kSub>(sb, ah, lo_off, stab + 128 * bb + m0, vmask, ys);
+        sb_mma<kSub>(sb, ah, lo_off, sfrag + 1024 * bb + 256 * kb + 16 * ma, vmask, ys);
         const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
 #pragma unroll
         for (int h = 0; h < kSub; ++h)
@@ -794,7 +833,7 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
-    const int per_sb = 1024 * m + 64 + (qtype == 1 ? 512 : 0);  // LDS bytes per staged superblock
+    const int per_sb = 1024 * m + 64 + (qtype == 1 ? 1024 : 0);  // LDS bytes per staged superblock
     p.xs_off = kSmWaves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
     int ch = (kSmLdsBudget - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
     if (ch > p.nb) ch = p.nb;
@@ -806,7 +845,7 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     ch = (p.T + p.G - 1) / p.G;  // the longest range
     p.CH = ch;
     p.RS = 512 * ch + 16;
-    p.flag_off = p.xs_off + 2 * m * p.RS + 64 * ch + (qtype == 1 ? 512 * ch : 0);
+    p.flag_off = p.xs_off + 2 * m * p.RS + 64 * ch + (qtype == 1 ? 1024 * ch : 0);
     p.lds = (size_t)p.flag_off + 16;
     // workspace: one counter per row group, then two partial tiles per workgroup
     p.part_off = ((rgs * 4 + 255) / 256) * 256;
