@@ -142,3 +142,31 @@ def test_tail_gate_up_fused(n, k, mq, with_x):
     assert torch.equal(payload(ms, n), payload(ms_ref, n))
     if with_x:
         assert torch.equal(x_out, x_ref)
+
+
+@pytest.mark.parametrize("qt,k", [("q4k", 256), ("q4k", 6656), ("q6k", 1024), ("q6k", 19968)])
+def test_staged_form_decodes_to_x(qt, k):
+    """The stored form itself: per scale group a back-scale 2^(e-22) with
+    max|x| < 2^e, each input the integer round(x 2^(22-e)) as three balanced
+    signed byte limbs in padded planes, and the f32 group sum of x."""
+    G = 32 if qt == "q4k" else 16
+    x = I.normal_f32(k, stream=59) * np.float32(3.0)
+    x[:G] = 0.0                      # an all-zero group
+    x[G:2 * G] *= np.float32(1e-30)  # a tiny group
+    x[2 * G] = np.float32(2.0 ** 20)  # a group with one large value
+    xs = staged(qt, dev(x), k).cpu().numpy()
+    P = k + k // 8
+    limbs = xs[: 3 * P].reshape(3, k // 128, 144)[:, :, :128].reshape(3, k).view(np.int8)
+    q = (limbs[0].astype(np.int64) << 16) + (limbs[1].astype(np.int64) << 8) + limbs[2]
+    tables = xs[3 * P:].view(np.float32)
+    assert tables.size == 2 * (k // G)
+    scale, gsum = tables[: k // G].astype(np.float64), tables[k // G:].astype(np.float64)
+    xg = x.astype(np.float64).reshape(-1, G)
+    qg = q.reshape(-1, G)
+    mx = np.abs(xg).max(axis=1)
+    e = np.where(mx > 0, np.floor(np.log2(np.where(mx > 0, mx, 1.0))) + 1, 0)  # max|x| < 2^e
+    assert np.array_equal(scale, np.exp2(e - 22))
+    assert np.all(np.abs(qg) <= 2 ** 22)
+    assert np.all(np.abs(xg - qg * scale[:, None]) <= 0.5 * scale[:, None])
+    # an f32 sum of G terms: within G * 2^-24 of sum |x|
+    assert np.all(np.abs(gsum - xg.sum(axis=1)) <= G * 2.0 ** -24 * np.abs(xg).sum(axis=1))
