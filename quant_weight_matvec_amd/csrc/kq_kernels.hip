@@ -662,12 +662,10 @@ int device_cus()
     return g_dev[dev].cus;
 }
 
-// Pick lanes-per-row, waves per workgroup, grid and depth for a matvec.  The
-// score favours every lane busy in every unit step and every wave slot holding
-// a row, then enough waves per CU.  Measured on MI355X at the FFN shapes: Q4_K
-// streams best with many waves (about 8+) and no look-ahead (depth 1); Q6_K,
-// whose 30-register units limit occupancy, streams best with a few waves per
-// CU each keeping 3 units in flight, which needs the 8-wave VGPR budget.
+// Pick lanes-per-row, waves per workgroup, grid and depth for a matvec from
+// the shapes measured best on MI355X at the FFN sizes (below).  Depth 2 (one
+// unit in flight ahead of the one computed) is best everywhere: deeper rings
+// cost registers and measured slower.
 kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, bool staged)
 {
     // Measured on MI355X (sweeps of lanes 8..32, waves 4..16, one or two
@@ -858,9 +856,10 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
                               const uint8_t *xs, float *mid, uint8_t *mid_s, int mid_group,
                               int n_rows, int k, const TailArgs *tail, hipStream_t stream)
 {
-    // Measured on MI355X at 19968 x 6656 (sweep of lanes 8/16, waves 8..16,
+    // Measured on MI355X at 19968 x 6656 (sweep of lanes 4/8, waves 4..16,
     // grid 1-2 per CU, depth 1-3): 8 lanes per row, one 12-wave workgroup per
-    // CU and one unit of look-ahead best (32.4 us, 4.6 TB/s).
+    // CU and one unit of look-ahead best (31.4 us, 4.8 TB/s; 16 waves within
+    // 1 %).  A 12-wave workgroup holds 80 rows of 8-row tasks in one round.
     const int tiles = (n_rows + 7) / 8;
     MatvecShape s{8, 12, tiles < device_cus() ? tiles : device_cus(), 2};
     const MatvecShape o = g_override[1];
@@ -958,7 +957,7 @@ const char *variant_names()
 {
     return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged] "
            "gate_up[q4k, mid staged out: 0/16/32] "
-           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups, 2 16-row tiles per wave] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
+           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; m<=8: 16 waves x 1 16-row tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

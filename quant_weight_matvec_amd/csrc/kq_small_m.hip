@@ -6,13 +6,14 @@
 //
 // Design for gfx950 (the pages' kernels use scalar f32 MACs on another GPU):
 //
-// * Matrix cores.  One 64-lane wave owns a tile of 16 weight rows.  For every
-//   scale sub-block it issues f16 MFMAs D[16 x 16] += A[16 x K'] B[K' x 16]
-//   with A = the (up to 16) activation rows and B = the sub-block's quants:
-//   Q4_K uses 16x16x32 (one 32-weight sub-block), Q6_K 16x16x16 (one
-//   16-weight sub-block).  Lane l holds output column l % 16 = its weight row,
-//   so the per-row scale d*sc (and the Q4_K min term) is applied in registers
-//   right after the MFMA.
+// * Matrix cores.  One 64-lane wave owns two tiles of 16 weight rows.  For
+//   every scale sub-block it issues f16 MFMAs D[16 x 16] += A[16 x K'] B[K' x
+//   16] with A = the (up to 16) activation rows and B = the sub-block's
+//   quants: Q4_K uses 16x16x32 (one 32-weight sub-block), Q6_K 16x16x16 (one
+//   16-weight sub-block); both tiles use the same A registers.  Lane l holds
+//   output column l % 16 = its weight row, so the per-row scale d*sc is
+//   applied in registers right after the MFMA.  The Q4_K min term is one more
+//   MFMA per tile, of the activation rows' group sums against the row's mins.
 // * Exact quant operands.  A quant q is turned into the f16 value 1024 + q by
 //   OR-ing it under the exponent of 1024 (0x6400), then 1024 (Q4_K) or 1056
 //   (Q6_K, folding the -32 offset) is subtracted: both steps are exact, so B
@@ -21,10 +22,11 @@
 //   scaled by a power of two so that its largest magnitude is below 2^15, then
 //   split into x_hi = f16(x) and x_lo = f16(x - x_hi); two MFMAs (hi, lo) per
 //   sub-block accumulate in f32.  The products q * x_hi and q * x_lo are exact
-//   in f32.  The Q4_K min term uses the f32 group sums of the scaled inputs.
+//   in f32.  The Q4_K group sums (of the scaled inputs, times 2^-5) are split
+//   into hi and lo halves the same way.
 //   A group holding a NaN or an infinity is staged as NaN, so the whole output
 //   row m becomes NaN.
-// * Stream-K split.  The work is the grid of (row group of 128 rows, superblock)
+// * Stream-K split.  The work is the grid of (row group of 256 rows, superblock)
 //   tiles; workgroup g takes the contiguous range [g T / G, (g+1) T / G).  A row
 //   group covered by one workgroup is stored directly.  Otherwise each
 //   contributing workgroup stores its partial tile in the workspace and counts
@@ -58,30 +60,29 @@ typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shape: waves per workgroup (one 16-row tile each), weight superblocks
-// in flight per wave, and workgroups per CU the grid is sized for.
-#ifndef KQ_SM_WAVES
-#define KQ_SM_WAVES 8
-#endif
-#ifndef KQ_SM_Q4_DEPTH
-#define KQ_SM_Q4_DEPTH 2
-#endif
-#ifndef KQ_SM_Q6_DEPTH
-#define KQ_SM_Q6_DEPTH 1
-#endif
-#ifndef KQ_SM_OCC
-#define KQ_SM_OCC 1
-#endif
-constexpr int kSmWaves = KQ_SM_WAVES;
-constexpr int kSmThreads = 64 * kSmWaves;
-#ifndef KQ_SM_SUB
-#define KQ_SM_SUB 2
-#endif
-constexpr int kSub = KQ_SM_SUB;                // 16-row sub-tiles per wave
-constexpr int kSmRows = 16 * kSub * kSmWaves;  // rows per row group
+// Launch shapes, one workgroup per CU, 256-row groups either way:
+// * up to 8 activation rows: 16 waves of one 16-row tile each (4 waves per
+//   SIMD hide more latency; the kernel fits 128 VGPRs);
+// * 9 to 16 rows: 8 waves of two tiles each, which share every activation
+//   operand they read, so a range of 8 superblocks of 16 activation rows still
+//   fits LDS beside the weight tiles.
+// Measured on MI355X at the verify shapes: the 16-wave form is 4-10 % faster
+// at M = 2..8 and 25 % slower at M = 16 (its larger tile area leaves room for
+// only 6-7 staged superblocks, and the grid needs a second round).
+template <int SUB, int WAVES, int Q4_DEPTH, int Q6_DEPTH>
+struct SmCfg {
+    static constexpr int kSub = SUB;      // 16-row tiles per wave
+    static constexpr int kWaves = WAVES;  // waves per workgroup
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kQ4Depth = Q4_DEPTH, kQ6Depth = Q6_DEPTH;  // tile sets in flight ahead
+};
+using SmNarrow = SmCfg<1, 16, 1, 1>;  // m <= 8
+using SmWide = SmCfg<2, 8, 2, 1>;     // m >= 9
+constexpr int kSmRows = 256;          // rows per row group: 16 kSub kWaves in both shapes
+static_assert(16 * SmNarrow::kSub * SmNarrow::kWaves == kSmRows, "row group");
+static_assert(16 * SmWide::kSub * SmWide::kWaves == kSmRows, "row group");
 constexpr uint32_t kBias = 0x64006400u;  // f16 1024.0 in both halves
-constexpr int kSmLdsMax = 160 * 1024;
-constexpr int kSmLdsBudget = kSmLdsMax / KQ_SM_OCC;  // per workgroup
+constexpr int kSmLdsMax = 160 * 1024;    // per workgroup (one per CU)
 
 struct SmArgs {
     const uint8_t *W;
@@ -503,11 +504,12 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
     uint8_t *sfrag = reinterpret_cast<uint8_t *>(etab + 16 * a.CH);
     const int ngroups = M * n;
     constexpr int B = 4;
-    for (int g0 = wave; g0 < ngroups; g0 += B * kSmWaves) {
+    const int nw = blockDim.x >> 6;
+    for (int g0 = wave; g0 < ngroups; g0 += B * nw) {
         f32x4 v[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const int gi = g0 + j * kSmWaves;
+            const int gi = g0 + j * nw;
             if (gi < ngroups) {
                 const int m = gi / n, bb = gi - m * n;
                 v[j] = *reinterpret_cast<const f32x4 *>(a.X + (int64_t)m * a.ldx +
@@ -516,7 +518,7 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const int gi = g0 + j * kSmWaves;
+            const int gi = g0 + j * nw;
             if (gi >= ngroups) break;  // wave-uniform
             const int m = gi / n, bb = gi - m * n;
             float mx = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
@@ -570,8 +572,9 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
 
 // This workgroup's share of row group rg is complete: store it, or publish it
 // as a partial tile and, if it is the last contributor, sum all of them.
-// The lane's outputs of sub-tile h are rows 16 (kSub wave + h) + r of the row
+// The lane's outputs of tile h are rows 16 (kSub wave + h) + r of the row
 // group, activation rows m0 .. m0 + 3.
+template <int kSub>
 __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, int gh, int g,
                                                const f32x4 (&yacc)[kSub], int wave, int r, int m0,
                                                int &last_flag)
@@ -611,7 +614,7 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
         // sum the contributors' partial tiles in workgroup order
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(a.ws, (short)0, a.ws_bytes, 0x00020000);
-        for (int e = threadIdx.x; e < M * (kSmRows / 4); e += kSmThreads) {
+        for (int e = threadIdx.x; e < M * (kSmRows / 4); e += blockDim.x) {
             const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
             f32x4 s;
             for (int c = gl; c <= gh; ++c) {
@@ -644,10 +647,12 @@ constexpr int kMaxSegs = 2;
 // compiler's waits count only the ring (a load, store or barrier under a
 // branch in the loop would make it wait for every load in flight at the next
 // merge).
-template <typename U, int DEPTH>
-__global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_kernel(SmArgs a)
+template <typename U, typename C>
+__global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int kSub = C::kSub;
+    constexpr int DEPTH = is_q4<U>() ? C::kQ4Depth : C::kQ6Depth;
     using TT = TileTraits<U>;
     using Sb = std::conditional_t<is_q4<U>(), Q4Sb, Q6Sb>;
     constexpr bool Q4 = is_q4<U>();
@@ -802,7 +807,7 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
             const int rq = rg_first + q;
             const int gl = rq == rg_first ? gl_first : gl_last;
             const int gh = rq == rg_first ? gh_first : gh_last;
-            finish_segment(a, rq, gl, gh, g, sy[q], wave, r, m0, last_flag);
+            finish_segment<kSub>(a, rq, gl, gh, g, sy[q], wave, r, m0, last_flag);
         }
     }
 }
@@ -810,6 +815,7 @@ __global__ void __launch_bounds__(kSmThreads, KQ_SM_OCC * kSmWaves / 4) small_m_
 struct SmPlan {
     int nb, T, G, CH, RS, part_off, flag_off, xs_off;
     size_t lds, ws;
+    bool narrow;  // the SmNarrow launch shape (m <= 8)
 };
 
 int sm_cus()
@@ -833,14 +839,16 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
+    p.narrow = m <= 8;
+    const int waves = p.narrow ? SmNarrow::kWaves : SmWide::kWaves;
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 1024 : 0);  // LDS bytes per staged superblock
-    p.xs_off = kSmWaves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
-    int ch = (kSmLdsBudget - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
+    p.xs_off = waves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
+    int ch = (kSmLdsMax - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
     if (ch > p.nb) ch = p.nb;
     if (ch < 1) ch = 1;
-    // one workgroup per CU (times the occupancy), more when a range would
-    // not fit in LDS at once: every range is then at most ch <= nb tiles long
-    p.G = p.T < KQ_SM_OCC * sm_cus() ? p.T : KQ_SM_OCC * sm_cus();
+    // one workgroup per CU, more when a range would not fit in LDS at once:
+    // every range is then at most ch <= nb tiles long
+    p.G = p.T < sm_cus() ? p.T : sm_cus();
     if ((p.T + p.G - 1) / p.G > ch) p.G = (p.T + ch - 1) / ch;
     ch = (p.T + p.G - 1) / p.G;  // the longest range
     p.CH = ch;
@@ -903,15 +911,19 @@ hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int6
     a.flag_off = p.flag_off;
     a.xs_off = p.xs_off;
     hipError_t e;
-#define KQ_SM_GO(U, D)                                                                         \
+#define KQ_SM_GO(U, C)                                                                         \
     {                                                                                         \
-        constexpr auto K = small_m_kernel<U, D>;                                              \
+        constexpr auto K = small_m_kernel<U, C>;                                              \
         if ((e = allow_lds<K>()) != hipSuccess) return e;                                     \
-        hipLaunchKernelGGL(K, dim3(p.G), dim3(kSmThreads), p.lds, stream, a);                  \
+        hipLaunchKernelGGL(K, dim3(p.G), dim3(C::kThreads), p.lds, stream, a);                 \
         return hipGetLastError();                                                             \
     }
-    if (qtype == 1) KQ_SM_GO(Q4Tile, KQ_SM_Q4_DEPTH)
-    KQ_SM_GO(Q6Tile, KQ_SM_Q6_DEPTH)
+    if (qtype == 1) {
+        if (p.narrow) KQ_SM_GO(Q4Tile, SmNarrow)
+        KQ_SM_GO(Q4Tile, SmWide)
+    }
+    if (p.narrow) KQ_SM_GO(Q6Tile, SmNarrow)
+    KQ_SM_GO(Q6Tile, SmWide)
 #undef KQ_SM_GO
 }
 
