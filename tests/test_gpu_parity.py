@@ -40,13 +40,13 @@ def test_tiny_q4k_512x1024():
 
 
 @pytest.mark.parametrize("n,k", [(1, 256), (3, 512), (17, 1024), (255, 2304), (1000, 6656),
-                                 (4097, 768), (129, 19968)])
+                                 (4097, 768), (129, 19968), (33, kq.KQ_MAX_K)])
 def test_q4k_shapes(n, k):
     print("ratio", _full_check("q4k", n, k, 1000 + n))
 
 
 @pytest.mark.parametrize("n,k", [(1, 256), (3, 512), (17, 1280), (255, 2304), (1000, 6656),
-                                 (4097, 768), (129, 19968)])
+                                 (4097, 768), (129, 19968), (33, kq.KQ_MAX_K)])
 def test_q6k_shapes(n, k):
     print("ratio", _full_check("q6k", n, k, 2000 + n))
 
@@ -284,7 +284,7 @@ def _mid_bound(gr, Sg, ur, Su):
 
 
 @pytest.mark.parametrize("n,k", [(1, 256), (5, 512), (129, 768), (1000, 6656), (4100, 1024),
-                                 (19968, 6656), (6656, 19968)])
+                                 (19968, 6656), (6656, 19968), (48, kq.KQ_MAX_K)])
 def test_ffn_gate_up_one_launch(n, k):
     """mid = silu(W_gate x) * (W_up x) from kq_ffn_gate_up_q4k against the
     oracle's gate and up rows (sampled at the large shapes), within the bound

@@ -66,7 +66,8 @@ def test_small_shapes_all_rows(qt, m):
 @pytest.mark.parametrize("qt,n,k", [("q4k", 1, 256), ("q6k", 1, 256), ("q4k", 5, 512),
                                     ("q6k", 17, 1280), ("q4k", 129, 768), ("q6k", 255, 2304),
                                     ("q4k", 1000, 6656), ("q6k", 77, 19968), ("q4k", 4100, 1024),
-                                    ("q6k", 2049, 4096), ("q4k", 257, 2816), ("q6k", 513, 1536)])
+                                    ("q6k", 2049, 4096), ("q4k", 257, 2816), ("q6k", 513, 1536),
+                                    ("q4k", 40, kq.KQ_MAX_K), ("q6k", 40, kq.KQ_MAX_K)])
 def test_ragged_shapes(qt, n, k):
     print("worst |dy|/S", check(qt, n, k, 5, 7100 + n, rows=sample_rows(n, 160, seed=n)))
 

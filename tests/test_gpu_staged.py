@@ -45,7 +45,8 @@ def plain(qt, W, x, n, k, gate=None):
 
 @pytest.mark.parametrize("qt,n,k", [("q4k", 1, 256), ("q4k", 77, 1024), ("q4k", 1000, 6656),
                                     ("q6k", 3, 256), ("q6k", 129, 2560), ("q6k", 700, 19968),
-                                    ("q4k", 6656, 19968)])
+                                    ("q4k", 6656, 19968), ("q4k", 33, kq.KQ_MAX_K),
+                                    ("q6k", 33, kq.KQ_MAX_K)])
 def test_staged_matvec_equals_f32(qt, n, k):
     W = dev(I.weight_matrix(qt, n, k, stream=41))
     x = dev(I.normal_f32(k, stream=42))
