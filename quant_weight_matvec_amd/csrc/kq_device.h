@@ -513,18 +513,28 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds)
                  : "memory");
 }
 
-__device__ __forceinline__ float block_sum_fixed(float v, float *red)
+// Sum over the workgroup in a fixed order (lanes, then waves in order); every
+// thread returns the same value.  `red` holds one float per wave and is read
+// by all threads at the end; block_sum_fresh is for a buffer no thread can
+// still be reading (one not used before in the kernel), block_sum_fixed waits
+// for earlier readers first.
+__device__ __forceinline__ float block_sum_fresh(float v, float *red)
 {
     v = group_sum<8>(v);
 #pragma unroll
     for (int o = 32; o >= 8; o >>= 1) v += __shfl_xor(v, o);
     const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    __syncthreads();  // `red` may still be read from the previous reduction
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     __syncthreads();
     float t = 0.0f;
     for (int w = 0; w < nw; ++w) t += red[w];
     return t;
+}
+
+__device__ __forceinline__ float block_sum_fixed(float v, float *red)
+{
+    __syncthreads();  // `red` may still be read from the previous reduction
+    return block_sum_fresh(v, red);
 }
 
 __device__ __forceinline__ float sumsq4(f32x4 v)

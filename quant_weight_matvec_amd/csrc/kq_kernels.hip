@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
                                                                 TailIn tl)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[16];
+    __shared__ float red[2][16];  // one buffer per reduction
     const int nsb = k >> 8;
     const int units = 2 * nsb;      // half-superblock units per row
     const int units2 = 2 * units;   // gate units, then up units
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         float ss = 0.0f;
 #pragma unroll
         for (int j = 0; j < kTailVec; ++j) ss += sumsq4(tp[j]);
-        ss = block_sum_fixed(ss, red);
+        ss = block_sum_fresh(ss, red[0]);
         const float inv_p = rsqrtf(ss * inv_n + tl.eps_post);
         float sr = 0.0f;
 #pragma unroll
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
                 reinterpret_cast<f32x4 *>(tl.res_out)[i] = tr[j];
             sr += sumsq4(tr[j]);
         }
-        sr = block_sum_fixed(sr, red);
+        sr = block_sum_fresh(sr, red[1]);
         ring_prologue();
         const float inv_r = rsqrtf(sr * inv_n + tl.eps_next);
         uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
                                                     float eps_post, float eps_next,
                                                     uint8_t *__restrict__ xs_out, int xs_group)
 {
-    __shared__ float red[16];
+    __shared__ float red[2][16];  // one buffer per reduction
     const int64_t off = (int64_t)blockIdx.x * n;
     f32x4 *r4 = reinterpret_cast<f32x4 *>(residual + off);
     const f32x4 *p4 = reinterpret_cast<const f32x4 *>(projected + off);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
 
     float ss = 0.0f;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) ss += sumsq4(p4[i]);
-    ss = block_sum_fixed(ss, red);
+    ss = block_sum_fresh(ss, red[0]);
     const float inv_p = rsqrtf(ss * inv_n + eps_post);
 
     float sr = 0.0f;
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
         r4[i] = v;
         sr += sumsq4(v);
     }
-    sr = block_sum_fixed(sr, red);
+    sr = block_sum_fresh(sr, red[1]);
     const float inv_r = rsqrtf(sr * inv_n + eps_next);
 
     uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
     const float *__restrict__ g_post, const float *__restrict__ g_next, int n, float eps_post,
     float eps_next, uint8_t *__restrict__ xs_out, int xs_group)
 {
-    __shared__ float red[kTailThreads / 64];
+    __shared__ float red[2][kTailThreads / 64];  // one buffer per reduction
     const int64_t off = (int64_t)blockIdx.x * n;
     f32x4 *r4 = reinterpret_cast<f32x4 *>(residual + off);
     const f32x4 *p4 = reinterpret_cast<const f32x4 *>(projected + off);
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
     float ss = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTailVec; ++j) ss += sumsq4(pv[j]);
-    ss = block_sum_fixed(ss, red);
+    ss = block_sum_fresh(ss, red[0]);
     const float inv_p = rsqrtf(ss * inv_n + eps_post);
 
     float sr = 0.0f;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
         if (i < n4) r4[i] = rv[j];
         sr += sumsq4(rv[j]);
     }
-    sr = block_sum_fixed(sr, red);
+    sr = block_sum_fresh(sr, red[1]);
     const float inv_r = rsqrtf(sr * inv_n + eps_next);
     uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
 #pragma unroll
