@@ -45,16 +45,18 @@ constexpr int kXPre = 80;
 // The dual-eps tail in registers: up to kTailVec float4 per thread, whole
 // waves, rows up to kTailRegMax wide.  tail_threads(n) is the block size of
 // the standalone tail; the fused form (q4k_gate_up_kernel with TAIL) lays its
-// threads out the same way so that both sum in the same order.
+// threads out the same way so that both sum in the same order.  Beyond four
+// waves the count is rounded up to a multiple of four, so each of a CU's four
+// SIMDs runs the same number of tail waves (the encode at the end is VALU
+// work, and the workgroup waits for its busiest SIMD).
 constexpr int kTailVec = 4;
 constexpr int kTailThreads = 512;
 constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
 
 __host__ __device__ constexpr int tail_threads(int n)
 {
-    return (((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64)) * 64 > 64
-               ? (((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64)) * 64
-               : 64;
+    const int w = ((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64);  // waves needed
+    return 64 * (w <= 1 ? 1 : (w <= 4 ? w : (w + 3) / 4 * 4));
 }
 
 // r + rms-normed p times the post gain, and the next input, one float4 each
