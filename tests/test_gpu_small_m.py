@@ -57,7 +57,7 @@ def check(qt, n, k, m, seed, rows=None, xscale=None, ldx=None):
 
 
 @pytest.mark.parametrize("qt", ["q4k", "q6k"])
-@pytest.mark.parametrize("m", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("m", [2, 3, 4, 7, 8, 9, 13, 16])
 def test_small_shapes_all_rows(qt, m):
     """Several row groups with a ragged last group, k of 11 superblocks."""
     print("worst |dy|/S", check(qt, 300, 2816, m, 7000 + m))
