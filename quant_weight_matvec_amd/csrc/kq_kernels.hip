@@ -214,8 +214,15 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
     // mid_group rows (it encodes them itself); otherwise an even row split.
     const int rg = mid_s ? mid_group : 1;
     const int ngr = n_rows / rg;
-    const int r_lo = rg * (int)((int64_t)blockIdx.x * ngr / gridDim.x);
-    const int r_hi = rg * (int)((int64_t)(blockIdx.x + 1) * ngr / gridDim.x);
+    // Workgroup b runs on XCD b mod 8.  An uneven split of the groups gives
+    // the shorter ranges to fixed slots mod 8, which would put them all on one
+    // XCD; each block of 8 workgroups takes its 8 ranges rotated by the block
+    // index instead, so every XCD gets its share of short ranges (the ranges
+    // stay contiguous and in place within the block).
+    const int slot = (gridDim.x & 7) ? (int)blockIdx.x
+                                     : (int)((blockIdx.x & ~7u) | ((blockIdx.x + (blockIdx.x >> 3)) & 7u));
+    const int r_lo = rg * (int)((int64_t)slot * ngr / gridDim.x);
+    const int r_hi = rg * (int)((int64_t)(slot + 1) * ngr / gridDim.x);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
