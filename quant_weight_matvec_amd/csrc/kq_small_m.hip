@@ -66,7 +66,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // * 9 to 16 rows: 8 waves of two tiles each, which share every activation
 //   operand they read, so a range of 8 superblocks of 16 activation rows still
 //   fits LDS beside the weight tiles.
-// Measured on MI355X at the verify shapes: the 16-wave form is 4-10 % faster
+// Measured on MI355X at the verify shapes: the 16-wave form is 3-9 % faster
 // at M = 2..8 and 25 % slower at M = 16 (its larger tile area leaves room for
 // only 6-7 staged superblocks, and the grid needs a second round).
 template <int SUB, int WAVES, int Q4_DEPTH, int Q6_DEPTH>
