@@ -51,6 +51,19 @@ kq_status kq_tune_set_chain_lanes(int lanes);
 kq_status kq_tune_set_matvec_impl(int qtype, int impl);
 
 /*
+ * The launch plan kq_matmul_small_m would use for this shape on a device of
+ * `cus` compute units (host arithmetic only; no device is touched), written
+ * to the host array out[6]: workgroups, superblocks in a workgroup's staged
+ * activation window, LDS bytes per workgroup, workspace bytes (as
+ * kq_matmul_small_m_workspace_bytes on such a device), threads per
+ * workgroup, tiles (256-row groups x superblocks per row).
+ *   n_rows >= 1, 2 <= m <= KQ_MAX_M, 1 <= cus <= 4096; qtype and k as for
+ *   kq_matmul_small_m.
+ * Errors: KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED, KQ_ERR_NULL.
+ */
+kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int cus, int64_t *out);
+
+/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of 256 threads and
  * writes grid*4 xor-folded words to the device buffer `out` (so the loads

@@ -472,6 +472,17 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
     return KQ_OK;
 }
 
+kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int cus,
+                               int64_t *out)
+{
+    kq_status s = check_small_m(qtype, n_rows, k, m);
+    if (s != KQ_OK) return s;
+    if (!out) return KQ_ERR_NULL;
+    if (n_rows < 1 || m < 2 || cus < 1 || cus > 4096) return KQ_ERR_SHAPE;
+    kqi::small_m_plan(qtype, (int)n_rows, (int)k, m, cus, out);
+    return KQ_OK;
+}
+
 kq_status kq_tune_set_matvec_impl(int qtype, int impl)
 {
     if ((qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) || impl < 0 || impl > 1) return KQ_ERR_SHAPE;

@@ -55,6 +55,9 @@ hipError_t launch_matvec_q4k_stream(const uint8_t *W, const float *x, float *y, 
 
 // Batched small-m kernel (kq_small_m.hip), m = 2..16.
 size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
+// The launch plan for a device of `cus` CUs: out = {workgroups, staged window
+// in superblocks, LDS bytes, workspace bytes, threads per workgroup, tiles}.
+void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out);
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream);

@@ -833,7 +833,7 @@ int sm_cus()
     return cached;
 }
 
-SmPlan make_plan(int qtype, int n_rows, int k, int m)
+SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
 {
     SmPlan p;
     p.nb = k / 256;
@@ -848,7 +848,7 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m)
     if (ch < 1) ch = 1;
     // one workgroup per CU, more when a range would not fit in LDS at once:
     // every range is then at most ch <= nb tiles long
-    p.G = p.T < sm_cus() ? p.T : sm_cus();
+    p.G = p.T < cus ? p.T : cus;
     if ((p.T + p.G - 1) / p.G > ch) p.G = (p.T + ch - 1) / ch;
     ch = (p.T + p.G - 1) / p.G;  // the longest range
     p.CH = ch;
@@ -882,14 +882,25 @@ namespace kqi {
 size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m)
 {
     if (m < 2) return 0;  // m = 1 runs as the matvec
-    return make_plan(qtype, n_rows, k, m).ws;
+    return make_plan(qtype, n_rows, k, m, sm_cus()).ws;
+}
+
+void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
+{
+    const SmPlan p = make_plan(qtype, n_rows, k, m, cus);
+    out[0] = p.G;
+    out[1] = p.CH;
+    out[2] = (int64_t)p.lds;
+    out[3] = (int64_t)p.ws;
+    out[4] = p.narrow ? SmNarrow::kThreads : SmWide::kThreads;
+    out[5] = p.T;
 }
 
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream)
 {
-    const SmPlan p = make_plan(qtype, n_rows, k, m);
+    const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
     if ((int64_t)p.ws > workspace_bytes) return hipErrorInvalidValue;
     SmArgs a;
     a.W = W;

@@ -254,3 +254,37 @@ def test_chain_validation():
     assert call(xo=R) == B.KQ_ERR_ALIAS
     assert call(xo=WS + 1024) == B.KQ_ERR_ALIAS
     assert call(en=C.c_float(float("inf"))) == B.KQ_ERR_SHAPE
+
+
+def test_small_m_plans_fit_and_cover():
+    """Host-side launch plans of the verify matmul over a sweep of shapes and
+    device sizes: the staged window fits LDS, every workgroup's range is at
+    most one row of superblocks (so it touches at most two 256-row groups,
+    which the kernel's two register segments assume), and the workspace is
+    requested exactly when a row group is split between workgroups."""
+    for qt in (B.KQ_QTYPE_Q4K, B.KQ_QTYPE_Q6K):
+        for m in (2, 3, 5, 8, 9, 12, 16):
+            for k in (256, 512, 1280, 6656, 19968, B.KQ_MAX_K):
+                for n in (1, 17, 256, 300, 4097, 19968):
+                    for cus in (80, 256, 304):
+                        p = kq.kq_tune_small_m_plan(qt, n, k, m, cus)
+                        nb, rgs = k // 256, (n + 255) // 256
+                        T, G = p["tiles"], p["grid"]
+                        assert T == rgs * nb
+                        assert min(T, cus) <= G <= T
+                        assert p["threads"] == (1024 if m <= 8 else 512)
+                        assert p["lds"] <= 160 * 1024, (qt, m, k, n, p)
+                        assert p["window"] == -(-T // G) and p["window"] <= nb
+                        split = False
+                        for g in range(G):
+                            t0, t1 = g * T // G, (g + 1) * T // G
+                            assert t1 > t0
+                            assert (t1 - 1) // nb - t0 // nb <= 1  # at most two row groups
+                            split |= t0 % nb != 0 or (t1 % nb != 0 and t1 < T)
+                        if split:
+                            assert p["workspace"] >= G * 2 * 16 * 256 * 4
+                        else:
+                            assert p["workspace"] == 0
+    assert kq.kq_tune_small_m_plan(1, 8, 1024, 4, 256)["workspace"] >= 0
+    with pytest.raises(kq.KQError):
+        kq.kq_tune_small_m_plan(1, 8, 1024, 1, 256)
