@@ -51,6 +51,19 @@ kq_status kq_tune_set_chain_lanes(int lanes);
 kq_status kq_tune_set_matvec_impl(int qtype, int impl);
 
 /*
+ * The automatic launch shape of an M = 1 matvec of n_rows x k (staged != 0:
+ * on a staged input) on a device of `cus` compute units, ignoring any
+ * kq_tune_set_shape override (host arithmetic only; no device is touched),
+ * written to the host array out[6]: lanes per row, waves per workgroup,
+ * workgroups, depth, LDS bytes per workgroup (the activation staging), and
+ * workgroups per CU the grid is sized for.
+ *   n_rows >= 1, 1 <= cus <= 4096; qtype and k as for the matvecs.
+ * Errors: KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED, KQ_ERR_NULL.
+ */
+kq_status kq_tune_matvec_plan(int qtype, int64_t n_rows, int64_t k, int staged, int cus,
+                              int64_t *out);
+
+/*
  * The launch plan kq_matmul_small_m would use for this shape on a device of
  * `cus` compute units (host arithmetic only; no device is touched), written
  * to the host array out[6]: workgroups, superblocks in a workgroup's staged

@@ -81,6 +81,7 @@ def lib() -> C.CDLL:
     L.kq_tune_set_chain_lanes.argtypes = [C.c_int]
     L.kq_tune_set_matvec_impl.argtypes = [C.c_int, C.c_int]
     L.kq_tune_small_m_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
+    L.kq_tune_matvec_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
     L.kq_staged_bytes.argtypes = [C.c_int, _i64]
     L.kq_staged_bytes.restype = _i64
     L.kq_stage_activation.argtypes = [C.c_int, _vp, _vp, _i64, _vp]
@@ -94,7 +95,7 @@ def lib() -> C.CDLL:
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
                "kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
-               "kq_tune_small_m_plan",
+               "kq_tune_small_m_plan", "kq_tune_matvec_plan",
                "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
@@ -269,6 +270,14 @@ def kq_tune_set_chain_lanes(lanes: int) -> None:
 
 def kq_tune_set_matvec_impl(qtype: int, impl: int) -> None:
     _check(lib().kq_tune_set_matvec_impl(int(qtype), int(impl)), "kq_tune_set_matvec_impl")
+
+
+def kq_tune_matvec_plan(qtype: int, n_rows: int, k: int, staged: bool, cus: int) -> dict:
+    """The automatic M = 1 matvec launch shape on a device of `cus` CUs (host arithmetic)."""
+    out = (C.c_int64 * 6)()
+    _check(lib().kq_tune_matvec_plan(int(qtype), int(n_rows), int(k), int(bool(staged)), int(cus),
+                                     C.cast(out, C.c_void_p)), "kq_tune_matvec_plan")
+    return dict(zip(("lanes", "waves", "grid", "depth", "lds", "per_cu"), out))
 
 
 def kq_tune_small_m_plan(qtype: int, n_rows: int, k: int, m: int, cus: int) -> dict:

@@ -472,6 +472,18 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
     return KQ_OK;
 }
 
+kq_status kq_tune_matvec_plan(int qtype, int64_t n_rows, int64_t k, int staged, int cus,
+                              int64_t *out)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    if (!out) return KQ_ERR_NULL;
+    if (n_rows < 1 || n_rows > INT32_MAX || cus < 1 || cus > 4096) return KQ_ERR_SHAPE;
+    kqi::matvec_plan(qtype, n_rows, (int)k, staged != 0, cus, out);
+    return KQ_OK;
+}
+
 kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int cus,
                                int64_t *out)
 {

@@ -83,6 +83,10 @@ hipError_t launch_ffn_chain(const uint8_t *const *wg, const uint8_t *const *wu,
 
 // The shape the automatic choice would use (for reports and tests).
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);
+// The automatic matvec launch shape on a device of `cus` CUs, without the
+// process-wide override: out = {lanes, waves, grid, depth, LDS bytes per
+// workgroup, workgroups per CU}.
+void matvec_plan(int qtype, int64_t n_rows, int k, bool staged, int cus, int64_t *out);
 
 const char *variant_names();
 

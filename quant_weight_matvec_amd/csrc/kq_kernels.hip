@@ -693,9 +693,13 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
     const int64_t tiles = (n_rows + 7) / 8;
     const int64_t k = 128 * (int64_t)units;
     const bool long_q4 = !q6 && k > 8192;
-    // two workgroups per CU only where both stagings fit in the CU's LDS
-    const bool two_per_cu = !q6 && n_rows >= 32 * 2 * (int64_t)cus &&
-                            (k <= 8192 || (staged && 2 * staged_bytes<32, KQ_LIMBS>(k) <= 160 * 1024));
+    // two workgroups per CU: short rows with many of them, or long rows on a
+    // staged x where both stagings fit in the CU's LDS (32 lanes per row: a
+    // workgroup needs only a few rows to keep its 8 waves busy)
+    const bool two_per_cu =
+        !q6 && ((k <= 8192 && n_rows >= 32 * 2 * (int64_t)cus) ||
+                (long_q4 && staged && n_rows >= 8 * 2 * (int64_t)cus &&
+                 2 * staged_bytes<32, KQ_LIMBS>(k) <= 160 * 1024));
     const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
     const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
     const int waves = (q6 || two_per_cu || staged) ? 8 : 16;
@@ -844,6 +848,17 @@ MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
 {
     (void)m;
     return resolve_shape(qtype, n_rows, (int)k);
+}
+
+void matvec_plan(int qtype, int64_t n_rows, int k, bool staged, int cus, int64_t *out)
+{
+    const MatvecShape s = choose_shape(qtype, n_rows, 2 * (k >> 8), cus, staged);
+    out[0] = s.lanes;
+    out[1] = s.waves;
+    out[2] = s.grid;
+    out[3] = s.depth;
+    out[4] = (int64_t)(qtype == 1 ? staging_bytes<32>(k) : staging_bytes<16>(k));
+    out[5] = s.grid > cus ? 2 : 1;  // workgroups per CU the grid is sized for
 }
 
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,

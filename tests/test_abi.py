@@ -288,3 +288,23 @@ def test_small_m_plans_fit_and_cover():
     assert kq.kq_tune_small_m_plan(1, 8, 1024, 4, 256)["workspace"] >= 0
     with pytest.raises(kq.KQError):
         kq.kq_tune_small_m_plan(1, 8, 1024, 1, 256)
+
+
+def test_matvec_plans_fit():
+    """Automatic M = 1 launch shapes over a sweep of shapes and device sizes:
+    a workgroup's activation staging fits LDS, and so do the stagings of all
+    workgroups a CU is meant to hold at once; the shape is one the kernels
+    are built for."""
+    for qt in (B.KQ_QTYPE_Q4K, B.KQ_QTYPE_Q6K):
+        for staged in (False, True):
+            for k in (256, 1024, 6656, 8192, 8448, 19968, B.KQ_MAX_K):
+                for n in (1, 7, 300, 6656, 19968, 100000):
+                    for cus in (80, 256, 304):
+                        p = kq.kq_tune_matvec_plan(qt, n, k, staged, cus)
+                        assert p["lanes"] in (4, 8, 16, 32, 64) and 1 <= p["waves"] <= 16
+                        assert p["depth"] in (1, 2, 3)
+                        assert 1 <= p["grid"] <= p["per_cu"] * cus
+                        assert p["per_cu"] * p["lds"] <= 160 * 1024, (qt, staged, k, n, cus, p)
+                        assert p["lds"] == kq.kq_staged_bytes(qt, k)  # the staging is the LDS
+    with pytest.raises(kq.KQError):
+        kq.kq_tune_matvec_plan(1, 0, 1024, False, 256)
