@@ -45,10 +45,34 @@
  *     updates `residual` in place.
  *   - Results are deterministic: every reduction runs in a fixed order and no
  *     output is written with atomics, so identical inputs give identical bits.
- *   - Accuracy: a matvec row agrees with the exact (binary64) result within
- *     1e-3 * sum_i |w_i x_i|; the tail's outputs within 2e-3 absolute.
- *   - The library holds no state across calls and is safe to call from
- *     several host threads on different streams.
+ *   - Accuracy of the M = 1 matvecs (f32 or staged input).  Each input enters
+ *     as x_i + e_i with |e_i| <= 2^-22 * max|x_j| over its scale group (32
+ *     consecutive inputs for a Q4_K matrix, 16 for Q6_K; a group whose largest
+ *     magnitude is below 2^-100 uses the fixed step of such a group instead,
+ *     |e_i| <= 2^-123).  Integer dot products are exact; the scales, the Q4_K
+ *     min term, the Q6_K -32 offset and the fixed-order sums are f32.  Row r
+ *     then satisfies
+ *       |y_r - exact_r| <= 2^-22 * sum_g max_g|x| * sum_{i in g} |w_ri|
+ *                          + 2^-17 * C_r,
+ *     with C_r = sum_i (|a_ri| + |b_ri|) |x_i| for the weight written as
+ *     w = a - b before the min or offset cancels (Q4_K a = d*sc*q, b =
+ *     dmin*m; Q6_K a = d*sc*q, b = 32*d*sc).  This meets the tolerance
+ *     1e-3 * S_r, S_r = sum_i |w_ri x_i|, whenever every group satisfies
+ *     max_g|x| * sum_{i in g}|w_ri| <= 2000 * sum_{i in g}|w_ri x_i| and
+ *     C_r <= 60 * S_r: activations whose in-group spread is moderate (about
+ *     3 for N(0,1) inputs).  One input thousands of times larger than the
+ *     rest of its group, on a near-zero weight, can exceed 1e-3 * S_r; the
+ *     bound above still holds.
+ *     kq_matmul_small_m (M >= 2): each input enters as x_i + e_i with
+ *     |e_i| <= 2^-22 |x_i| + 2^-39 * max|x| over its 256-input superblock of
+ *     its activation row.  The tail's outputs agree within 2e-3 absolute.
+ *   - Calls hold no per-call state between them.  Process-wide state: the
+ *     device attributes each launcher caches, the kernel attribute set on
+ *     first use, the launch-shape override of kq_tune.h (benchmarks only; it
+ *     changes the split of the work, never the definition of the result),
+ *     and the scratch array of kq_matmul_small_m_noalloc.  Calls are safe
+ *     from several host threads on different streams, except concurrently
+ *     with kq_tune_set_shape.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -79,7 +103,6 @@ typedef int kq_status;
 #define KQ_MAX_K 40960      /* largest k (inputs per row) any matvec accepts */
 #define KQ_MAX_M 16         /* largest activation batch of kq_matmul_small_m */
 #define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
-#define KQ_MAX_CHAIN_HIDDEN 16384 /* largest hidden size of kq_ffn_chain */
 #define KQ_STAGED_LIMBS 3   /* byte limbs per input in a staged activation */
 #define KQ_MAX_FUSED_TAIL_K 8192 /* largest k of kq_ffn_tail_gate_up_q4k */
 
@@ -284,60 +307,6 @@ kq_status kq_fused_residual_norm_staged(float *residual, const float *projected,
                                         void *next_in_s, int next_qtype, const float *g_post,
                                         const float *g_next, int64_t rows, int64_t n,
                                         float eps_post, float eps_next, void *stream);
-
-/*
- * One decode token through `layers` FFN layers in a single persistent launch:
- * the FFN weight stream of the decode graph (Ch 10 "The forward pass at a
- * glance", section 10.3, boxes 11-13, recorded once per token; Ch 19 "The down
- * projection + residual", section 19.1).  With x_0 = x_in, for l = 0..layers-1:
- *   mid      = silu(W_gate[l] x_l) * (W_up[l] x_l)
- *   p        = W_down[l] mid
- *   residual = residual + rms_norm(p, eps_post) * g_post[l]
- *   x_{l+1}  = rms_norm(residual, eps_next) * g_next[l]
- * and x_out = x_layers.  Each step meets the tolerance of the matching
- * single-op call; results are deterministic but not bitwise equal to a chain
- * of single-op calls (the lane splits differ).
- *   w_gate, w_up    DEVICE array [layers] of device pointers, each to Q4_K
- *                   weights [ffn x hidden], 16-byte aligned.
- *   w_down          DEVICE array [layers] of device pointers to down_qtype
- *                   weights [hidden x ffn] (Q6_K 4-byte, Q4_K 16-byte aligned).
- *   down_qtype      KQ_QTYPE_Q6K or KQ_QTYPE_Q4K.
- *   g_post, g_next  DEVICE arrays [layers] of device pointers to [hidden] f32
- *                   gains, 16-byte aligned.
- *   x_in [hidden] f32 in, residual [hidden] f32 in/out, x_out [hidden] f32 out;
- *                   16-byte aligned and pairwise disjoint.
- *   hidden, ffn     multiples of 256; hidden <= KQ_MAX_CHAIN_HIDDEN,
- *                   ffn <= KQ_MAX_K; layers >= 1.
- *   workspace       device buffer of at least kq_ffn_chain_workspace_bytes()
- *                   bytes, 256-byte aligned, zeroed once before its first use;
- *                   a completed call leaves its control words zero again.
- *                   Calls sharing a workspace must not overlap in time.
- * The launch is cooperative (one workgroup per CU, all co-resident) and returns
- * KQ_ERR_LAUNCH if the device cannot host it.  The pointer tables live in
- * device memory and are checked by the kernel: a NULL or misaligned entry
- * makes it do nothing and record error 2 in the workspace; a grid barrier
- * that does not complete within about a second records error 1 and ends the
- * launch.  kq_ffn_chain_error() reads that word.
- * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE (also: workspace too small), KQ_ERR_ALIGN,
- * KQ_ERR_ALIAS, KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
- */
-kq_status kq_ffn_chain(const void *const *w_gate, const void *const *w_up,
-                       const void *const *w_down, int down_qtype, const float *const *g_post,
-                       const float *const *g_next, int64_t layers, int64_t hidden, int64_t ffn,
-                       const float *x_in, float *residual, float *x_out, float eps_post,
-                       float eps_next, void *workspace, int64_t workspace_bytes, void *stream);
-
-/* Workspace bytes kq_ffn_chain needs for these sizes (0 if they are invalid). */
-int64_t kq_ffn_chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype);
-
-/*
- * Synchronous: copies the error word of a kq_ffn_chain workspace to *error
- * (0 = none, 1 = barrier timeout, 2 = bad pointer table).  Waits for the
- * device to finish the work already enqueued on the default stream's device
- * memory (a blocking hipMemcpy).  Errors: KQ_ERR_NULL, KQ_ERR_ALIGN,
- * KQ_ERR_LAUNCH.
- */
-kq_status kq_ffn_chain_error(const void *workspace, int *error);
 
 /* Static text for a status code (never NULL). */
 const char *kq_status_string(kq_status s);

@@ -37,20 +37,6 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
                             int *grid, int *depth);
 
 /*
- * Lanes per weight row in the gate/up phase of kq_ffn_chain (2, 4 or 8;
- * default 4), process-wide.  Errors: KQ_ERR_SHAPE.
- */
-kq_status kq_tune_set_chain_lanes(int lanes);
-
-/*
- * Matvec implementation for qtype, process-wide: 0 = register-ring kernels
- * (each lane group streams its own rows), 1 = in-order LDS stream (each
- * workgroup reads its contiguous run of superblocks in address order through
- * an LDS ring; Q4_K only).  Errors: KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED.
- */
-kq_status kq_tune_set_matvec_impl(int qtype, int impl);
-
-/*
  * The automatic launch shape of an M = 1 matvec of n_rows x k (staged != 0:
  * on a staged input) on a device of `cus` compute units, ignoring any
  * kq_tune_set_shape override (host arithmetic only; no device is touched),

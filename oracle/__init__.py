@@ -97,8 +97,9 @@ class Oracle:
         m = X.shape[0]
         if X.shape[1] != k or W.size != n_rows * (k // 256) * BLOCK_BYTES[qt]:
             raise ValueError("shape mismatch")
-        Y = np.empty((m, n_rows), np.float64)
-        S = np.empty((m, n_rows), np.float64)
+        # NaN-filled, so a row the library failed to write cannot pass for a value
+        Y = np.full((m, n_rows), np.nan)
+        S = np.full((m, n_rows), np.nan)
         rc = self.lib.orc_matmul(qt, _p(W, _u8p), _p(X), k, n_rows, k, m, _p(Y), _p(S),
                                  int(nthreads))
         if rc:

@@ -233,16 +233,31 @@ int orc_matmul(int qtype, const uint8_t *W, const double *X, int64_t ldx,
     if (n_rows < nthreads) nthreads = n_rows > 0 ? (int)n_rows : 1;
     orc_mm_job jobs[256];
     pthread_t th[256];
+    int started[256];
+    /* Rows are split into contiguous ranges, one per thread.  Every row is
+     * computed by exactly one job in the same order whatever the thread
+     * count, so the results do not depend on it. */
     for (int t = 0; t < nthreads; ++t) {
+#if ORC_PLANT == 13
+        int64_t r1 = n_rows * (t + 1) / nthreads;
+        if (t + 1 < nthreads && r1 > n_rows * t / nthreads) --r1; /* drops a row per range */
+        jobs[t] = (orc_mm_job){qtype, W, X, ldx, n_rows, k, m, Y, S, n_rows * t / nthreads, r1};
+#else
         jobs[t] = (orc_mm_job){qtype, W, X, ldx, n_rows, k, m, Y, S,
                                n_rows * t / nthreads, n_rows * (t + 1) / nthreads};
+#endif
     }
     if (nthreads == 1) {
         orc_mm_worker(&jobs[0]);
         return 0;
     }
-    for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, orc_mm_worker, &jobs[t]);
-    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    /* a job whose thread cannot be started runs on the calling thread */
+    for (int t = 0; t < nthreads; ++t)
+        started[t] = pthread_create(&th[t], NULL, orc_mm_worker, &jobs[t]) == 0;
+    for (int t = 0; t < nthreads; ++t)
+        if (!started[t]) orc_mm_worker(&jobs[t]);
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t]) pthread_join(th[t], NULL);
     return 0;
 }
 

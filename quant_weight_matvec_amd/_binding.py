@@ -73,13 +73,6 @@ def lib() -> C.CDLL:
     L.kq_tune_get_shape.argtypes = [C.c_int, _i64, _i64, C.POINTER(C.c_int),
                                     C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]
     L.kq_probe_read_bw.argtypes = [_vp, _i64, _vp, C.c_int, _vp]
-    L.kq_ffn_chain.argtypes = [_vp, _vp, _vp, C.c_int, _vp, _vp, _i64, _i64, _i64, _vp, _vp,
-                               _vp, C.c_float, C.c_float, _vp, _i64, _vp]
-    L.kq_ffn_chain_workspace_bytes.argtypes = [_i64, _i64, C.c_int]
-    L.kq_ffn_chain_workspace_bytes.restype = _i64
-    L.kq_ffn_chain_error.argtypes = [_vp, C.POINTER(C.c_int)]
-    L.kq_tune_set_chain_lanes.argtypes = [C.c_int]
-    L.kq_tune_set_matvec_impl.argtypes = [C.c_int, C.c_int]
     L.kq_tune_small_m_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
     L.kq_tune_matvec_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
     L.kq_staged_bytes.argtypes = [C.c_int, _i64]
@@ -94,7 +87,6 @@ def lib() -> C.CDLL:
     for fn in ("kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
-               "kq_ffn_chain", "kq_ffn_chain_error", "kq_tune_set_chain_lanes", "kq_tune_set_matvec_impl",
                "kq_tune_small_m_plan", "kq_tune_matvec_plan",
                "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
@@ -239,37 +231,6 @@ def kq_tune_get_shape(qtype: int, n_rows: int, k: int) -> tuple[int, int, int, i
 def kq_probe_read_bw(buf, nbytes: int, out, grid: int, stream=None) -> None:
     _check(lib().kq_probe_read_bw(_ptr(buf), int(nbytes), _ptr(out), int(grid), _stream(stream)),
            "kq_probe_read_bw")
-
-
-def kq_ffn_chain(w_gate, w_up, w_down, down_qtype: int, g_post, g_next, layers: int, hidden: int,
-                 ffn: int, x_in, residual, x_out, eps_post: float = 1e-8, eps_next: float = 1e-5,
-                 workspace=None, workspace_bytes: int = 0, stream=None) -> None:
-    """Pointer tables (w_gate, w_up, w_down, g_post, g_next) are device arrays
-    of device pointers, e.g. int64 CUDA tensors built from data_ptr()s."""
-    rc = lib().kq_ffn_chain(_ptr(w_gate), _ptr(w_up), _ptr(w_down), int(down_qtype),
-                            _ptr(g_post), _ptr(g_next), int(layers), int(hidden), int(ffn),
-                            _ptr(x_in), _ptr(residual), _ptr(x_out), float(eps_post),
-                            float(eps_next), _ptr(workspace), int(workspace_bytes),
-                            _stream(stream))
-    _check(rc, "kq_ffn_chain")
-
-
-def kq_ffn_chain_workspace_bytes(hidden: int, ffn: int, down_qtype: int) -> int:
-    return int(lib().kq_ffn_chain_workspace_bytes(int(hidden), int(ffn), int(down_qtype)))
-
-
-def kq_ffn_chain_error(workspace) -> int:
-    e = C.c_int()
-    _check(lib().kq_ffn_chain_error(_ptr(workspace), C.byref(e)), "kq_ffn_chain_error")
-    return e.value
-
-
-def kq_tune_set_chain_lanes(lanes: int) -> None:
-    _check(lib().kq_tune_set_chain_lanes(int(lanes)), "kq_tune_set_chain_lanes")
-
-
-def kq_tune_set_matvec_impl(qtype: int, impl: int) -> None:
-    _check(lib().kq_tune_set_matvec_impl(int(qtype), int(impl)), "kq_tune_set_matvec_impl")
 
 
 def kq_tune_matvec_plan(qtype: int, n_rows: int, k: int, staged: bool, cus: int) -> dict:

@@ -355,64 +355,6 @@ kq_status kq_fused_residual_norm_staged(float *residual, const float *projected,
                                      staged_group(next_qtype), (hipStream_t)stream));
 }
 
-int64_t kq_ffn_chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype)
-{
-    if ((down_qtype != KQ_QTYPE_Q4K && down_qtype != KQ_QTYPE_Q6K) || hidden < KQ_QK ||
-        ffn < KQ_QK || hidden % KQ_QK || ffn % KQ_QK || hidden > KQ_MAX_CHAIN_HIDDEN ||
-        ffn > KQ_MAX_K)
-        return 0;
-    return (int64_t)kqi::chain_workspace_bytes(hidden, ffn, down_qtype);
-}
-
-kq_status kq_ffn_chain(const void *const *w_gate, const void *const *w_up,
-                       const void *const *w_down, int down_qtype, const float *const *g_post,
-                       const float *const *g_next, int64_t layers, int64_t hidden, int64_t ffn,
-                       const float *x_in, float *residual, float *x_out, float eps_post,
-                       float eps_next, void *workspace, int64_t workspace_bytes, void *stream)
-{
-    if (!w_gate || !w_up || !w_down || !g_post || !g_next || !x_in || !residual || !x_out ||
-        !workspace)
-        return KQ_ERR_NULL;
-    if (down_qtype != KQ_QTYPE_Q4K && down_qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
-    if (layers < 1 || layers > 100000 || hidden < KQ_QK || ffn < KQ_QK || hidden % KQ_QK ||
-        ffn % KQ_QK)
-        return KQ_ERR_SHAPE;
-    if (hidden > KQ_MAX_CHAIN_HIDDEN || ffn > KQ_MAX_K) return KQ_ERR_UNSUPPORTED;
-    if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
-        return KQ_ERR_SHAPE;
-    if (!aligned(w_gate, 8) || !aligned(w_up, 8) || !aligned(w_down, 8) || !aligned(g_post, 8) ||
-        !aligned(g_next, 8) || !aligned(x_in, 16) || !aligned(residual, 16) ||
-        !aligned(x_out, 16) || !aligned(workspace, 256))
-        return KQ_ERR_ALIGN;
-    const int64_t need = (int64_t)kqi::chain_workspace_bytes(hidden, ffn, down_qtype);
-    if (workspace_bytes < need) return KQ_ERR_SHAPE;
-    const int64_t hb = hidden * 4;
-    if (overlap(x_out, hb, residual, hb) || overlap(x_out, hb, x_in, hb) ||
-        overlap(residual, hb, x_in, hb) || overlap(workspace, workspace_bytes, x_out, hb) ||
-        overlap(workspace, workspace_bytes, residual, hb) ||
-        overlap(workspace, workspace_bytes, x_in, hb))
-        return KQ_ERR_ALIAS;
-    kq_status s = check_device();
-    if (s != KQ_OK) return s;
-    if (kqi::chain_lds_bytes(hidden, ffn, down_qtype, kqi::chain_grid()) > 160 * 1024)
-        return KQ_ERR_UNSUPPORTED;
-    return from_hip(kqi::launch_ffn_chain(
-        (const uint8_t *const *)w_gate, (const uint8_t *const *)w_up,
-        (const uint8_t *const *)w_down, down_qtype, g_post, g_next, (int)layers, (int)hidden,
-        (int)ffn, x_in, residual, x_out, eps_post, eps_next, workspace, (hipStream_t)stream));
-}
-
-kq_status kq_ffn_chain_error(const void *workspace, int *error)
-{
-    if (!workspace || !error) return KQ_ERR_NULL;
-    if (!aligned(workspace, 256)) return KQ_ERR_ALIGN;
-    uint32_t w[3] = {0, 0, 0};
-    if (hipMemcpy(w, workspace, sizeof w, hipMemcpyDeviceToHost) != hipSuccess)
-        return KQ_ERR_LAUNCH;
-    *error = (int)w[2];
-    return KQ_OK;
-}
-
 const char *kq_status_string(kq_status s)
 {
     switch (s) {
@@ -492,21 +434,6 @@ kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int 
     if (!out) return KQ_ERR_NULL;
     if (n_rows < 1 || m < 2 || cus < 1 || cus > 4096) return KQ_ERR_SHAPE;
     kqi::small_m_plan(qtype, (int)n_rows, (int)k, m, cus, out);
-    return KQ_OK;
-}
-
-kq_status kq_tune_set_matvec_impl(int qtype, int impl)
-{
-    if ((qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) || impl < 0 || impl > 1) return KQ_ERR_SHAPE;
-    if (impl == 1 && qtype != KQ_QTYPE_Q4K) return KQ_ERR_UNSUPPORTED;
-    kqi::set_matvec_impl(qtype, impl);
-    return KQ_OK;
-}
-
-kq_status kq_tune_set_chain_lanes(int lanes)
-{
-    if (lanes != 2 && lanes != 4 && lanes != 8) return KQ_ERR_SHAPE;
-    kqi::set_chain_lanes(lanes);
     return KQ_OK;
 }
 

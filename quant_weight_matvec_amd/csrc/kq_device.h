@@ -91,6 +91,21 @@ __host__ __device__ constexpr int64_t plane_bytes(int64_t k) { return k + (k >> 
 // Byte offset of input j within a plane.
 __host__ __device__ constexpr int plane_off(int j) { return j + ((j >> 7) << 4); }
 
+// Smallest group exponent: a group whose largest magnitude is below 2^kMinExp
+// is encoded on the grid of 2^(kMinExp - QB) (absolute error at most
+// 2^(kMinExp - QB - 1)) instead of its own, so its back-scale stays a normal
+// float; with the group's own exponent it would underflow to zero below
+// about 2^-127 and drop the group from the dot product.
+constexpr int kMinExp = -100;
+
+// Encodes float4 number i of a k-vector (n4 = k/4 float4) into the planes and
+// the group tables.  Preconditions: the TPG = GROUP/4 consecutive lanes that
+// hold one scale group all call it together with consecutive i (the group max
+// and sum are DPP reductions over them), and 0 <= i < n4 for those lanes; a
+// call with i >= n4 stores nothing (whole groups are either all in range or
+// all out of it, since n4 is a multiple of TPG).  Per input the rounding error
+// is at most 2^(e - QB - 1) <= 2^-QB * max|x over the group|, e the exponent
+// with max|x| < 2^e.
 template <int GROUP, int LIMBS>
 __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict__ plane, int n4,
                                             float *__restrict__ tscale, float *__restrict__ tsum)
@@ -99,7 +114,7 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
     constexpr int QB = limb_bits<LIMBS>();
     const float mx = group_max<TPG>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     const float sm = group_sum<TPG>((v.x + v.y) + (v.z + v.w));
-    const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
+    const int e = max(__builtin_amdgcn_frexp_expf(mx), kMinExp);  // mx < 2^e
     const int sh = QB - e;
     // q = x * 2^sh rounded to nearest even, |q| <= 2^QB.  Adding 1.5 * 2^23
     // rounds once and leaves q in the low mantissa bits of a float in
@@ -129,7 +144,10 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
         pk[0] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u;
         pk[1] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u;
     }
-    // word i holds inputs 4i..4i+3; a plane is n4 + n4/8 words
+    // word i holds inputs 4i..4i+3; a plane is n4 + n4/8 words.  Past the end
+    // (i >= n4) the word index would land in the next plane or, for the last
+    // plane, in the scale and sum tables, so nothing is stored.
+    if (i >= n4) return;
     const int pw = n4 + (n4 >> 3), wi = i + ((i >> 5) << 2);
 #pragma unroll
     for (int l = 0; l < LIMBS; ++l) plane[l * pw + wi] = pk[l];

@@ -44,15 +44,6 @@ hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs
                              int n_rows, int k, hipStream_t stream);
 // staged form of x with scale groups of `group` (16 or 32)
 hipError_t launch_stage(const float *x, uint8_t *xs, int k, int group, hipStream_t stream);
-// In-order LDS-streaming matvec (kq_stream.hip).  matvec_impl(qtype): 0 =
-// register-ring kernels of kq_kernels.hip, 1 = LDS stream (Q4_K).
-int matvec_impl(int qtype);
-void set_matvec_impl(int qtype, int impl);
-size_t q4k_stream_lds(int n_rows, int k, int grid, int nbuf, int *rows_per_wg, int *x_bytes,
-                      int *part_off, int *ring_off);
-hipError_t launch_matvec_q4k_stream(const uint8_t *W, const float *x, float *y, int n_rows, int k,
-                                    const float *silu_gate, int grid, int nbuf, hipStream_t stream);
-
 // Batched small-m kernel (kq_small_m.hip), m = 2..16.
 size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
 // The launch plan for a device of `cus` CUs: out = {workgroups, staged window
@@ -69,17 +60,6 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
                              hipStream_t stream);
-
-// Persistent FFN chain (kq_chain.hip).
-size_t chain_workspace_bytes(int64_t hidden, int64_t ffn, int down_qtype);
-size_t chain_lds_bytes(int64_t hidden, int64_t ffn, int down_qtype, int grid);
-int chain_grid();
-void set_chain_lanes(int lanes);
-hipError_t launch_ffn_chain(const uint8_t *const *wg, const uint8_t *const *wu,
-                            const uint8_t *const *wd, int down_qtype, const float *const *gpost,
-                            const float *const *gnext, int layers, int hidden, int ffn,
-                            const float *x_in, float *residual, float *x_out, float eps_post,
-                            float eps_next, void *workspace, hipStream_t stream);
 
 // The shape the automatic choice would use (for reports and tests).
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);

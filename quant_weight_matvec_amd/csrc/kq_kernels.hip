@@ -19,8 +19,9 @@
 //    a signed integer of LIMBS*8-1 bits stored as LIMBS signed bytes in
 //    separate planes.  The inner loop is then v_dot4_i32_i8 of raw quant
 //    bytes against each byte plane: four multiply-adds per instruction and no
-//    per-weight float conversion.  With three limbs the value keeps 23 bits
-//    relative to the group maximum.
+//    per-weight float conversion.  With three limbs an input is rounded to a
+//    multiple of 2^(e-22), e the group exponent (max|x| < 2^e), so its error
+//    is at most 2^-22 times the group's largest magnitude.
 //  * Work split: `lanes` lanes share a row and walk its half-superblock units
 //    (128 weights) in stride; a wave holds 64/lanes rows; a workgroup owns a
 //    contiguous row range.  Per-lane partial sums are folded with a fixed
@@ -864,13 +865,6 @@ void matvec_plan(int qtype, int64_t n_rows, int k, bool staged, int cus, int64_t
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
                              int n_rows, int k, const float *silu_gate, hipStream_t stream)
 {
-    if (matvec_impl(1) == 1 && !xs) {
-        const int grid = device_cus();
-        for (int nbuf = 7; nbuf >= 2; --nbuf)
-            if (q4k_stream_lds(n_rows, k, grid, nbuf, nullptr, nullptr, nullptr, nullptr) <=
-                160 * 1024)
-                return launch_matvec_q4k_stream(W, x, y, n_rows, k, silu_gate, grid, nbuf, stream);
-    }
     return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k, xs != nullptr), W, x, xs, y,
                                     n_rows, k,
                                     silu_gate, stream);

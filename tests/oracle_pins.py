@@ -249,6 +249,24 @@ def pin_matvec_vs_numpy(o):
         assert np.array_equal(y0, Y[2]) and np.array_equal(s0, S[2]), "small-M row != matvec"
 
 
+def pin_threaded_matmul_equals_single_thread(o):
+    """The row split over threads changes nothing: every row is computed by one
+    job in the same order, so Y and S are bitwise those of one thread, for
+    thread counts that do and do not divide the row count (37 rows)."""
+    rng = np.random.default_rng(17)
+    n, k, m = 37, 512, 3
+    for qt in ("q4k", "q6k"):
+        W, D = _random_encoded(qt, rng, n, k)
+        X = rng.standard_normal((m, k))
+        Y1, S1 = o.matmul(qt, W, X, n, k, nthreads=1)
+        Yref = X @ D.T
+        assert np.all(np.abs(Y1 - Yref) <= 1e-12 * S1), f"{qt} single-thread vs numpy"
+        for t in (2, 3, 16, 64):
+            Yt, St = o.matmul(qt, W, X, n, k, nthreads=t)
+            assert np.array_equal(Yt, Y1) and np.array_equal(St, S1), \
+                f"{qt} matmul with {t} threads differs from one thread"
+
+
 # --------------------------------------------------------------------------
 # SiLU-gated product
 def pin_silu(o):
@@ -336,6 +354,6 @@ def pin_ffn_layer_composition(o):
 ALL_PINS = [
     pin_f16_exhaustive, pin_q4k_onehot, pin_q4k_scale_and_min_fields, pin_q6k_onehot,
     pin_q6k_qh_lanes, pin_q6k_scale_fields, pin_closed_forms, pin_exact_integer_inputs,
-    pin_matvec_vs_numpy, pin_silu, pin_rms_norm_invariants, pin_tail_worked_example,
+    pin_matvec_vs_numpy, pin_threaded_matmul_equals_single_thread, pin_silu, pin_rms_norm_invariants, pin_tail_worked_example,
     pin_tail_rows_and_invariants, pin_ffn_layer_composition,
 ]

@@ -252,31 +252,6 @@ def test_graph_replay_matches_eager():
         _ = torch.randn(1000, device="cuda").sum().item()  # eager work between replays
 
 
-# ---------------------------------------------------------------- in-order LDS stream (Q4_K)
-@pytest.mark.parametrize("n,k", [(1, 256), (77, 1024), (1000, 6656), (4100, 768),
-                                 (19968, 6656), (6656, 19968)])
-def test_q4k_lds_stream_impl(n, k):
-    """The alternative Q4_K matvec (each workgroup streams its contiguous run
-    of superblocks through an LDS ring) against the oracle, plain and with the
-    SiLU epilogue; sampled rows at the full shapes."""
-    W = weights("q4k", n, k, 9100 + n)
-    x = I.normal_f32(k, stream=9101 + n)
-    g = I.normal_f32(n, stream=9102 + n)
-    Wd, xd, gd = dev(W), dev(x), dev(g)
-    rows = sample_rows(n, 192, seed=n)
-    yr, S = oracle_rows("q4k", W, x, rows, k)
-    kq.kq_tune_set_matvec_impl(kq.KQ_QTYPE_Q4K, 1)
-    try:
-        y = gpu_matvec("q4k", Wd, xd, n, k)
-        ys = gpu_matvec("q4k", Wd, xd, n, k, gd)
-    finally:
-        kq.kq_tune_set_matvec_impl(kq.KQ_QTYPE_Q4K, 0)
-    assert_matvec_close(y[rows], yr, S, what=f"stream {n}x{k}")
-    gg = g.astype(np.float64)
-    silu = gg / (1.0 + np.exp(-gg))
-    assert np.allclose(ys, silu * y, rtol=1e-6, atol=1e-30), "SiLU epilogue"
-
-
 # ---------------------------------------------------------------- gate + up in one launch
 def _mid_bound(gr, Sg, ur, Su):
     dg, du = 1e-3 * Sg, 1e-3 * Su

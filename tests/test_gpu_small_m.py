@@ -48,6 +48,9 @@ def check(qt, n, k, m, seed, rows=None, xscale=None, ldx=None):
     if xscale is not None:
         X[:, :k] *= np.asarray(xscale, np.float32).reshape(-1, 1)
     Yg = run(qt, dev(W), dev(X), ldx, n, k, m)
+    # every output written, also outside the sampled rows (a partial tile of
+    # the stream-K split that never arrives would leave its rows NaN)
+    assert np.all(np.isfinite(Yg)), f"{qt} {n}x{k} m={m}: non-finite outputs"
     rows = np.arange(n) if rows is None else rows
     Yr, S = O.matmul(qt, np.ascontiguousarray(W[rows]), X[:, :k], len(rows), k, nthreads=NTHREADS)
     worst = 0.0

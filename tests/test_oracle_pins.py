@@ -22,6 +22,7 @@ PLANTS = {
     10: "f16 exponent bias 16",
     11: "matvec drops the last superblock of each row",
     12: "activation index reversed inside each superblock",
+    13: "threaded row split leaves one row of each range uncomputed",
 }
 
 
