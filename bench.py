@@ -80,7 +80,6 @@ STAGED_BYTES = {
 PASS_BYTES = LAYERS * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
 WEIGHT_BYTES_PASS = LAYERS * (2 * q4k_bytes(FFN, HIDDEN) + q6k_bytes(HIDDEN, FFN))
 KERNEL_SYMBOL = {
-    "chain": "ffn_chain_kernel",
     "gate": "q4k_matvec_kernel<..., false>",
     "up_silu": "q4k_matvec_kernel<..., true>",
     "down": "q6k_matvec_kernel",
@@ -97,11 +96,10 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-CHAIN_SOURCES = ("kq_chain.hip", "kq_device.h")
 GATE_UP_SOURCES = ("kq_kernels.hip", "kq_device.h")
 
 
-def kernel_source_hash(files=CHAIN_SOURCES) -> str:
+def kernel_source_hash(files=GATE_UP_SOURCES) -> str:
     """Hash of the sources a kernel's machine code is built from; a committed
     counter summary is used only while it matches."""
     h = hashlib.sha256()
@@ -142,31 +140,6 @@ class FFNChain:
                     for _ in range(2)]
         self.mid_s = torch.empty(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, FFN), dtype=u8, device=dev)
         self.R = [self.residual, torch.empty(HIDDEN, device=dev)]  # residual ping-pong
-
-    def build_chain(self):
-        """Device pointer tables and workspace for kq_ffn_chain."""
-        torch, kq = self.torch, self.kq
-        tab = lambda ts: torch.tensor([t.data_ptr() for t in ts], dtype=torch.int64, device="cuda")
-        self.tables = [tab(self.Wg), tab(self.Wu), tab(self.Wd), tab(self.gp), tab(self.gn)]
-        self.ws_bytes = kq.kq_ffn_chain_workspace_bytes(HIDDEN, FFN, kq.KQ_QTYPE_Q6K)
-        self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.int32, device="cuda")
-        self.x_out = torch.empty(HIDDEN, device="cuda")
-
-    def run_chain(self, ev=None):
-        kq = self.kq
-        self.entry_norm()
-        wg, wu, wd, gp, gn = self.tables
-        call = lambda: kq.kq_ffn_chain(wg, wu, wd, kq.KQ_QTYPE_Q6K, gp, gn, self.layers, HIDDEN,
-                                       FFN, self.x[0], self.residual, self.x_out, 1e-8, 1e-5,
-                                       self.ws, self.ws_bytes)
-        if ev is None:
-            call()
-        else:
-            a, b = ev.pair()
-            a.record()
-            call()
-            b.record()
-            ev.note("chain", a, b)
 
     def entry_norm(self):
         # x_0 = rms_norm(residual, 1e-5) with unit gain: the tail with a zero
@@ -320,32 +293,108 @@ class EventLog:
         return {k: np.array(v) for k, v in out.items()}
 
 
-def read_ceiling(torch, kq, nbytes=4 << 30, reps=5):
+def graph_of(torch, calls):
+    """The launches of `calls` (a list of no-argument functions) captured as
+    one graph on a side stream."""
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s_):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, launches, reps=5, warm=2):
+    """Per-launch microseconds of each of `reps` replays of a graph of
+    `launches` back-to-back launches (HIP events on the replay stream), after
+    `warm` untimed replays: (median, CV, all)."""
+    for _ in range(warm):
+        g.replay()
+    times = []
+    for _ in range(reps):
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ea.record()
+        g.replay()
+        eb.record()
+        torch.cuda.synchronize()
+        times.append(ea.elapsed_time(eb) * 1e3 / launches)
+    t = np.array(times)
+    return float(np.median(t)), float(np.std(t) / np.mean(t)), [round(float(v), 3) for v in t]
+
+
+# the matvec weight streams the probe windows are matched to
+WINDOWS = {"q4k_19968x6656": q4k_bytes(FFN, HIDDEN), "q6k_6656x19968": q6k_bytes(HIDDEN, FFN),
+           "gate_up_pair": 2 * q4k_bytes(FFN, HIDDEN)}
+
+
+def read_ceiling(torch, kq, nbytes=4 << 30, reps=5, launches=52):
+    """The HBM read ceiling the matvecs are compared with.
+    (1) One pass over a 4 GiB buffer for a sweep of probe variants (workgroup
+    size and count, loads in flight per thread, non-temporal or normal loads,
+    grid-stride or one contiguous chunk per workgroup); median of `reps`.
+    (2) With the best variant and with the chunked one, windows of the sizes
+    the matvecs stream, at rotating offsets through the 4 GiB buffer, as a
+    graph of `launches` back-to-back launches timed like the isolated matvecs
+    (so the two compare like with like)."""
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(7)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    grid = cus * 8
-    out = torch.empty(grid * 4, dtype=torch.int32, device="cuda")
-    kq.kq_probe_read_bw(buf, nbytes, out, grid)
+    out = torch.empty(cus * 64 * 16, dtype=torch.int32, device="cuda")
     E = torch.cuda.Event
-    times = []
-    for _ in range(reps):
-        a, b = E(enable_timing=True), E(enable_timing=True)
-        a.record()
-        kq.kq_probe_read_bw(buf, nbytes, out, grid)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) / 1e3)
-    del buf
-    return nbytes / np.median(times) / 1e9
+    sweep = []
+    for block in (256, 512, 1024):
+        for per_cu in (1, 2, 4, 8, 16):
+            grid = cus * per_cu
+            if grid * block > cus * 2048 * 4:  # beyond four workgroups' worth of waves per CU
+                continue
+            for unroll in (4, 8, 16):
+                for flags in (0, 1, 2, 3):
+                    kq.kq_probe_read_bw(buf, nbytes, out, grid, block, unroll, flags)
+                    ts = []
+                    for _ in range(reps):
+                        a, b = E(enable_timing=True), E(enable_timing=True)
+                        a.record()
+                        kq.kq_probe_read_bw(buf, nbytes, out, grid, block, unroll, flags)
+                        b.record()
+                        torch.cuda.synchronize()
+                        ts.append(a.elapsed_time(b) / 1e3)
+                    sweep.append({"grid": grid, "block": block, "unroll": unroll,
+                                  "nontemporal": bool(flags & 1), "chunked": bool(flags & 2),
+                                  "GBps": round(nbytes / float(np.median(ts)) / 1e9, 1)})
+    sweep.sort(key=lambda r: -r["GBps"])
+    best = sweep[0]
+    best_chunk = next(r for r in sweep if r["chunked"])
+    windows = {}
+    for name, wb in WINDOWS.items():
+        wb16 = (wb + 4095) // 4096 * 4096
+        nwin = nbytes // wb16
+        for label, v in (("best", best), ("chunked", best_chunk)):
+            fl = (1 if v["nontemporal"] else 0) | (2 if v["chunked"] else 0)
+            calls = [lambda o=(i % nwin) * wb16, v=v, fl=fl: kq.kq_probe_read_bw(
+                buf[o // 4:], wb16, out, v["grid"], v["block"], v["unroll"], fl)
+                for i in range(launches)]
+            g = graph_of(torch, calls)
+            med, cv, _ = time_graph(torch, g, launches, reps)
+            del g
+            windows[f"{name}_{label}"] = {"bytes": wb16, "windows_rotated": int(nwin),
+                                          "us_median": round(med, 3), "us_cv": round(cv, 4),
+                                          "GBps": round(wb16 / med / 1e3, 1)}
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"GBps_4GiB_best": best["GBps"], "best_variant": best, "best_chunked": best_chunk,
+            "sweep_top": sweep[:8], "sweep_worst": sweep[-3:], "size_matched": windows}
 
 
-def isolated_matvecs(torch, kq, I, reps=5):
-    """Single matvecs at the FFN shapes, each launch on a different one of
-    >= 1 GiB of weight copies so the Infinity Cache cannot serve them: a graph
-    of two launches per copy, replayed `reps` times between HIP events on the
-    replay stream; time per launch = elapsed / launches.  Each shape with x
-    in f32 (every workgroup encodes it) and with x staged beforehand (the form
+def isolated_matvecs(torch, kq, I, reps=5, launches=52):
+    """Single matvecs at the FFN shapes, timed as the pass runs them: a graph
+    of `launches` back-to-back launches, each on the next of >= 1 GiB of
+    weight copies (so the Infinity Cache cannot serve them), replayed `reps`
+    times between HIP events on the replay stream; per-launch time = replay
+    time / launches; median and CV over the replays.  Each shape with x in
+    f32 (every workgroup encodes it) and with x staged beforehand (the form
     the pass hands between launches)."""
     out = {}
     cases = [("q4k_19968x6656", "q4k", FFN, HIDDEN), ("q4k_6656x19968", "q4k", HIDDEN, FFN),
@@ -360,33 +409,18 @@ def isolated_matvecs(torch, kq, I, reps=5):
         kq.kq_stage_activation(qtype, x, xs, k)
         y = torch.empty(n, device="cuda")
         fn = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
+        nl = max(launches, ncopy)
         for form, call, xbytes in (
                 ("", lambda c: fn(c, x, y, n, k), 4 * k),
                 ("_staged", lambda c: kq.kq_matvec_staged(qtype, c, xs, y, n, k), xs.numel())):
-            launches = 2 * ncopy
-            s_ = torch.cuda.Stream()
-            s_.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s_):
-                for i in range(launches):
-                    call(copies[i % ncopy])
-            torch.cuda.synchronize()
-            g.replay()
-            times = []
-            for _ in range(reps):
-                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                ea.record()
-                g.replay()
-                eb.record()
-                torch.cuda.synchronize()
-                times.append(ea.elapsed_time(eb) * 1e3 / launches)
+            g = graph_of(torch, [lambda c=copies[i % ncopy]: call(c) for i in range(nl)])
+            med, cv, all_ = time_graph(torch, g, nl, reps)
             del g
-            us = float(np.mean(times))
             nbytes = W.numel() + xbytes + 4 * n
-            out[name + form] = {"us_avg": round(us, 3), "us_cv": round(float(np.std(times) / us), 4),
-                                "GBps": round(nbytes / us / 1e3, 1),
-                                "frac_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+            out[name + form] = {"us_median": round(med, 3), "us_cv": round(cv, 4),
+                                "us_replays": all_, "launches_per_replay": nl,
+                                "GBps": round(nbytes / med / 1e3, 1),
+                                "frac_peak": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
                                 "copies_rotated": ncopy, "bytes": nbytes}
             if not form:  # the automatic shape of the f32 form (the staged form may differ)
                 out[name]["shape"] = list(kq.kq_tune_get_shape(qtype, n, k))
@@ -443,32 +477,54 @@ def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
     return out
 
 
-def cpu_baseline(I, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(I, budget_s=8.0):
     """The oracle (plain C, binary64) on a bounded sample of the same pass:
-    layer 0's FFN (gate, up, silu, down, tail) at full size, repeated until
-    about budget_s seconds of CPU work."""
+    layer 0's FFN (gate, up, silu, down, tail) at full size, repeated for
+    about budget_s seconds, on one thread and on all the cores this process
+    may use (at most 16: the CPU share of one GPU on the box)."""
     import oracle
     o = oracle.get()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(16, avail))
     Wg = I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, 0, I.ROLE_W_GATE))
     Wu = I.q4k_matrix(FFN, HIDDEN, stream=I.stream_id(4, 0, I.ROLE_W_UP))
     Wd = I.q6k_matrix(HIDDEN, FFN, stream=I.stream_id(4, 0, I.ROLE_W_DOWN))
     gp, gn = I.gains_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_GPOST)), I.gains_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_GNEXT))
     res = I.normal_f32(HIDDEN, stream=I.stream_id(4, 0, I.ROLE_RESID)).astype(np.float64)
     x = o.rms_norm(res, 1e-5)
-    runs, t0 = 0, time.time()
-    while True:
-        o.ffn_layer(Wg, Wu, Wd, HIDDEN, FFN, x, res, gp, gn, nthreads=threads)
-        runs += 1
-        if time.time() - t0 >= budget_s:
-            break
-    dt = time.time() - t0
     layer_bytes = WEIGHT_BYTES_PASS / LAYERS
-    return {"value": round(layer_bytes * runs / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{runs} run(s) of layer 0 of the 52-layer FFN pass (gate, up, silu, down, tail; "
-                      f"{layer_bytes / 1e6:.1f} MB of weights each) in {dt:.1f}s; "
-                      f"pass-equivalent {dt / runs * LAYERS:.1f} s/token"}
+
+    def run(nt):
+        runs, t0 = 0, time.time()
+        while True:
+            o.ffn_layer(Wg, Wu, Wd, HIDDEN, FFN, x, res, gp, gn, nthreads=nt)
+            runs += 1
+            if time.time() - t0 >= budget_s:
+                break
+        dt = time.time() - t0
+        return runs, dt, layer_bytes * runs / dt / 1e9
+
+    r1, d1, v1 = run(1)
+    rn, dn, vn = run(threads)
+    return {"value": round(vn, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rn} run(s) of layer 0 of the 52-layer FFN pass (gate, up, silu, down, "
+                      f"tail; {layer_bytes / 1e6:.1f} MB of weights each) on {threads} threads in "
+                      f"{dn:.1f}s; pass-equivalent {dn / rn * LAYERS:.1f} s/token",
+            "cpu_model": cpu_model(), "cores_available": avail,
+            "single_thread": {"value": round(v1, 3), "unit": "GB/s", "cores": 1,
+                              "sample": f"{r1} run(s) of the same layer on one thread in {d1:.1f}s; "
+                                        f"pass-equivalent {d1 / r1 * LAYERS:.1f} s/token"}}
 
 
 def load_pmc(symbol_key: str, src_hash: str):
@@ -495,6 +551,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time uncaptured launches instead of a graph")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu"),
+                    help="run one section alone (for profiler runs) and print its results")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the decode path is "
@@ -508,7 +566,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kq.lib()
     log(kq.kq_build_info())
-    src_hash = {"gate_up": kernel_source_hash(GATE_UP_SOURCES), "chain": kernel_source_hash(CHAIN_SOURCES)}
+    src_hash = {"gate_up": kernel_source_hash(GATE_UP_SOURCES)}
 
     if args.calibration_copy:
         # a plain copy kernel of known size: 1 GiB read, 1 GiB written
@@ -521,11 +579,22 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
+    if args.only and args.only != "pass":
+        log(f"section {args.only} only")
+        sec = {"isolated": lambda: {"isolated_matvec": isolated_matvecs(torch, kq, I)},
+               "small_m": lambda: {"small_m": small_m_sweep(torch, kq, I)},
+               "probe": lambda: {"read_ceiling": read_ceiling(torch, kq)},
+               "cpu": lambda: {"cpu_baseline": cpu_baseline(I)}}[args.only]()
+        print(json.dumps({"section": args.only, **sec, "build": kq.kq_build_info()}), flush=True)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        return
+    if args.only == "pass":
+        args.no_extras = args.no_cpu_baseline = True
+
     chain = FFNChain(torch, kq, I, args.layers)
-    chain.build_chain()
     layers = args.layers
     pass_bytes = layers * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
-    bytes_chain_launch = pass_bytes - BYTES["tail"]  # the entry norm is its own launch
     stream = torch.cuda.current_stream()
 
     def timed(fn, steps):
@@ -579,18 +648,7 @@ def main():
     graph4 = capture(four_pass)
     per_op4_ms, _ = timed((lambda: graph4.replay()) if graph4 is not None else four_pass,
                           args.steps)
-    for _ in range(max(1, args.warmup)):
-        chain.run_chain()
-    torch.cuda.synchronize()
-    assert kq.kq_ffn_chain_error(chain.ws) == 0, "chain kernel reported an error"
-    chain_ms, _ = timed(chain.run_chain, args.steps)
-    assert kq.kq_ffn_chain_error(chain.ws) == 0, "chain kernel reported an error"
-    ev = EventLog(torch)
-    for _ in range(max(2, min(args.steps, 5))):
-        chain.run_chain(ev)
-
     per_kernel = chain.per_kernel_us(max(2, min(args.steps, 5))) if graph_t is not None else {}
-    per = ev.summary()
     kernels = {}
     for name, avg in per_kernel.items():  # per-op kernels: graph of one launch per layer
         nb = GATE_UP_BYTES if name == "gate_up" else (STAGED_BYTES.get(name) or BYTES[name])
@@ -600,13 +658,6 @@ def main():
                          "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
                          "timing": f"graph of {layers} back-to-back launches (one per layer), "
                                    "HIP events on the replay stream"}
-    for name, us in per.items():  # the persistent chain: events around each launch
-        avg = float(np.mean(us))
-        gbps = bytes_chain_launch / (avg * 1e-6) / 1e9
-        kernels[name] = {"symbol": KERNEL_SYMBOL[name], "launches": int(us.size), "us_avg": round(avg, 3),
-                         "us_median": round(float(np.median(us)), 3), "bytes_per_launch": bytes_chain_launch,
-                         "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                         "timing": "HIP events around each launch"}
     # the dominant kernel of the timed step: gate+up+SiLU (150 MB of its ~260 MB per layer)
     dk = kernels.get("tail_gate_up")
     roofline = None
@@ -626,20 +677,19 @@ def main():
         "graph_4_launches_per_layer": {"ms_per_step": round(per_op4_ms, 4),
                                        "GBps": round(pass_bytes / (per_op4_ms * 1e-3) / 1e9, 1),
                                        "launches_per_step": 4 * layers + 1},
-        "persistent_chain": {"ms_per_step": round(chain_ms, 4),
-                             "GBps": round(pass_bytes / (chain_ms * 1e-3) / 1e9, 1),
-                             "launches_per_step": 2,
-                             "traffic_per_launch": load_pmc("chain", kernel_source_hash(CHAIN_SOURCES))},
     }
 
     extras = {}
     if not args.no_extras:
         log("read-stream ceiling probe")
-        ceil = read_ceiling(torch, kq)
-        extras["read_ceiling_GBps"] = round(ceil, 1)
+        rc = read_ceiling(torch, kq)
+        extras["read_ceiling"] = rc
+        extras["read_ceiling_GBps"] = rc["GBps_4GiB_best"]
         if roofline is not None:
-            roofline["frac_of_read_ceiling"] = round(dk["GBps"] / ceil, 4)
-        del chain, graph_t, graph_s, graph_f, graph4  # free 13.4 GB before the isolated runs
+            roofline["frac_of_read_ceiling"] = round(dk["GBps"] / rc["GBps_4GiB_best"], 4)
+            roofline["frac_of_size_matched_read"] = round(
+                dk["GBps"] / rc["size_matched"]["gate_up_pair_best"]["GBps"], 4)
+        chain = graph_t = graph_s = graph_f = graph4 = None  # free 13.4 GB before the isolated runs
         torch.cuda.empty_cache()
         log("isolated matvecs with weight rotation")
         extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
@@ -679,6 +729,14 @@ def main():
     }
     rec.update(extras)
     print(json.dumps(rec), flush=True)
+    # Drop the graphs and device buffers and let the device drain before the
+    # interpreter exits, so no captured graph or tensor outlives the runtime
+    # (and a profiler's own teardown) at exit.
+    chain = graph_t = graph_s = graph_f = graph4 = None  # noqa: F841
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

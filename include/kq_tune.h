@@ -64,15 +64,20 @@ kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int 
 
 /*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
- * `buf` once with 16-byte loads over `grid` workgroups of 256 threads and
- * writes grid*4 xor-folded words to the device buffer `out` (so the loads
- * cannot be dropped).  Its duration gives the measured HBM read ceiling the
- * matvec bandwidths are compared with.
- *   bytes  multiple of 16; buf 16-byte aligned; out [grid*4] uint32.
+ * `buf` once with 16-byte loads over `grid` workgroups of `block` threads and
+ * writes grid*block/64 xor-folded words to the device buffer `out` (so the
+ * loads cannot be dropped).  Its duration gives the measured HBM read ceiling
+ * the matvec bandwidths are compared with.
+ *   bytes   multiple of 16; buf 16-byte aligned; out [grid*block/64] uint32.
+ *   block   64..1024, a multiple of 64.
+ *   unroll  1, 4, 8 or 16 loads in flight per thread.
+ *   flags   bit 0: non-temporal loads; bit 1: each workgroup reads one
+ *           contiguous chunk (else the grid strides over the buffer).
  * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS, KQ_ERR_LAUNCH,
  * KQ_ERR_DEVICE.
  */
-kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, void *stream);
+kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, int block,
+                           int unroll, int flags, void *stream);
 
 #ifdef __cplusplus
 }

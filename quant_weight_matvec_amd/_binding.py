@@ -72,7 +72,7 @@ def lib() -> C.CDLL:
     L.kq_tune_set_shape.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int]
     L.kq_tune_get_shape.argtypes = [C.c_int, _i64, _i64, C.POINTER(C.c_int),
                                     C.POINTER(C.c_int), C.POINTER(C.c_int), C.POINTER(C.c_int)]
-    L.kq_probe_read_bw.argtypes = [_vp, _i64, _vp, C.c_int, _vp]
+    L.kq_probe_read_bw.argtypes = [_vp, _i64, _vp, C.c_int, C.c_int, C.c_int, C.c_int, _vp]
     L.kq_tune_small_m_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
     L.kq_tune_matvec_plan.argtypes = [C.c_int, _i64, _i64, C.c_int, C.c_int, _vp]
     L.kq_staged_bytes.argtypes = [C.c_int, _i64]
@@ -228,9 +228,10 @@ def kq_tune_get_shape(qtype: int, n_rows: int, k: int) -> tuple[int, int, int, i
     return a.value, b.value, c.value, d.value
 
 
-def kq_probe_read_bw(buf, nbytes: int, out, grid: int, stream=None) -> None:
-    _check(lib().kq_probe_read_bw(_ptr(buf), int(nbytes), _ptr(out), int(grid), _stream(stream)),
-           "kq_probe_read_bw")
+def kq_probe_read_bw(buf, nbytes: int, out, grid: int, block: int = 256, unroll: int = 8,
+                     flags: int = 1, stream=None) -> None:
+    _check(lib().kq_probe_read_bw(_ptr(buf), int(nbytes), _ptr(out), int(grid), int(block),
+                                  int(unroll), int(flags), _stream(stream)), "kq_probe_read_bw")
 
 
 def kq_tune_matvec_plan(qtype: int, n_rows: int, k: int, staged: bool, cus: int) -> dict:

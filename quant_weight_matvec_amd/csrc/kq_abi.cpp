@@ -437,15 +437,20 @@ kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int 
     return KQ_OK;
 }
 
-kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, void *stream)
+kq_status kq_probe_read_bw(const void *buf, int64_t bytes, uint32_t *out, int grid, int block,
+                           int unroll, int flags, void *stream)
 {
     if (!buf || !out) return KQ_ERR_NULL;
     if (bytes < 16 || bytes % 16 || grid < 1) return KQ_ERR_SHAPE;
+    if (block < 64 || block > 1024 || block % 64) return KQ_ERR_SHAPE;
+    if ((unroll != 1 && unroll != 4 && unroll != 8 && unroll != 16) || flags < 0 || flags > 3)
+        return KQ_ERR_SHAPE;
     if (!aligned(buf, 16) || !aligned(out, 4)) return KQ_ERR_ALIGN;
-    if (overlap(out, (int64_t)grid * 16, buf, bytes)) return KQ_ERR_ALIAS;
+    if (overlap(out, (int64_t)grid * (block / 64) * 4, buf, bytes)) return KQ_ERR_ALIAS;
     kq_status s = check_device();
     if (s != KQ_OK) return s;
-    return from_hip(kqi::launch_read_probe(buf, bytes, out, grid, (hipStream_t)stream));
+    return from_hip(kqi::launch_read_probe(buf, bytes, out, grid, block, unroll, flags,
+                                           (hipStream_t)stream));
 }
 
 }  // extern "C"

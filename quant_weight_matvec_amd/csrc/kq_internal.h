@@ -58,8 +58,8 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        float eps_post, float eps_next, uint8_t *xs_out, int xs_group,
                        hipStream_t stream);
 
-hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
-                             hipStream_t stream);
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid, int block,
+                             int unroll, int flags, hipStream_t stream);
 
 // The shape the automatic choice would use (for reports and tests).
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m);

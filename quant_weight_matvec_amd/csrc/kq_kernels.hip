@@ -622,25 +622,39 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Read-stream probe: every byte of a buffer read once with 16-byte loads in
-// a grid-stride loop (each wave instruction covers 1 KB of consecutive
-// bytes), folded with xor so the loads stay live.  It measures the HBM read
-// ceiling that the matvecs are compared with; it is not on the decode path.
-__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict__ p, int64_t n16,
-                                                         uint32_t *__restrict__ out)
+// Read-stream probe: every byte of a buffer read once with 16-byte loads,
+// folded with xor so the loads stay live.  It measures the HBM read ceiling
+// that the matvecs are compared with; it is not on the decode path.
+// Variants: U loads in flight per thread; NT non-temporal loads; CHUNK: each
+// workgroup reads one contiguous chunk of the buffer (as a matvec workgroup
+// reads its own rows) instead of the whole grid striding over it together
+// (each wave instruction then covers 1 KB of consecutive bytes either way).
+template <int U, bool NT, bool CHUNK>
+__global__ void read_probe_kernel(const u32x4 *__restrict__ p, int64_t n16,
+                                  uint32_t *__restrict__ out)
 {
-    constexpr int U = 8;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t i, end, stride;
+    if constexpr (CHUNK) {
+        const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+        const int64_t lo = (int64_t)blockIdx.x * per;
+        end = min(lo + per, n16);
+        i = lo + threadIdx.x;
+        stride = blockDim.x;
+    } else {
+        end = n16;
+        i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        stride = (int64_t)gridDim.x * blockDim.x;
+    }
     uint32_t acc = 0;
-    for (; i + (U - 1) * stride < n16; i += U * stride) {
+    for (; i + (U - 1) * stride < end; i += U * stride) {
         u32x4 v[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = __builtin_nontemporal_load(p + i + j * stride);
+        for (int j = 0; j < U; ++j)
+            v[j] = NT ? __builtin_nontemporal_load(p + i + j * stride) : p[i + j * stride];
 #pragma unroll
         for (int j = 0; j < U; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
     }
-    for (; i < n16; i += stride) {
+    for (; i < end; i += stride) {
         const u32x4 v = p[i];
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
@@ -963,12 +977,31 @@ hipError_t launch_stage(const float *x, uint8_t *xs, int k, int group, hipStream
     return hipGetLastError();
 }
 
-hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid,
-                             hipStream_t stream)
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid, int block,
+                             int unroll, int flags, hipStream_t stream)
 {
-    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, stream,
-                       reinterpret_cast<const u32x4 *>(buf), bytes / 16, out);
-    return hipGetLastError();
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(buf);
+    const int64_t n16 = bytes / 16;
+    const bool nt = flags & 1, chunk = flags & 2;
+#define KQ_PROBE(U)                                                                             \
+    if (unroll == U) {                                                                          \
+        if (nt && chunk)                                                                        \
+            hipLaunchKernelGGL((read_probe_kernel<U, true, true>), dim3(grid), dim3(block), 0,  \
+                               stream, p, n16, out);                                            \
+        else if (nt)                                                                            \
+            hipLaunchKernelGGL((read_probe_kernel<U, true, false>), dim3(grid), dim3(block), 0, \
+                               stream, p, n16, out);                                            \
+        else if (chunk)                                                                         \
+            hipLaunchKernelGGL((read_probe_kernel<U, false, true>), dim3(grid), dim3(block), 0, \
+                               stream, p, n16, out);                                            \
+        else                                                                                    \
+            hipLaunchKernelGGL((read_probe_kernel<U, false, false>), dim3(grid), dim3(block),   \
+                               0, stream, p, n16, out);                                         \
+        return hipGetLastError();                                                               \
+    }
+    KQ_PROBE(1) KQ_PROBE(4) KQ_PROBE(8) KQ_PROBE(16)
+#undef KQ_PROBE
+    return hipErrorInvalidValue;
 }
 
 const char *variant_names()

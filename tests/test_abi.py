@@ -118,6 +118,19 @@ def test_small_m_validation():
     assert q(1, 0, 1024, 4) == 0 and q(2, 8, 1024, 1) == 0        # empty, or m = 1 (matvec)
 
 
+def test_probe_validation():
+    f = kq.lib().kq_probe_read_bw
+    P, O = 0x100000, 0x900000
+    assert f(None, 1 << 20, O, 256, 256, 8, 1, None) == B.KQ_ERR_NULL
+    assert f(P, 1000, O, 256, 256, 8, 1, None) == B.KQ_ERR_SHAPE         # not whole 16 B
+    assert f(P, 1 << 20, O, 256, 100, 8, 1, None) == B.KQ_ERR_SHAPE      # block % 64
+    assert f(P, 1 << 20, O, 256, 2048, 8, 1, None) == B.KQ_ERR_SHAPE     # block > 1024
+    assert f(P, 1 << 20, O, 256, 256, 3, 1, None) == B.KQ_ERR_SHAPE      # unroll
+    assert f(P, 1 << 20, O, 256, 256, 8, 4, None) == B.KQ_ERR_SHAPE      # flags
+    assert f(P + 4, 1 << 20, O, 256, 256, 8, 1, None) == B.KQ_ERR_ALIGN
+    assert f(P, 1 << 20, P + 64, 256, 256, 8, 1, None) == B.KQ_ERR_ALIAS
+
+
 def test_tail_validation():
     f = kq.lib().kq_fused_residual_norm
     R, P, O, GP, GN = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000

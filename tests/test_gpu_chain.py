@@ -223,10 +223,15 @@ def test_pass_modes_bitwise(layers, hidden, ffn, down):
 FULL = dict(layers=52, hidden=6656, ffn=19968)
 
 # End-to-end GPU-vs-oracle difference of the 52-layer pass measured on MI355X
-# (max |dx|, max |dres|; every pass mode gives the same bits).  The end-to-end
-# check allows a few times this, so a regression by an order of magnitude
-# fails even where the amplification bound is loose.
-E2E_RECORDED = None
+# (max |dx|, max |dres|), per start: "oracle_x0" starts the GPU from the
+# oracle's entry norm (the single-op pass), "gpu_x0" from the GPU's own entry
+# norm (every pass mode of run_pass, which give the same bits).  The stack is
+# ill-conditioned (the oracle itself moves by 1.6e-2 under a 1e-7 relative
+# perturbation of its start), so the two starts end 5x apart.  The end-to-end
+# check allows 5x the recorded difference, so a regression by an order of
+# magnitude fails even where the amplification bound is loose; a change of the
+# kernels' summation order moves these values and they are then re-recorded.
+E2E_RECORDED = {"oracle_x0": (1.220e-02, 7.554e-02), "gpu_x0": (2.360e-03, 1.616e-02)}
 
 
 @pytest.fixture(scope="module")
@@ -272,7 +277,7 @@ def teacher_forced(full):
     return worst
 
 
-def check_end_to_end(full, xe, re, worst):
+def check_end_to_end(full, xe, re, worst, start):
     """(ii) end to end.  If the oracle itself moves by more than the 2e-3
     tolerance under a 1e-7 perturbation, the stack is ill-conditioned at that
     tolerance and the end-to-end result is held to the per-layer error
@@ -291,10 +296,9 @@ def check_end_to_end(full, xe, re, worst):
         amp = sens / 1e-7
         assert max(dx, dr) <= 10 * amp * max(worst, 1e-7) + 2e-3, "end-to-end drift too large"
         assert max(dx / 1.0, dr / max(1.0, np.max(np.abs(r)))) < 0.1, "gross end-to-end error"
-    if E2E_RECORDED is not None:
-        rx, rr = E2E_RECORDED
-        assert dx <= max(4 * rx, 2e-3) and dr <= max(4 * rr, 2e-3), \
-            f"end-to-end difference grew past 4x the recorded ({rx:.2e}, {rr:.2e})"
+    rx, rr = E2E_RECORDED[start]
+    assert dx <= max(5 * rx, 2e-3) and dr <= max(5 * rr, 2e-3), \
+        f"end-to-end difference grew past 5x the recorded ({rx:.2e}, {rr:.2e})"
 
 
 def test_op_pass_52_layers_full_size(full, teacher_forced):
@@ -303,7 +307,7 @@ def test_op_pass_52_layers_full_size(full, teacher_forced):
     replay equal to the eager pass; the staged pass equals it bit for bit."""
     st = full["st"]
     xe, re = st.run_ops(full["x0"], full["r0"], replays=3)
-    check_end_to_end(full, xe, re, teacher_forced)
+    check_end_to_end(full, xe, re, teacher_forced, "oracle_x0")
     xs_, rs_ = st.run_ops(full["x0"], full["r0"], replays=3, staged=True)
     assert np.array_equal(xe, xs_) and np.array_equal(re, rs_)
 
@@ -316,4 +320,4 @@ def test_pass_modes_52_layers_full_size(full, teacher_forced):
     a = st.run_pass(full["r0"], "f32")
     c = st.run_pass(full["r0"], "fusedtail", replays=3)
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
-    check_end_to_end(full, c[0], c[1], teacher_forced)
+    check_end_to_end(full, c[0], c[1], teacher_forced, "gpu_x0")
