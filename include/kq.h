@@ -178,6 +178,30 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
                             int64_t workspace_bytes, void *stream);
 
 /*
+ * kq_matmul_small_m without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * kq_matmul_small_m (bit for bit: the same kernels on the same grid), except
+ * that the partial tiles and counters of the split over k live in a
+ * library-owned device array of KQ_SMALL_M_SCRATCH_BYTES (16 KiB of counters,
+ * one per 256-row group, then 16 MiB of partial tiles), one per GPU, held
+ * until the process ends.  The call allocates nothing.
+ *   Returns KQ_ERR_UNSUPPORTED when the shape needs more than that array
+ *   holds (more than 4096 row groups of 256 rows, or a split over more than
+ *   512 workgroups; kq_matmul_small_m with a workspace takes any shape).
+ *   KQ_ERR_DEVICE if the array's device address cannot be obtained.
+ * Every call on a GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race and may return wrong results; calls ordered on one stream do not.
+ * The counters start at zero (cleared by the first call on each GPU that
+ * needs them) and every completed call leaves them at zero.
+ */
+#define KQ_SMALL_M_SCRATCH_BYTES (16 * 1024 + 16 * 1024 * 1024)
+kq_status kq_matmul_small_m_noalloc(int qtype, const void *W, const float *X, int64_t ldx,
+                                    float *Y, int64_t ldy, int64_t n_rows, int64_t k, int m,
+                                    void *stream);
+
+/*
  * Workspace bytes kq_matmul_small_m needs for this shape on the current
  * device (0 if none), or a negative kq_status for arguments it would reject
  * (KQ_ERR_SHAPE, KQ_ERR_UNSUPPORTED, KQ_ERR_DEVICE).  Synchronous, no GPU work.

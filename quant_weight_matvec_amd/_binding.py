@@ -30,6 +30,7 @@ KQ_QTYPE_Q6K = 2
 KQ_MAX_K = 40960
 KQ_MAX_M = 16
 KQ_MAX_TAIL_N = 32768
+KQ_SMALL_M_SCRATCH_BYTES = 16 * 1024 + 16 * 1024 * 1024
 
 
 class KQLibraryMissing(RuntimeError):
@@ -61,6 +62,8 @@ def lib() -> C.CDLL:
     L.kq_ffn_gate_up_q4k.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
     L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp,
                                     _i64, _vp]
+    L.kq_matmul_small_m_noalloc.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
+                                            C.c_int, _vp]
     L.kq_matmul_small_m_workspace_bytes.argtypes = [C.c_int, _i64, _i64, C.c_int]
     L.kq_matmul_small_m_workspace_bytes.restype = _i64
     L.kq_fused_residual_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, C.c_float,
@@ -88,7 +91,7 @@ def lib() -> C.CDLL:
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
                "kq_tune_small_m_plan", "kq_tune_matvec_plan",
-               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_fused_residual_norm",
+               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_matmul_small_m_noalloc", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
     _lib = L
@@ -148,6 +151,13 @@ def kq_matmul_small_m(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: i
                                  int(n_rows), int(k), int(m), _ptr(workspace),
                                  int(workspace_bytes), _stream(stream))
     _check(rc, "kq_matmul_small_m")
+
+
+def kq_matmul_small_m_noalloc(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: int,
+                              m: int, stream=None) -> None:
+    rc = lib().kq_matmul_small_m_noalloc(int(qtype), _ptr(W), _ptr(X), int(ldx), _ptr(Y),
+                                         int(ldy), int(n_rows), int(k), int(m), _stream(stream))
+    _check(rc, "kq_matmul_small_m_noalloc")
 
 
 def kq_matmul_small_m_workspace_bytes(qtype: int, n_rows: int, k: int, m: int) -> int:

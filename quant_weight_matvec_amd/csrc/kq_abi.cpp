@@ -162,6 +162,40 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
                                              (hipStream_t)stream));
 }
 
+kq_status kq_matmul_small_m_noalloc(int qtype, const void *W, const float *X, int64_t ldx,
+                                    float *Y, int64_t ldy, int64_t n_rows, int64_t k, int m,
+                                    void *stream)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (!W || !X || !Y) return KQ_ERR_NULL;
+    kq_status s = check_small_m(qtype, n_rows, k, m);
+    if (s != KQ_OK) return s;
+    if (ldx < k || ldx % 4 || ldy < n_rows || ldy < 1) return KQ_ERR_SHAPE;
+    const uintptr_t walign = qtype == KQ_QTYPE_Q4K ? 16 : 4;
+    if (!aligned(W, walign) || !aligned(X, 16) || !aligned(Y, 4)) return KQ_ERR_ALIGN;
+    const int64_t blk = qtype == KQ_QTYPE_Q4K ? KQ_Q4K_BLOCK_BYTES : KQ_Q6K_BLOCK_BYTES;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * blk;
+    const int64_t ybytes = ((int64_t)(m - 1) * ldy + n_rows) * 4;
+    const int64_t xbytes = ((int64_t)(m - 1) * ldx + k) * 4;
+    if (overlap(Y, ybytes, W, wbytes) || overlap(Y, ybytes, X, xbytes)) return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    // host arithmetic on the launch plan: a shape the scratch array cannot
+    // hold is rejected before any device call
+    if (!kqi::small_m_noalloc_fits(qtype, (int)n_rows, (int)k, m)) return KQ_ERR_UNSUPPORTED;
+    if ((s = check_device()) != KQ_OK) return s;
+    if (m == 1)
+        return from_hip(qtype == KQ_QTYPE_Q4K
+                            ? kqi::launch_matvec_q4k((const uint8_t *)W, X, nullptr, Y,
+                                                     (int)n_rows, (int)k, nullptr,
+                                                     (hipStream_t)stream)
+                            : kqi::launch_matvec_q6k((const uint8_t *)W, X, nullptr, Y,
+                                                     (int)n_rows, (int)k, (hipStream_t)stream));
+    const hipError_t e = kqi::launch_small_m_noalloc(qtype, (const uint8_t *)W, X, ldx, Y, ldy,
+                                                     (int)n_rows, (int)k, m, (hipStream_t)stream);
+    if (e == hipErrorInvalidSymbol || e == hipErrorInvalidDevice) return KQ_ERR_DEVICE;
+    return from_hip(e);
+}
+
 kq_status kq_fused_residual_norm(float *residual, const float *projected, float *next_in,
                                  const float *g_post, const float *g_next, int64_t rows,
                                  int64_t n, float eps_post, float eps_next, void *stream)

@@ -49,6 +49,12 @@ size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m);
 // The launch plan for a device of `cus` CUs: out = {workgroups, staged window
 // in superblocks, LDS bytes, workspace bytes, threads per workgroup, tiles}.
 void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out);
+// kq_matmul_small_m_noalloc: the plan fits the library's scratch array, and
+// the launch with the partial tiles and counters there (m = 2..16).
+bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m);
+hipError_t launch_small_m_noalloc(int qtype, const uint8_t *W, const float *X, int64_t ldx,
+                                  float *Y, int64_t ldy, int n_rows, int k, int m,
+                                  hipStream_t stream);
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream);

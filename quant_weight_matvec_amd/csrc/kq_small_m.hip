@@ -44,7 +44,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
+
+#include "kq.h"
 
 #include "kq_device.h"
 #include "kq_internal.h"
@@ -875,6 +878,74 @@ hipError_t allow_lds()
     return e;
 }
 
+// The plan's launch, with the partial tiles at byte part_off of ws (counters
+// at its start) and ws_bytes the bytes the kernel may touch there.
+hipError_t launch_plan(const SmPlan &p, int qtype, const uint8_t *W, const float *X, int64_t ldx,
+                       float *Y, int64_t ldy, int n_rows, int k, int m, uint8_t *ws, int part_off,
+                       int64_t ws_bytes, hipStream_t stream)
+{
+    SmArgs a;
+    a.W = W;
+    a.X = X;
+    a.Y = Y;
+    a.ws = ws;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.n_rows = n_rows;
+    a.k = k;
+    a.m = m;
+    a.nb = p.nb;
+    a.T = p.T;
+    a.G = p.G;
+    a.CH = p.CH;
+    a.RS = p.RS;
+    a.part_off = part_off;
+    a.ws_bytes = (int)ws_bytes;
+    a.flag_off = p.flag_off;
+    a.xs_off = p.xs_off;
+    hipError_t e;
+#define KQ_SM_GO(U, C)                                                                         \
+    {                                                                                         \
+        constexpr auto K = small_m_kernel<U, C>;                                              \
+        if ((e = allow_lds<K>()) != hipSuccess) return e;                                     \
+        hipLaunchKernelGGL(K, dim3(p.G), dim3(C::kThreads), p.lds, stream, a);                 \
+        return hipGetLastError();                                                             \
+    }
+    if (qtype == 1) {
+        if (p.narrow) KQ_SM_GO(Q4Tile, SmNarrow)
+        KQ_SM_GO(Q4Tile, SmWide)
+    }
+    if (p.narrow) KQ_SM_GO(Q6Tile, SmNarrow)
+    KQ_SM_GO(Q6Tile, SmWide)
+#undef KQ_SM_GO
+}
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch for kq_matmul_small_m_noalloc: one counter per 256-row
+// group in the first kNaCounterBytes, then the partial tiles of up to
+// kNaPartBytes / (2 * 16 * kSmRows * 4) workgroups.  Each GPU the library runs
+// on holds its own copy of the array until the process ends.  In host code
+// `scratch` is a host-side stand-in for the symbol, not a device address: its
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr int kNaCounterBytes = 16 * 1024;
+constexpr size_t kNaPartBytes = (size_t)16 << 20;
+static_assert(kNaCounterBytes + kNaPartBytes == KQ_SMALL_M_SCRATCH_BYTES, "kq.h size");
+__device__ __align__(256) uint8_t scratch[kNaCounterBytes + kNaPartBytes];
+
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct NaDev {
+    uint8_t *ptr;  // device address of `scratch` on this device
+    bool zeroed;   // the counter words have been cleared on this device
+};
+NaDev g_na[kMaxDevices];
+std::mutex g_na_mutex;
+
 }  // namespace
 
 namespace kqi {
@@ -902,40 +973,66 @@ hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int6
 {
     const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
     if ((int64_t)p.ws > workspace_bytes) return hipErrorInvalidValue;
-    SmArgs a;
-    a.W = W;
-    a.X = X;
-    a.Y = Y;
-    a.ws = reinterpret_cast<uint8_t *>(workspace);
-    a.ldx = ldx;
-    a.ldy = ldy;
-    a.n_rows = n_rows;
-    a.k = k;
-    a.m = m;
-    a.nb = p.nb;
-    a.T = p.T;
-    a.G = p.G;
-    a.CH = p.CH;
-    a.RS = p.RS;
-    a.part_off = p.part_off;
-    a.ws_bytes = (int)p.ws;
-    a.flag_off = p.flag_off;
-    a.xs_off = p.xs_off;
-    hipError_t e;
-#define KQ_SM_GO(U, C)                                                                         \
-    {                                                                                         \
-        constexpr auto K = small_m_kernel<U, C>;                                              \
-        if ((e = allow_lds<K>()) != hipSuccess) return e;                                     \
-        hipLaunchKernelGGL(K, dim3(p.G), dim3(C::kThreads), p.lds, stream, a);                 \
-        return hipGetLastError();                                                             \
+    return launch_plan(p, qtype, W, X, ldx, Y, ldy, n_rows, k, m,
+                       reinterpret_cast<uint8_t *>(workspace), p.part_off, (int64_t)p.ws, stream);
+}
+
+bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m)
+{
+    if (m < 2) return true;
+    const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
+    if (p.ws == 0) return true;  // no row group is split: the scratch is not used
+    const int64_t rgs = ((int64_t)n_rows + kSmRows - 1) / kSmRows;
+    const int64_t parts = (int64_t)p.G * 2 * 16 * kSmRows * 4;
+    return 4 * rgs <= kNaCounterBytes && parts <= (int64_t)kNaPartBytes;
+}
+
+hipError_t launch_small_m_noalloc(int qtype, const uint8_t *W, const float *X, int64_t ldx,
+                                  float *Y, int64_t ldy, int n_rows, int k, int m,
+                                  hipStream_t stream)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
+    uint8_t *base;
+    bool clear = false;
+    {
+        std::lock_guard<std::mutex> lock(g_na_mutex);
+        if (!g_na[dev].ptr) {
+            void *ptr = nullptr;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!ptr) return hipErrorInvalidSymbol;
+            g_na[dev].ptr = reinterpret_cast<uint8_t *>(ptr);
+        }
+        base = g_na[dev].ptr;
+        if (p.ws > 0 && !g_na[dev].zeroed) {  // the first call that uses the counters
+            clear = true;
+            g_na[dev].zeroed = true;
+        }
     }
-    if (qtype == 1) {
-        if (p.narrow) KQ_SM_GO(Q4Tile, SmNarrow)
-        KQ_SM_GO(Q4Tile, SmWide)
+    if (p.ws > 0) {
+        // every call leaves the counters it used at zero; they start at zero
+        // from the first call's clear (a fill kernel, not a memset, so that
+        // a call under graph capture records a kernel node)
+        if (clear) {
+            const int words = kNaCounterBytes / 4;
+            hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                               reinterpret_cast<uint32_t *>(base), words);
+            if ((e = hipGetLastError()) != hipSuccess) {
+                std::lock_guard<std::mutex> lock(g_na_mutex);
+                g_na[dev].zeroed = false;
+                return e;
+            }
+        }
+        const int64_t need = kNaCounterBytes + (int64_t)p.G * 2 * 16 * kSmRows * 4;
+        if (need > (int64_t)sizeof(scratch)) return hipErrorInvalidValue;
+        return launch_plan(p, qtype, W, X, ldx, Y, ldy, n_rows, k, m, base, kNaCounterBytes, need,
+                           stream);
     }
-    if (p.narrow) KQ_SM_GO(Q6Tile, SmNarrow)
-    KQ_SM_GO(Q6Tile, SmWide)
-#undef KQ_SM_GO
+    return launch_plan(p, qtype, W, X, ldx, Y, ldy, n_rows, k, m, base, kNaCounterBytes, 0, stream);
 }
 
 }  // namespace kqi

@@ -118,6 +118,30 @@ def test_small_m_validation():
     assert q(1, 0, 1024, 4) == 0 and q(2, 8, 1024, 1) == 0        # empty, or m = 1 (matvec)
 
 
+def test_small_m_noalloc_validation():
+    """The no-allocation small-M entry: the workspace version's checks, and a
+    shape whose split needs more than the library's scratch array is refused
+    on the host (KQ_ERR_UNSUPPORTED) before any device call."""
+    f = kq.lib().kq_matmul_small_m_noalloc
+    a = lambda *v: f(*v, None)
+    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 0) == B.KQ_ERR_SHAPE      # m = 0
+    assert a(1, W, X, 1024, Y, 8, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
+    assert a(1, W, X, 1000, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldx < k
+    assert a(1, W, X, 1024, Y, 7, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldy < n_rows
+    assert a(1, None, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_NULL
+    assert a(2, W + 2, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_ALIGN
+    assert a(1, W, X, 1024, X + 4 * 1024, 8, 8, 1024, 4) == B.KQ_ERR_ALIAS
+    assert a(1, W, X, 1024, Y, 8, 0, 1024, 4) == B.KQ_OK             # empty
+    # far-apart fake addresses so that only the size decides
+    Wb, Xb, Yb = 1 << 40, 2 << 40, 3 << 40
+    n, k, m = 19968, 40960, 16
+    plan = kq.kq_tune_small_m_plan(B.KQ_QTYPE_Q4K, n, k, m, 256)
+    assert plan["workspace"] > 0 and plan["grid"] * 2 * 16 * 256 * 4 > 16 << 20
+    assert a(1, Wb, Xb, k, Yb, n, n, k, m) == B.KQ_ERR_UNSUPPORTED
+    assert B.KQ_SMALL_M_SCRATCH_BYTES == 16 * 1024 + 16 * 1024 * 1024
+
+
 def test_probe_validation():
     f = kq.lib().kq_probe_read_bw
     P, O = 0x100000, 0x900000
