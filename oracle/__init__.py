@@ -20,8 +20,10 @@ from . import build as _build
 
 QTYPE_Q4K = 1
 QTYPE_Q6K = 2
-_QT = {"q4k": QTYPE_Q4K, "q6k": QTYPE_Q6K, QTYPE_Q4K: QTYPE_Q4K, QTYPE_Q6K: QTYPE_Q6K}
-BLOCK_BYTES = {QTYPE_Q4K: 144, QTYPE_Q6K: 210}
+QTYPE_Q5K = 3
+_QT = {"q4k": QTYPE_Q4K, "q6k": QTYPE_Q6K, "q5k": QTYPE_Q5K, QTYPE_Q4K: QTYPE_Q4K,
+       QTYPE_Q6K: QTYPE_Q6K, QTYPE_Q5K: QTYPE_Q5K}
+BLOCK_BYTES = {QTYPE_Q4K: 144, QTYPE_Q6K: 210, QTYPE_Q5K: 176}
 
 _LIBS: dict[int, C.CDLL] = {}
 _dp = C.POINTER(C.c_double)
@@ -85,6 +87,20 @@ class Oracle:
         rc = self.lib.orc_dequant_rows(qt, _p(W, _u8p), n_rows, k, _p(out))
         if rc:
             raise ValueError(f"orc_dequant_rows rc={rc}")
+        return out
+
+    def embedding(self, qtype, E, tokens, vocab: int, hidden: int) -> np.ndarray:
+        """Rows tokens[t] of the embedding table E (vocab rows of `hidden`
+        weights, one token per row; the lookup of Ch 10 "The forward pass at a
+        glance", section 10.3, box 1), dequantized: [len(tokens)][hidden].
+        Tokens outside [0, vocab) give rows of NaN."""
+        qt = _QT[qtype]
+        E = _u8(E).reshape(vocab, -1)
+        tok = np.asarray(tokens, np.int64).reshape(-1)
+        out = np.full((tok.size, hidden), np.nan)
+        ok = (tok >= 0) & (tok < vocab)
+        if ok.any():
+            out[ok] = self.dequant(qt, E[tok[ok]], int(ok.sum()), hidden)
         return out
 
     def matmul(self, qtype, W, X, n_rows: int, k: int, nthreads: int = 1):

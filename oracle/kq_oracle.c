@@ -23,6 +23,14 @@
  *         weight = d * scale_s * q - dmin * min_s   (the min is subtracted).
  *   Q6_K: 128 B low 4 bits | 64 B high 2 bits | 16 int8 scales (sub-blocks of
  *         16) | d f16.   weight = d * scale_s * (q - 32).
+ *   Q5_K: d f16 | dmin f16 | 12 B of 6-bit (scale, min) pairs packed as in
+ *         Q4_K | 32 B of high bits | 128 B of low nibbles (176 B; the pages
+ *         name the type, in the pinned decode kernels of Ch 4 "Pipeline state
+ *         objects and the three kernel sources", section 4.4, but give no
+ *         layout).  Weight i of chunk c = i / 64: low 4 bits as the Q4_K
+ *         nibble of the same position, high bit = bit 2c (first 32 of the
+ *         chunk) or 2c+1 (last 32) of high-bit byte i mod 32; q = 0..31.
+ *         weight = d * scale_s * q - dmin * min_s.
  *
  * Parity against external k-quant producers is unpinned (no external file or
  * decoder is available); the tests pin this reading by one-hot brute force,
@@ -45,8 +53,10 @@
 #define ORC_QK 256
 #define ORC_Q4K_BYTES 144
 #define ORC_Q6K_BYTES 210
+#define ORC_Q5K_BYTES 176
 #define ORC_QTYPE_Q4K 1
 #define ORC_QTYPE_Q6K 2
+#define ORC_QTYPE_Q5K 3
 
 /* ------------------------------------------------------------------------ */
 /* binary16 decode.  IEEE 754 half: 1 sign bit, 5 exponent bits with bias 15,
@@ -148,18 +158,75 @@ void orc_dequant_q6k(const uint8_t *blk, double *w)
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Q5_K superblock -> 256 weights.  The asymmetric "scale x index - min" of
+ * Q4_K with a 5-bit index (Ch 5, section 5.5); field packing as stated in the
+ * header comment. */
+void orc_dequant_q5k(const uint8_t *blk, double *w)
+{
+    const double d = rd_f16(blk + 0);
+    const double dmin = rd_f16(blk + 2);
+    const uint8_t *S = blk + 4;    /* 12 bytes of packed 6-bit fields */
+    const uint8_t *qh = blk + 16;  /* 32 bytes of high bits */
+#if ORC_PLANT == 16
+    const uint8_t *qs = blk + 32;  /* low nibbles read from the wrong offset */
+#else
+    const uint8_t *qs = blk + 48;  /* 128 bytes of low nibbles */
+#endif
+    int sc[8], mn[8];
+    for (int s = 0; s < 4; ++s) {
+        sc[s] = S[s] & 63;
+        mn[s] = S[s + 4] & 63;
+    }
+    for (int s = 4; s < 8; ++s) {
+        sc[s] = (S[s + 4] & 15) | ((S[s - 4] >> 6) << 4);
+        mn[s] = (S[s + 4] >> 4) | ((S[s] >> 6) << 4);
+    }
+    for (int i = 0; i < ORC_QK; ++i) {
+        int c = i / 64, t = i % 64, j = t % 32;
+        int byte = qs[32 * c + j];
+        int lo = (t < 32) ? (byte & 15) : (byte >> 4);
+#if ORC_PLANT == 14
+        int bit = c;                          /* one bit per chunk, not two */
+#else
+        int bit = 2 * c + (t >= 32 ? 1 : 0);
+#endif
+        int hi = (qh[j] >> bit) & 1;
+#if ORC_PLANT == 15
+        int q = lo | (hi << 5);
+#else
+        int q = lo | (hi << 4);
+#endif
+        int s = i / 32;
+        w[i] = d * sc[s] * q - dmin * mn[s];
+    }
+}
+
+static int64_t orc_block_bytes(int qtype)
+{
+    return qtype == ORC_QTYPE_Q4K ? ORC_Q4K_BYTES
+         : qtype == ORC_QTYPE_Q6K ? ORC_Q6K_BYTES
+         : qtype == ORC_QTYPE_Q5K ? ORC_Q5K_BYTES : 0;
+}
+
+static void orc_dequant_block(int qtype, const uint8_t *blk, double *w)
+{
+    if (qtype == ORC_QTYPE_Q4K) orc_dequant_q4k(blk, w);
+    else if (qtype == ORC_QTYPE_Q6K) orc_dequant_q6k(blk, w);
+    else orc_dequant_q5k(blk, w);
+}
+
 int orc_dequant_rows(int qtype, const uint8_t *W, int64_t n_rows, int64_t k, double *out)
 {
     if (k % ORC_QK) return -2;
     int64_t nsb = k / ORC_QK;
-    int64_t bb = (qtype == ORC_QTYPE_Q4K) ? ORC_Q4K_BYTES : ORC_Q6K_BYTES;
-    if (qtype != ORC_QTYPE_Q4K && qtype != ORC_QTYPE_Q6K) return -5;
+    int64_t bb = orc_block_bytes(qtype);
+    if (!bb) return -5;
     for (int64_t r = 0; r < n_rows; ++r)
         for (int64_t b = 0; b < nsb; ++b) {
             const uint8_t *blk = W + (r * nsb + b) * bb;
             double *dst = out + r * k + b * ORC_QK;
-            if (qtype == ORC_QTYPE_Q4K) orc_dequant_q4k(blk, dst);
-            else orc_dequant_q6k(blk, dst);
+            orc_dequant_block(qtype, blk, dst);
         }
     return 0;
 }
@@ -185,7 +252,7 @@ static void *orc_mm_worker(void *arg)
 {
     orc_mm_job *J = (orc_mm_job *)arg;
     const int64_t nsb = J->k / ORC_QK;
-    const int64_t bb = (J->qtype == ORC_QTYPE_Q4K) ? ORC_Q4K_BYTES : ORC_Q6K_BYTES;
+    const int64_t bb = orc_block_bytes(J->qtype);
     double w[ORC_QK];
     for (int64_t r = J->r0; r < J->r1; ++r) {
         for (int64_t mm = 0; mm < J->m; ++mm) {
@@ -198,8 +265,7 @@ static void *orc_mm_worker(void *arg)
         for (int64_t b = 0; b < nsb; ++b) {
 #endif
             const uint8_t *blk = J->W + (r * nsb + b) * bb;
-            if (J->qtype == ORC_QTYPE_Q4K) orc_dequant_q4k(blk, w);
-            else orc_dequant_q6k(blk, w);
+            orc_dequant_block(J->qtype, blk, w);
             for (int64_t mm = 0; mm < J->m; ++mm) {
                 const double *x = J->X + mm * J->ldx + b * ORC_QK;
                 double acc = J->Y[mm * J->n_rows + r];
@@ -226,7 +292,7 @@ static void *orc_mm_worker(void *arg)
 int orc_matmul(int qtype, const uint8_t *W, const double *X, int64_t ldx,
                int64_t n_rows, int64_t k, int64_t m, double *Y, double *S, int nthreads)
 {
-    if (qtype != ORC_QTYPE_Q4K && qtype != ORC_QTYPE_Q6K) return -5;
+    if (!orc_block_bytes(qtype)) return -5;
     if (k <= 0 || k % ORC_QK || n_rows < 0 || m < 1 || ldx < k) return -2;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

@@ -14,6 +14,9 @@ section 5.5 for the block idea):
   6-bit scales and mins) and 16-143 (the 4-bit quants) are uniform random
   bytes, which makes every 6-bit field uniform on 0..63 and every nibble
   uniform on 0..15.
+* Q5_K superblock, 176 bytes: bytes 0-3 ``d`` and ``dmin`` as for Q4_K; bytes
+  4-175 (packed 6-bit scales and mins, the high bits, the low nibbles) are
+  uniform random bytes, which makes every 5-bit quant uniform on 0..31.
 * Q6_K superblock, 210 bytes: bytes 0-191 (low 4 bits and high 2 bits of the
   quants) are uniform random bytes; bytes 192-207 are int8 scales uniform on
   -32..31; bytes 208-209 ``d`` is f16 from U[1e-3, 1e-2].
@@ -36,6 +39,7 @@ BASE_SEED = 0x4B514D56  # "KQMV"
 QK = 256
 Q4K_BLOCK_BYTES = 144
 Q6K_BLOCK_BYTES = 210
+Q5K_BLOCK_BYTES = 176
 ROW_BLOCK = 256  # rows per independently seeded generator
 
 # roles inside one configuration (stream = cfg << 24 | layer << 8 | role)
@@ -67,6 +71,14 @@ def _q4k_rows(seed: int, stream: int, block: int, rows: int, nsb: int) -> np.nda
     dd = _f16_uniform_bytes(rng, 2 * nblk, 1e-3, 1e-2).reshape(nblk, 4)
     raw[:, 0:4] = dd
     return raw.reshape(rows, nsb * Q4K_BLOCK_BYTES)
+
+
+def _q5k_rows(seed: int, stream: int, block: int, rows: int, nsb: int) -> np.ndarray:
+    rng = _rng(seed, stream, block)
+    nblk = rows * nsb
+    raw = _random_bytes(rng, nblk * Q5K_BLOCK_BYTES).reshape(nblk, Q5K_BLOCK_BYTES)
+    raw[:, 0:4] = _f16_uniform_bytes(rng, 2 * nblk, 1e-3, 1e-2).reshape(nblk, 4)
+    return raw.reshape(rows, nsb * Q5K_BLOCK_BYTES)
 
 
 def _q6k_rows(seed: int, stream: int, block: int, rows: int, nsb: int) -> np.ndarray:
@@ -135,10 +147,23 @@ def gains_f32(n: int, seed: int = BASE_SEED, stream: int = 0) -> np.ndarray:
     return normal_f32(n, seed, stream, 1.0, 0.1)
 
 
+def q5k_matrix(n_rows: int, k: int, seed: int = BASE_SEED, stream: int = 0,
+               row_lo: int = 0, row_hi: int | None = None) -> np.ndarray:
+    """Q5_K weight bytes, shape [rows, (k/256)*176] uint8, rows row_lo..row_hi-1."""
+    return _gen_matrix(_q5k_rows, seed, stream, n_rows, k, Q5K_BLOCK_BYTES, row_lo, row_hi)
+
+
+def token_ids(n: int, vocab: int, seed: int = BASE_SEED, stream: int = 0) -> np.ndarray:
+    """int32 token ids, uniform on 0..vocab-1."""
+    return _rng(seed, stream, 0x7FFFFFFE).integers(0, vocab, size=n).astype(np.int32)
+
+
 def weight_matrix(qtype: str, n_rows: int, k: int, seed: int = BASE_SEED, stream: int = 0,
                   row_lo: int = 0, row_hi: int | None = None) -> np.ndarray:
     if qtype == "q4k":
         return q4k_matrix(n_rows, k, seed, stream, row_lo, row_hi)
+    if qtype == "q5k":
+        return q5k_matrix(n_rows, k, seed, stream, row_lo, row_hi)
     if qtype == "q6k":
         return q6k_matrix(n_rows, k, seed, stream, row_lo, row_hi)
     raise ValueError(qtype)

@@ -14,6 +14,10 @@ high nibble = m[s] bits 0-3; byte s-4 bits 6-7 = sc[s] bits 4-5; byte s bits
 6-7 = m[s] bits 4-5.  Nibble byte 16 + 32c + j: low nibble = weight 64c + j,
 high nibble = weight 64c + 32 + j.
 
+Q5_K (176 B): d f16 @0, dmin f16 @2, the 12 packed bytes of Q4_K @4, 32 bytes
+of high bits @16, nibbles @48 laid out as Q4_K's @16.  Weight 64c + j (j < 32)
+takes bit 2c of high-bit byte j, weight 64c + 32 + j bit 2c + 1.
+
 Q6_K (210 B): ql @0 (128 B), qh @128 (64 B), int8 scales @192 (16), d f16 @208.
 For half h and j < 32: weight 128h + j uses the low nibble of ql[64h + j] and
 bits 0-1 of qh[32h + j]; weight 128h+32+j the low nibble of ql[64h+32+j] and
@@ -61,6 +65,20 @@ def encode_q4k(d: float, dmin: float, sc, m, q) -> np.ndarray:
     return out
 
 
+def encode_q5k(d: float, dmin: float, sc, m, q) -> np.ndarray:
+    q = np.asarray(q, dtype=np.int64).reshape(256)
+    assert q.min() >= 0 and q.max() < 32
+    q4 = encode_q4k(d, dmin, sc, m, q & 15)  # header and nibbles as in Q4_K
+    out = np.zeros(176, np.uint8)
+    out[0:16] = q4[0:16]
+    out[48:176] = q4[16:144]
+    for c in range(4):
+        for j in range(32):
+            out[16 + j] |= (q[64 * c + j] >> 4) << (2 * c)
+            out[16 + j] |= (q[64 * c + 32 + j] >> 4) << (2 * c + 1)
+    return out
+
+
 def encode_q6k(d: float, sc, q) -> np.ndarray:
     sc = [int(v) for v in sc]
     q = np.asarray(q, dtype=np.int64).reshape(256)
@@ -90,6 +108,12 @@ def dense_q4k(d: float, dmin: float, sc, m, q) -> np.ndarray:
     return d * np.asarray(sc, np.float64)[s] * q - dmin * np.asarray(m, np.float64)[s]
 
 
+def dense_q5k(d: float, dmin: float, sc, m, q) -> np.ndarray:
+    """Weight values of one Q5_K superblock straight from its fields (the same
+    formula as Q4_K with 5-bit quants)."""
+    return dense_q4k(d, dmin, sc, m, q)
+
+
 def dense_q6k(d: float, sc, q) -> np.ndarray:
     d = f16_value(d)
     q = np.asarray(q, np.float64).reshape(256)
@@ -105,3 +129,8 @@ def random_q4k_fields(rng: np.random.Generator):
 def random_q6k_fields(rng: np.random.Generator):
     return dict(d=float(rng.uniform(1e-3, 1e-2)), sc=rng.integers(-32, 32, 16),
                 q=rng.integers(0, 64, 256))
+
+
+def random_q5k_fields(rng: np.random.Generator):
+    return dict(d=float(rng.uniform(1e-3, 1e-2)), dmin=float(rng.uniform(1e-3, 1e-2)),
+                sc=rng.integers(0, 64, 8), m=rng.integers(0, 64, 8), q=rng.integers(0, 32, 256))

@@ -178,6 +178,72 @@ def pin_closed_forms(o):
 
 
 # --------------------------------------------------------------------------
+# Q5_K field mapping: one-hot brute force, each high-bit lane alone from raw
+# bytes, each 6-bit field alone, closed forms
+def pin_q5k_onehot(o):
+    for k in (256, 1024):
+        nsb = k // 256
+        rows, vals = [], []
+        for p in range(k):
+            v = 1 + (p % 31)  # 1..31: half the positions carry the high bit
+            blocks = []
+            for b in range(nsb):
+                q = np.zeros(256, np.int64)
+                if b == p // 256:
+                    q[p % 256] = v
+                blocks.append(E.encode_q5k(1.0, 0.0, [1] * 8, [0] * 8, q))
+            rows.append(np.concatenate(blocks))
+            vals.append(v)
+        x = np.arange(1, k + 1, dtype=np.float64)
+        y, _ = o.matvec("q5k", np.stack(rows), x, k, k)
+        assert np.array_equal(y, np.array(vals, np.float64) * x), f"Q5_K one-hot positions wrong at k={k}"
+
+
+def pin_q5k_high_bit_lanes(o):
+    """Raw bytes: only bit b of high-bit byte j set (d = 1, every scale 1, no
+    mins, all nibbles 0): exactly one weight, 16, at input 64 (b // 2) +
+    32 (b % 2) + j."""
+    base = E.encode_q5k(1.0, 0.0, [1] * 8, [0] * 8, np.zeros(256))
+    rows, pos = [], []
+    for j in range(32):
+        for b in range(8):
+            blk = base.copy()
+            blk[16 + j] = 1 << b
+            rows.append(blk)
+            pos.append(64 * (b // 2) + 32 * (b % 2) + j)
+    x = np.arange(1, 257, dtype=np.float64)
+    y, _ = o.matvec("q5k", np.stack(rows), x, len(rows), 256)
+    assert np.array_equal(y, 16.0 * x[np.array(pos)]), "Q5_K high-bit lanes decode wrong"
+
+
+def pin_q5k_scale_and_min_fields(o):
+    x = np.arange(1, 257, dtype=np.float64)
+    sub_sum = np.array([x[32 * s:32 * s + 32].sum() for s in range(8)])
+    rows, want = [], []
+    for s in range(8):
+        for v in range(64):
+            sc = [0] * 8
+            sc[s] = v
+            rows.append(E.encode_q5k(1.0, 0.0, sc, [0] * 8, np.full(256, 17)))
+            want.append(17 * v * sub_sum[s])
+            m = [0] * 8
+            m[s] = v
+            rows.append(E.encode_q5k(0.0, 1.0, [0] * 8, m, np.zeros(256)))
+            want.append(-v * sub_sum[s])
+    y, _ = o.matvec("q5k", np.stack(rows), x, len(rows), 256)
+    assert np.array_equal(y, np.array(want)), "Q5_K scale/min fields decode wrong"
+
+
+def pin_q5k_closed_forms(o):
+    # all-equal fields with x = 1: y = k (d a c - dmin b), at the largest quant
+    d, dmin = E.f16_value(0.0078125), E.f16_value(0.001953125)
+    for c in (0, 16, 31):
+        blk = E.encode_q5k(d, dmin, [5] * 8, [3] * 8, np.full(256, c))
+        y, _ = o.matvec("q5k", np.stack([np.concatenate([blk] * 4)]), np.ones(1024), 1, 1024)
+        assert y[0] == 1024 * (d * 5 * c - dmin * 3), f"Q5_K all-equal closed form at q={c}"
+
+
+# --------------------------------------------------------------------------
 # exactness on integer activations: with x in {-3..3} every product is a
 # multiple of 2^-24 and the f64 sums are exact, so y * 2^24 must equal an
 # int64 sum computed from the encoded field values.
@@ -186,15 +252,15 @@ def pin_exact_integer_inputs(o):
     n, k = 8, 1024
     nsb = k // 256
     x = rng.integers(-3, 4, k)
-    for qt in ("q4k", "q6k"):
+    for qt in ("q4k", "q6k", "q5k"):
         W, want = [], []
         for _ in range(n):
             row, acc = [], 0
             for b in range(nsb):
                 xs = x[256 * b:256 * b + 256]
-                if qt == "q4k":
-                    f = E.random_q4k_fields(rng)
-                    row.append(E.encode_q4k(**f))
+                if qt in ("q4k", "q5k"):
+                    f = E.random_q4k_fields(rng) if qt == "q4k" else E.random_q5k_fields(rng)
+                    row.append(E.encode_q4k(**f) if qt == "q4k" else E.encode_q5k(**f))
                     D = int(round(E.f16_value(f["d"]) * 2**24))
                     Dm = int(round(E.f16_value(f["dmin"]) * 2**24))
                     s = np.arange(256) // 32
@@ -225,6 +291,10 @@ def _random_encoded(qt, rng, n, k):
                 f = E.random_q4k_fields(rng)
                 row.append(E.encode_q4k(**f))
                 drow.append(E.dense_q4k(**f))
+            elif qt == "q5k":
+                f = E.random_q5k_fields(rng)
+                row.append(E.encode_q5k(**f))
+                drow.append(E.dense_q5k(**f))
             else:
                 f = E.random_q6k_fields(rng)
                 row.append(E.encode_q6k(**f))
@@ -237,7 +307,7 @@ def _random_encoded(qt, rng, n, k):
 def pin_matvec_vs_numpy(o):
     rng = np.random.default_rng(3)
     n, k, m = 24, 1024, 5
-    for qt in ("q4k", "q6k"):
+    for qt in ("q4k", "q6k", "q5k"):
         W, D = _random_encoded(qt, rng, n, k)
         X = rng.standard_normal((m, k))
         Y, S = o.matmul(qt, W, X, n, k)
@@ -255,7 +325,7 @@ def pin_threaded_matmul_equals_single_thread(o):
     thread counts that do and do not divide the row count (37 rows)."""
     rng = np.random.default_rng(17)
     n, k, m = 37, 512, 3
-    for qt in ("q4k", "q6k"):
+    for qt in ("q4k", "q6k", "q5k"):
         W, D = _random_encoded(qt, rng, n, k)
         X = rng.standard_normal((m, k))
         Y1, S1 = o.matmul(qt, W, X, n, k, nthreads=1)
@@ -265,6 +335,22 @@ def pin_threaded_matmul_equals_single_thread(o):
             Yt, St = o.matmul(qt, W, X, n, k, nthreads=t)
             assert np.array_equal(Yt, Y1) and np.array_equal(St, S1), \
                 f"{qt} matmul with {t} threads differs from one thread"
+
+
+# --------------------------------------------------------------------------
+# embedding lookup: rows of the table dequantized, out-of-range tokens NaN
+def pin_embedding_gather(o):
+    rng = np.random.default_rng(21)
+    vocab, hidden = 40, 512
+    for qt in ("q4k", "q5k"):
+        W, D = _random_encoded(qt, rng, vocab, hidden)
+        tokens = np.array([0, 39, 7, 7, 12, -1, 40, 3])
+        got = o.embedding(qt, W, tokens, vocab, hidden)
+        for t, row in zip(tokens, got):
+            if 0 <= t < vocab:
+                assert np.array_equal(row, D[t]), f"{qt} embedding row {t}"
+            else:
+                assert np.all(np.isnan(row)), f"{qt} out-of-range token {t} not NaN"
 
 
 # --------------------------------------------------------------------------
@@ -353,7 +439,9 @@ def pin_ffn_layer_composition(o):
 
 ALL_PINS = [
     pin_f16_exhaustive, pin_q4k_onehot, pin_q4k_scale_and_min_fields, pin_q6k_onehot,
-    pin_q6k_qh_lanes, pin_q6k_scale_fields, pin_closed_forms, pin_exact_integer_inputs,
-    pin_matvec_vs_numpy, pin_threaded_matmul_equals_single_thread, pin_silu, pin_rms_norm_invariants, pin_tail_worked_example,
+    pin_q6k_qh_lanes, pin_q6k_scale_fields, pin_closed_forms, pin_q5k_onehot,
+    pin_q5k_high_bit_lanes, pin_q5k_scale_and_min_fields, pin_q5k_closed_forms,
+    pin_exact_integer_inputs, pin_matvec_vs_numpy, pin_threaded_matmul_equals_single_thread,
+    pin_embedding_gather, pin_silu, pin_rms_norm_invariants, pin_tail_worked_example,
     pin_tail_rows_and_invariants, pin_ffn_layer_composition,
 ]

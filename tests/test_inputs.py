@@ -51,3 +51,21 @@ def test_vectors():
     g = I.gains_f32(100000, stream=4)
     assert abs(g.mean() - 1) < 0.002 and abs(g.std() - 0.1) < 0.002
     assert np.array_equal(I.normal_f32((4, 8), stream=3).ravel(), I.normal_f32(32, stream=3))
+
+
+def test_q5k_field_distributions():
+    W = I.q5k_matrix(256, 4096, stream=1).reshape(-1, 176)
+    assert np.array_equal(W.reshape(256, -1), I.q5k_matrix(256, 4096, stream=1))
+    d = W[:, 0:2].copy().view("<f2").astype(np.float64).ravel()
+    assert d.min() >= 1e-3 - 1e-6 and d.max() <= 1e-2 + 1e-5
+    bits = np.unpackbits(W[:, 16:48].ravel())
+    assert abs(bits.mean() - 0.5) < 0.01  # every high bit uniform
+    nib = np.concatenate([W[:, 48:] & 15, W[:, 48:] >> 4]).ravel()
+    assert nib.max() == 15 and abs(nib.mean() - 7.5) < 0.05
+
+
+def test_token_ids():
+    t = I.token_ids(100000, 202048, stream=7)
+    assert t.dtype == np.int32 and t.min() >= 0 and t.max() < 202048
+    assert np.array_equal(t, I.token_ids(100000, 202048, stream=7))
+    assert abs(t.mean() / 202048 - 0.5) < 0.01

@@ -23,6 +23,9 @@ PLANTS = {
     11: "matvec drops the last superblock of each row",
     12: "activation index reversed inside each superblock",
     13: "threaded row split leaves one row of each range uncomputed",
+    14: "Q5_K high bit taken from bit c of the chunk, not bit 2c or 2c+1",
+    15: "Q5_K high bit worth 32 instead of 16",
+    16: "Q5_K low nibbles read from the high-bit bytes' offset",
 }
 
 
