@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HIDDEN, FFN, LAYERS = 6656, 19968, 52
+QDIM, KVDIM, VOCAB = 4096, 256, 202048  # attention projection and vocabulary sizes
 PEAK_HBM_GBPS = 8000.0
 Q4K_BLOCK, Q6K_BLOCK = 144, 210
 FULL_MODEL_TOKEN_BYTES = 16_756_681_056  # pages' per-token weight bytes (Ch 1, section 1.3)
@@ -80,8 +81,8 @@ STAGED_BYTES = {
 PASS_BYTES = LAYERS * (GATE_UP_BYTES + BYTES["down"] + BYTES["tail"]) + BYTES["tail"]
 WEIGHT_BYTES_PASS = LAYERS * (2 * q4k_bytes(FFN, HIDDEN) + q6k_bytes(HIDDEN, FFN))
 KERNEL_SYMBOL = {
-    "gate": "q4k_matvec_kernel<..., false>",
-    "up_silu": "q4k_matvec_kernel<..., true>",
+    "gate": "q45k_matvec_kernel<4, ..., false>",
+    "up_silu": "q45k_matvec_kernel<4, ..., true>",
     "down": "q6k_matvec_kernel",
     "tail": "tail_reg_kernel",
     "gate_up": "q4k_gate_up_kernel",
@@ -429,6 +430,64 @@ def isolated_matvecs(torch, kq, I, reps=5, launches=52):
     return out
 
 
+# The decode matvec shapes outside the FFN (Ch 10 "The forward pass at a
+# glance", section 10.3): the attention projections as one group on one input
+# (Q, K, V, gate), K or V alone, o_proj, and the LM head, in both weight types.
+DECODE_SHAPES = [
+    ("qkvg_group", [QDIM, KVDIM, KVDIM, QDIM], HIDDEN),
+    ("kv_alone", [KVDIM], HIDDEN),
+    ("q_alone", [QDIM], HIDDEN),
+    ("o_proj", [HIDDEN], QDIM),
+    ("lm_head", [VOCAB], HIDDEN),
+]
+
+
+def decode_shapes(torch, kq, I, reps=5, launches=52, max_launches=1200):
+    """Each shape as a graph of back-to-back launches, each launch on the next
+    of >= 1 GiB of weight copies (at most max_launches copies; fewer copies
+    of a small matrix still exceed the 256 MB Infinity Cache), median and CV
+    over `reps` replays.  Bytes per launch: the weights once, x in, y out."""
+    out = {}
+    for qt in ("q4k", "q6k"):
+        qtype = kq.KQ_QTYPE_Q4K if qt == "q4k" else kq.KQ_QTYPE_Q6K
+        rowb = lambda k: (k // 256) * (Q4K_BLOCK if qt == "q4k" else Q6K_BLOCK)
+        for name, rows, k in DECODE_SHAPES:
+            wb = [n * rowb(k) for n in rows]
+            set_bytes = sum(wb)
+            ncopy = int(min(max_launches, max(2, np.ceil((1 << 30) / set_bytes))))
+            host = [I.weight_matrix(qt, n, k, stream=800 + i) for i, n in enumerate(rows)]
+            buf = torch.empty(ncopy * set_bytes, dtype=torch.uint8, device="cuda")
+            first = torch.from_numpy(np.concatenate([h.reshape(-1) for h in host])).cuda()
+            for c in range(ncopy):
+                buf[c * set_bytes:(c + 1) * set_bytes].copy_(first)
+            del host, first
+            offs = np.concatenate([[0], np.cumsum(wb)[:-1]])
+            x = torch.from_numpy(I.normal_f32(k, stream=810)).cuda()
+            ys = [torch.empty(n, device="cuda") for n in rows]
+            base = buf.data_ptr()
+
+            def call(c):
+                Ws = [base + c * set_bytes + int(o) for o in offs]
+                if len(rows) == 1:
+                    fn = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
+                    fn(Ws[0], x, ys[0], rows[0], k)
+                else:
+                    kq.kq_matvec_group(qtype, Ws, ys, rows, x, k)
+            nl = max(launches, ncopy)
+            g = graph_of(torch, [lambda c=(i % ncopy): call(c) for i in range(nl)])
+            med, cv, _ = time_graph(torch, g, nl, reps)
+            del g, buf
+            torch.cuda.empty_cache()
+            nbytes = set_bytes + 4 * k + 4 * sum(rows)
+            out[f"{name}_{qt}"] = {"rows": rows, "k": k, "bytes": nbytes, "copies_rotated": ncopy,
+                                   "launches_per_replay": nl, "us_median": round(med, 3),
+                                   "us_cv": round(cv, 4), "GBps": round(nbytes / med / 1e3, 1),
+                                   "frac_peak": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
+                                   "shape": list(kq.kq_tune_get_shape(qtype, sum(rows), k))}
+            log(f"  {name}_{qt}: {med:.2f} us, {nbytes / med / 1e3:.0f} GB/s")
+    return out
+
+
 def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
     """kq_matmul_small_m at the verify shapes, M = 1..16: per-launch time from a
     graph of launches over >= 1 GiB of rotated weight copies (so the Infinity
@@ -551,7 +610,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time uncaptured launches instead of a graph")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
-    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu"),
+    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu", "shapes"),
                     help="run one section alone (for profiler runs) and print its results")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -584,6 +643,7 @@ def main():
         sec = {"isolated": lambda: {"isolated_matvec": isolated_matvecs(torch, kq, I)},
                "small_m": lambda: {"small_m": small_m_sweep(torch, kq, I)},
                "probe": lambda: {"read_ceiling": read_ceiling(torch, kq)},
+               "shapes": lambda: {"decode_shapes": decode_shapes(torch, kq, I)},
                "cpu": lambda: {"cpu_baseline": cpu_baseline(I)}}[args.only]()
         print(json.dumps({"section": args.only, **sec, "build": kq.kq_build_info()}), flush=True)
         torch.cuda.synchronize()
@@ -695,6 +755,8 @@ def main():
         extras["isolated_matvec"] = isolated_matvecs(torch, kq, I)
         log("small-M verify matmul sweep")
         extras["small_m"] = small_m_sweep(torch, kq, I)
+        log("other decode matvec shapes")
+        extras["decode_shapes"] = decode_shapes(torch, kq, I)
 
     cpu = None
     if not args.no_cpu_baseline:

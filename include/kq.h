@@ -25,6 +25,12 @@
  *   Q6_K, 210 B: low 4 bits @0 (128 B), high 2 bits @128 (64 B), 16 int8
  *     scales for sub-blocks of 16 @192, d f16 @208.
  *     weight = d * scale_s * (q - 32).
+ *   Q5_K, 176 B: d f16 @0, dmin f16 @2, the 12 bytes of 6-bit scales and mins
+ *     of Q4_K @4, 32 B of fifth bits @16 (byte j: bit 2c for weight 64c + j,
+ *     bit 2c+1 for weight 64c + 32 + j), 128 B of low 4 bits @48 laid out as
+ *     Q4_K's quants.  weight = d * scale_s * q - dmin * min_s, q = 0..31.
+ *     (The pages name Q5_K among the pinned decode kernels, Ch 4 "Pipeline
+ *     state objects and the three kernel sources", section 4.4.)
  *   A weight matrix with n_rows outputs and k inputs is stored row-major:
  *   row r is k/256 consecutive superblocks starting at byte
  *   r * (k/256) * block_bytes, and superblock b of a row covers inputs
@@ -96,10 +102,12 @@ typedef int kq_status;
 
 #define KQ_QTYPE_Q4K 1
 #define KQ_QTYPE_Q6K 2
+#define KQ_QTYPE_Q5K 3
 
 #define KQ_QK 256           /* weights per superblock */
 #define KQ_Q4K_BLOCK_BYTES 144
 #define KQ_Q6K_BLOCK_BYTES 210
+#define KQ_Q5K_BLOCK_BYTES 176
 #define KQ_MAX_K 40960      /* largest k (inputs per row) any matvec accepts */
 #define KQ_MAX_M 16         /* largest activation batch of kq_matmul_small_m */
 #define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
@@ -134,6 +142,74 @@ kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows,
  */
 kq_status kq_ffn_gate_up_q4k(const void *W_gate, const void *W_up, const float *x, float *mid,
                              int64_t n_rows, int64_t k, void *stream);
+
+/*
+ * Q5_K decode matvec: kq_matvec_q4k for Q5_K weights (same arguments,
+ * alignment, epilogue, errors and accuracy contract; W is
+ * n_rows * (k/256) * 176 bytes, 16-byte aligned).
+ */
+kq_status kq_matvec_q5k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        const float *silu_gate, void *stream);
+
+/*
+ * Embedding lookup (Ch 10 "The forward pass at a glance", section 10.3, box 1:
+ * the token's row of the [vocab x hidden] table becomes the residual stream):
+ * for t < n_tokens, out[t * hidden + i] = weight i of row tokens[t] of E,
+ * dequantized.  Each value is the f32 nearest the exact weight (the products
+ * d * scale * q and dmin * min are exact in f32; only their difference
+ * rounds), so the result is exact up to that one rounding.
+ *   qtype     KQ_QTYPE_Q4K or KQ_QTYPE_Q5K.
+ *   E         [vocab * (hidden/256) * block bytes], 16-byte aligned; row v is
+ *             token v.
+ *   vocab     1 .. 2^31 - 1.   hidden  multiple of 256, <= KQ_MAX_K.
+ *   tokens    [n_tokens] int32 (DEVICE memory), 4-byte aligned.  A token
+ *             outside [0, vocab) is not an error: its output row is all NaN
+ *             and no row of E is read for it.
+ *   n_tokens  0 .. 2^31 - 1 (0 enqueues nothing).
+ *   out       [n_tokens][hidden] f32, 16-byte aligned; must not overlap E or
+ *             tokens.
+ * Errors: KQ_ERR_NULL, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_ALIAS,
+ * KQ_ERR_UNSUPPORTED, KQ_ERR_LAUNCH, KQ_ERR_DEVICE.
+ */
+kq_status kq_embedding(int qtype, const void *E, int64_t vocab, int64_t hidden,
+                       const int32_t *tokens, int64_t n_tokens, float *out, void *stream);
+
+/*
+ * Several matvecs on one input in one launch: the attention projections of a
+ * decode layer (Q, K, V and the output gate) read the same normed input and
+ * write disjoint outputs, issued as one concurrent group (Ch 10 "The forward
+ * pass at a glance", section 10.3, box 4 and fusion (e); Q [6656->4096],
+ * K and V [6656->256], gate [6656->4096]).  For i < count and r < n_rows[i]:
+ *   y[i][r] = sum_j w_i[r,j] * x[j],
+ * with every matrix of weight type qtype and k inputs.  The input is staged
+ * once per workgroup for all of them, and rows of all matrices are spread
+ * over the GPU together, so a 256-row matrix in the group does not leave most
+ * of the GPU idle.  Each y[i] equals, bit for bit, the single-matrix matvec
+ * of that qtype on the same x launched with the same shape (the launch shape
+ * follows the total row count, so it may differ from a lone call's, and the
+ * result then agrees within the tolerance).
+ *   qtype    KQ_QTYPE_Q4K, KQ_QTYPE_Q5K or KQ_QTYPE_Q6K.
+ *   count    1 .. KQ_MAX_GROUP.
+ *   W, y, n_rows  HOST arrays of `count` entries: device pointers to each
+ *            matrix (alignment as for the matvec of qtype) and to its output
+ *            [n_rows[i]] f32 (4-byte aligned), and the row counts (>= 0;
+ *            their sum < 2^31).  A member with 0 rows is skipped; its W and
+ *            y may be NULL.
+ *   x        [k] f32, 16-byte aligned; k as for the matvecs.
+ * No output may overlap an input or another output.
+ * Errors as kq_matvec_q4k; count out of range is KQ_ERR_SHAPE.
+ */
+#define KQ_MAX_GROUP 4
+kq_status kq_matvec_group(int qtype, int count, const void *const *W, float *const *y,
+                          const int64_t *n_rows, const float *x, int64_t k, void *stream);
+
+/*
+ * kq_matvec_group on a staged input: xs = kq_staged_bytes(qtype, k) bytes,
+ * 16-byte aligned (same results, bit for bit, as on the f32 vector the stage
+ * was made from).
+ */
+kq_status kq_matvec_group_staged(int qtype, int count, const void *const *W, float *const *y,
+                                 const int64_t *n_rows, const void *xs, int64_t k, void *stream);
 
 /*
  * Q6_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows.
@@ -176,6 +252,29 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
 kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ldx, float *Y,
                             int64_t ldy, int64_t n_rows, int64_t k, int m, void *workspace,
                             int64_t workspace_bytes, void *stream);
+
+/*
+ * The FFN entry for the verify batch (Ch 10 "The forward pass at a glance",
+ * section 10.3, box 11, for M rows: Ch 36 "Prefill vs decode", section 36.4):
+ * for m < M and r < n_rows,
+ *   Mid[m * ldm + r] = silu((W_gate X[m])[r]) * (W_up X[m])[r],
+ * silu(z) = z / (1 + exp(-z)); both matrices Q4_K, n_rows x k.  M = 1 runs the
+ * one-launch gate+up kernel (the result of kq_ffn_gate_up_q4k); M >= 2 runs
+ * the matrix-core kernel twice (gate into Mid, then up with the SiLU product
+ * applied as each output is stored), each within the kq_matmul_small_m
+ * accuracy of its own matvec.
+ *   X, ldx, m, workspace, workspace_bytes  as for kq_matmul_small_m with
+ *          qtype KQ_QTYPE_Q4K (the same workspace size serves both launches).
+ *   Mid    [M][ldm] f32 output, ldm >= n_rows, 4-byte aligned; must not
+ *          overlap W_gate, W_up, X or the workspace.
+ * A layer of the verify batch is this call, kq_matmul_small_m on Mid (the
+ * down projection) and kq_fused_residual_norm over the M rows.
+ * Errors as kq_matmul_small_m.
+ */
+kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const float *X,
+                                     int64_t ldx, float *Mid, int64_t ldm, int64_t n_rows,
+                                     int64_t k, int m, void *workspace, int64_t workspace_bytes,
+                                     void *stream);
 
 /*
  * kq_matmul_small_m without a workspace argument, for callers that cannot

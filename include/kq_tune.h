@@ -19,7 +19,7 @@ extern "C" {
 
 /*
  * Process-wide override of the launch shape of the M = 1 matvec of `qtype`
- * (KQ_QTYPE_Q4K or KQ_QTYPE_Q6K): `lanes` lanes per weight row (4, 8, 16, 32
+ * (KQ_QTYPE_Q4K, KQ_QTYPE_Q5K or KQ_QTYPE_Q6K): `lanes` lanes per weight row (4, 8, 16, 32
  * or 64), `waves` wavefronts per workgroup (1..16), `grid` workgroups,
  * `depth` half-superblock units kept in flight per lane (1..3).  A zero field
  * keeps the automatic choice for that field; all zeros restores it.

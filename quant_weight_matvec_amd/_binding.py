@@ -27,9 +27,11 @@ KQ_ERR_LAUNCH = -6
 KQ_ERR_DEVICE = -7
 KQ_QTYPE_Q4K = 1
 KQ_QTYPE_Q6K = 2
+KQ_QTYPE_Q5K = 3
 KQ_MAX_K = 40960
 KQ_MAX_M = 16
 KQ_MAX_TAIL_N = 32768
+KQ_MAX_GROUP = 4
 KQ_SMALL_M_SCRATCH_BYTES = 16 * 1024 + 16 * 1024 * 1024
 
 
@@ -59,9 +61,15 @@ def lib() -> C.CDLL:
     L = C.CDLL(LIB_PATH)
     L.kq_matvec_q4k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp]
     L.kq_matvec_q6k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
+    L.kq_matvec_q5k.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp]
+    L.kq_embedding.argtypes = [C.c_int, _vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    L.kq_matvec_group.argtypes = [C.c_int, C.c_int, _vp, _vp, _vp, _vp, _i64, _vp]
+    L.kq_matvec_group_staged.argtypes = [C.c_int, C.c_int, _vp, _vp, _vp, _vp, _i64, _vp]
     L.kq_ffn_gate_up_q4k.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
     L.kq_matmul_small_m.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int, _vp,
                                     _i64, _vp]
+    L.kq_ffn_gate_up_q4k_small_m.argtypes = [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, C.c_int,
+                                             _vp, _i64, _vp]
     L.kq_matmul_small_m_noalloc.argtypes = [C.c_int, _vp, _vp, _i64, _vp, _i64, _i64, _i64,
                                             C.c_int, _vp]
     L.kq_matmul_small_m_workspace_bytes.argtypes = [C.c_int, _i64, _i64, C.c_int]
@@ -91,7 +99,9 @@ def lib() -> C.CDLL:
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
                "kq_tune_small_m_plan", "kq_tune_matvec_plan",
-               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_matmul_small_m_noalloc", "kq_fused_residual_norm",
+               "kq_probe_read_bw", "kq_matvec_q4k", "kq_matvec_q6k", "kq_matvec_group",
+               "kq_matvec_q5k", "kq_embedding",
+               "kq_matvec_group_staged", "kq_ffn_gate_up_q4k", "kq_matmul_small_m", "kq_matmul_small_m_noalloc", "kq_ffn_gate_up_q4k_small_m", "kq_fused_residual_norm",
                "kq_tune_set_shape", "kq_tune_get_shape"):
         getattr(L, fn).restype = C.c_int
     _lib = L
@@ -134,6 +144,19 @@ def kq_matvec_q4k(W, x, y, n_rows: int, k: int, silu_gate=None, stream=None) -> 
     _check(rc, "kq_matvec_q4k")
 
 
+def kq_matvec_q5k(W, x, y, n_rows: int, k: int, silu_gate=None, stream=None) -> None:
+    rc = lib().kq_matvec_q5k(_ptr(W), _ptr(x), _ptr(y), int(n_rows), int(k), _ptr(silu_gate),
+                             _stream(stream))
+    _check(rc, "kq_matvec_q5k")
+
+
+def kq_embedding(qtype: int, E, vocab: int, hidden: int, tokens, n_tokens: int, out,
+                 stream=None) -> None:
+    rc = lib().kq_embedding(int(qtype), _ptr(E), int(vocab), int(hidden), _ptr(tokens),
+                            int(n_tokens), _ptr(out), _stream(stream))
+    _check(rc, "kq_embedding")
+
+
 def kq_ffn_gate_up_q4k(W_gate, W_up, x, mid, n_rows: int, k: int, stream=None) -> None:
     rc = lib().kq_ffn_gate_up_q4k(_ptr(W_gate), _ptr(W_up), _ptr(x), _ptr(mid), int(n_rows),
                                   int(k), _stream(stream))
@@ -145,12 +168,47 @@ def kq_matvec_q6k(W, x, y, n_rows: int, k: int, stream=None) -> None:
     _check(rc, "kq_matvec_q6k")
 
 
+def _group_args(W, y, n_rows):
+    n = len(W)
+    if len(y) != n or len(n_rows) != n:
+        raise ValueError("W, y and n_rows need one entry per matrix")
+    Wa = (C.c_void_p * max(n, 1))(*[_ptr(w) for w in W])
+    ya = (C.c_void_p * max(n, 1))(*[_ptr(v) for v in y])
+    na = (C.c_int64 * max(n, 1))(*[int(r) for r in n_rows])
+    return n, Wa, ya, na
+
+
+def kq_matvec_group(qtype: int, W, y, n_rows, x, k: int, stream=None) -> None:
+    """W, y, n_rows: sequences (one entry per matrix) of weights, outputs and row counts."""
+    n, Wa, ya, na = _group_args(W, y, n_rows)
+    rc = lib().kq_matvec_group(int(qtype), n, C.cast(Wa, C.c_void_p), C.cast(ya, C.c_void_p),
+                               C.cast(na, C.c_void_p), _ptr(x), int(k), _stream(stream))
+    _check(rc, "kq_matvec_group")
+
+
+def kq_matvec_group_staged(qtype: int, W, y, n_rows, xs, k: int, stream=None) -> None:
+    n, Wa, ya, na = _group_args(W, y, n_rows)
+    rc = lib().kq_matvec_group_staged(int(qtype), n, C.cast(Wa, C.c_void_p),
+                                      C.cast(ya, C.c_void_p), C.cast(na, C.c_void_p), _ptr(xs),
+                                      int(k), _stream(stream))
+    _check(rc, "kq_matvec_group_staged")
+
+
 def kq_matmul_small_m(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: int, m: int,
                       workspace=None, workspace_bytes: int = 0, stream=None) -> None:
     rc = lib().kq_matmul_small_m(int(qtype), _ptr(W), _ptr(X), int(ldx), _ptr(Y), int(ldy),
                                  int(n_rows), int(k), int(m), _ptr(workspace),
                                  int(workspace_bytes), _stream(stream))
     _check(rc, "kq_matmul_small_m")
+
+
+def kq_ffn_gate_up_q4k_small_m(W_gate, W_up, X, ldx: int, Mid, ldm: int, n_rows: int, k: int,
+                               m: int, workspace=None, workspace_bytes: int = 0,
+                               stream=None) -> None:
+    rc = lib().kq_ffn_gate_up_q4k_small_m(_ptr(W_gate), _ptr(W_up), _ptr(X), int(ldx), _ptr(Mid),
+                                          int(ldm), int(n_rows), int(k), int(m), _ptr(workspace),
+                                          int(workspace_bytes), _stream(stream))
+    _check(rc, "kq_ffn_gate_up_q4k_small_m")
 
 
 def kq_matmul_small_m_noalloc(qtype: int, W, X, ldx: int, Y, ldy: int, n_rows: int, k: int,

@@ -73,6 +73,38 @@ kq_status kq_matvec_q4k(const void *W, const float *x, float *y, int64_t n_rows,
                                            silu_gate, (hipStream_t)stream));
 }
 
+kq_status kq_matvec_q5k(const void *W, const float *x, float *y, int64_t n_rows, int64_t k,
+                        const float *silu_gate, void *stream)
+{
+    const int64_t rowb = (k / KQ_QK) * KQ_Q5K_BLOCK_BYTES;
+    kq_status s = check_matvec(W, rowb, 16, x, y, n_rows, k, silu_gate);
+    if (s != KQ_OK) return s;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_matvec_q5k((const uint8_t *)W, x, nullptr, y, (int)n_rows, (int)k,
+                                           silu_gate, (hipStream_t)stream));
+}
+
+kq_status kq_embedding(int qtype, const void *E, int64_t vocab, int64_t hidden,
+                       const int32_t *tokens, int64_t n_tokens, float *out, void *stream)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q5K) return KQ_ERR_SHAPE;
+    if (!E || !tokens || !out) return KQ_ERR_NULL;
+    if (vocab < 1 || vocab > INT32_MAX || n_tokens < 0 || n_tokens > INT32_MAX)
+        return KQ_ERR_SHAPE;
+    kq_status s = check_k(hidden);
+    if (s != KQ_OK) return s;
+    if (!aligned(E, 16) || !aligned(tokens, 4) || !aligned(out, 16)) return KQ_ERR_ALIGN;
+    const int64_t blk = qtype == KQ_QTYPE_Q4K ? KQ_Q4K_BLOCK_BYTES : KQ_Q5K_BLOCK_BYTES;
+    const int64_t ob = n_tokens * hidden * 4;
+    if (overlap(out, ob, E, vocab * (hidden / KQ_QK) * blk) || overlap(out, ob, tokens, n_tokens * 4))
+        return KQ_ERR_ALIAS;
+    if (n_tokens == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    return from_hip(kqi::launch_embedding(qtype, (const uint8_t *)E, tokens, (int)n_tokens, out,
+                                          (int)vocab, (int)hidden, (hipStream_t)stream));
+}
+
 kq_status kq_ffn_gate_up_q4k(const void *W_gate, const void *W_up, const float *x, float *mid,
                              int64_t n_rows, int64_t k, void *stream)
 {
@@ -105,8 +137,93 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
                                            (hipStream_t)stream));
 }
 
+// Shared checks of kq_matvec_group and kq_matvec_group_staged; xbytes is the
+// size of the input (f32 or staged).
+static kq_status check_group(int qtype, int count, const void *const *W, float *const *y,
+                             const int64_t *n_rows, const void *x, int64_t xbytes, int64_t k,
+                             int64_t *total)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K && qtype != KQ_QTYPE_Q5K)
+        return KQ_ERR_SHAPE;
+    if (count < 1 || count > KQ_MAX_GROUP) return KQ_ERR_SHAPE;
+    if (!W || !y || !n_rows || !x) return KQ_ERR_NULL;
+    kq_status s = check_k(k);
+    if (s != KQ_OK) return s;
+    const bool q4 = qtype != KQ_QTYPE_Q6K;  // Q4_K and Q5_K: 16-byte aligned superblocks
+    const int64_t rowb = (k / KQ_QK) * (qtype == KQ_QTYPE_Q4K   ? KQ_Q4K_BLOCK_BYTES
+                                        : qtype == KQ_QTYPE_Q5K ? KQ_Q5K_BLOCK_BYTES
+                                                                : KQ_Q6K_BLOCK_BYTES);
+    int64_t t = 0;
+    for (int i = 0; i < count; ++i) {
+        if (n_rows[i] < 0 || n_rows[i] > INT32_MAX) return KQ_ERR_SHAPE;
+        if (n_rows[i] == 0) continue;  // an empty member's pointers are never used
+        if (!W[i] || !y[i]) return KQ_ERR_NULL;
+        t += n_rows[i];
+        if (t > INT32_MAX) return KQ_ERR_SHAPE;
+        if (!aligned(W[i], q4 ? 16 : 4) || !aligned(y[i], 4)) return KQ_ERR_ALIGN;
+    }
+    if (!aligned(x, 16)) return KQ_ERR_ALIGN;
+    for (int i = 0; i < count; ++i) {
+        const int64_t yb = n_rows[i] * 4;
+        if (overlap(y[i], yb, x, xbytes)) return KQ_ERR_ALIAS;
+        for (int j = 0; j < count; ++j) {
+            if (overlap(y[i], yb, W[j], n_rows[j] * rowb)) return KQ_ERR_ALIAS;
+            if (j > i && overlap(y[i], yb, y[j], n_rows[j] * 4)) return KQ_ERR_ALIAS;
+        }
+    }
+    *total = t;
+    return KQ_OK;
+}
+
+static kq_status run_group(int qtype, int count, const void *const *W, float *const *y,
+                           const int64_t *n_rows, const float *x, const void *xs, int64_t k,
+                           void *stream)
+{
+    const uint8_t *w[KQ_MAX_GROUP];
+    float *o[KQ_MAX_GROUP];
+    int rows[KQ_MAX_GROUP];
+    int c = 0;
+    for (int i = 0; i < count; ++i) {
+        if (n_rows[i] == 0) continue;  // an empty matrix takes no segment
+        w[c] = (const uint8_t *)W[i];
+        o[c] = y[i];
+        rows[c] = (int)n_rows[i];
+        ++c;
+    }
+    if (c == 0) return KQ_OK;
+    kq_status s = check_device();
+    if (s != KQ_OK) return s;
+    return from_hip(kqi::launch_matvec_group(qtype, c, w, o, rows, x, (const uint8_t *)xs,
+                                             (int)k, (hipStream_t)stream));
+}
+
+kq_status kq_matvec_group(int qtype, int count, const void *const *W, float *const *y,
+                          const int64_t *n_rows, const float *x, int64_t k, void *stream)
+{
+    int64_t total = 0;
+    kq_status s = check_group(qtype, count, W, y, n_rows, x, k * 4, k, &total);
+    if (s != KQ_OK) return s;
+    return run_group(qtype, count, W, y, n_rows, x, nullptr, k, stream);
+}
+
+static int64_t staged_size(int qtype, int64_t k);
+
+kq_status kq_matvec_group_staged(int qtype, int count, const void *const *W, float *const *y,
+                                 const int64_t *n_rows, const void *xs, int64_t k, void *stream)
+{
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K && qtype != KQ_QTYPE_Q5K)
+        return KQ_ERR_SHAPE;
+    const kq_status sk = check_k(k);
+    if (sk != KQ_OK) return sk;
+    int64_t total = 0;
+    kq_status s = check_group(qtype, count, W, y, n_rows, xs, staged_size(qtype, k), k, &total);
+    if (s != KQ_OK) return s;
+    return run_group(qtype, count, W, y, n_rows, nullptr, xs, k, stream);
+}
+
 static kq_status check_small_m(int qtype, int64_t n_rows, int64_t k, int m)
 {
+    if (qtype == KQ_QTYPE_Q5K) return KQ_ERR_UNSUPPORTED;  // matrix-core path: Q4_K, Q6_K
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
     if (m < 1 || n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
     if (m > KQ_MAX_M) return KQ_ERR_UNSUPPORTED;
@@ -126,6 +243,7 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
                             int64_t ldy, int64_t n_rows, int64_t k, int m, void *workspace,
                             int64_t workspace_bytes, void *stream)
 {
+    if (qtype == KQ_QTYPE_Q5K) return KQ_ERR_UNSUPPORTED;
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
     if (!W || !X || !Y) return KQ_ERR_NULL;
     kq_status s = check_small_m(qtype, n_rows, k, m);
@@ -162,10 +280,52 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
                                              (hipStream_t)stream));
 }
 
+kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const float *X,
+                                     int64_t ldx, float *Mid, int64_t ldm, int64_t n_rows,
+                                     int64_t k, int m, void *workspace, int64_t workspace_bytes,
+                                     void *stream)
+{
+    if (!W_gate || !W_up || !X || !Mid) return KQ_ERR_NULL;
+    kq_status s = check_small_m(KQ_QTYPE_Q4K, n_rows, k, m);
+    if (s != KQ_OK) return s;
+    if (ldx < k || ldx % 4 || ldm < n_rows || ldm < 1 || workspace_bytes < 0) return KQ_ERR_SHAPE;
+    if (!aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(X, 16) || !aligned(Mid, 4) ||
+        !aligned(workspace, 256))
+        return KQ_ERR_ALIGN;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    const int64_t mbytes = ((int64_t)(m - 1) * ldm + n_rows) * 4;
+    const int64_t xbytes = ((int64_t)(m - 1) * ldx + k) * 4;
+    if (overlap(Mid, mbytes, W_gate, wbytes) || overlap(Mid, mbytes, W_up, wbytes) ||
+        overlap(Mid, mbytes, X, xbytes))
+        return KQ_ERR_ALIAS;
+    if (n_rows == 0) return KQ_OK;
+    if ((s = check_device()) != KQ_OK) return s;
+    const hipStream_t st = (hipStream_t)stream;
+    if (m == 1)
+        return from_hip(kqi::launch_gate_up_q4k((const uint8_t *)W_gate, (const uint8_t *)W_up, X,
+                                                nullptr, Mid, nullptr, 0, (int)n_rows, (int)k,
+                                                nullptr, st));
+    const int64_t need = (int64_t)kqi::small_m_workspace_bytes(KQ_QTYPE_Q4K, (int)n_rows, (int)k, m);
+    if (need > 0) {
+        if (!workspace) return KQ_ERR_NULL;
+        if (workspace_bytes < need) return KQ_ERR_SHAPE;
+        if (overlap(workspace, need, Mid, mbytes) || overlap(workspace, need, X, xbytes) ||
+            overlap(workspace, need, W_gate, wbytes) || overlap(workspace, need, W_up, wbytes))
+            return KQ_ERR_ALIAS;
+    }
+    hipError_t e = kqi::launch_small_m_mfma(KQ_QTYPE_Q4K, (const uint8_t *)W_gate, X, ldx, Mid, ldm,
+                                            (int)n_rows, (int)k, m, workspace, workspace_bytes, st);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(kqi::launch_small_m_mfma(KQ_QTYPE_Q4K, (const uint8_t *)W_up, X, ldx, Mid, ldm,
+                                             (int)n_rows, (int)k, m, workspace, workspace_bytes, st,
+                                             Mid, ldm));
+}
+
 kq_status kq_matmul_small_m_noalloc(int qtype, const void *W, const float *X, int64_t ldx,
                                     float *Y, int64_t ldy, int64_t n_rows, int64_t k, int m,
                                     void *stream)
 {
+    if (qtype == KQ_QTYPE_Q5K) return KQ_ERR_UNSUPPORTED;
     if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
     if (!W || !X || !Y) return KQ_ERR_NULL;
     kq_status s = check_small_m(qtype, n_rows, k, m);
@@ -227,7 +387,8 @@ kq_status kq_fused_residual_norm(float *residual, const float *projected, float 
 // 32 inputs for Q4_K, 16 for Q6_K.
 static int staged_group(int qtype)
 {
-    return qtype == KQ_QTYPE_Q4K ? 32 : (qtype == KQ_QTYPE_Q6K ? 16 : 0);
+    // Q4_K and Q5_K: sub-blocks of 32 inputs; Q6_K: 16
+    return (qtype == KQ_QTYPE_Q4K || qtype == KQ_QTYPE_Q5K) ? 32 : (qtype == KQ_QTYPE_Q6K ? 16 : 0);
 }
 
 static int64_t staged_size(int qtype, int64_t k)
@@ -267,22 +428,27 @@ kq_status kq_matvec_staged(int qtype, const void *W, const void *xs, float *y, i
     if (n_rows < 0 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;
     kq_status s = check_k(k);
     if (s != KQ_OK) return s;
-    const bool q4 = qtype == KQ_QTYPE_Q4K;
-    if (!aligned(W, q4 ? 16 : 4) || !aligned(xs, 16) || !aligned(y, 4) ||
+    const bool q6 = qtype == KQ_QTYPE_Q6K;
+    if (!aligned(W, q6 ? 4 : 16) || !aligned(xs, 16) || !aligned(y, 4) ||
         (silu_gate && !aligned(silu_gate, 4)))
         return KQ_ERR_ALIGN;
-    const int64_t wbytes = n_rows * (k / KQ_QK) * (q4 ? KQ_Q4K_BLOCK_BYTES : KQ_Q6K_BLOCK_BYTES);
+    const int64_t blk = qtype == KQ_QTYPE_Q4K   ? KQ_Q4K_BLOCK_BYTES
+                        : qtype == KQ_QTYPE_Q5K ? KQ_Q5K_BLOCK_BYTES
+                                                : KQ_Q6K_BLOCK_BYTES;
+    const int64_t wbytes = n_rows * (k / KQ_QK) * blk;
     const int64_t ybytes = n_rows * 4;
     if (overlap(y, ybytes, W, wbytes) || overlap(y, ybytes, xs, staged_size(qtype, k)) ||
         overlap(y, ybytes, silu_gate, silu_gate ? ybytes : 0))
         return KQ_ERR_ALIAS;
     if (n_rows == 0) return KQ_OK;
     if ((s = check_device()) != KQ_OK) return s;
-    return from_hip(q4 ? kqi::launch_matvec_q4k((const uint8_t *)W, nullptr, (const uint8_t *)xs, y,
-                                                (int)n_rows, (int)k, silu_gate,
-                                                (hipStream_t)stream)
-                       : kqi::launch_matvec_q6k((const uint8_t *)W, nullptr, (const uint8_t *)xs, y,
-                                                (int)n_rows, (int)k, (hipStream_t)stream));
+    const uint8_t *w = (const uint8_t *)W, *xsb = (const uint8_t *)xs;
+    const hipStream_t st = (hipStream_t)stream;
+    if (qtype == KQ_QTYPE_Q4K)
+        return from_hip(kqi::launch_matvec_q4k(w, nullptr, xsb, y, (int)n_rows, (int)k, silu_gate, st));
+    if (qtype == KQ_QTYPE_Q5K)
+        return from_hip(kqi::launch_matvec_q5k(w, nullptr, xsb, y, (int)n_rows, (int)k, silu_gate, st));
+    return from_hip(kqi::launch_matvec_q6k(w, nullptr, xsb, y, (int)n_rows, (int)k, st));
 }
 
 kq_status kq_ffn_gate_up_q4k_staged(const void *W_gate, const void *W_up, const void *xs,
@@ -423,7 +589,7 @@ const char *kq_build_info(void)
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)
 {
-    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K && qtype != KQ_QTYPE_Q5K) return KQ_ERR_SHAPE;
     if (lanes && lanes != 4 && lanes != 8 && lanes != 16 && lanes != 32 && lanes != 64)
         return KQ_ERR_SHAPE;
     if (waves < 0 || waves > 16 || grid < 0 || depth < 0 || depth > 3) return KQ_ERR_SHAPE;
@@ -434,7 +600,7 @@ kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth
 kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, int *waves,
                             int *grid, int *depth)
 {
-    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K && qtype != KQ_QTYPE_Q5K) return KQ_ERR_SHAPE;
     if (!lanes || !waves || !grid || !depth) return KQ_ERR_NULL;
     kq_status s = check_k(k);
     if (s != KQ_OK) return s;
@@ -451,7 +617,7 @@ kq_status kq_tune_get_shape(int qtype, int64_t n_rows, int64_t k, int *lanes, in
 kq_status kq_tune_matvec_plan(int qtype, int64_t n_rows, int64_t k, int staged, int cus,
                               int64_t *out)
 {
-    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K) return KQ_ERR_SHAPE;
+    if (qtype != KQ_QTYPE_Q4K && qtype != KQ_QTYPE_Q6K && qtype != KQ_QTYPE_Q5K) return KQ_ERR_SHAPE;
     kq_status s = check_k(k);
     if (s != KQ_OK) return s;
     if (!out) return KQ_ERR_NULL;

@@ -18,6 +18,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQ4Bytes = 144;
 constexpr int kQ6Bytes = 210;
+constexpr int kQ5Bytes = 176;
 
 __device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c)
 {
@@ -303,6 +304,47 @@ __device__ __forceinline__ float lane_group_sum(float v)
 }
 
 // ---------------------------------------------------------------------------
+// Up to kMaxSegs weight matrices of one type and k that share one activation
+// vector, launched as one matvec (the pages' concurrent projection group,
+// Ch 10 "The forward pass at a glance", section 10.3, box 4): their rows are
+// numbered back to back, segment s holding rows [end[s-1], end[s]) of that
+// numbering (end[-1] = 0), and row r of the numbering is row r - end[s-1] of
+// matrix W[s], written to y[s].  Unused segments have end = INT_MAX.  Lanes
+// pick their row's segment with selects (no indexed kernel-argument load).
+constexpr int kMaxSegs = 4;
+struct MatSegs {
+    const uint8_t *W[kMaxSegs];
+    float *y[kMaxSegs];
+    int end[kMaxSegs];
+};
+
+__device__ __forceinline__ int seg_of(const MatSegs &m, int r)
+{
+    return (r >= m.end[0]) + (r >= m.end[1]) + (r >= m.end[2]);
+}
+
+__device__ __forceinline__ int seg_start(const MatSegs &m, int s)
+{
+    return s == 0 ? 0 : (s == 1 ? m.end[0] : (s == 2 ? m.end[1] : m.end[2]));
+}
+
+// First byte of row r (of the joint numbering) in its own matrix.
+__device__ __forceinline__ const uint8_t *seg_row(const MatSegs &m, int r, int64_t row_bytes)
+{
+    const int s = seg_of(m, r);
+    const uint8_t *w = s == 0 ? m.W[0] : (s == 1 ? m.W[1] : (s == 2 ? m.W[2] : m.W[3]));
+    return w + (int64_t)(r - seg_start(m, s)) * row_bytes;
+}
+
+// Output element of row r (of the joint numbering).
+__device__ __forceinline__ float *seg_out(const MatSegs &m, int r)
+{
+    const int s = seg_of(m, r);
+    float *y = s == 0 ? m.y[0] : (s == 1 ? m.y[1] : (s == 2 ? m.y[2] : m.y[3]));
+    return y + (r - seg_start(m, s));
+}
+
+// ---------------------------------------------------------------------------
 // Q4_K unit = one half superblock (sub-blocks 4h..4h+3, 128 weights): the
 // 16-byte header and 64 contiguous bytes of nibbles.
 struct Q4Unit {
@@ -387,6 +429,125 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
     }
     return out;
 }
+
+// ---------------------------------------------------------------------------
+// Q5_K unit = one half superblock (sub-blocks 4h..4h+3): the 16-byte header
+// (d, dmin and the 6-bit scales and mins packed as in Q4_K), all 32 bytes of
+// high bits (byte j holds the fifth bit of weight 64c + j in bit 2c and of
+// weight 64c + 32 + j in bit 2c + 1), and the unit's 64 bytes of low nibbles
+// (laid out as Q4_K's, at byte 48).  A 176-byte superblock keeps 16-byte
+// alignment, so every load is a 16-byte vector load.
+struct Q5Unit {
+    u32x4 hdr;
+    u32x4 qh[2];
+    u32x4 q[4];
+};
+
+__device__ __forceinline__ Q5Unit q5_load(const uint8_t *__restrict__ sb, int h)
+{
+    Q5Unit u;
+    u.hdr = *reinterpret_cast<const u32x4 *>(sb);
+    u.qh[0] = *reinterpret_cast<const u32x4 *>(sb + 16);
+    u.qh[1] = *reinterpret_cast<const u32x4 *>(sb + 32);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(sb + 48 + 64 * h);
+    u.q[0] = p[0];
+    u.q[1] = p[1];
+    u.q[2] = p[2];
+    u.q[3] = p[3];
+    return u;
+}
+
+// Contribution of one Q5_K unit; as q4_unit_dot with each quant byte
+// completed by its fifth bit (values 0..31, still a signed byte operand).
+template <int LIMBS>
+__device__ __forceinline__ float q5_unit_dot(const Q5Unit &u, int h, int base, int k,
+                                             const uint8_t *__restrict__ planes,
+                                             const float *__restrict__ tscale,
+                                             const float *__restrict__ tsum)
+{
+    const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
+    const uint32_t sc_lo = S0 & 0x3F3F3F3Fu, mn_lo = S1 & 0x3F3F3F3Fu;
+    const uint32_t sc_hi = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+    const uint32_t mn_hi = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+    const uint32_t scb = h ? sc_hi : sc_lo;
+    const uint32_t mnb = h ? mn_hi : mn_lo;
+    const float d = half_lo(u.hdr.x), dmin = half_hi(u.hdr.x);
+
+    int acc[4][LIMBS];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) acc[s][l] = 0;
+    const int P = (int)plane_bytes(k);
+    const uint8_t *xp = planes + (base >> 3);
+
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        // 16 bytes = inputs j0..j0+15 of sub-block 2c (low nibbles, fifth bit
+        // 2c) and of sub-block 2c+1 (high nibbles, bit 2c+1), c = 2h + p/2,
+        // j0 = 16 (p & 1); the fifth bits sit in high-bit bytes j0..j0+15.
+        const int plo = base + 64 * (p >> 1) + 16 * (p & 1);
+        const int slo = 2 * (p >> 1);
+        const int sh = 4 * h + 2 * (p >> 1);  // bit 2c of each high-bit byte
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t qh = u.qh[p & 1][w] >> sh;
+            lo[w] = (u.q[p][w] & 0x0F0F0F0Fu) | ((qh << 4) & 0x10101010u);
+            hi[w] = ((u.q[p][w] >> 4) & 0x0F0F0F0Fu) | ((qh << 3) & 0x10101010u);
+        }
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) {
+            const u32x4 xl = *reinterpret_cast<const u32x4 *>(xp + l * P + plo);
+            const u32x4 xh = *reinterpret_cast<const u32x4 *>(xp + l * P + plo + 32);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc[slo][l] = sdot4(lo[w], xl[w], acc[slo][l]);
+                acc[slo + 1][l] = sdot4(hi[w], xh[w], acc[slo + 1][l]);
+            }
+        }
+    }
+
+    const int g0 = base >> 5;
+    const f32x4 gs = *reinterpret_cast<const f32x4 *>(tscale + g0);
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(tsum + g0);
+    float out = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const float sc = (float)((scb >> (8 * s)) & 0xFFu);
+        const float mn = (float)((mnb >> (8 * s)) & 0xFFu);
+        const float v = combine_limbs<LIMBS>(acc[s]);
+        out += (d * sc) * (gs[s] * v) - (dmin * mn) * gm[s];
+    }
+    return out;
+}
+
+// The superblock format of a Q4_K-style matvec: 4 = Q4_K, 5 = Q5_K.
+template <int FMT> struct KFmt;
+template <> struct KFmt<4> {
+    using Unit = Q4Unit;
+    static constexpr int kBytes = kQ4Bytes;
+    static __device__ __forceinline__ Unit load(const uint8_t *sb, int h) { return q4_load(sb, h); }
+    template <int LIMBS>
+    static __device__ __forceinline__ float dot(const Unit &u, int h, int base, int k,
+                                                const uint8_t *planes, const float *tscale,
+                                                const float *tsum)
+    {
+        return q4_unit_dot<LIMBS>(u, h, base, k, planes, tscale, tsum);
+    }
+};
+template <> struct KFmt<5> {
+    using Unit = Q5Unit;
+    static constexpr int kBytes = kQ5Bytes;
+    static __device__ __forceinline__ Unit load(const uint8_t *sb, int h) { return q5_load(sb, h); }
+    template <int LIMBS>
+    static __device__ __forceinline__ float dot(const Unit &u, int h, int base, int k,
+                                                const uint8_t *planes, const float *tscale,
+                                                const float *tsum)
+    {
+        return q5_unit_dot<LIMBS>(u, h, base, k, planes, tscale, tsum);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Q6_K unit = one half superblock h: ql bytes 64h..64h+63, qh bytes

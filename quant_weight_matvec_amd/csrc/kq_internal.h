@@ -40,6 +40,16 @@ struct TailArgs {
 hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x,
                               const uint8_t *xs, float *mid, uint8_t *mid_s, int mid_group,
                               int n_rows, int k, const TailArgs *tail, hipStream_t stream);
+// Up to 4 matrices of one type and k sharing x (or its staged form xs) in one
+// launch: matrix i has rows[i] rows and writes y[i] (counts validated).
+hipError_t launch_matvec_group(int qtype, int count, const uint8_t *const *W, float *const *y,
+                               const int *rows, const float *x, const uint8_t *xs, int k,
+                               hipStream_t stream);
+hipError_t launch_matvec_q5k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, const float *silu_gate, hipStream_t stream);
+// Embedding rows: qtype 1 (Q4_K) or 3 (Q5_K); one workgroup per token.
+hipError_t launch_embedding(int qtype, const uint8_t *E, const int32_t *tokens, int n_tokens,
+                            float *out, int vocab, int hidden, hipStream_t stream);
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
                              int n_rows, int k, hipStream_t stream);
 // staged form of x with scale groups of `group` (16 or 32)
@@ -55,9 +65,11 @@ bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m);
 hipError_t launch_small_m_noalloc(int qtype, const uint8_t *W, const float *X, int64_t ldx,
                                   float *Y, int64_t ldy, int n_rows, int k, int m,
                                   hipStream_t stream);
+// gate (nullable): Y = silu(gate) * (W X), gate [m][ldg]; it may be Y itself.
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
-                               int64_t workspace_bytes, hipStream_t stream);
+                               int64_t workspace_bytes, hipStream_t stream,
+                               const float *gate = nullptr, int64_t ldg = 0);
 // xs_out (nullable): also write next_in staged, groups of xs_group, per row
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,

@@ -85,18 +85,22 @@ struct TailIn {
 // first DEPTH loads are issued before the activation staging (so HBM is busy
 // while x is converted), and every step issues the load DEPTH units ahead
 // before computing the current one.  DEPTH = 0 loads and computes in turn.
-template <int LANES, int LIMBS, int DEPTH, int WMAX, bool SILU>
-__global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__restrict__ W,
-                                                               const float *__restrict__ x,
-                                                               const uint8_t *__restrict__ xs,
-                                                               float *__restrict__ y,
-                                                               const float *__restrict__ gate,
-                                                               int n_rows, int k)
+// The rows are those of up to kMaxSegs matrices sharing x (MatSegs); a plain
+// matvec is one segment.  n_rows counts the rows of all segments.  FMT is the
+// superblock format: 4 = Q4_K, 5 = Q5_K (the same scales, mins and 32-input
+// sub-blocks, one more bit per quant).
+template <int FMT, int LANES, int LIMBS, int DEPTH, int WMAX, bool SILU>
+__global__ __launch_bounds__(64 * WMAX) void q45k_matvec_kernel(const MatSegs segs,
+                                                                const float *__restrict__ x,
+                                                                const uint8_t *__restrict__ xs,
+                                                                const float *__restrict__ gate,
+                                                                int n_rows, int k)
 {
+    using F = KFmt<FMT>;
     extern __shared__ __align__(16) uint8_t smem[];
     const int nsb = k >> 8;
     const int units = 2 * nsb;
-    const int64_t row_bytes = (int64_t)nsb * kQ4Bytes;
+    const int64_t row_bytes = (int64_t)nsb * F::kBytes;
     const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
     const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
     const int lane = threadIdx.x & 63;
@@ -112,17 +116,17 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
-    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    const uint8_t *rowp = seg_row(segs, rv ? r : r_lo, row_bytes);
     // Loads are unconditional: a lane past the row's last unit re-reads that
     // unit, a lane without a row reads the workgroup's first row (its result
     // is dropped), so every wave issues the same loads in the same order and
     // waits only for the unit it is about to use.
     auto load = [&](int st) {
         const int u = min(sub + LANES * st, units - 1);
-        return q4_load(rowp + (int64_t)(u >> 1) * kQ4Bytes, h);
+        return F::load(rowp + (int64_t)(u >> 1) * F::kBytes, h);
     };
     constexpr int R = DEPTH + 1;
-    Q4Unit ring[R];
+    typename F::Unit ring[R];
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {  // slot by slot, as the loop issues them
         ring[j] = load(j);
@@ -147,8 +151,8 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
             __builtin_amdgcn_sched_barrier(0);
             const int u = sub + LANES * st;
             const int uc = min(u, units - 1);  // the unit that was loaded
-            const float d = q4_unit_dot<LIMBS>(ring[j], h, 256 * (uc >> 1) + 128 * h, k, planes,
-                                               tscale, tsum);
+            const float d = F::template dot<LIMBS>(ring[j], h, 256 * (uc >> 1) + 128 * h, k,
+                                                   planes, tscale, tsum);
             acc += (rv && u < units) ? d : 0.0f;
         };
         // whole passes of R steps: constant slot indices and no branch between
@@ -168,12 +172,12 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_matvec_kernel(const uint8_t *__
                 const float g = gate[r];
                 acc = (g / (1.0f + __expf(-g))) * acc;
             }
-            y[r] = acc;
+            *seg_out(segs, r) = acc;
         }
         t0 += nwaves * RPT;
         r = t0 + lane / LANES;
         rv = r < r_hi;
-        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        rowp = seg_row(segs, rv ? r : r_lo, row_bytes);
         if (t0 < r_hi) {
 #pragma unroll
             for (int j = 0; j < DEPTH; ++j) {
@@ -400,11 +404,10 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
 }
 
 template <int LANES, int LIMBS, int DEPTH, int WMAX>
-__global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__restrict__ W,
+__global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const MatSegs segs,
                                                                const float *__restrict__ x,
                                                                const uint8_t *__restrict__ xs,
-                                                               float *__restrict__ y, int n_rows,
-                                                               int k)
+                                                               int n_rows, int k)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int nsb = k >> 8;
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
-    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    const uint8_t *rowp = seg_row(segs, rv ? r : r_lo, row_bytes);
     // unconditional loads, as in q4k_matvec_kernel
     auto load = [&](int st) {
         const int u = min(sub + LANES * st, units - 1);
@@ -468,11 +471,11 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const uint8_t *__
         for (int j = 0; j + 1 < R; ++j)
             if (s0 + j < steps) step(j, s0 + j, false);
         acc = lane_group_sum<LANES>(acc);
-        if (sub == 0 && rv) y[r] = acc;
+        if (sub == 0 && rv) *seg_out(segs, r) = acc;
         t0 += nwaves * RPT;
         r = t0 + lane / LANES;
         rv = r < r_hi;
-        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        rowp = seg_row(segs, rv ? r : r_lo, row_bytes);
         if (t0 < r_hi) {
 #pragma unroll
             for (int j = 0; j < DEPTH; ++j) {
@@ -622,6 +625,65 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Embedding lookup (Ch 10 "The forward pass at a glance", section 10.3, box 1:
+// one row of the token table turned into the residual stream): out[t] is row
+// tokens[t] of E dequantized.  One workgroup per token, one thread per
+// 32-weight sub-block: its scale and min from the superblock header, its 32
+// quants (Q5_K: and their fifth bits), 32 floats out.  Each weight is
+// (d * sc) * q - dmin * m, products exact in f32, so the one rounding is that
+// of the subtraction: the f32 value nearest the exact weight.  A token outside
+// [0, vocab) gives a row of NaN and reads nothing.
+template <int FMT>
+__global__ __launch_bounds__(256) void embedding_kernel(const uint8_t *__restrict__ E,
+                                                        const int32_t *__restrict__ tokens,
+                                                        float *__restrict__ out, int vocab,
+                                                        int hidden)
+{
+    const int t = blockIdx.x;
+    const int tok = tokens[t];
+    const int nsb = hidden >> 8;
+    f32x4 *o = reinterpret_cast<f32x4 *>(out + (int64_t)t * hidden);
+    if (tok < 0 || tok >= vocab) {  // uniform across the workgroup
+        const float nan = __builtin_nanf("");
+        for (int i = threadIdx.x; i < (hidden >> 2); i += blockDim.x) o[i] = (f32x4){nan, nan, nan, nan};
+        return;
+    }
+    constexpr int B = KFmt<FMT>::kBytes;
+    const uint8_t *row = E + (int64_t)tok * nsb * B;
+    for (int i = threadIdx.x; i < nsb * 8; i += blockDim.x) {
+        const int b = i >> 3, s = i & 7, c = s >> 1, hn = s & 1;
+        const uint8_t *sb = row + (int64_t)b * B;
+        const u32x4 hdr = *reinterpret_cast<const u32x4 *>(sb);
+        // the 12 bytes of packed 6-bit fields are hdr.y, hdr.z, hdr.w
+        auto byte = [&](int j) -> uint32_t {
+            const uint32_t w = j < 4 ? hdr.y : (j < 8 ? hdr.z : hdr.w);
+            return (w >> (8 * (j & 3))) & 0xFFu;
+        };
+        const uint32_t sc = s < 4 ? (byte(s) & 63u) : ((byte(s + 4) & 15u) | ((byte(s - 4) >> 6) << 4));
+        const uint32_t mn = s < 4 ? (byte(s + 4) & 63u) : ((byte(s + 4) >> 4) | ((byte(s) >> 6) << 4));
+        const float dsc = half_lo(hdr.x) * (float)sc, dm = half_hi(hdr.x) * (float)mn;
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(sb + (FMT == 5 ? 48 : 16) + 32 * c);
+        const u32x4 q[2] = {qp[0], qp[1]};
+        u32x4 qh[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+        if constexpr (FMT == 5) {
+            qh[0] = *reinterpret_cast<const u32x4 *>(sb + 16);
+            qh[1] = *reinterpret_cast<const u32x4 *>(sb + 32);
+        }
+        f32x4 *dst = o + 64 * b + 8 * s;  // inputs 256 b + 32 s ..
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const uint32_t qw = q[w >> 2][w & 3];
+            uint32_t v = hn ? (qw >> 4) & 0x0F0F0F0Fu : qw & 0x0F0F0F0Fu;
+            if constexpr (FMT == 5) v |= ((qh[w >> 2][w & 3] >> s) & 0x01010101u) << 4;
+            f32x4 r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = dsc * (float)((v >> (8 * e)) & 0xFFu) - dm;
+            dst[w] = r;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Read-stream probe: every byte of a buffer read once with 16-byte loads,
 // folded with xor so the loads stay live.  It measures the HBM read ceiling
 // that the matvecs are compared with; it is not on the decode path.
@@ -670,7 +732,7 @@ struct DevInfo {
 };
 
 DevInfo g_dev[64];
-kqi::MatvecShape g_override[3] = {};
+kqi::MatvecShape g_override[4] = {};
 
 int device_cus()
 {
@@ -692,12 +754,22 @@ int device_cus()
 // cost registers and measured slower.
 kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, bool staged)
 {
-    // Measured on MI355X (sweeps of lanes 8..32, waves 4..16, one or two
-    // workgroups per CU, look-ahead 0..2 units):
+    // Measured on MI355X (sweeps of lanes 8..64, waves 4..16, a quarter to two
+    // workgroups per CU, look-ahead 0..2 units, each shape timed as a graph of
+    // launches over >= 1 GiB of rotated copies):
     //   Q4_K 19968 x 6656: 8 lanes, 8 waves, 2 workgroups per CU, 1 unit ahead
     //   Q4_K 6656 x 19968: 32 lanes, 16 waves, 1 workgroup per CU (staged x:
     //                      8 waves, 2 workgroups per CU), 1 unit ahead
     //   Q6_K 6656 x 19968: 8 lanes, 8 waves, 1 workgroup per CU, 1 unit ahead
+    //   Q6_K, k <= 8192 and many rows per CU (202048 x 6656): no look-ahead
+    //     (201 us against 219: the one-slot ring leaves registers for waves);
+    //     at 19968 x 6656 also 32 lanes and two workgroups per CU
+    //   few rows per CU (the attention projections: 256, 4096 and 8704 rows
+    //     over k = 6656, 6656 rows over k = 4096): the time is the latency of
+    //     a few units per lane, so a row takes 16..64 lanes (one unit or two
+    //     each) and the rows spread over all CUs: K or V alone 7.8 -> 4.5 us
+    //     (Q4_K), 9.3 -> 5.1 us (Q6_K); Q 8.4 -> 6.5 us; the four projections
+    //     in one group 11.1 -> 9.8 us; o_proj 7.0 -> 6.3 us.
     // 8 lanes per row keep a row's loads contiguous and the lane reduction to
     // DPP moves; a long Q4_K row (k > 8192) is better split 32 ways (9-13 %
     // faster at k = 19968).  Waves without rows still share the conversion of
@@ -705,8 +777,24 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
     // (Q6_K's ring needs more than 128 VGPRs, which caps it at 8 waves); a
     // staged x is only copied, and then 8 waves are best.
     const bool q6 = qtype == 2;
-    const int64_t tiles = (n_rows + 7) / 8;
     const int64_t k = 128 * (int64_t)units;
+    const int64_t rpc = n_rows / (cus > 0 ? cus : 1);  // rows per CU
+    auto fit = [&](int lanes, int waves, int64_t per_cu, int depth) {
+        // grid: per_cu workgroups per CU, but no more than there are wave-sized
+        // row groups to hand out
+        const int64_t rows_per_wave = 64 / lanes;
+        const int64_t row_groups = (n_rows + rows_per_wave - 1) / rows_per_wave;
+        int64_t g = per_cu * cus;
+        if (g > row_groups) g = row_groups;
+        return kqi::MatvecShape{lanes, waves, (int)(g > 0 ? g : 1), depth};
+    };
+    if (k <= 8192 && rpc < 48) {
+        if (rpc < 8) return fit(64, 16, 1, q6 ? 1 : 2);
+        if (units >= 48) return q6 ? fit(64, 8, 2, 1) : (rpc < 24 ? fit(32, 8, 1, 2) : fit(64, 16, 1, 2));
+        return q6 ? fit(8, 4, 1, 2) : fit(16, 8, 1, 2);
+    }
+    if (q6 && k <= 8192 && rpc < 100) return fit(32, 8, 2, 1);  // 28.2 -> 25.7 us at 19968 x 6656
+    const int64_t tiles = (n_rows + 7) / 8;
     const bool long_q4 = !q6 && k > 8192;
     // two workgroups per CU: short rows with many of them, or long rows on a
     // staged x where both stagings fit in the CU's LDS (32 lanes per row: a
@@ -718,7 +806,8 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
     const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
     const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
     const int waves = (q6 || two_per_cu || staged) ? 8 : 16;
-    return kqi::MatvecShape{long_q4 ? 32 : 8, waves, grid, 2};
+    const int depth = (q6 && k <= 8192 && rpc >= 100) ? 1 : 2;
+    return kqi::MatvecShape{long_q4 ? 32 : 8, waves, grid, depth};
 }
 
 // Raise a kernel's dynamic-LDS limit once to the largest staging size any
@@ -752,37 +841,35 @@ kqi::MatvecShape resolve_shape(int qtype, int64_t n_rows, int k, bool staged = f
     return s;
 }
 
-template <int LANES, int DEPTH, int WMAX>
-hipError_t launch_q4k_cfg(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
-                          int n_rows, int k, const float *gate, kqi::MatvecShape s,
-                          hipStream_t stream)
+template <int FMT, int LANES, int DEPTH, int WMAX>
+hipError_t launch_q45k_cfg(const MatSegs &segs, const float *x, const uint8_t *xs, int n_rows,
+                           int k, const float *gate, kqi::MatvecShape s, hipStream_t stream)
 {
     const size_t lds = staging_bytes<32>(k);
     hipError_t e;
     if (gate) {
-        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, true>;
+        constexpr auto kern = q45k_matvec_kernel<FMT, LANES, KQ_LIMBS, DEPTH, WMAX, true>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y,
+        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, segs, x, xs,
                            gate, n_rows, k);
     } else {
-        constexpr auto kern = q4k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX, false>;
+        constexpr auto kern = q45k_matvec_kernel<FMT, LANES, KQ_LIMBS, DEPTH, WMAX, false>;
         if ((e = allow_lds<kern>(lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y,
+        hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, segs, x, xs,
                            gate, n_rows, k);
     }
     return hipGetLastError();
 }
 
 template <int LANES, int DEPTH, int WMAX>
-hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
-                          int n_rows, int k, const float *, kqi::MatvecShape s,
-                          hipStream_t stream)
+hipError_t launch_q6k_cfg(const MatSegs &segs, const float *x, const uint8_t *xs, int n_rows,
+                          int k, const float *, kqi::MatvecShape s, hipStream_t stream)
 {
     const size_t lds = staging_bytes<16>(k);
     constexpr auto kern = q6k_matvec_kernel<LANES, KQ_LIMBS, DEPTH, WMAX>;
     hipError_t e = allow_lds<kern>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, W, x, xs, y, n_rows,
+    hipLaunchKernelGGL(kern, dim3(s.grid), dim3(64 * s.waves), lds, stream, segs, x, xs, n_rows,
                        k);
     return hipGetLastError();
 }
@@ -791,15 +878,15 @@ hipError_t launch_q6k_cfg(const uint8_t *W, const float *x, const uint8_t *xs, f
 // in flight per lane 1..3 (look-ahead 0..2), and a workgroup-size class (up to 8 waves gets the 256-VGPR budget
 // of two waves per SIMD; up to 16 waves the 128-VGPR budget).
 template <template <int, int, int> class F>
-hipError_t dispatch_shape(kqi::MatvecShape s, const uint8_t *W, const float *x,
-                          const uint8_t *xs, float *y, int n_rows, int k, const float *gate,
+hipError_t dispatch_shape(kqi::MatvecShape s, const MatSegs &segs, const float *x,
+                          const uint8_t *xs, int n_rows, int k, const float *gate,
                           hipStream_t stream)
 {
     const bool small = s.waves <= 8;
 #define KQ_CASE(L, D)                                                                        \
     if (s.lanes == L && s.depth == D)                                                        \
-        return small ? F<L, D - 1, 8>::go(W, x, xs, y, n_rows, k, gate, s, stream)           \
-                     : F<L, D - 1, 16>::go(W, x, xs, y, n_rows, k, gate, s, stream);
+        return small ? F<L, D - 1, 8>::go(segs, x, xs, n_rows, k, gate, s, stream)           \
+                     : F<L, D - 1, 16>::go(segs, x, xs, n_rows, k, gate, s, stream);
 #define KQ_CASES(L) KQ_CASE(L, 1) KQ_CASE(L, 2) KQ_CASE(L, 3)
     KQ_CASES(4) KQ_CASES(8) KQ_CASES(16) KQ_CASES(32) KQ_CASES(64)
 #undef KQ_CASES
@@ -829,21 +916,42 @@ hipError_t launch_gate_up_cfg(const uint8_t *Wg, const uint8_t *Wu, const float 
 
 template <int L, int D, int WM>
 struct Q4Launch {
-    static hipError_t go(const uint8_t *W, const float *x, const uint8_t *xs, float *y, int n,
-                         int k, const float *g, kqi::MatvecShape s, hipStream_t st)
+    static hipError_t go(const MatSegs &segs, const float *x, const uint8_t *xs, int n, int k,
+                         const float *g, kqi::MatvecShape s, hipStream_t st)
     {
-        return launch_q4k_cfg<L, D, WM>(W, x, xs, y, n, k, g, s, st);
+        return launch_q45k_cfg<4, L, D, WM>(segs, x, xs, n, k, g, s, st);
+    }
+};
+
+template <int L, int D, int WM>
+struct Q5Launch {
+    static hipError_t go(const MatSegs &segs, const float *x, const uint8_t *xs, int n, int k,
+                         const float *g, kqi::MatvecShape s, hipStream_t st)
+    {
+        return launch_q45k_cfg<5, L, D, WM>(segs, x, xs, n, k, g, s, st);
     }
 };
 
 template <int L, int D, int WM>
 struct Q6Launch {
-    static hipError_t go(const uint8_t *W, const float *x, const uint8_t *xs, float *y, int n,
-                         int k, const float *g, kqi::MatvecShape s, hipStream_t st)
+    static hipError_t go(const MatSegs &segs, const float *x, const uint8_t *xs, int n, int k,
+                         const float *g, kqi::MatvecShape s, hipStream_t st)
     {
-        return launch_q6k_cfg<L, D, WM>(W, x, xs, y, n, k, g, s, st);
+        return launch_q6k_cfg<L, D, WM>(segs, x, xs, n, k, g, s, st);
     }
 };
+
+// One matrix as a one-segment table.
+MatSegs one_seg(const uint8_t *W, float *y, int n_rows)
+{
+    MatSegs m;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        m.W[i] = W;
+        m.y[i] = y;
+        m.end[i] = i == 0 ? n_rows : INT32_MAX;
+    }
+    return m;
+}
 
 }  // namespace
 
@@ -851,12 +959,12 @@ namespace kqi {
 
 void set_shape_override(int qtype, MatvecShape s)
 {
-    if (qtype == 1 || qtype == 2) g_override[qtype] = s;
+    if (qtype >= 1 && qtype <= 3) g_override[qtype] = s;
 }
 
 MatvecShape get_shape_override(int qtype)
 {
-    return (qtype == 1 || qtype == 2) ? g_override[qtype] : MatvecShape{0, 0, 0, 0};
+    return (qtype >= 1 && qtype <= 3) ? g_override[qtype] : MatvecShape{0, 0, 0, 0};
 }
 
 MatvecShape auto_shape(int qtype, int64_t n_rows, int64_t k, int m)
@@ -872,16 +980,41 @@ void matvec_plan(int qtype, int64_t n_rows, int k, bool staged, int cus, int64_t
     out[1] = s.waves;
     out[2] = s.grid;
     out[3] = s.depth;
-    out[4] = (int64_t)(qtype == 1 ? staging_bytes<32>(k) : staging_bytes<16>(k));
+    out[4] = (int64_t)(qtype == 2 ? staging_bytes<16>(k) : staging_bytes<32>(k));
     out[5] = s.grid > cus ? 2 : 1;  // workgroups per CU the grid is sized for
 }
 
 hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
                              int n_rows, int k, const float *silu_gate, hipStream_t stream)
 {
-    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k, xs != nullptr), W, x, xs, y,
-                                    n_rows, k,
-                                    silu_gate, stream);
+    return dispatch_shape<Q4Launch>(resolve_shape(1, n_rows, k, xs != nullptr),
+                                    one_seg(W, y, n_rows), x, xs, n_rows, k, silu_gate, stream);
+}
+
+hipError_t launch_matvec_group(int qtype, int count, const uint8_t *const *W, float *const *y,
+                               const int *rows, const float *x, const uint8_t *xs, int k,
+                               hipStream_t stream)
+{
+    MatSegs m;
+    int total = 0;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        const int j = i < count ? i : count - 1;
+        m.W[i] = W[j];
+        m.y[i] = y[j];
+        if (i < count) total += rows[i];
+        m.end[i] = i < count ? total : INT32_MAX;
+    }
+    const MatvecShape s = resolve_shape(qtype, total, k, xs != nullptr);
+    if (qtype == 1) return dispatch_shape<Q4Launch>(s, m, x, xs, total, k, nullptr, stream);
+    if (qtype == 3) return dispatch_shape<Q5Launch>(s, m, x, xs, total, k, nullptr, stream);
+    return dispatch_shape<Q6Launch>(s, m, x, xs, total, k, nullptr, stream);
+}
+
+hipError_t launch_matvec_q5k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
+                             int n_rows, int k, const float *silu_gate, hipStream_t stream)
+{
+    return dispatch_shape<Q5Launch>(resolve_shape(3, n_rows, k, xs != nullptr),
+                                    one_seg(W, y, n_rows), x, xs, n_rows, k, silu_gate, stream);
 }
 
 hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float *x,
@@ -938,9 +1071,8 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
 hipError_t launch_matvec_q6k(const uint8_t *W, const float *x, const uint8_t *xs, float *y,
                              int n_rows, int k, hipStream_t stream)
 {
-    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k, xs != nullptr), W, x, xs, y, n_rows,
-                                    k, nullptr,
-                                    stream);
+    return dispatch_shape<Q6Launch>(resolve_shape(2, n_rows, k, xs != nullptr),
+                                    one_seg(W, y, n_rows), x, xs, n_rows, k, nullptr, stream);
 }
 
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
@@ -963,6 +1095,18 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
     if (threads > 1024) threads = 1024;
     hipLaunchKernelGGL(tail_kernel, dim3(rows), dim3(threads), 0, stream, residual, projected,
                        next_in, g_post, g_next, n, eps_post, eps_next, xs_out, xs_group);
+    return hipGetLastError();
+}
+
+hipError_t launch_embedding(int qtype, const uint8_t *E, const int32_t *tokens, int n_tokens,
+                            float *out, int vocab, int hidden, hipStream_t stream)
+{
+    if (qtype == 3)
+        hipLaunchKernelGGL(embedding_kernel<5>, dim3(n_tokens), dim3(256), 0, stream, E, tokens,
+                           out, vocab, hidden);
+    else
+        hipLaunchKernelGGL(embedding_kernel<4>, dim3(n_tokens), dim3(256), 0, stream, E, tokens,
+                           out, vocab, hidden);
     return hipGetLastError();
 }
 
@@ -1006,7 +1150,8 @@ hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int 
 
 const char *variant_names()
 {
-    return "q4k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged] "
+    return "q4k/q5k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged,group<=4] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged,group<=4] "
+           "embedding[q4k,q5k] "
            "gate_up[q4k, mid staged out: 0/16/32] "
            "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; m<=8: 16 waves x 1 16-row tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }

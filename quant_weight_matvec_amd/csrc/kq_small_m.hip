@@ -102,7 +102,22 @@ struct SmArgs {
     int ws_bytes;
     int flag_off;       // LDS byte offset of the last-arrival flag
     int xs_off;         // LDS byte offset of the staged activations
+    const float *gate;  // nullable: Y = silu(gate) * (W X), gate [M][ldg] (may be Y itself)
+    int64_t ldg;
 };
+
+// The value stored for output (m, row): the product, or with a gate the
+// SiLU-gated product silu(g) * v, silu(g) = g / (1 + e^-g).  The gate element
+// is read by the thread that then writes the same position of Y, so Y may be
+// the gate's own buffer.
+__device__ __forceinline__ float sm_out(const SmArgs &a, int m, int row, float v)
+{
+    if (a.gate) {
+        const float g = a.gate[(int64_t)m * a.ldg + row];
+        v = (g / (1.0f + __expf(-g))) * v;
+    }
+    return v;
+}
 
 __device__ __forceinline__ int first_tile(int g, int T, int G)
 {
@@ -591,7 +606,8 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
             if (row < a.n_rows) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (m0 + i < M) a.Y[(int64_t)(m0 + i) * a.ldy + row] = yacc[h][i];
+                    if (m0 + i < M)
+                        a.Y[(int64_t)(m0 + i) * a.ldy + row] = sm_out(a, m0 + i, row, yacc[h][i]);
             }
         }
         return;
@@ -632,7 +648,7 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = row0 + 4 * q + i;
-                if (row < a.n_rows) a.Y[(int64_t)m * a.ldy + row] = s[i];
+                if (row < a.n_rows) a.Y[(int64_t)m * a.ldy + row] = sm_out(a, m, row, s[i]);
             }
         }
         if (threadIdx.x == 0) st_agent(cnt + rg, 0u);
@@ -882,9 +898,12 @@ hipError_t allow_lds()
 // at its start) and ws_bytes the bytes the kernel may touch there.
 hipError_t launch_plan(const SmPlan &p, int qtype, const uint8_t *W, const float *X, int64_t ldx,
                        float *Y, int64_t ldy, int n_rows, int k, int m, uint8_t *ws, int part_off,
-                       int64_t ws_bytes, hipStream_t stream)
+                       int64_t ws_bytes, hipStream_t stream, const float *gate = nullptr,
+                       int64_t ldg = 0)
 {
     SmArgs a;
+    a.gate = gate;
+    a.ldg = ldg;
     a.W = W;
     a.X = X;
     a.Y = Y;
@@ -969,12 +988,14 @@ void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
 
 hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
-                               int64_t workspace_bytes, hipStream_t stream)
+                               int64_t workspace_bytes, hipStream_t stream, const float *gate,
+                               int64_t ldg)
 {
     const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
     if ((int64_t)p.ws > workspace_bytes) return hipErrorInvalidValue;
     return launch_plan(p, qtype, W, X, ldx, Y, ldy, n_rows, k, m,
-                       reinterpret_cast<uint8_t *>(workspace), p.part_off, (int64_t)p.ws, stream);
+                       reinterpret_cast<uint8_t *>(workspace), p.part_off, (int64_t)p.ws, stream,
+                       gate, ldg);
 }
 
 bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m)

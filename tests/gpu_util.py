@@ -28,6 +28,8 @@ def gpu_matvec(qt: str, Wd: torch.Tensor, xd: torch.Tensor, n: int, k: int,
     y = nan_like(n)
     if qt == "q4k":
         kq.kq_matvec_q4k(Wd, xd, y, n, k, gate)
+    elif qt == "q5k":
+        kq.kq_matvec_q5k(Wd, xd, y, n, k, gate)
     else:
         assert gate is None
         kq.kq_matvec_q6k(Wd, xd, y, n, k)

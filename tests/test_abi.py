@@ -42,7 +42,7 @@ def test_status_strings_and_build_info():
         assert s.startswith("KQ_")
     assert kq.kq_status_string(-99) == "KQ_ERR_UNKNOWN"
     info = kq.kq_build_info()
-    assert "gfx950" in info and "q4k_matvec" in info
+    assert "gfx950" in info and "q5k_matvec" in info and "q6k_matvec" in info
 
 
 W, X, Y, G = 0x100000, 0x200000, 0x300000, 0x400000  # fake, aligned, never dereferenced
@@ -95,11 +95,48 @@ def test_gate_up_validation():
     assert f(W, U, X, M, 0, 1024, None) == B.KQ_OK
 
 
+def test_group_validation():
+    f = kq.lib().kq_matvec_group
+    arr = lambda t, v: (t * len(v))(*v)
+    P, I64 = C.c_void_p, C.c_int64
+    W0, W1, Y0, Y1 = 1 << 40, 2 << 40, 3 << 40, 4 << 40
+    X0 = 5 << 40
+
+    def call(qt=1, count=2, W=(W0, W1), y=(Y0, Y1), n=(256, 4096), x=X0, k=6656):
+        return f(qt, count, arr(P, W), arr(P, y), arr(I64, n), x, k, None)
+
+    assert call() == B.KQ_ERR_DEVICE or call() == B.KQ_OK or call() < 0  # reaches the device check
+    assert call(qt=4) == B.KQ_ERR_SHAPE                                # qtype 3 is Q5_K
+    assert call(count=0) == B.KQ_ERR_SHAPE
+    assert call(count=5, W=(W0,) * 5, y=(Y0,) * 5, n=(1,) * 5) == B.KQ_ERR_SHAPE
+    assert call(W=(W0, None)) == B.KQ_ERR_NULL
+    assert call(y=(None, Y1)) == B.KQ_ERR_NULL
+    assert call(x=None) == B.KQ_ERR_NULL
+    assert call(n=(-1, 4)) == B.KQ_ERR_SHAPE
+    assert call(n=(2**31 - 1, 4)) == B.KQ_ERR_SHAPE                 # total past 2^31
+    assert call(k=1000) == B.KQ_ERR_SHAPE
+    assert call(k=B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
+    assert call(W=(W0 + 8, W1)) == B.KQ_ERR_ALIGN                   # Q4_K weights 16-byte aligned
+    assert call(qt=2, W=(W0 + 4, W1)) == B.KQ_OK or call(qt=2, W=(W0 + 4, W1)) == B.KQ_ERR_DEVICE
+    assert call(qt=2, W=(W0 + 2, W1)) == B.KQ_ERR_ALIGN             # Q6_K weights 4-byte aligned
+    assert call(y=(Y0 + 2, Y1)) == B.KQ_ERR_ALIGN
+    assert call(x=X0 + 4) == B.KQ_ERR_ALIGN
+    assert call(y=(Y0, Y0 + 512)) == B.KQ_ERR_ALIAS                 # outputs overlap
+    assert call(y=(W1 + 64, Y1)) == B.KQ_ERR_ALIAS                  # output inside a matrix
+    assert call(y=(X0 + 16, Y1)) == B.KQ_ERR_ALIAS                  # output inside x
+    assert call(n=(0, 0)) == B.KQ_OK                                 # nothing to do
+    assert call(W=(None, None), y=(None, None), n=(0, 0)) == B.KQ_OK  # empty members: no pointers
+    g = kq.lib().kq_matvec_group_staged
+    assert g(1, 1, arr(P, (W0,)), arr(P, (Y0,)), arr(I64, (8,)), X0 + 8, 1024, None) == B.KQ_ERR_ALIGN
+    assert g(1, 1, arr(P, (W0,)), arr(P, (Y0,)), arr(I64, (8,)), Y0 - 1024, 1024, None) == B.KQ_ERR_ALIAS
+
+
 def test_small_m_validation():
     f = kq.lib().kq_matmul_small_m
     WS = 0x600000
     a = lambda *v, ws=WS, wsb=1 << 20: f(*v, ws, wsb, None)
-    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(4, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_UNSUPPORTED  # Q5_K: no matrix-core path
     assert a(1, W, X, 1024, Y, 8, 8, 1024, 0) == B.KQ_ERR_SHAPE      # m = 0
     assert a(1, W, X, 1024, Y, 8, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
     assert a(1, W, X, 1000, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldx < k
@@ -113,7 +150,8 @@ def test_small_m_validation():
     assert a(1, W, X, 1024, Y, 8, 0, 1024, 4) == B.KQ_OK             # empty
     q = kq.lib().kq_matmul_small_m_workspace_bytes
     assert q(1, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
-    assert q(3, 8, 1024, 4) == B.KQ_ERR_SHAPE
+    assert q(4, 8, 1024, 4) == B.KQ_ERR_SHAPE
+    assert q(3, 8, 1024, 4) == B.KQ_ERR_UNSUPPORTED
     assert q(1, 8, 300, 4) == B.KQ_ERR_SHAPE
     assert q(1, 0, 1024, 4) == 0 and q(2, 8, 1024, 1) == 0        # empty, or m = 1 (matvec)
 
@@ -124,7 +162,8 @@ def test_small_m_noalloc_validation():
     on the host (KQ_ERR_UNSUPPORTED) before any device call."""
     f = kq.lib().kq_matmul_small_m_noalloc
     a = lambda *v: f(*v, None)
-    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(4, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # qtype
+    assert a(3, W, X, 1024, Y, 8, 8, 1024, 4) == B.KQ_ERR_UNSUPPORTED  # Q5_K: no matrix-core path
     assert a(1, W, X, 1024, Y, 8, 8, 1024, 0) == B.KQ_ERR_SHAPE      # m = 0
     assert a(1, W, X, 1024, Y, 8, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
     assert a(1, W, X, 1000, Y, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE      # ldx < k
@@ -178,18 +217,20 @@ def test_staged_validation():
     # inputs), then a scale and a sum per group (32 for Q4_K, 16 for Q6_K)
     assert kq.kq_staged_bytes(B.KQ_QTYPE_Q4K, 6656) == 3 * (6656 + 832) + 8 * 6656 // 32
     assert kq.kq_staged_bytes(B.KQ_QTYPE_Q6K, 19968) == 3 * (19968 + 2496) + 8 * 19968 // 16
-    assert L.kq_staged_bytes(3, 1024) == B.KQ_ERR_SHAPE
+    assert L.kq_staged_bytes(4, 1024) == B.KQ_ERR_SHAPE
+    assert L.kq_staged_bytes(3, 1024) == L.kq_staged_bytes(1, 1024)  # Q5_K: groups of 32
     assert L.kq_staged_bytes(1, 1000) == B.KQ_ERR_SHAPE
     assert L.kq_staged_bytes(1, B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
     XS = 0x600000
     st = L.kq_stage_activation
-    assert st(3, X, XS, 1024, None) == B.KQ_ERR_SHAPE
+    assert st(4, X, XS, 1024, None) == B.KQ_ERR_SHAPE
     assert st(1, None, XS, 1024, None) == B.KQ_ERR_NULL
     assert st(1, X, XS, 1000, None) == B.KQ_ERR_SHAPE
     assert st(1, X, XS + 8, 1024, None) == B.KQ_ERR_ALIGN
     assert st(1, X, X + 1024, 1024, None) == B.KQ_ERR_ALIAS
     mv = L.kq_matvec_staged
-    assert mv(3, W, XS, Y, 8, 1024, None, None) == B.KQ_ERR_SHAPE
+    assert mv(4, W, XS, Y, 8, 1024, None, None) == B.KQ_ERR_SHAPE
+    assert mv(3, W + 8, XS, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN   # Q5_K weights 16-byte aligned
     assert mv(1, W, None, Y, 8, 1024, None, None) == B.KQ_ERR_NULL
     assert mv(2, W, XS, Y, 8, 1024, G, None) == B.KQ_ERR_UNSUPPORTED    # no SiLU epilogue for Q6_K
     assert mv(1, W + 4, XS, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN
@@ -200,7 +241,7 @@ def test_staged_validation():
     gu = L.kq_ffn_gate_up_q4k_staged
     U, M, MS = 0x500000, 0x700000, 0x800000
     assert gu(W, U, None, M, MS, 2, 512, 1024, None) == B.KQ_ERR_NULL
-    assert gu(W, U, XS, M, MS, 3, 512, 1024, None) == B.KQ_ERR_SHAPE     # mid_qtype
+    assert gu(W, U, XS, M, MS, 4, 512, 1024, None) == B.KQ_ERR_SHAPE     # mid_qtype
     assert gu(W, U, XS, M, MS, 2, 500, 1024, None) == B.KQ_ERR_SHAPE     # staged mid: n_rows % 256
     assert gu(W, U, XS, M, MS + 8, 2, 512, 1024, None) == B.KQ_ERR_ALIGN
     assert gu(W, U, XS, M, M + 16, 2, 512, 1024, None) == B.KQ_ERR_ALIAS  # mid_s on mid
@@ -210,7 +251,7 @@ def test_staged_validation():
     R, P, O, GP, GN, OS = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x900000
     e = (C.c_float(1e-8), C.c_float(1e-5), None)
     assert tl(R, P, O, None, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_NULL
-    assert tl(R, P, O, OS, 3, GP, GN, 1, 6656, *e) == B.KQ_ERR_SHAPE
+    assert tl(R, P, O, OS, 4, GP, GN, 1, 6656, *e) == B.KQ_ERR_SHAPE
     assert tl(R, P, O, OS, 1, GP, GN, 1, 6660, *e) == B.KQ_ERR_SHAPE      # n % 256
     assert tl(R, P, O, OS + 4, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_ALIGN
     assert tl(R, P, O, O + 64, 1, GP, GN, 1, 6656, *e) == B.KQ_ERR_ALIAS  # staged on next_in
@@ -228,7 +269,7 @@ def test_tail_gate_up_validation():
     assert a(*ok[:4], None, *ok[5:]) == B.KQ_ERR_NULL                  # residual_out
     assert a(*ok[:11], 0, 1024) == B.KQ_ERR_SHAPE                      # n_rows 0
     assert a(*ok[:11], 500, 1024) == B.KQ_ERR_SHAPE                    # staged mid: n_rows % 256
-    assert a(*ok[:10], 3, 512, 1024) == B.KQ_ERR_SHAPE                 # mid_qtype
+    assert a(*ok[:10], 4, 512, 1024) == B.KQ_ERR_SHAPE                 # mid_qtype
     assert a(*ok[:12], 1000) == B.KQ_ERR_SHAPE
     assert a(*ok[:12], 8448) == B.KQ_ERR_UNSUPPORTED                   # k > KQ_MAX_FUSED_TAIL_K
     assert f(*ok, C.c_float(-1.0), C.c_float(1e-5), None) == B.KQ_ERR_SHAPE
@@ -240,11 +281,48 @@ def test_tail_gate_up_validation():
     assert a(*ok[:9], M + 16, *ok[10:]) == B.KQ_ERR_ALIAS              # mid_s on mid
 
 
+def test_q5k_and_embedding_validation():
+    q5 = kq.lib().kq_matvec_q5k
+    assert q5(None, X, Y, 8, 1024, None, None) == B.KQ_ERR_NULL
+    assert q5(W + 8, X, Y, 8, 1024, None, None) == B.KQ_ERR_ALIGN
+    assert q5(W, X, Y, 8, 1000, None, None) == B.KQ_ERR_SHAPE
+    assert q5(W, X, W + 64, 8, 1024, None, None) == B.KQ_ERR_ALIAS
+    assert q5(W, X, Y, 0, 1024, None, None) == B.KQ_OK
+    e = kq.lib().kq_embedding
+    E0, T0, O0 = 1 << 40, 2 << 40, 3 << 40
+    assert e(2, E0, 100, 1024, T0, 4, O0, None) == B.KQ_ERR_SHAPE        # Q6_K tables: not supported
+    assert e(1, None, 100, 1024, T0, 4, O0, None) == B.KQ_ERR_NULL
+    assert e(1, E0, 0, 1024, T0, 4, O0, None) == B.KQ_ERR_SHAPE
+    assert e(1, E0, 100, 1000, T0, 4, O0, None) == B.KQ_ERR_SHAPE
+    assert e(1, E0, 100, 1024, T0, -1, O0, None) == B.KQ_ERR_SHAPE
+    assert e(1, E0 + 8, 100, 1024, T0, 4, O0, None) == B.KQ_ERR_ALIGN
+    assert e(3, E0, 100, 1024, T0 + 2, 4, O0, None) == B.KQ_ERR_ALIGN
+    assert e(1, E0, 100, 1024, T0, 4, O0 + 4, None) == B.KQ_ERR_ALIGN
+    assert e(1, E0, 100, 1024, T0, 4, E0 + 1024, None) == B.KQ_ERR_ALIAS  # output inside the table
+    assert e(1, E0, 100, 1024, T0, 4, T0, None) == B.KQ_ERR_ALIAS         # output on the tokens
+    assert e(3, E0, 100, 1024, T0, 0, O0, None) == B.KQ_OK
+
+
+def test_verify_gate_up_validation():
+    f = kq.lib().kq_ffn_gate_up_q4k_small_m
+    U, M_, WS = 1 << 40, 2 << 40, 3 << 40
+    a = lambda *v, ws=WS, wsb=1 << 20: f(*v, ws, wsb, None)
+    assert a(None, U, X, 1024, M_, 8, 8, 1024, 4) == B.KQ_ERR_NULL
+    assert a(W, U, X, 1024, M_, 8, 8, 1024, 0) == B.KQ_ERR_SHAPE
+    assert a(W, U, X, 1024, M_, 8, 8, 1024, 17) == B.KQ_ERR_UNSUPPORTED
+    assert a(W, U, X, 1000, M_, 8, 8, 1024, 4) == B.KQ_ERR_SHAPE     # ldx < k
+    assert a(W, U, X, 1024, M_, 7, 8, 1024, 4) == B.KQ_ERR_SHAPE     # ldm < n_rows
+    assert a(W, U + 4, X, 1024, M_, 8, 8, 1024, 4) == B.KQ_ERR_ALIGN
+    assert a(W, U, X, 1024, M_, 8, 8, 1024, 4, ws=WS + 16) == B.KQ_ERR_ALIGN
+    assert a(W, U, X, 1024, U + 128, 8, 8, 1024, 4) == B.KQ_ERR_ALIAS  # Mid inside W_up
+    assert a(W, U, X, 1024, M_, 8, 0, 1024, 4) == B.KQ_OK
+
+
 def test_tune_validation():
     with pytest.raises(kq.KQError):
         kq.kq_tune_set_shape(1, lanes=12)
     with pytest.raises(kq.KQError):
-        kq.kq_tune_set_shape(3, lanes=8)
+        kq.kq_tune_set_shape(4, lanes=8)
     with pytest.raises(kq.KQError):
         kq.kq_tune_set_shape(1, waves=17)
 

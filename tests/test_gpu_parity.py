@@ -45,10 +45,11 @@ def test_q4k_shapes(n, k):
     print("ratio", _full_check("q4k", n, k, 1000 + n))
 
 
+@pytest.mark.parametrize("qt", ["q6k", "q5k"])
 @pytest.mark.parametrize("n,k", [(1, 256), (3, 512), (17, 1280), (255, 2304), (1000, 6656),
                                  (4097, 768), (129, 19968), (33, kq.KQ_MAX_K)])
-def test_q6k_shapes(n, k):
-    print("ratio", _full_check("q6k", n, k, 2000 + n))
+def test_q6k_q5k_shapes(qt, n, k):
+    print("ratio", _full_check(qt, n, k, 2000 + n))
 
 
 @pytest.mark.parametrize("qt,n,k", [("q4k", 19968, 6656), ("q4k", 6656, 19968),
@@ -109,12 +110,14 @@ def test_zero_and_nan_activation():
 def test_every_launch_shape(lanes, waves, grid, depth):
     n = 301
     try:
-        for qt, qti, k in (("q4k", kq.KQ_QTYPE_Q4K, 1792), ("q6k", kq.KQ_QTYPE_Q6K, 2816)):
+        for qt, qti, k in (("q4k", kq.KQ_QTYPE_Q4K, 1792), ("q6k", kq.KQ_QTYPE_Q6K, 2816),
+                           ("q5k", kq.KQ_QTYPE_Q5K, 1280)):
             kq.kq_tune_set_shape(qti, lanes, waves, grid, depth)
             _full_check(qt, n, k, 5000 + lanes)
     finally:
         kq.kq_tune_set_shape(kq.KQ_QTYPE_Q4K)
         kq.kq_tune_set_shape(kq.KQ_QTYPE_Q6K)
+        kq.kq_tune_set_shape(kq.KQ_QTYPE_Q5K)
 
 
 def test_failed_call_leaves_output_untouched():
