@@ -399,9 +399,11 @@ def isolated_matvecs(torch, kq, I, reps=5, launches=52):
     the pass hands between launches)."""
     out = {}
     cases = [("q4k_19968x6656", "q4k", FFN, HIDDEN), ("q4k_6656x19968", "q4k", HIDDEN, FFN),
-             ("q6k_6656x19968", "q6k", HIDDEN, FFN)]
+             ("q6k_6656x19968", "q6k", HIDDEN, FFN), ("q5k_19968x6656", "q5k", FFN, HIDDEN)]
+    QTYPES = {"q4k": kq.KQ_QTYPE_Q4K, "q5k": kq.KQ_QTYPE_Q5K, "q6k": kq.KQ_QTYPE_Q6K}
+    FNS = {"q4k": kq.kq_matvec_q4k, "q5k": kq.kq_matvec_q5k, "q6k": kq.kq_matvec_q6k}
     for name, qt, n, k in cases:
-        qtype = kq.KQ_QTYPE_Q4K if qt == "q4k" else kq.KQ_QTYPE_Q6K
+        qtype = QTYPES[qt]
         W = torch.from_numpy(I.weight_matrix(qt, n, k, stream=777)).cuda()
         ncopy = max(2, int(np.ceil((1 << 30) / W.numel())))
         copies = [W] + [W.clone() for _ in range(ncopy - 1)]
@@ -409,7 +411,7 @@ def isolated_matvecs(torch, kq, I, reps=5, launches=52):
         xs = torch.empty(kq.kq_staged_bytes(qtype, k), dtype=torch.uint8, device="cuda")
         kq.kq_stage_activation(qtype, x, xs, k)
         y = torch.empty(n, device="cuda")
-        fn = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
+        fn = FNS[qt]
         nl = max(launches, ncopy)
         for form, call, xbytes in (
                 ("", lambda c: fn(c, x, y, n, k), 4 * k),
@@ -485,6 +487,65 @@ def decode_shapes(torch, kq, I, reps=5, launches=52, max_launches=1200):
                                    "frac_peak": round(nbytes / med / 1e3 / PEAK_HBM_GBPS, 4),
                                    "shape": list(kq.kq_tune_get_shape(qtype, sum(rows), k))}
             log(f"  {name}_{qt}: {med:.2f} us, {nbytes / med / 1e3:.0f} GB/s")
+    return out
+
+
+def verify_pass(torch, kq, chain, ms=(1, 2, 4, 8, 16), reps=3):
+    """The speculative-verify batch through the 52-layer FFN pass (Ch 10
+    "The forward pass at a glance", sections 10.2-10.3; Ch 36 section 36.4):
+    for M activation rows, per layer kq_ffn_gate_up_q4k_small_m (gate, up and
+    the SiLU product), kq_matmul_small_m (Q6_K down) and kq_fused_residual_norm
+    over the M rows; the entry norm first.  Captured as one graph and replayed;
+    tokens/s = M / time per pass, GB/s = the pass's weight bytes / time."""
+    Q4, Q6 = kq.KQ_QTYPE_Q4K, kq.KQ_QTYPE_Q6K
+    L = chain.layers
+    out = {}
+    res0 = torch.randn(16, HIDDEN, device="cuda")
+    ones, zeros = torch.ones(HIDDEN, device="cuda"), torch.zeros(16, HIDDEN, device="cuda")
+    for m in ms:
+        need = max(kq.kq_matmul_small_m_workspace_bytes(Q4, FFN, HIDDEN, m),
+                   kq.kq_matmul_small_m_workspace_bytes(Q6, HIDDEN, FFN, m))
+        ws = torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda")
+        R = res0[:m].clone()
+        X = [torch.empty(m, HIDDEN, device="cuda") for _ in range(2)]
+        mid = torch.empty(m, FFN, device="cuda")
+        P = torch.empty(m, HIDDEN, device="cuda")
+
+        def run():
+            kq.kq_fused_residual_norm(R, zeros[:m], X[0], ones, ones, m, HIDDEN)
+            for l in range(L):
+                kq.kq_ffn_gate_up_q4k_small_m(chain.Wg[l], chain.Wu[l], X[l % 2], HIDDEN, mid, FFN,
+                                              FFN, HIDDEN, m, ws, need)
+                kq.kq_matmul_small_m(Q6, chain.Wd[l], mid, FFN, P, HIDDEN, HIDDEN, FFN, m, ws, need)
+                kq.kq_fused_residual_norm(R, P, X[(l + 1) % 2], chain.gp[l], chain.gn[l], m, HIDDEN)
+        run()
+        torch.cuda.synchronize()
+        g = graph_of(torch, [run])
+        launches = 1 + L * (3 if m == 1 else 4)
+        med, cv, _ = time_graph(torch, g, 1, reps)
+        del g
+        wb = WEIGHT_BYTES_PASS * L // LAYERS
+        out[f"m{m}"] = {"us_per_pass": round(med, 1), "us_cv": round(cv, 4),
+                        "tokens_per_s": round(m / med * 1e6, 1),
+                        "weight_GBps": round(wb / med / 1e3, 1), "launches": launches}
+        log(f"  verify pass M={m}: {med / 1e3:.3f} ms, {m / med * 1e6:.0f} tokens/s")
+    return out
+
+
+def embedding_lookup(torch, kq, I, reps=5, launches=52):
+    """kq_embedding of 16 tokens (a verify batch) from the [202048 x 6656]
+    Q4_K and Q5_K tables: 16 rows of 3744 / 4576 B gathered and dequantized."""
+    out = {}
+    for qt, qtype in (("q4k", kq.KQ_QTYPE_Q4K), ("q5k", kq.KQ_QTYPE_Q5K)):
+        E = torch.from_numpy(I.weight_matrix(qt, VOCAB, HIDDEN, stream=820)).cuda()
+        tok = torch.from_numpy(I.token_ids(16 * launches, VOCAB, stream=821)).cuda()
+        o = torch.empty(16, HIDDEN, device="cuda")
+        g = graph_of(torch, [lambda i=i: kq.kq_embedding(qtype, E, VOCAB, HIDDEN, tok[16 * i:],
+                                                         16, o) for i in range(launches)])
+        med, cv, _ = time_graph(torch, g, launches, reps)
+        del g, E
+        torch.cuda.empty_cache()
+        out[qt] = {"tokens": 16, "us_median": round(med, 3), "us_cv": round(cv, 4)}
     return out
 
 
@@ -610,7 +671,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time uncaptured launches instead of a graph")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
-    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu", "shapes"),
+    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu", "shapes",
+                                       "embedding"),
                     help="run one section alone (for profiler runs) and print its results")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -644,6 +706,7 @@ def main():
                "small_m": lambda: {"small_m": small_m_sweep(torch, kq, I)},
                "probe": lambda: {"read_ceiling": read_ceiling(torch, kq)},
                "shapes": lambda: {"decode_shapes": decode_shapes(torch, kq, I)},
+               "embedding": lambda: {"embedding": embedding_lookup(torch, kq, I)},
                "cpu": lambda: {"cpu_baseline": cpu_baseline(I)}}[args.only]()
         print(json.dumps({"section": args.only, **sec, "build": kq.kq_build_info()}), flush=True)
         torch.cuda.synchronize()
@@ -741,6 +804,8 @@ def main():
 
     extras = {}
     if not args.no_extras:
+        log("verify batch through the 52-layer pass")
+        extras["verify_pass"] = verify_pass(torch, kq, chain)
         log("read-stream ceiling probe")
         rc = read_ceiling(torch, kq)
         extras["read_ceiling"] = rc
@@ -757,6 +822,8 @@ def main():
         extras["small_m"] = small_m_sweep(torch, kq, I)
         log("other decode matvec shapes")
         extras["decode_shapes"] = decode_shapes(torch, kq, I)
+        log("embedding lookup")
+        extras["embedding"] = embedding_lookup(torch, kq, I)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -57,8 +57,10 @@ def build(out: str = LIB, verbose: bool = False) -> str:
 
 
 def asm(source: str = "kq_kernels.hip", out_dir: str | None = None) -> str:
-    """Write the gfx950 assembly of one source (for inspection)."""
-    out_dir = out_dir or os.path.join(ROOT, "_work")
+    """Write the gfx950 assembly of one source (for inspection) into out_dir,
+    by default a new temporary directory; returns the file's path."""
+    import tempfile
+    out_dir = out_dir or tempfile.mkdtemp(prefix="kq_asm_")
     os.makedirs(out_dir, exist_ok=True)
     out = os.path.join(out_dir, os.path.splitext(source)[0] + ".s")
     cmd = [hipcc(), *flags(), "--cuda-device-only", "-S", "-o", out, os.path.join(CSRC, source)]

@@ -803,9 +803,12 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
         !q6 && ((k <= 8192 && n_rows >= 32 * 2 * (int64_t)cus) ||
                 (long_q4 && staged && n_rows >= 8 * 2 * (int64_t)cus &&
                  2 * staged_bytes<32, KQ_LIMBS>(k) <= 160 * 1024));
-    const int64_t gmax = two_per_cu ? 2 * (int64_t)cus : (int64_t)cus;
+    // very many rows per CU (the LM head, 789 rows per CU): one 16-wave
+    // workgroup per CU streams 4-5 % faster than two 8-wave ones
+    const bool huge = !q6 && k <= 8192 && rpc >= 256;
+    const int64_t gmax = (two_per_cu && !huge) ? 2 * (int64_t)cus : (int64_t)cus;
     const int grid = (int)(tiles < gmax ? (tiles > 0 ? tiles : 1) : gmax);
-    const int waves = (q6 || two_per_cu || staged) ? 8 : 16;
+    const int waves = huge ? 16 : ((q6 || two_per_cu || staged) ? 8 : 16);
     const int depth = (q6 && k <= 8192 && rpc >= 100) ? 1 : 2;
     return kqi::MatvecShape{long_q4 ? 32 : 8, waves, grid, depth};
 }
