@@ -6,26 +6,27 @@
 //
 // Design for gfx950 (the pages' kernels use scalar f32 MACs on another GPU):
 //
-// * Matrix cores.  One 64-lane wave owns two tiles of 16 weight rows.  For
-//   every scale sub-block it issues f16 MFMAs D[16 x 16] += A[16 x K'] B[K' x
-//   16] with A = the (up to 16) activation rows and B = the sub-block's
-//   quants: Q4_K uses 16x16x32 (one 32-weight sub-block), Q6_K 16x16x16 (one
-//   16-weight sub-block); both tiles use the same A registers.  Lane l holds
-//   output column l % 16 = its weight row, so the per-row scale d*sc is
-//   applied in registers right after the MFMA.  The Q4_K min term is one more
-//   MFMA per tile, of the activation rows' group sums against the row's mins.
+// * Matrix cores.  A wave owns one or two tiles of 16 weight rows and issues
+//   f16 MFMAs D[16 x 16] += A[16 x K'] B[K' x 16] with A = the (up to 16)
+//   activation rows and B = quants of the tile's rows: lane l holds output
+//   column l % 16 = its weight row.  Every tile of a wave uses the same A
+//   registers.  The Q4_K min term is one more MFMA per tile, of the
+//   activation rows' 32-input group sums against the row's mins.
 // * Exact quant operands.  A quant q is turned into the f16 value 1024 + q by
-//   OR-ing it under the exponent of 1024 (0x6400), then 1024 (Q4_K) or 1056
-//   (Q6_K, folding the -32 offset) is subtracted: both steps are exact, so B
-//   holds the integers q or q - 32 exactly.
+//   OR-ing it under the exponent of 1024 (0x6400) and the bias is removed
+//   exactly.  Q4_K (16x16x32): each lane loads its own bytes of the
+//   superblock (no LDS round trip) and folds its sub-block's 6-bit scale into
+//   B with one exact f16 fused multiply-add, q sc <= 945 < 2^11, so one MFMA
+//   spans four sub-blocks and d is applied once per superblock.  Q6_K
+//   (16x16x16): q sc does not fit f16 exactly (up to 32 * 128), so a tile goes
+//   through LDS, each 16-input sub-block gets its own MFMA pair and d sc is
+//   applied to its result.
 // * Activations at ~22 bits.  Each (row m, superblock) group of 256 inputs is
 //   scaled by a power of two so that its largest magnitude is below 2^15, then
-//   split into x_hi = f16(x) and x_lo = f16(x - x_hi); two MFMAs (hi, lo) per
-//   sub-block accumulate in f32.  The products q * x_hi and q * x_lo are exact
-//   in f32.  The Q4_K group sums (of the scaled inputs, times 2^-5) are split
+//   split into x_hi = f16(x) and x_lo = f16(x - x_hi); a hi and a lo MFMA per
+//   step accumulate in f32.  The products q * x_hi and q * x_lo are exact in
+//   f32.  The Q4_K group sums (of the scaled inputs, times 2^-5) are split
 //   into hi and lo halves the same way.
-//   A group holding a NaN or an infinity is staged as NaN, so the whole output
-//   row m becomes NaN.
 // * Stream-K split.  The work is the grid of (row group of 256 rows, superblock)
 //   tiles; workgroup g takes the contiguous range [g T / G, (g+1) T / G).  A row
 //   group covered by one workgroup is stored directly.  Otherwise each
@@ -58,29 +59,27 @@ using namespace kqd;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Launch shapes, one workgroup per CU, 256-row groups either way:
+// Q6_K launch shapes, one workgroup per CU, 256-row groups either way:
 // * up to 8 activation rows: 16 waves of one 16-row tile each (4 waves per
 //   SIMD hide more latency; the kernel fits 128 VGPRs);
 // * 9 to 16 rows: 8 waves of two tiles each, which share every activation
 //   operand they read, so a range of 8 superblocks of 16 activation rows still
 //   fits LDS beside the weight tiles.
-// Measured on MI355X at the verify shapes: the 16-wave form is 3-9 % faster
-// at M = 2..8 and 25 % slower at M = 16 (its larger tile area leaves room for
-// only 6-7 staged superblocks, and the grid needs a second round).
-template <int SUB, int WAVES, int Q4_DEPTH, int Q6_DEPTH>
+template <int SUB, int WAVES, int DEPTH>
 struct SmCfg {
     static constexpr int kSub = SUB;      // 16-row tiles per wave
     static constexpr int kWaves = WAVES;  // waves per workgroup
     static constexpr int kThreads = 64 * WAVES;
-    static constexpr int kQ4Depth = Q4_DEPTH, kQ6Depth = Q6_DEPTH;  // tile sets in flight ahead
+    static constexpr int kDepth = DEPTH;  // tile sets in flight ahead
 };
-using SmNarrow = SmCfg<1, 16, 1, 1>;  // m <= 8
-using SmWide = SmCfg<2, 8, 2, 1>;     // m >= 9
+using SmNarrow = SmCfg<1, 16, 1>;  // m <= 8
+using SmWide = SmCfg<2, 8, 1>;     // m >= 9
 constexpr int kSmRows = 256;          // rows per row group: 16 kSub kWaves in both shapes
 static_assert(16 * SmNarrow::kSub * SmNarrow::kWaves == kSmRows, "row group");
 static_assert(16 * SmWide::kSub * SmWide::kWaves == kSmRows, "row group");
@@ -148,17 +147,6 @@ __device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v)
 // those bytes straight from memory would cost one L1 tag lookup per lane per
 // few bytes.)  Slot s of the tile is handled by lane s % 64 in load i = s / 64.
 
-// Q4_K: 16 rows x 9 pieces of 16 bytes (rows are 16-byte aligned).
-constexpr int kQ4Pieces = 9;
-constexpr int kQ4Slots = 16 * kQ4Pieces;   // 144
-constexpr int kQ4Loads = 3;                // ceil(144 / 64)
-constexpr int kQ4RowLds = 144;             // LDS bytes per row of a tile
-constexpr int kQ4TileLds = 16 * kQ4RowLds;
-
-struct Q4Tile {
-    u32x4 c[kQ4Loads];
-};
-
 // Q6_K: a superblock starts 2-byte aligned when its global index is odd.  A row
 // of the tile is read from the 4-byte aligned address a at or below it: 13
 // pieces of 16 bytes cover [a, a + 208) and a tail covers [a + 208, sb + 210)
@@ -179,10 +167,6 @@ struct Q6Tile {
 };
 
 template <typename U> struct TileTraits;
-template <> struct TileTraits<Q4Tile> {
-    static constexpr int kPieces = kQ4Pieces, kLoads = kQ4Loads,
-                         kRowLds = kQ4RowLds, kTileLds = kQ4TileLds, kBlk = kQ4Bytes;
-};
 template <> struct TileTraits<Q6Tile> {
     static constexpr int kPieces = kQ6Pieces, kLoads = kQ6Loads,
                          kRowLds = kQ6RowLds, kTileLds = kQ6TileLds, kBlk = kQ6Bytes;
@@ -212,21 +196,6 @@ __device__ __forceinline__ void tile_rows(TileAddr<U> &ta, int rg, int slice, in
     ta.tail_off = (int64_t)row * row_bytes;
 }
 
-__device__ __forceinline__ Q4Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q4Tile> &ta,
-                                            int b, int lane)
-{
-    // Every lane loads (a lane past the tile's last piece re-reads that
-    // piece; store_tile drops it): no branch between the loads and their use.
-    Q4Tile u;
-#pragma unroll
-    for (int i = 0; i < kQ4Loads; ++i) {
-        const int slot = min(64 * i + lane, kQ4Slots - 1);
-        u.c[i] = *reinterpret_cast<const u32x4 *>(W + ta.row_off[i] + (int64_t)b * kQ4Bytes +
-                                                  16 * (slot % kQ4Pieces));
-    }
-    return u;
-}
-
 __device__ __forceinline__ Q6Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q6Tile> &ta,
                                             int b, int lane)
 {
@@ -249,15 +218,6 @@ __device__ __forceinline__ Q6Tile load_tile(const uint8_t *__restrict__ W, const
     return u;
 }
 
-__device__ __forceinline__ void store_tile(const Q4Tile &u, uint8_t *tile, int lane)
-{
-#pragma unroll
-    for (int i = 0; i < kQ4Loads; ++i) {
-        const int slot = 64 * i + lane;
-        if (slot < kQ4Slots) *reinterpret_cast<u32x4 *>(tile + 16 * slot) = u.c[i];
-    }
-}
-
 __device__ __forceinline__ void store_tile(const Q6Tile &u, uint8_t *tile, int lane)
 {
 #pragma unroll
@@ -273,24 +233,6 @@ __device__ __forceinline__ void store_tile(const Q6Tile &u, uint8_t *tile, int l
 }
 
 // What one lane needs of its row's superblock, read back from the LDS tile.
-struct Q4Sb {
-    u32x4 hdr;      // d, dmin, 12 bytes of packed 6-bit scales and mins
-    uint32_t q[8];  // chunk c: bytes 16 + 32c + 8kb .. +7 as q[2c], q[2c+1]
-};
-
-__device__ __forceinline__ Q4Sb read_sb(const uint8_t *__restrict__ row, int kb, int, Q4Sb *)
-{
-    Q4Sb u;
-    u.hdr = *reinterpret_cast<const u32x4 *>(row);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(row + 16 + 32 * c + 8 * kb);
-        u.q[2 * c] = v.x;
-        u.q[2 * c + 1] = v.y;
-    }
-    return u;
-}
-
 struct Q6Sb {
     uint32_t w[24];  // ql windows u = 0..7 (w[2u], w[2u+1]); qh windows v = 0..3 (w[16+2v], ..)
     u32x4 hs;        // scale bytes, aligned window
@@ -339,100 +281,14 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s, uint32_t vmask)
     return and_or(w >> s, vmask, kBias);
 }
 
-// Contribution of one Q4_K superblock of each of the wave's NS sub-tiles to the
-// lane's 4 outputs per sub-tile, in units of the staged (scaled) activations.
-// `ah` points at the lane's activation row in the hi plane at this
-// superblock's first input + 8 kb; the lo plane is `lo_off` bytes further.
-// `sf` = the lane's A fragment of the superblock's min-term table (see
-// stage_chunk).  Every activation operand read from LDS serves all NS
-// sub-tiles.
-//
-// The min term sum_s dmin m_s (sum of x over sub-block s) is one more MFMA per
-// tile: A = the 8 group sums of each activation row (hi and lo halves in K),
-// B = the row's 8 six-bit mins as exact f16 integers.
-template <int NS>
-__device__ __forceinline__ void sb_mma(const Q4Sb (&u)[NS], const uint8_t *__restrict__ ah,
-                                       int lo_off, const uint8_t *__restrict__ sf, uint32_t vmask,
-                                       f32x4 (&ys)[NS])
-{
-    uint32_t scA[NS], mnA[NS], scB[NS], mnB[NS];
-    float d[NS], dmin[NS];
-#pragma unroll
-    for (int h = 0; h < NS; ++h) {
-        const uint32_t S0 = u[h].hdr.y, S1 = u[h].hdr.z, S2 = u[h].hdr.w;
-        scA[h] = S0 & 0x3F3F3F3Fu;
-        mnA[h] = S1 & 0x3F3F3F3Fu;
-        scB[h] = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
-        mnB[h] = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
-        d[h] = half_lo(u[h].hdr.x);
-        dmin[h] = half_hi(u[h].hdr.x);
-        ys[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    const h8 off = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
-    f32x4 dm[NS];
-    {
-        // mins of sub-blocks 0,2 | 1,3 | 4,6 | 5,7 as f16 pairs (the table's
-        // order within a row)
-        const h8 As = *reinterpret_cast<const h8 *>(sf);
-#pragma unroll
-        for (int h = 0; h < NS; ++h) {
-            const u32x4 bq = {(mnA[h] & 0x00FF00FFu) | kBias, ((mnA[h] >> 8) & 0x00FF00FFu) | kBias,
-                              (mnB[h] & 0x00FF00FFu) | kBias, ((mnB[h] >> 8) & 0x00FF00FFu) | kBias};
-            dm[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(As, as_h8(bq) - off,
-                                                           (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-        }
-    }
-#pragma unroll
-    for (int c0 = 0; c0 < 4; c0 += 2) {
-        // sub-blocks 2c0 .. 2c0+3: all hi MFMAs, then all lo MFMAs
-        h8 B[NS][4];
-        f32x4 acc[NS][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = c0 + (j >> 1), hn = j & 1, s = 2 * c + hn;
-            const h8 Ahi = *reinterpret_cast<const h8 *>(ah + 64 * s);
-#pragma unroll
-            for (int h = 0; h < NS; ++h) {
-                const uint32_t w0 = u[h].q[2 * c], w1 = u[h].q[2 * c + 1];
-                const u32x4 bq = {nib_pair(w0, 4 * hn, vmask), nib_pair(w0, 4 * hn + 8, vmask),
-                                  nib_pair(w1, 4 * hn, vmask), nib_pair(w1, 4 * hn + 8, vmask)};
-                B[h][j] = as_h8(bq) - off;
-                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    Ahi, B[h][j], (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * (2 * c0 + j));
-#pragma unroll
-            for (int h = 0; h < NS; ++h)
-                acc[h][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B[h][j], acc[h][j], 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int s = 2 * c0 + j;
-#pragma unroll
-            for (int h = 0; h < NS; ++h) {
-                const uint32_t scw = s < 4 ? scA[h] : scB[h];
-                const float c1 = d[h] * (float)((scw >> (8 * (s & 3))) & 0xFFu);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ys[h][i] = fmaf(c1, acc[h][j][i], ys[h][i]);
-            }
-        }
-    }
-    // the table holds the group sums times 2^-5
-#pragma unroll
-    for (int h = 0; h < NS; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ys[h][i] = fmaf(-32.0f * dmin[h], dm[h][i], ys[h][i]);
-}
-
-// The same for Q6_K superblocks; `ah` = the lane's activation row at the
-// superblock's first input + 4 kb.
+// Contribution of one Q6_K superblock of each of the wave's NS sub-tiles to the
+// lane's 4 outputs per sub-tile, in units of the staged (scaled) activations:
+// one MFMA per 16-input sub-block and plane, scaled by d sc after it.  `ah` =
+// the lane's activation row in the hi plane at the superblock's first input +
+// 4 kb; the lo plane is `lo_off` bytes further.
 template <int NS>
 __device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__restrict__ ah,
-                                       int lo_off, const uint8_t *__restrict__, uint32_t vmask,
-                                       f32x4 (&ys)[NS])
+                                       int lo_off, uint32_t vmask, f32x4 (&ys)[NS])
 {
     uint32_t L[NS][8], H[NS][4], sc[NS][4];
     float d[NS];
@@ -496,11 +352,6 @@ __device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__res
     }
 }
 
-template <typename U>
-__device__ __forceinline__ constexpr bool is_q4()
-{
-    return TileTraits<U>::kBlk == kQ4Bytes;
-}
 
 // ---------------------------------------------------------------------------
 // Staging of the activations of superblocks [cb, cb + n) into LDS slots so, so + 1, ...
@@ -509,79 +360,99 @@ __device__ __forceinline__ constexpr bool is_q4()
 // for slot c and row m, [c][0][m] and [c][1][m] are the hi and lo f16 halves
 // of 2^-5 times the sums of the row's 8 scaled 32-input groups (below 2^15 in
 // magnitude), groups in the order 0,2,1,3,4,6,5,7, and [c][2..3][m] are zero:
-// lane (r, kb) of the min-term MFMA reads [c][kb][r] as its A fragment.  One
-// wave converts one (row, superblock) group of 256 inputs.
-template <bool Q4>
+// lane (r, kb) of the min-term MFMA reads [c][kb][r] as its A fragment.
+//
+// Eight lanes convert one (row, superblock) group of 256 inputs, 32
+// consecutive inputs each: the group maximum is a DPP reduction over the
+// eight, and a lane's 32 inputs are one 32-input group of the min-term table,
+// summed in the lane.  A wave converts 8 groups at a time and issues the loads
+// of BL such rounds before converting any, so that a workgroup's whole window
+// usually arrives in one memory round trip.  A group holding a NaN or an
+// infinity is staged with a NaN, so the whole output row m becomes NaN.
+template <bool Q4, int BL>
 __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem,
                                             int so = 0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 3, j8 = lane & 7;
     const int M = a.m, RS = a.RS;
     uint8_t *hi = smem, *lo = smem + M * RS;
     int *etab = reinterpret_cast<int *>(smem + 2 * M * RS);
     uint8_t *sfrag = reinterpret_cast<uint8_t *>(etab + 16 * a.CH);
     const int ngroups = M * n;
-    constexpr int B = 4;
     const int nw = blockDim.x >> 6;
-    for (int g0 = wave; g0 < ngroups; g0 += B * nw) {
-        f32x4 v[B];
+    for (int r0 = wave; 8 * r0 < ngroups; r0 += BL * nw) {
+        f32x4 v[BL][8];
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int gi = g0 + j * nw;
-            if (gi < ngroups) {
-                const int m = gi / n, bb = gi - m * n;
-                v[j] = *reinterpret_cast<const f32x4 *>(a.X + (int64_t)m * a.ldx +
-                                                        256 * (int64_t)(cb + bb) + 4 * lane);
-            }
+        for (int b = 0; b < BL; ++b) {
+            // a group past the end re-reads the last one (its results are dropped)
+            const int gi = min(8 * (r0 + b * nw) + grp, ngroups - 1);
+            const int m = gi / n, bb = gi - m * n;
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(
+                a.X + (int64_t)m * a.ldx + 256 * (int64_t)(cb + bb) + 32 * j8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[b][i] = src[i];
         }
 #pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int gi = g0 + j * nw;
-            if (gi >= ngroups) break;  // wave-uniform
-            const int m = gi / n, bb = gi - m * n;
-            float mx = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
-            mx = group_max<8>(mx);
+        for (int b = 0; b < BL; ++b) {
+            if (8 * (r0 + b * nw) >= ngroups) break;  // wave-uniform
+            const int gi = 8 * (r0 + b * nw) + grp;
+            const bool act = gi < ngroups;  // the same for the 8 lanes of a group
+            const int gc = min(gi, ngroups - 1);
+            const int m = gc / n, bb = gc - m * n;
+            float mx = 0.0f;
 #pragma unroll
-            for (int o = 8; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            for (int i = 0; i < 8; ++i)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[b][i].x), fabsf(v[b][i].y)),
+                                     fmaxf(fabsf(v[b][i].z), fabsf(v[b][i].w))));
+            mx = group_max<8>(mx);
             const bool fin = mx <= FLT_MAX;  // false for Inf and NaN
             const int e = __builtin_amdgcn_frexp_expf(mx);  // mx < 2^e
             const int sh = 15 - e;
-            const f32x4 s = {ldexpf(v[j].x, sh), ldexpf(v[j].y, sh), ldexpf(v[j].z, sh),
-                             ldexpf(v[j].w, sh)};
-            _Float16 h[4], l[4];
+            const int sbb = so + bb;  // LDS slot of this superblock
+            const int boff = m * RS + 2 * (256 * sbb + 32 * j8);
+            float sm = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                h[i] = (_Float16)s[i];
-                l[i] = (_Float16)(s[i] - (float)h[i]);
-                if (!fin) {
-                    h[i] = (_Float16)__builtin_nanf("");
-                    l[i] = h[i];
+            for (int q = 0; q < 4; ++q) {
+                uint32_t ph[4], pl[4];
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    const f32x4 x = v[b][2 * q + i2];
+                    const f32x4 sv = {ldexpf(x.x, sh), ldexpf(x.y, sh), ldexpf(x.z, sh),
+                                      ldexpf(x.w, sh)};
+                    _Float16 h[4], l[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        h[c] = (_Float16)sv[c];
+                        l[c] = (_Float16)(sv[c] - (float)h[c]);
+                    }
+                    // 4 consecutive inputs stored in the order 0, 2, 1, 3
+                    ph[2 * i2] = __builtin_bit_cast(uint32_t, (h2){h[0], h[2]});
+                    ph[2 * i2 + 1] = __builtin_bit_cast(uint32_t, (h2){h[1], h[3]});
+                    pl[2 * i2] = __builtin_bit_cast(uint32_t, (h2){l[0], l[2]});
+                    pl[2 * i2 + 1] = __builtin_bit_cast(uint32_t, (h2){l[1], l[3]});
+                    if constexpr (Q4) sm += (sv.x + sv.y) + (sv.z + sv.w);
+                }
+                if (q == 0 && !fin) ph[0] = 0x7E007E00u;  // f16 NaN pair
+                if (act) {
+                    *reinterpret_cast<u32x4 *>(hi + boff + 16 * q) = (u32x4){ph[0], ph[1], ph[2], ph[3]};
+                    *reinterpret_cast<u32x4 *>(lo + boff + 16 * q) = (u32x4){pl[0], pl[1], pl[2], pl[3]};
                 }
             }
-            // inputs 4 lane .. 4 lane + 3 stored in the order 0, 2, 1, 3
-            const int sbb = so + bb;  // LDS slot of this superblock
-            const int boff = m * RS + 2 * (256 * sbb + 4 * lane);
-            const u32x2 ph = {__builtin_bit_cast(uint32_t, (h4){h[0], h[2], h[1], h[3]}.xy),
-                              __builtin_bit_cast(uint32_t, (h4){h[0], h[2], h[1], h[3]}.zw)};
-            const u32x2 pl = {__builtin_bit_cast(uint32_t, (h4){l[0], l[2], l[1], l[3]}.xy),
-                              __builtin_bit_cast(uint32_t, (h4){l[0], l[2], l[1], l[3]}.zw)};
-            *reinterpret_cast<u32x2 *>(hi + boff) = ph;
-            *reinterpret_cast<u32x2 *>(lo + boff) = pl;
-            if (lane == 0) etab[16 * sbb + m] = e - 15;
-            if constexpr (Q4) {
-                const float sm = 0.03125f * group_sum<8>((s.x + s.y) + (s.z + s.w));
-                _Float16 *sf = reinterpret_cast<_Float16 *>(sfrag + 1024 * sbb) + 8 * m;
-                if ((lane & 7) == 0) {
-                    const int g = lane >> 3;
-                    const int pos = (g & 4) | ((g & 1) << 1) | ((g >> 1) & 1);  // 0,2,1,3,4,6,5,7
-                    const _Float16 hs = fin ? (_Float16)sm : (_Float16)__builtin_nanf("");
+            if (act) {
+                if (j8 == 0) etab[16 * sbb + m] = e - 15;
+                if constexpr (Q4) {
+                    const float s5 = 0.03125f * sm;
+                    _Float16 *sf = reinterpret_cast<_Float16 *>(sfrag + 1024 * sbb) + 8 * m;
+                    const int pos = (j8 & 4) | ((j8 & 1) << 1) | ((j8 >> 1) & 1);  // 0,2,1,3,4,6,5,7
+                    const _Float16 hs = fin ? (_Float16)s5 : (_Float16)__builtin_nanf("");
                     sf[pos] = hs;
-                    sf[128 + pos] = fin ? (_Float16)(sm - (float)hs) : hs;
-                }
-                if (lane == 1) {
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    *reinterpret_cast<u32x4 *>(sf + 256) = z;
-                    *reinterpret_cast<u32x4 *>(sf + 384) = z;
+                    sf[128 + pos] = fin ? (_Float16)(s5 - (float)hs) : hs;
+                    if (j8 == 1) {
+                        const u32x4 z = {0u, 0u, 0u, 0u};
+                        *reinterpret_cast<u32x4 *>(sf + 256) = z;
+                        *reinterpret_cast<u32x4 *>(sf + 384) = z;
+                    }
                 }
             }
         }
@@ -630,25 +501,59 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
     }
     __syncthreads();
     if (last_flag) {
-        // sum the contributors' partial tiles in workgroup order
+        // Sum the contributors' partial tiles in workgroup order.  A thread
+        // takes up to kE quads of 4 rows of one activation row and issues the
+        // loads of 4 contributors for all of them before it adds any (loads
+        // past the last contributor or quad re-read the last one, in bounds,
+        // and are not used), so the sum waits for few memory round trips.
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(a.ws, (short)0, a.ws_bytes, 0x00020000);
-        for (int e = threadIdx.x; e < M * (kSmRows / 4); e += blockDim.x) {
-            const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
-            f32x4 s;
-            for (int c = gl; c <= gh; ++c) {
-                const int sl = (first_tile(c, a.T, a.G) / nb == rg) ? 0 : 1;
-                const uint32_t off = (uint32_t)a.part_off +
-                                     4u * (uint32_t)((2 * c + sl) * (16 * kSmRows) +
-                                                     m * kSmRows + 4 * q);
-                const f32x4 v = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 16 /* sc1 */));
-                s = (c == gl) ? v : s + v;
+        // quads per thread: 16 waves take up to 8 activation rows (512 quads),
+        // 8 waves of two tiles up to 16 (1024 quads)
+        constexpr int kE = kSub;
+        const int nq = M * (kSmRows / 4);
+        // every contributor after the first starts its range inside this row
+        // group (slot 0); the first one owns the group's first tile and
+        // starts in it or in an earlier group (slot 1)
+        const int sl_first = first_tile(gl, a.T, a.G) < rg * nb ? 1 : 0;
+        for (int e0 = threadIdx.x; e0 < nq; e0 += kE * blockDim.x) {
+            f32x4 sum[kE];
+            for (int c0 = gl; c0 <= gh; c0 += 4) {
+                f32x4 v[4][kE];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = min(c0 + j, gh);
+                    const int sl = c == gl ? sl_first : 0;
+#pragma unroll
+                    for (int x = 0; x < kE; ++x) {
+                        const int e = min(e0 + x * (int)blockDim.x, nq - 1);
+                        const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
+                        const uint32_t off = (uint32_t)a.part_off +
+                                             4u * (uint32_t)((2 * c + sl) * (16 * kSmRows) +
+                                                             m * kSmRows + 4 * q);
+                        v[j][x] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0,
+                                                                         16 /* sc1 */));
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int x = 0; x < kE; ++x)
+                        if (c0 + j <= gh) sum[x] = (c0 + j == gl) ? v[j][x] : sum[x] + v[j][x];
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + 4 * q + i;
-                if (row < a.n_rows) a.Y[(int64_t)m * a.ldy + row] = sm_out(a, m, row, s[i]);
+            for (int x = 0; x < kE; ++x) {
+                const int e = e0 + x * (int)blockDim.x;
+                if (e < nq) {
+                    const int m = e / (kSmRows / 4), q = e - m * (kSmRows / 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = row0 + 4 * q + i;
+                        if (row < a.n_rows)
+                            a.Y[(int64_t)m * a.ldy + row] = sm_out(a, m, row, sum[x][i]);
+                    }
+                }
             }
         }
         if (threadIdx.x == 0) st_agent(cnt + rg, 0u);
@@ -658,6 +563,10 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
 // A workgroup's range is at most one row of superblocks long, so it touches at
 // most two row groups (segments).
 constexpr int kMaxSegs = 2;
+// Staging rounds (8 groups of 256 inputs each) a wave loads at once: with 16
+// waves (m <= 8) one covers the 8 rows x 8 superblocks of the verify window,
+// with 8 waves two cover its 16 rows x 8 superblocks
+constexpr int stage_batch(int waves) { return waves >= 16 ? 1 : 2; }
 
 // The workgroup stages the activations of every superblock its range touches
 // once, up front (the host sizes the grid so that they fit in LDS), and keeps
@@ -671,10 +580,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int kSub = C::kSub;
-    constexpr int DEPTH = is_q4<U>() ? C::kQ4Depth : C::kQ6Depth;
+    constexpr int DEPTH = C::kDepth;
     using TT = TileTraits<U>;
-    using Sb = std::conditional_t<is_q4<U>(), Q4Sb, Q6Sb>;
-    constexpr bool Q4 = is_q4<U>();
+    using Sb = Q6Sb;
     constexpr int BLK = TT::kBlk;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kb = lane >> 4, r = lane & 15, m0 = 4 * kb;
@@ -686,10 +594,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
     uint8_t *tile = smem + wave * TT::kTileLds;  // this wave's weight tile
     const int lo_off = M * a.RS;
     const int *etab = reinterpret_cast<const int *>(xs + 2 * M * a.RS);
-    const uint8_t *sfrag = reinterpret_cast<const uint8_t *>(etab + 16 * a.CH);  // Q4_K min term
     int &last_flag = *reinterpret_cast<int *>(smem + a.flag_off);
     uint32_t vmask;  // kept in a VGPR for v_and_or_b32
-    asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(Q4 ? 0x000F000Fu : 0x00FF00FFu));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(0x00FF00FFu));
 
     // next tile to load: row group rl, superblock bl; the wave's sub-tile h
     // is slice kSub wave + h of the row group
@@ -755,8 +662,8 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
     if (t0 < t1) {
         const int w = t1 - t0;  // at most nb
         const int n1 = min(w, nb - cb);
-        stage_chunk<Q4>(a, cb, n1, xs);
-        if (w > n1) stage_chunk<Q4>(a, 0, w - n1, xs, n1);
+        stage_chunk<false, stage_batch(C::kWaves)>(a, cb, n1, xs);
+        if (w > n1) stage_chunk<false, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1);
         __syncthreads();
     }
     // One step: compute the tiles in ring slot u.
@@ -774,9 +681,9 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
             sb[h] = read_sb(tile + TT::kRowLds * r, kb, sh, (Sb *)nullptr);
         }
         const int bb = b >= cb ? b - cb : b + nb - cb;  // LDS slot of superblock b
-        const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + (Q4 ? 8 : 4) * kb);
+        const uint8_t *ah = xs + ma * a.RS + 2 * (256 * bb + 4 * kb);
         f32x4 ys[kSub];
-        sb_mma<kSub>(sb, ah, lo_off, sfrag + 1024 * bb + 256 * kb + 16 * ma, vmask, ys);
+        sb_mma<kSub>(sb, ah, lo_off, vmask, ys);
         const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
 #pragma unroll
         for (int h = 0; h < kSub; ++h)
@@ -831,6 +738,257 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
     }
 }
 
+// ---------------------------------------------------------------------------
+// Q4_K with per-lane weight loads (no LDS round trip for the weights).
+//
+// Lane (r, kb) of a 16-row tile reads, per superblock, its row's 16-byte
+// header and the 32 quant bytes of chunk kb (bytes 16 + 32 kb .. 47 + 32 kb of
+// the superblock) straight from memory: the low nibbles of that chunk are
+// sub-block 2 kb, the high nibbles sub-block 2 kb + 1.  MFMA j = 4 hn + jj of a
+// plane takes from lane kb the inputs 64 kb + 32 hn + 8 jj .. + 7 (each 4-group
+// in the staged order 0, 2, 1, 3), so the four lanes of a row feed four
+// different sub-blocks into one MFMA.  Each lane therefore folds its
+// sub-block's scale into its B values, exactly: one fused multiply-add in f16
+// turns the biased quant 1024 + q into (1024 + q) sc - 1024 sc = q sc, an
+// integer <= 15 * 63 = 945 < 2^11.  A high nibble is used where it sits, as
+// 1024 + 16 q, with the factors sc / 16 and -64 sc (both exact), so only the
+// odd bytes of a dword need a shift.  The 8 MFMAs of a plane then sum the whole
+// superblock and d is applied once.
+template <int NS, int WAVES, int DEPTH>
+struct SmQ4Cfg {
+    static constexpr int kSub = NS;       // 16-row tiles per wave
+    static constexpr int kWaves = WAVES;  // waves per workgroup
+    static constexpr int kThreads = 64 * WAVES;
+    static constexpr int kDepth = DEPTH;  // superblock steps in flight ahead
+};
+using SmQ4Narrow = SmQ4Cfg<1, 16, 2>;  // m <= 8
+using SmQ4Wide = SmQ4Cfg<2, 8, 2>;     // m >= 9
+static_assert(16 * SmQ4Narrow::kSub * SmQ4Narrow::kWaves == kSmRows, "row group");
+static_assert(16 * SmQ4Wide::kSub * SmQ4Wide::kWaves == kSmRows, "row group");
+
+
+struct Q4Own {
+    u32x4 hdr;  // d, dmin, 12 bytes of packed 6-bit scales and mins
+    u32x4 q0;   // quant bytes 32 kb .. 32 kb + 15 of the superblock's 128
+    u32x4 q1;   // quant bytes 32 kb + 16 .. 32 kb + 31
+};
+
+// p = the superblock's first byte (16-byte aligned)
+__device__ __forceinline__ Q4Own load_own(const uint8_t *__restrict__ p, int kb)
+{
+    Q4Own u;
+    u.hdr = *reinterpret_cast<const u32x4 *>(p);
+    u.q0 = *reinterpret_cast<const u32x4 *>(p + 16 + 32 * kb);
+    u.q1 = *reinterpret_cast<const u32x4 *>(p + 32 + 32 * kb);
+    return u;
+}
+
+__device__ __forceinline__ h8 splat8(_Float16 v) { return (h8){v, v, v, v, v, v, v, v}; }
+
+// One superblock of each of the wave's NS tiles: ys[h] = the lane's 4 outputs
+// of tile h (activation rows 4 kb .. 4 kb + 3, weight row r), in units of the
+// staged (scaled) activations.  `ah` = the lane's activation row in the hi
+// plane at the superblock's input 64 kb; the lo plane is `lo_off` bytes
+// further; `sf` = the lane's A fragment of the min-term table.
+template <int NS>
+__device__ __forceinline__ void q4_own_mma(const Q4Own (&u)[NS], const uint8_t *__restrict__ ah,
+                                           int lo_off, const uint8_t *__restrict__ sf, int kb,
+                                           uint32_t mlo, uint32_t mhi, f32x4 (&ys)[NS])
+{
+    const h8 off = {1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
+    const h8 As = *reinterpret_cast<const h8 *>(sf);
+    h8 f0[NS], c0[NS], f1[NS], c1[NS];
+    float d[NS], dmin[NS];
+    f32x4 dm[NS];
+#pragma unroll
+    for (int h = 0; h < NS; ++h) {
+        const uint32_t S0 = u[h].hdr.y, S1 = u[h].hdr.z, S2 = u[h].hdr.w;
+        // scales of sub-blocks 0..3 and 4..7; this lane's are 2 kb and 2 kb + 1
+        const uint32_t scA = S0 & 0x3F3F3F3Fu;
+        const uint32_t scB = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+        const uint32_t scw = kb < 2 ? scA : scB;
+        const int sh = 16 * (kb & 1);
+        const _Float16 s0 = (_Float16)(float)((scw >> sh) & 0xFFu);
+        const _Float16 s1 = (_Float16)(float)((scw >> (sh + 8)) & 0xFFu);
+        f0[h] = splat8(s0);
+        c0[h] = splat8(s0 * (_Float16)-1024.0f);
+        f1[h] = splat8(s1 * (_Float16)0.0625f);
+        c1[h] = splat8(s1 * (_Float16)-64.0f);
+        d[h] = half_lo(u[h].hdr.x);
+        dmin[h] = half_hi(u[h].hdr.x);
+        // the min term: A = the activation rows' 8 group sums, B = the row's
+        // 8 mins in the table's order 0,2,1,3,4,6,5,7
+        const uint32_t mnA = S1 & 0x3F3F3F3Fu;
+        const uint32_t mnB = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
+        const u32x4 bq = {(mnA & 0x00FF00FFu) | kBias, ((mnA >> 8) & 0x00FF00FFu) | kBias,
+                          (mnB & 0x00FF00FFu) | kBias, ((mnB >> 8) & 0x00FF00FFu) | kBias};
+        dm[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(As, as_h8(bq) - off,
+                                                       (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+    }
+    // two accumulators per tile (even and odd jj), each taking both planes
+    f32x4 acc[NS][2];
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[h][c] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int hn = 0; hn < 2; ++hn) {
+        const uint32_t msk = hn ? mhi : mlo;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const h8 Ahi = *reinterpret_cast<const h8 *>(ah + 64 * hn + 16 * jj);
+            const h8 Alo = *reinterpret_cast<const h8 *>(ah + lo_off + 64 * hn + 16 * jj);
+#pragma unroll
+            for (int h = 0; h < NS; ++h) {
+                const u32x4 &q = jj < 2 ? u[h].q0 : u[h].q1;
+                const uint32_t w0 = q[2 * (jj & 1)], w1 = q[2 * (jj & 1) + 1];
+                // f16 pairs (bytes 0, 2) and (bytes 1, 3) of each dword
+                const u32x4 bq = {and_or(w0, msk, kBias), and_or(w0 >> 8, msk, kBias),
+                                  and_or(w1, msk, kBias), and_or(w1 >> 8, msk, kBias)};
+                const h8 B = __builtin_elementwise_fma(as_h8(bq), hn ? f1[h] : f0[h],
+                                                       hn ? c1[h] : c0[h]);
+                acc[h][jj & 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, acc[h][jj & 1], 0, 0, 0);
+                acc[h][jj & 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, acc[h][jj & 1], 0, 0, 0);
+            }
+        }
+    }
+    // the table holds the group sums times 2^-5
+#pragma unroll
+    for (int h = 0; h < NS; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ys[h][i] = fmaf(d[h], acc[h][0][i] + acc[h][1][i], -32.0f * dmin[h] * dm[h][i]);
+}
+
+// The same work split, staging and fix-up as small_m_kernel; the steady-state
+// step holds only the ring's own loads and the LDS reads of the activations.
+template <typename C>
+__global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_q4_kernel(SmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int NS = C::kSub;
+    constexpr int DEPTH = C::kDepth;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = lane >> 4, r = lane & 15, m0 = 4 * kb;
+    const int g = blockIdx.x, nb = a.nb, M = a.m;
+    const int t0 = first_tile(g, a.T, a.G), t1 = first_tile(g + 1, a.T, a.G);
+    const int64_t row_bytes = (int64_t)nb * kQ4Bytes;
+    const int ma = min(r, M - 1);  // activation row this lane feeds into A
+    uint8_t *xs = smem + a.xs_off;
+    const int lo_off = M * a.RS;
+    const int *etab = reinterpret_cast<const int *>(xs + 2 * M * a.RS);
+    const uint8_t *sfrag = reinterpret_cast<const uint8_t *>(etab + 16 * a.CH);
+    int &last_flag = *reinterpret_cast<int *>(smem + a.flag_off);
+    uint32_t mlo, mhi;  // nibble masks, kept in VGPRs for v_and_or_b32
+    asm volatile("v_mov_b32 %0, %1" : "=v"(mlo) : "s"(0x000F000Fu));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(mhi) : "s"(0x00F000F0u));
+
+    // next superblock to load: row group rl, superblock bl; lrow[h] = byte
+    // offset in W of this lane's row of tile h (clamped to the matrix, so
+    // loads past the workgroup's last tile stay inside W and go unused)
+    int rl = t0 / nb, bl = t0 - rl * nb;
+    int64_t lrow[NS];
+    auto set_lrow = [&]() {
+#pragma unroll
+        for (int h = 0; h < NS; ++h)
+            lrow[h] = (int64_t)min(rl * kSmRows + 16 * (NS * wave + h) + r, a.n_rows - 1) *
+                      row_bytes;
+    };
+    set_lrow();
+    struct Set {
+        Q4Own t[NS];
+    };
+    auto load_next = [&]() {
+        Set u;
+#pragma unroll
+        for (int h = 0; h < NS; ++h)
+            u.t[h] = load_own(a.W + lrow[h] + (int64_t)bl * kQ4Bytes, kb);
+        if (++bl == nb) {
+            bl = 0;
+            ++rl;
+            set_lrow();
+        }
+        return u;
+    };
+    constexpr int R = DEPTH + 1;
+    Set ring[R];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+        ring[i] = load_next();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    int t = t0, rg = t0 / nb, b = t0 - rg * nb;
+    const int cb = b;
+    f32x4 yacc[NS];
+#pragma unroll
+    for (int h = 0; h < NS; ++h) yacc[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 sy[kMaxSegs][NS];
+    int seg = 0;
+    const int rg_first = t0 / nb, rg_last = (t1 - 1) / nb;
+    const int gl_first = owner(rg_first * nb, a.T, a.G);
+    const int gh_first = owner(rg_first * nb + nb - 1, a.T, a.G);
+    const int gl_last = owner(rg_last * nb, a.T, a.G);
+    const int gh_last = owner(rg_last * nb + nb - 1, a.T, a.G);
+    if (t0 < t1) {
+        const int w = t1 - t0;
+        const int n1 = min(w, nb - cb);
+        stage_chunk<true, stage_batch(C::kWaves)>(a, cb, n1, xs);
+        if (w > n1) stage_chunk<true, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1);
+        __syncthreads();
+    }
+    auto step = [&](const Set &u) __attribute__((always_inline)) {
+        const int bb = b >= cb ? b - cb : b + nb - cb;  // LDS slot of superblock b
+        const uint8_t *ah = xs + ma * a.RS + 2 * 256 * bb + 128 * kb;
+        f32x4 ys[NS];
+        q4_own_mma<NS>(u.t, ah, lo_off, sfrag + 1024 * bb + 256 * kb + 16 * ma, kb, mlo, mhi, ys);
+        const i32x4 ex = *reinterpret_cast<const i32x4 *>(etab + 16 * bb + m0);
+#pragma unroll
+        for (int h = 0; h < NS; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yacc[h][i] += ldexpf(ys[h][i], ex[i]);
+        ++t;
+        ++b;
+        if (b == nb || t == t1) {
+#pragma unroll
+            for (int q = 0; q < kMaxSegs; ++q)
+#pragma unroll
+                for (int h = 0; h < NS; ++h) sy[q][h] = (q == seg) ? yacc[h] : sy[q][h];
+            ++seg;
+#pragma unroll
+            for (int h = 0; h < NS; ++h) yacc[h] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            if (b == nb) {
+                b = 0;
+                ++rg;
+            }
+        }
+    };
+    const int rounds = (t1 - t0) / R, rem = (t1 - t0) - R * rounds;
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            ring[(j + DEPTH) % R] = load_next();
+            __builtin_amdgcn_sched_barrier(0);
+            step(ring[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j)
+        if (j < rem) step(ring[j]);
+#pragma unroll
+    for (int q = 0; q < kMaxSegs; ++q) {
+        if (q < seg) {
+            const int rq = rg_first + q;
+            const int gl = rq == rg_first ? gl_first : gl_last;
+            const int gh = rq == rg_first ? gh_first : gh_last;
+            finish_segment<NS>(a, rq, gl, gh, g, sy[q], wave, r, m0, last_flag);
+        }
+    }
+}
+
 struct SmPlan {
     int nb, T, G, CH, RS, part_off, flag_off, xs_off;
     size_t lds, ws;
@@ -859,9 +1017,9 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
     p.narrow = m <= 8;
-    const int waves = p.narrow ? SmNarrow::kWaves : SmWide::kWaves;
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 1024 : 0);  // LDS bytes per staged superblock
-    p.xs_off = waves * (qtype == 1 ? kQ4TileLds : kQ6TileLds);  // weight tiles first
+    // Q6_K: the waves' weight tiles first; Q4_K keeps no weights in LDS
+    p.xs_off = qtype == 1 ? 0 : (p.narrow ? SmNarrow::kWaves : SmWide::kWaves) * kQ6TileLds;
     int ch = (kSmLdsMax - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
     if (ch > p.nb) ch = p.nb;
     if (ch < 1) ch = 1;
@@ -930,12 +1088,20 @@ hipError_t launch_plan(const SmPlan &p, int qtype, const uint8_t *W, const float
         hipLaunchKernelGGL(K, dim3(p.G), dim3(C::kThreads), p.lds, stream, a);                 \
         return hipGetLastError();                                                             \
     }
+#define KQ_SM_Q4_GO(C)                                                                        \
+    {                                                                                         \
+        constexpr auto K = small_m_q4_kernel<C>;                                              \
+        if ((e = allow_lds<K>()) != hipSuccess) return e;                                     \
+        hipLaunchKernelGGL(K, dim3(p.G), dim3(C::kThreads), p.lds, stream, a);                 \
+        return hipGetLastError();                                                             \
+    }
     if (qtype == 1) {
-        if (p.narrow) KQ_SM_GO(Q4Tile, SmNarrow)
-        KQ_SM_GO(Q4Tile, SmWide)
+        if (p.narrow) KQ_SM_Q4_GO(SmQ4Narrow)
+        KQ_SM_Q4_GO(SmQ4Wide)
     }
     if (p.narrow) KQ_SM_GO(Q6Tile, SmNarrow)
     KQ_SM_GO(Q6Tile, SmWide)
+#undef KQ_SM_Q4_GO
 #undef KQ_SM_GO
 }
 
@@ -982,7 +1148,8 @@ void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
     out[1] = p.CH;
     out[2] = (int64_t)p.lds;
     out[3] = (int64_t)p.ws;
-    out[4] = p.narrow ? SmNarrow::kThreads : SmWide::kThreads;
+    out[4] = qtype == 1 ? (p.narrow ? SmQ4Narrow::kThreads : SmQ4Wide::kThreads)
+                        : (p.narrow ? SmNarrow::kThreads : SmWide::kThreads);
     out[5] = p.T;
 }
 
