@@ -273,14 +273,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t vmask, uint32_t 
     return r;
 }
 
-// f16 pairs (1024 + nibble of byte 0, 1024 + nibble of byte 2) etc. from one
-// dword of packed nibbles; `s` selects the nibble (0 low, 4 high) and the byte
-// pair (0: bytes 0 and 2, 8: bytes 1 and 3).
-__device__ __forceinline__ uint32_t nib_pair(uint32_t w, int s, uint32_t vmask)
-{
-    return and_or(w >> s, vmask, kBias);
-}
-
 // Contribution of one Q6_K superblock of each of the wave's NS sub-tiles to the
 // lane's 4 outputs per sub-tile, in units of the staged (scaled) activations:
 // one MFMA per 16-input sub-block and plane, scaled by d sc after it.  `ah` =
