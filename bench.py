@@ -549,10 +549,11 @@ def embedding_lookup(torch, kq, I, reps=5, launches=52):
     return out
 
 
-def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
+def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=5, launches=52):
     """kq_matmul_small_m at the verify shapes, M = 1..16: per-launch time from a
-    graph of launches over >= 1 GiB of rotated weight copies (so the Infinity
-    Cache cannot serve them), with GB/s (weights once + X + Y) and GFLOP/s."""
+    graph of 52 launches over >= 1 GiB of rotated weight copies (so the
+    Infinity Cache cannot serve them), median and CV of 5 replays, with GB/s
+    (weights once + X + Y) and GFLOP/s."""
     out = {}
     cases = [("q4k_19968x6656", kq.KQ_QTYPE_Q4K, "q4k", FFN, HIDDEN),
              ("q6k_6656x19968", kq.KQ_QTYPE_Q6K, "q6k", HIDDEN, FFN)]
@@ -569,25 +570,13 @@ def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=3):
             call = lambda c: kq.kq_matmul_small_m(qti, c, X, k, Y, n, n, k, m, ws, nbytes)
             for c in copies:
                 call(c)
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                for c in copies:
-                    call(c)
-            torch.cuda.synchronize()
-            for _ in range(3):  # steady clocks before timing
-                g.replay()
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ea.record()
-            for _ in range(reps):
-                g.replay()
-            eb.record()
-            torch.cuda.synchronize()
-            us = ea.elapsed_time(eb) * 1e3 / (reps * ncopy)
+            # graph of 52 launches over the rotated copies (a copy may repeat,
+            # far enough apart that the Infinity Cache no longer holds it)
+            g = graph_of(torch, [lambda c=copies[i % ncopy]: call(c) for i in range(launches)])
+            us, cv, all_us = time_graph(torch, g, launches, reps=reps, warm=3)
             b = W.numel() + 4 * m * (n + k)
-            res[f"m{m}"] = {"us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+            res[f"m{m}"] = {"us": round(us, 3), "us_cv": round(cv, 4), "us_replays": all_us,
+                            "GBps": round(b / us / 1e3, 1),
                             "frac_peak": round(b / us / 1e3 / PEAK_HBM_GBPS, 4),
                             "GFLOPs": round(2.0 * m * n * k / us / 1e3, 1), "bytes": b}
             del g, ws

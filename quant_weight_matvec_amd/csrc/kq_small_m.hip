@@ -361,9 +361,17 @@ __device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__res
 // of BL such rounds before converting any, so that a workgroup's whole window
 // usually arrives in one memory round trip.  A group holding a NaN or an
 // infinity is staged with a NaN, so the whole output row m becomes NaN.
-template <bool Q4, int BL>
+//
+// `after_loads` runs once in every wave, right after the wave's first round of
+// loads is issued (the first round's loads are unconditional; a wave without
+// groups re-reads the last one).  With 8 waves (16 activation rows, a heavy
+// staging) the kernel issues its first weight loads there, behind the
+// activations, so that the conversion waits for the activations only and the
+// weights stream in meanwhile (Q6_K at M = 16: 47 us against 49-50 us); with
+// 16 waves the staging is one light round and the weights go first.
+template <bool Q4, int BL, typename F>
 __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem,
-                                            int so = 0)
+                                            int so, F &&after_loads)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, j8 = lane & 7;
@@ -373,8 +381,8 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
     uint8_t *sfrag = reinterpret_cast<uint8_t *>(etab + 16 * a.CH);
     const int ngroups = M * n;
     const int nw = blockDim.x >> 6;
-    for (int r0 = wave; 8 * r0 < ngroups; r0 += BL * nw) {
-        f32x4 v[BL][8];
+    typedef f32x4 Round[BL][8];
+    auto load_round = [&](int r0, Round &v) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < BL; ++b) {
             // a group past the end re-reads the last one (its results are dropped)
@@ -385,6 +393,8 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[b][i] = src[i];
         }
+    };
+    auto convert_round = [&](int r0, const Round &v) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < BL; ++b) {
             if (8 * (r0 + b * nw) >= ngroups) break;  // wave-uniform
@@ -448,6 +458,17 @@ __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint
                 }
             }
         }
+    };
+    {
+        Round v;
+        load_round(wave, v);
+        after_loads();
+        if (8 * wave < ngroups) convert_round(wave, v);
+    }
+    for (int r0 = wave + BL * nw; 8 * r0 < ngroups; r0 += BL * nw) {
+        Round v;
+        load_round(r0, v);
+        convert_round(r0, v);
     }
 }
 
@@ -619,11 +640,13 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
     // workgroup's last tile read clamped rows (tile_rows) and are never used.
     constexpr int R = DEPTH + 1;
     Tiles ring[R];
+    auto ring_prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-        ring[i] = load_next();
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int i = 0; i < DEPTH; ++i) {
+            ring[i] = load_next();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
     // tile being computed: row group rg, superblock b; the staged window
     // starts at superblock cb
@@ -651,11 +674,17 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_kernel(SmA
     const int gl_last = owner(rg_last * nb, a.T, a.G);
     const int gh_last = owner(rg_last * nb + nb - 1, a.T, a.G);
     // the window of superblocks cb, cb + 1, ... (mod nb) the range touches
-    if (t0 < t1) {
+    {
+        // the host sizes the grid so that every workgroup has tiles (t0 < t1)
         const int w = t1 - t0;  // at most nb
         const int n1 = min(w, nb - cb);
-        stage_chunk<false, stage_batch(C::kWaves)>(a, cb, n1, xs);
-        if (w > n1) stage_chunk<false, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1);
+        if constexpr (C::kWaves >= 16) {  // one light staging round: weights first
+            ring_prologue();
+            stage_chunk<false, stage_batch(C::kWaves)>(a, cb, n1, xs, 0, [] {});
+        } else {
+            stage_chunk<false, stage_batch(C::kWaves)>(a, cb, n1, xs, 0, ring_prologue);
+        }
+        if (w > n1) stage_chunk<false, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1, [] {});
         __syncthreads();
     }
     // One step: compute the tiles in ring slot u.
@@ -906,11 +935,13 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_q4_kernel(
     };
     constexpr int R = DEPTH + 1;
     Set ring[R];
+    auto ring_prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-        ring[i] = load_next();
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int i = 0; i < DEPTH; ++i) {
+            ring[i] = load_next();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
     int t = t0, rg = t0 / nb, b = t0 - rg * nb;
     const int cb = b;
@@ -924,11 +955,17 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_q4_kernel(
     const int gh_first = owner(rg_first * nb + nb - 1, a.T, a.G);
     const int gl_last = owner(rg_last * nb, a.T, a.G);
     const int gh_last = owner(rg_last * nb + nb - 1, a.T, a.G);
-    if (t0 < t1) {
+    {
+        // the host sizes the grid so that every workgroup has tiles (t0 < t1)
         const int w = t1 - t0;
         const int n1 = min(w, nb - cb);
-        stage_chunk<true, stage_batch(C::kWaves)>(a, cb, n1, xs);
-        if (w > n1) stage_chunk<true, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1);
+        if constexpr (C::kWaves >= 16) {  // one light staging round: weights first
+            ring_prologue();
+            stage_chunk<true, stage_batch(C::kWaves)>(a, cb, n1, xs, 0, [] {});
+        } else {
+            stage_chunk<true, stage_batch(C::kWaves)>(a, cb, n1, xs, 0, ring_prologue);
+        }
+        if (w > n1) stage_chunk<true, stage_batch(C::kWaves)>(a, 0, w - n1, xs, n1, [] {});
         __syncthreads();
     }
     auto step = [&](const Set &u) __attribute__((always_inline)) {
