@@ -1156,7 +1156,7 @@ const char *variant_names()
     return "q4k/q5k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged,group<=4] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged,group<=4] "
            "embedding[q4k,q5k] "
            "gate_up[q4k, mid staged out: 0/16/32] "
-           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; q4k: per-lane weight loads, sub-block scale folded into B; q6k: weight tiles through LDS; m<=8: 16 waves x 1 16-row tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
+           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; q4k: per-lane weight loads, sub-block scale folded into B, 16 waves x 1 16-row tile; q6k: weight tiles through LDS, m<=8: 16 waves x 1 tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

@@ -364,11 +364,11 @@ __device__ __forceinline__ void sb_mma(const Q6Sb (&u)[NS], const uint8_t *__res
 //
 // `after_loads` runs once in every wave, right after the wave's first round of
 // loads is issued (the first round's loads are unconditional; a wave without
-// groups re-reads the last one).  With 8 waves (16 activation rows, a heavy
-// staging) the kernel issues its first weight loads there, behind the
+// groups re-reads the last one).  With 8 waves (Q6_K at 9..16 activation rows,
+// a heavy staging) the kernel issues its first weight loads there, behind the
 // activations, so that the conversion waits for the activations only and the
-// weights stream in meanwhile (Q6_K at M = 16: 47 us against 49-50 us); with
-// 16 waves the staging is one light round and the weights go first.
+// weights stream in meanwhile; with 16 waves the staging is one light round
+// and the weights go first.
 template <bool Q4, int BL, typename F>
 __device__ __forceinline__ void stage_chunk(const SmArgs &a, int cb, int n, uint8_t *smem,
                                             int so, F &&after_loads)
@@ -577,8 +577,8 @@ __device__ __forceinline__ void finish_segment(const SmArgs &a, int rg, int gl, 
 // most two row groups (segments).
 constexpr int kMaxSegs = 2;
 // Staging rounds (8 groups of 256 inputs each) a wave loads at once: with 16
-// waves (m <= 8) one covers the 8 rows x 8 superblocks of the verify window,
-// with 8 waves two cover its 16 rows x 8 superblocks
+// waves one covers 16 rows x 8 superblocks of the verify window, with 8 waves
+// (Q6_K, m > 8) two do
 constexpr int stage_batch(int waves) { return waves >= 16 ? 1 : 2; }
 
 // The workgroup stages the activations of every superblock its range touches
@@ -782,10 +782,13 @@ struct SmQ4Cfg {
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kDepth = DEPTH;  // superblock steps in flight ahead
 };
-using SmQ4Narrow = SmQ4Cfg<1, 16, 2>;  // m <= 8
-using SmQ4Wide = SmQ4Cfg<2, 8, 2>;     // m >= 9
-static_assert(16 * SmQ4Narrow::kSub * SmQ4Narrow::kWaves == kSmRows, "row group");
-static_assert(16 * SmQ4Wide::kSub * SmQ4Wide::kWaves == kSmRows, "row group");
+// Every m: 16 waves of one tile.  Q4_K keeps no weights in LDS, so the staged
+// window of 16 activation rows still fits beside nothing else, and 16 waves
+// stage it in one light round; measured at 19968 x 6656 against 8 waves of
+// two tiles (which share each A operand): M = 12 29.0-29.4 us against 31.9,
+// M = 16 31.1-31.3 us against 32.8-32.9, M <= 8 the same kernel.
+using SmQ4 = SmQ4Cfg<1, 16, 2>;
+static_assert(16 * SmQ4::kSub * SmQ4::kWaves == kSmRows, "row group");
 
 
 struct Q4Own {
@@ -1021,7 +1024,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_q4_kernel(
 struct SmPlan {
     int nb, T, G, CH, RS, part_off, flag_off, xs_off;
     size_t lds, ws;
-    bool narrow;  // the SmNarrow launch shape (m <= 8)
+    bool narrow;  // the 16-wave launch shape (Q4_K, and Q6_K with m <= 8)
 };
 
 int sm_cus()
@@ -1045,7 +1048,7 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
-    p.narrow = m <= 8;
+    p.narrow = qtype == 1 || m <= 8;  // the 16-wave shape
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 1024 : 0);  // LDS bytes per staged superblock
     // Q6_K: the waves' weight tiles first; Q4_K keeps no weights in LDS
     p.xs_off = qtype == 1 ? 0 : (p.narrow ? SmNarrow::kWaves : SmWide::kWaves) * kQ6TileLds;
@@ -1125,8 +1128,7 @@ hipError_t launch_plan(const SmPlan &p, int qtype, const uint8_t *W, const float
         return hipGetLastError();                                                             \
     }
     if (qtype == 1) {
-        if (p.narrow) KQ_SM_Q4_GO(SmQ4Narrow)
-        KQ_SM_Q4_GO(SmQ4Wide)
+        KQ_SM_Q4_GO(SmQ4)
     }
     if (p.narrow) KQ_SM_GO(Q6Tile, SmNarrow)
     KQ_SM_GO(Q6Tile, SmWide)
@@ -1177,8 +1179,7 @@ void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
     out[1] = p.CH;
     out[2] = (int64_t)p.lds;
     out[3] = (int64_t)p.ws;
-    out[4] = qtype == 1 ? (p.narrow ? SmQ4Narrow::kThreads : SmQ4Wide::kThreads)
-                        : (p.narrow ? SmNarrow::kThreads : SmWide::kThreads);
+    out[4] = qtype == 1 ? SmQ4::kThreads : (p.narrow ? SmNarrow::kThreads : SmWide::kThreads);
     out[5] = p.T;
 }
 
