@@ -1024,7 +1024,7 @@ __global__ void __launch_bounds__(C::kThreads, C::kWaves / 4) small_m_q4_kernel(
 struct SmPlan {
     int nb, T, G, CH, RS, part_off, flag_off, xs_off;
     size_t lds, ws;
-    bool narrow;  // the 16-wave launch shape (Q4_K, and Q6_K with m <= 8)
+    bool narrow;  // the 16-wave launch shape
 };
 
 int sm_cus()
@@ -1048,8 +1048,16 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
     p.nb = k / 256;
     const int rgs = (n_rows + kSmRows - 1) / kSmRows;
     p.T = rgs * p.nb;
-    p.narrow = qtype == 1 || m <= 8;  // the 16-wave shape
     const int per_sb = 1024 * m + 64 + (qtype == 1 ? 1024 : 0);  // LDS bytes per staged superblock
+    // the 16-wave shape: always for Q4_K; for Q6_K when the window of a
+    // one-round grid still fits LDS beside 16 waves' weight tiles (up to
+    // m = 12 at the verify shape), else 8 waves of two tiles
+    {
+        const int64_t g1 = p.T < cus ? p.T : cus;
+        const int64_t need = (p.T + g1 - 1) / g1;
+        const int64_t fit16 = (kSmLdsMax - SmNarrow::kWaves * kQ6TileLds - 16 - 32 * m) / per_sb;
+        p.narrow = qtype == 1 || m <= 8 || fit16 >= (need < p.nb ? need : p.nb);
+    }
     // Q6_K: the waves' weight tiles first; Q4_K keeps no weights in LDS
     p.xs_off = qtype == 1 ? 0 : (p.narrow ? SmNarrow::kWaves : SmWide::kWaves) * kQ6TileLds;
     int ch = (kSmLdsMax - p.xs_off - 16 - 32 * m) / per_sb;  // superblocks that fit
