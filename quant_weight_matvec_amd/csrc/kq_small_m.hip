@@ -38,7 +38,8 @@
 //   range touches into LDS once, before its loop (hi and lo planes, each
 //   4-group of inputs stored in the order 0,2,1,3 to match how the quant bytes
 //   unpack into f16 pairs); the grid is sized so that every range fits.  The
-//   first weight loads are issued before the staging, so HBM keeps streaming.
+//   first weight loads go out with the staging's first loads (before them with
+//   16 waves, right after them with 8), so HBM keeps streaming.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -66,11 +67,13 @@ typedef uint32_t u32_a2 __attribute__((aligned(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Q6_K launch shapes, one workgroup per CU, 256-row groups either way:
-// * up to 8 activation rows: 16 waves of one 16-row tile each (4 waves per
-//   SIMD hide more latency; the kernel fits 128 VGPRs);
-// * 9 to 16 rows: 8 waves of two tiles each, which share every activation
-//   operand they read, so a range of 8 superblocks of 16 activation rows still
-//   fits LDS beside the weight tiles.
+// * 16 waves of one 16-row tile each (4 waves per SIMD hide more latency; the
+//   kernel fits 128 VGPRs) whenever the staged window of a one-round grid fits
+//   LDS beside their 16 weight tiles: up to 8 activation rows always, up to 12
+//   at the verify shape;
+// * otherwise 8 waves of two tiles each, which share every activation operand
+//   they read, so a range of 8 superblocks of 16 activation rows still fits
+//   LDS beside the weight tiles.
 template <int SUB, int WAVES, int DEPTH>
 struct SmCfg {
     static constexpr int kSub = SUB;      // 16-row tiles per wave
@@ -78,9 +81,9 @@ struct SmCfg {
     static constexpr int kThreads = 64 * WAVES;
     static constexpr int kDepth = DEPTH;  // tile sets in flight ahead
 };
-using SmNarrow = SmCfg<1, 16, 1>;  // m <= 8
-using SmWide = SmCfg<2, 8, 1>;     // m >= 9
-constexpr int kSmRows = 256;          // rows per row group: 16 kSub kWaves in both shapes
+using SmNarrow = SmCfg<1, 16, 1>;  // the 16-wave shape
+using SmWide = SmCfg<2, 8, 1>;     // the 8-wave shape
+constexpr int kSmRows = 256;          // rows per row group: 16 kSub kWaves in every shape
 static_assert(16 * SmNarrow::kSub * SmNarrow::kWaves == kSmRows, "row group");
 static_assert(16 * SmWide::kSub * SmWide::kWaves == kSmRows, "row group");
 constexpr uint32_t kBias = 0x64006400u;  // f16 1024.0 in both halves
@@ -199,8 +202,10 @@ __device__ __forceinline__ void tile_rows(TileAddr<U> &ta, int rg, int slice, in
 __device__ __forceinline__ Q6Tile load_tile(const uint8_t *__restrict__ W, const TileAddr<Q6Tile> &ta,
                                             int b, int lane)
 {
-    // Unconditional loads, as for Q4_K.  The tail is one dword at sb+206
-    // (2-byte aligned, inside the superblock): the last two scales, needed
+    // Every lane loads (a lane past the tile's last piece re-reads that piece;
+    // store_tile drops it): no branch between the loads and their use.  The
+    // tail is one dword at sb+206 (2-byte aligned, inside the superblock): the
+    // last two scales, needed
     // when a = sb - 2 and already in the pieces when a = sb, then d.
     // store_tile picks the word [a + 208, a + 212) the pieces would have
     // continued with (not here: touching loaded data at load time would wait
@@ -783,13 +788,12 @@ struct SmQ4Cfg {
     static constexpr int kDepth = DEPTH;  // superblock steps in flight ahead
 };
 // Every m: 16 waves of one tile.  Q4_K keeps no weights in LDS, so the staged
-// window of 16 activation rows still fits beside nothing else, and 16 waves
+// window of 16 activation rows fits whatever the wave count, and 16 waves
 // stage it in one light round; measured at 19968 x 6656 against 8 waves of
 // two tiles (which share each A operand): M = 12 29.0-29.4 us against 31.9,
 // M = 16 31.1-31.3 us against 32.8-32.9, M <= 8 the same kernel.
 using SmQ4 = SmQ4Cfg<1, 16, 2>;
 static_assert(16 * SmQ4::kSub * SmQ4::kWaves == kSmRows, "row group");
-
 
 struct Q4Own {
     u32x4 hdr;  // d, dmin, 12 bytes of packed 6-bit scales and mins
