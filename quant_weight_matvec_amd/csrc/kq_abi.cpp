@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <string>
+
 #include "kq.h"
 #include "kq_tune.h"
 #include "kq_internal.h"
@@ -576,15 +578,15 @@ const char *kq_status_string(kq_status s)
 
 const char *kq_build_info(void)
 {
-    static char buf[512];
-    static int done = 0;
-    if (!done) {
+    // built once, thread-safely (function-local static initialisation)
+    static const std::string info = [] {
+        char buf[512];
         snprintf(buf, sizeof buf, "libkq target=gfx950 hip=%d.%d.%d git=%s variants: %s",
                  HIP_VERSION_MAJOR, HIP_VERSION_MINOR, HIP_VERSION_PATCH, KQ_GIT_SHA,
                  kqi::variant_names());
-        done = 1;
-    }
-    return buf;
+        return std::string(buf);
+    }();
+    return info.c_str();
 }
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)

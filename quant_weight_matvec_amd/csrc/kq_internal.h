@@ -5,7 +5,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kqi {
+
+// Process-wide per-device state covers devices 0 .. kMaxDevices - 1.
+constexpr int kMaxDevices = 64;
+// The current device's compute-unit count (256 if it cannot be read), cached
+// per device; safe from several host threads.
+int device_cus();
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device, once
+// per device (`done` holds one bit per device and belongs to that kernel);
+// safe from several host threads (two may both set the same attribute).
+hipError_t raise_lds_limit(const void *kernel, std::atomic<uint64_t> &done, int bytes);
 
 // Launch shape of a matvec: `lanes` lanes cooperate on one weight row, a
 // workgroup has `waves` wavefronts, and `grid` workgroups split the rows into

@@ -727,26 +727,9 @@ __global__ void read_probe_kernel(const u32x4 *__restrict__ p, int64_t n16,
 
 // ---------------------------------------------------------------------------
 // Host side: launch shapes.
-struct DevInfo {
-    int cus = 0;
-};
-
-DevInfo g_dev[64];
 kqi::MatvecShape g_override[4] = {};
 
-int device_cus()
-{
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (g_dev[dev].cus == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        g_dev[dev].cus = cus;
-    }
-    return g_dev[dev].cus;
-}
+int device_cus() { return kqi::device_cus(); }
 
 // Pick lanes-per-row, waves per workgroup, grid and depth for a matvec from
 // the shapes measured best on MI355X at the FFN sizes (below).  Depth 2 (one
@@ -819,12 +802,9 @@ kqi::MatvecShape choose_shape(int qtype, int64_t n_rows, int units, int cus, boo
 template <auto KERN>
 hipError_t allow_lds(size_t bytes)
 {
-    static int done = 0;
-    if (bytes <= 65536 || done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e == hipSuccess) done = 1;
-    return e;
+    static std::atomic<uint64_t> done{0};
+    if (bytes <= 65536) return hipSuccess;
+    return kqi::raise_lds_limit(reinterpret_cast<const void *>(KERN), done, 160 * 1024);
 }
 
 template <int GROUP>
@@ -959,6 +939,33 @@ MatSegs one_seg(const uint8_t *W, float *y, int n_rows)
 }  // namespace
 
 namespace kqi {
+
+int device_cus()
+{
+    static std::atomic<int> cus[kMaxDevices];  // static storage: starts at zero
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int c = cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+hipError_t raise_lds_limit(const void *kernel, std::atomic<uint64_t> &done, int bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < kMaxDevices) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 void set_shape_override(int qtype, MatvecShape s)
 {

@@ -1031,20 +1031,7 @@ struct SmPlan {
     bool narrow;  // the 16-wave launch shape
 };
 
-int sm_cus()
-{
-    static int cached = 0;
-    if (!cached) {
-        int dev = 0, c = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            c > 0)
-            cached = c;
-        else
-            cached = 256;
-    }
-    return cached;
-}
+int sm_cus() { return kqi::device_cus(); }
 
 SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
 {
@@ -1090,10 +1077,8 @@ SmPlan make_plan(int qtype, int n_rows, int k, int m, int cus)
 template <auto KERN>
 hipError_t allow_lds()
 {
-    static hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(KERN),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                              kSmLdsMax);
-    return e;
+    static std::atomic<uint64_t> done{0};
+    return kqi::raise_lds_limit(reinterpret_cast<const void *>(KERN), done, kSmLdsMax);
 }
 
 // The plan's launch, with the partial tiles at byte part_off of ws (counters
