@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -97,16 +98,80 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-GATE_UP_SOURCES = ("kq_kernels.hip", "kq_device.h")
+LIB_PATH = os.path.join(ROOT, "quant_weight_matvec_amd", "libkq.so")
+# instantiations whose machine code a committed counter summary covers
+PMC_KERNELS = {"gate_up": "q4k_gate_up_kernel", "down": "q6k_matvec_kernel"}
 
 
-def kernel_source_hash(files=GATE_UP_SOURCES) -> str:
-    """Hash of the sources a kernel's machine code is built from; a committed
-    counter summary is used only while it matches."""
+def _elf_sections(elf: bytes):
+    """Section headers of a little-endian ELF64 image: name, type, addr, offset, size, link."""
+    shoff = struct.unpack_from("<Q", elf, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    secs = []
+    for i in range(shnum):
+        name, typ, _fl, addr, off, size, link = struct.unpack_from("<IIQQQQI", elf, shoff + i * shentsize)
+        secs.append({"name_off": name, "type": typ, "addr": addr, "off": off, "size": size, "link": link})
+    names = secs[shstrndx]["off"]
+    for sec in secs:
+        start = names + sec["name_off"]
+        sec["name"] = elf[start:elf.index(b"\0", start)].decode()
+    return secs
+
+
+def kernel_code(name_part: str, lib_path: str = LIB_PATH):
+    """[(symbol, machine code bytes)] of every gfx950 kernel whose symbol
+    contains `name_part`, sorted by symbol, read from the code objects the
+    library embeds (uncompressed clang offload bundles in its .hip_fatbin
+    section); [] if the library or the section is missing."""
+    if not os.path.exists(lib_path):
+        return []
+    with open(lib_path, "rb") as f:
+        data = f.read()
+    fat = [s for s in _elf_sections(data) if s["name"] == ".hip_fatbin"]
+    if not fat:
+        return []
+    fat = data[fat[0]["off"]:fat[0]["off"] + fat[0]["size"]]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    found = []
+    pos = fat.find(magic)
+    while pos >= 0:
+        p = pos + len(magic)
+        n_entries = struct.unpack_from("<Q", fat, p)[0]
+        p += 8
+        for _ in range(n_entries):
+            off, size, tlen = struct.unpack_from("<QQQ", fat, p)
+            triple = fat[p + 24:p + 24 + tlen].decode()
+            p += 24 + tlen
+            if not triple.endswith("gfx950"):
+                continue
+            co = fat[pos + off:pos + off + size]
+            secs = _elf_sections(co)
+            for symtab in (s for s in secs if s["type"] == 2):  # SHT_SYMTAB
+                strs = secs[symtab["link"]]["off"]
+                for i in range(symtab["size"] // 24):
+                    st_name, st_info, _o, shndx, value, sz = struct.unpack_from(
+                        "<IBBHQQ", co, symtab["off"] + 24 * i)
+                    nm = co[strs + st_name:co.index(b"\0", strs + st_name)].decode()
+                    if (st_info & 0xF) == 2 and sz and name_part in nm:  # STT_FUNC
+                        sec = secs[shndx]
+                        start = sec["off"] + value - sec["addr"]
+                        found.append((nm, co[start:start + sz]))
+        pos = fat.find(magic, pos + len(magic))
+    return sorted(found)
+
+
+def kernel_code_hash(name_part: str, lib_path: str = LIB_PATH):
+    """Hash of the machine code of every kernel `kernel_code` finds. A
+    committed counter summary is used only while this matches: edits that
+    leave the kernel's code unchanged keep it valid, any change to that code
+    drops it. None if no such kernel is found."""
+    code = kernel_code(name_part, lib_path)
+    if not code:
+        return None
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "quant_weight_matvec_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for nm, body in code:
+        h.update(nm.encode())
+        h.update(body)
     return h.hexdigest()[:16]
 
 
@@ -636,15 +701,15 @@ def cpu_baseline(I, budget_s=8.0):
                                         f"pass-equivalent {d1 / r1 * LAYERS:.1f} s/token"}}
 
 
-def load_pmc(symbol_key: str, src_hash: str):
+def load_pmc(symbol_key: str, code_hash):
     """HBM traffic per launch from a committed counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the kernel's current machine code; else None."""
     path = os.path.join(ROOT, "profiles", f"pmc_{symbol_key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != src_hash:
+    if code_hash is None or d.get("kernel_code_hash") != code_hash:
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -676,7 +741,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kq.lib()
     log(kq.kq_build_info())
-    src_hash = {"gate_up": kernel_source_hash(GATE_UP_SOURCES)}
+    code_hash = {k: kernel_code_hash(v) for k, v in PMC_KERNELS.items()}
 
     if args.calibration_copy:
         # a plain copy kernel of known size: 1 GiB read, 1 GiB written
@@ -776,7 +841,7 @@ def main():
     if dk is not None:
         roofline = {"kernel": dk["symbol"], "bound": "hbm", "achieved": dk["GBps"],
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dk["frac_peak"],
-                    "traffic": load_pmc("gate_up", kernel_source_hash(GATE_UP_SOURCES)),
+                    "traffic": load_pmc("gate_up", code_hash["gate_up"]),
                     "bytes_per_launch": dk["bytes_per_launch"], "us_avg": dk["us_avg"]}
     alternatives = {
         "graph_3_launches_per_layer_staged_activations": {
@@ -842,7 +907,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "kernel_source_hash": src_hash,
+        "kernel_code_hash": code_hash,
         "build": kq.kq_build_info(),
     }
     rec.update(extras)

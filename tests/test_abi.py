@@ -406,3 +406,23 @@ def test_matvec_plans_fit():
                             (qt, k, n, cus, p, static)
     with pytest.raises(kq.KQError):
         kq.kq_tune_matvec_plan(1, 0, 1024, False, 256)
+
+
+def test_kernel_code_hash_reads_the_built_code_object():
+    """bench.py keys its committed HBM counter summaries to a hash of the
+    kernel's machine code, read with its own ELF/offload-bundle reader; the
+    kernels it finds must be the ones the LLVM tools list from the same code
+    object, and the hash must separate kernel families."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    meta = CO.kernels()
+    assert sorted(n for n, _ in bench.kernel_code("")) == sorted(meta)
+    for part in bench.PMC_KERNELS.values():
+        code = bench.kernel_code(part)
+        assert [n for n, _ in code] == sorted(n for n in meta if part in n)
+        assert all(len(body) >= 4 and len(body) % 4 == 0 for _, body in code)
+        assert bench.kernel_code_hash(part) == bench.kernel_code_hash(part)
+    hashes = {bench.kernel_code_hash(p) for p in bench.PMC_KERNELS.values()}
+    assert None not in hashes and len(hashes) == len(bench.PMC_KERNELS)
+    assert bench.kernel_code_hash("no_such_kernel_name") is None
