@@ -33,7 +33,15 @@ kq_status check_k(int64_t k)
     return KQ_OK;
 }
 
-kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_LAUNCH; }
+// the HIP error behind this thread's last KQ_ERR_LAUNCH
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+kq_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return KQ_OK;
+    g_last_hip_error = e;
+    return KQ_ERR_LAUNCH;
+}
 
 kq_status check_device()
 {
@@ -557,6 +565,8 @@ kq_status kq_fused_residual_norm_staged(float *residual, const float *projected,
                                      staged_group(next_qtype), (hipStream_t)stream));
 }
 
+const char *kq_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
 const char *kq_status_string(kq_status s)
 {
     switch (s) {
@@ -587,6 +597,48 @@ const char *kq_build_info(void)
         return std::string(buf);
     }();
     return info.c_str();
+}
+
+int64_t kq_ffn_pass_workspace_bytes(int64_t hidden, int64_t ffn)
+{
+    kq_status s = check_k(hidden);
+    if (s != KQ_OK) return s;
+    if ((s = check_k(ffn)) != KQ_OK) return s;
+    if (hidden > KQ_MAX_FUSED_TAIL_K || ffn > KQ_MAX_PASS_FFN) return KQ_ERR_UNSUPPORTED;
+    return (int64_t)kqi::pass_ws_layout((int)hidden, (int)ffn).total;
+}
+
+kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *residual,
+                              float *x_out, const float *g_entry, void *workspace,
+                              int64_t workspace_bytes, int64_t hidden, int64_t ffn,
+                              float eps_post, float eps_next, void *stream)
+{
+    if (!layers || !residual || !x_out || !workspace) return KQ_ERR_NULL;
+    if (n_layers < 1) return KQ_ERR_SHAPE;
+    const int64_t need = kq_ffn_pass_workspace_bytes(hidden, ffn);
+    if (need < 0) return (kq_status)need;
+    if (workspace_bytes < need) return KQ_ERR_SHAPE;
+    if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
+        return KQ_ERR_SHAPE;
+    if (!aligned(layers, 8) || !aligned(residual, 16) || !aligned(x_out, 16) ||
+        !aligned(g_entry, 16) || !aligned(workspace, 256))
+        return KQ_ERR_ALIGN;
+    const int64_t vb = hidden * 4, tb = (int64_t)n_layers * (int64_t)sizeof(kq_ffn_layer);
+    const void *bufs[] = {residual, x_out, g_entry, workspace, layers};
+    const int64_t lens[] = {vb, vb, g_entry ? vb : 0, workspace_bytes, tb};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(bufs[i], lens[i], bufs[j], lens[j])) return KQ_ERR_ALIAS;
+    kq_status s = check_device();
+    if (s != KQ_OK) return s;
+    return from_hip(kqi::launch_ffn_pass(layers, n_layers, residual, x_out, g_entry,
+                                         (uint8_t *)workspace, (int)hidden, (int)ffn, eps_post,
+                                         eps_next, (hipStream_t)stream));
+}
+
+kq_status kq_tune_set_pass(int waves, int depth_gate_up, int depth_down)
+{
+    return kqi::set_pass_variant(waves, depth_gate_up, depth_down) ? KQ_OK : KQ_ERR_UNSUPPORTED;
 }
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)

@@ -107,10 +107,13 @@ constexpr int kMinExp = -100;
 // all out of it, since n4 is a multiple of TPG).  Per input the rounding error
 // is at most 2^(e - QB - 1) <= 2^-QB * max|x over the group|, e the exponent
 // with max|x| < 2^e.
-template <int GROUP, int LIMBS>
+// With AGENT the stores are agent-scope (coherent across the XCDs' L2s), for
+// a staged vector that other workgroups of the same launch read.
+template <int GROUP, int LIMBS, bool AGENT = false>
 __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict__ plane, int n4,
                                             float *__restrict__ tscale, float *__restrict__ tsum)
 {
+    #pragma clang fp contract(off)
     constexpr int TPG = GROUP / 4;  // threads per group, one float4 each
     constexpr int QB = limb_bits<LIMBS>();
     const float mx = group_max<TPG>(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -150,12 +153,24 @@ __device__ __forceinline__ void stage_group(f32x4 v, int i, uint32_t *__restrict
     // plane, in the scale and sum tables, so nothing is stored.
     if (i >= n4) return;
     const int pw = n4 + (n4 >> 3), wi = i + ((i >> 5) << 2);
+    if constexpr (AGENT) {
 #pragma unroll
-    for (int l = 0; l < LIMBS; ++l) plane[l * pw + wi] = pk[l];
-    if ((i & (TPG - 1)) == 0) {
-        const int g = i / TPG;
-        tscale[g] = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
-        tsum[g] = sm;
+        for (int l = 0; l < LIMBS; ++l)
+            __hip_atomic_store(plane + l * pw + wi, pk[l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((i & (TPG - 1)) == 0) {
+            const int g = i / TPG;
+            const float sc = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
+            __hip_atomic_store(tscale + g, sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(tsum + g, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l) plane[l * pw + wi] = pk[l];
+        if ((i & (TPG - 1)) == 0) {
+            const int g = i / TPG;
+            tscale[g] = isfinite(sm) ? ldexpf(1.0f, e - QB) : __builtin_nanf("");
+            tsum[g] = sm;
+        }
     }
 }
 
@@ -271,20 +286,20 @@ __device__ __forceinline__ void stage_activation(const float *__restrict__ x, in
 // run of consecutive lanes holds float4 number i = i0 + t of the vector (k
 // values), and whole scale groups of lanes take part.  Output layout as in
 // LDS, at `out` in global memory.
-template <int GROUP, int LIMBS>
+template <int GROUP, int LIMBS, bool AGENT = false>
 __device__ __forceinline__ void stage_group_global(f32x4 v, int i, uint8_t *__restrict__ out, int k)
 {
     uint32_t *plane = reinterpret_cast<uint32_t *>(out);
     float *tscale = reinterpret_cast<float *>(out + LIMBS * plane_bytes(k));
     float *tsum = tscale + k / GROUP;
-    stage_group<GROUP, LIMBS>(v, i, plane, k >> 2, tscale, tsum);
+    stage_group<GROUP, LIMBS, AGENT>(v, i, plane, k >> 2, tscale, tsum);
 }
 
 template <int LIMBS>
 __device__ __forceinline__ float combine_limbs(const int *acc)
 {
-    if constexpr (LIMBS == 3)
-        return (float)acc[0] * 65536.0f + (float)(acc[1] * 256 + acc[2]);
+    if constexpr (LIMBS == 3)  // (the product is exact: one rounding either way)
+        return __builtin_fmaf((float)acc[0], 65536.0f, (float)(acc[1] * 256 + acc[2]));
     else
         return (float)(acc[0] * 256 + acc[1]);
 }
@@ -372,6 +387,7 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
                                              const float *__restrict__ tscale,
                                              const float *__restrict__ tsum)
 {
+    #pragma clang fp contract(off)
     // 6-bit scales and mins of sub-blocks 4h..4h+3, one per byte.
     const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
     // both halves' forms, then a per-lane select: a branch on h would split
@@ -425,7 +441,10 @@ __device__ __forceinline__ float q4_unit_dot(const Q4Unit &u, int h, int base, i
         const float sc = (float)((scb >> (8 * s)) & 0xFFu);
         const float mn = (float)((mnb >> (8 * s)) & 0xFFu);
         const float v = combine_limbs<LIMBS>(acc[s]);
-        out += (d * sc) * (gs[s] * v) - (dmin * mn) * gm[s];
+        // one fused multiply-add per sub-block (gs * v is exact: a power of
+        // two times an integer), then a plain add: the rounding does not
+        // depend on how the compiler contracts the expression
+        out += __builtin_fmaf(d * sc, gs[s] * v, -((dmin * mn) * gm[s]));
     }
     return out;
 }
@@ -465,6 +484,7 @@ __device__ __forceinline__ float q5_unit_dot(const Q5Unit &u, int h, int base, i
                                              const float *__restrict__ tscale,
                                              const float *__restrict__ tsum)
 {
+    #pragma clang fp contract(off)
     const uint32_t S0 = u.hdr.y, S1 = u.hdr.z, S2 = u.hdr.w;
     const uint32_t sc_lo = S0 & 0x3F3F3F3Fu, mn_lo = S1 & 0x3F3F3F3Fu;
     const uint32_t sc_hi = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
@@ -517,7 +537,10 @@ __device__ __forceinline__ float q5_unit_dot(const Q5Unit &u, int h, int base, i
         const float sc = (float)((scb >> (8 * s)) & 0xFFu);
         const float mn = (float)((mnb >> (8 * s)) & 0xFFu);
         const float v = combine_limbs<LIMBS>(acc[s]);
-        out += (d * sc) * (gs[s] * v) - (dmin * mn) * gm[s];
+        // one fused multiply-add per sub-block (gs * v is exact: a power of
+        // two times an integer), then a plain add: the rounding does not
+        // depend on how the compiler contracts the expression
+        out += __builtin_fmaf(d * sc, gs[s] * v, -((dmin * mn) * gm[s]));
     }
     return out;
 }
@@ -596,12 +619,16 @@ __device__ __forceinline__ uint32_t realign(uint32_t hi, uint32_t lo, int shift)
     return __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)shift);
 }
 
-template <int LIMBS>
+// SPLIT keeps the two halves of the unit apart in the schedule (the second
+// half's LDS reads are not hoisted into the first), for kernels that cannot
+// give the dot product the registers of both halves at once.
+template <int LIMBS, bool SPLIT = false>
 __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
                                              const uint8_t *__restrict__ planes,
                                              const float *__restrict__ tscale,
                                              const float *__restrict__ tsum)
 {
+    #pragma clang fp contract(off)
     const int sh = u.shift;
     // the unit's 128 inputs lie inside one padded 128-input run of each plane
     const int P = (int)plane_bytes(k);
@@ -631,6 +658,7 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
     float out = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
+        if constexpr (SPLIT) __builtin_amdgcn_sched_barrier(0);
         int acc[4][LIMBS];
 #pragma unroll
         for (int g = 0; g < 4; ++g)
@@ -663,7 +691,10 @@ __device__ __forceinline__ float q6_unit_dot(const Q6Unit &u, int base, int k,
             const float gsc = (li < 4) ? gsA[li] : gsB[li - 4];
             const float gsum = (li < 4) ? gmA[li] : gmB[li - 4];
             const float v = combine_limbs<LIMBS>(acc[g]);
-            out += (d * (float)scv) * (gsc * v - 32.0f * gsum);
+            // written as fused multiply-adds (gsc * v is exact, a power of
+            // two times an integer), so that the rounding does not depend on
+            // how the compiler schedules or contracts the expression
+            out = __builtin_fmaf(d * (float)scv, __builtin_fmaf(gsc, v, -32.0f * gsum), out);
         }
     }
     return out;
@@ -716,9 +747,50 @@ __device__ __forceinline__ float block_sum_fixed(float v, float *red)
     return block_sum_fresh(v, red);
 }
 
+// The tail's floating-point steps are written as explicit fused
+// multiply-adds, with contraction off inside the helpers (as in the dot
+// products and the encode), so that every kernel that runs a tail
+// (standalone, fused into gate+up, or inside the one-launch pass) rounds the
+// same way: a product a helper returns is rounded before any caller adds it
+// (the compiler would otherwise fuse it into the caller's next addition where
+// it has no other use, and not where it does).
 __device__ __forceinline__ float sumsq4(f32x4 v)
 {
-    return v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    #pragma clang fp contract(off)
+    return __builtin_fmaf(v.w, v.w, __builtin_fmaf(v.z, v.z, __builtin_fmaf(v.x, v.x, v.y * v.y)));
+}
+
+// ---------------------------------------------------------------------------
+// The dual-eps tail in registers: up to kTailVec float4 per thread, whole
+// waves, rows up to kTailRegMax wide.  tail_threads(n) is the block size of
+// the standalone tail; the fused form (q4k_gate_up_kernel with TAIL) lays its
+// threads out the same way so that both sum in the same order.  Beyond four
+// waves the count is rounded up to a multiple of four, so each of a CU's four
+// SIMDs runs the same number of tail waves (the encode at the end is VALU
+// work, and the workgroup waits for its busiest SIMD).
+constexpr int kTailVec = 4;
+constexpr int kTailThreads = 512;
+constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
+
+__host__ __device__ constexpr int tail_threads(int n)
+{
+    const int w = ((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64);  // waves needed
+    return 64 * (w <= 1 ? 1 : (w <= 4 ? w : (w + 3) / 4 * 4));
+}
+
+// r + rms-normed p times the post gain, and the next input, one float4 each
+__device__ __forceinline__ f32x4 tail_add(f32x4 r, f32x4 p, float inv_p, f32x4 g)
+{
+    #pragma clang fp contract(off)
+    const f32x4 q = p * inv_p;
+    return {__builtin_fmaf(q.x, g.x, r.x), __builtin_fmaf(q.y, g.y, r.y),
+            __builtin_fmaf(q.z, g.z, r.z), __builtin_fmaf(q.w, g.w, r.w)};
+}
+
+__device__ __forceinline__ f32x4 tail_next(f32x4 r, float inv_r, f32x4 g)
+{
+    #pragma clang fp contract(off)
+    return (r * inv_r) * g;
 }
 
 }  // namespace kqd

@@ -43,34 +43,6 @@ using namespace kqd;
 // workgroup: 80 / WMAX float4 per thread cover k = 20480 in one round trip.
 constexpr int kXPre = 80;
 
-// The dual-eps tail in registers: up to kTailVec float4 per thread, whole
-// waves, rows up to kTailRegMax wide.  tail_threads(n) is the block size of
-// the standalone tail; the fused form (q4k_gate_up_kernel with TAIL) lays its
-// threads out the same way so that both sum in the same order.  Beyond four
-// waves the count is rounded up to a multiple of four, so each of a CU's four
-// SIMDs runs the same number of tail waves (the encode at the end is VALU
-// work, and the workgroup waits for its busiest SIMD).
-constexpr int kTailVec = 4;
-constexpr int kTailThreads = 512;
-constexpr int kTailRegMax = 4 * kTailVec * kTailThreads;  // 8192
-
-__host__ __device__ constexpr int tail_threads(int n)
-{
-    const int w = ((n >> 2) + kTailVec * 64 - 1) / (kTailVec * 64);  // waves needed
-    return 64 * (w <= 1 ? 1 : (w <= 4 ? w : (w + 3) / 4 * 4));
-}
-
-// r + rms-normed p times the post gain, and the next input, one float4 each
-__device__ __forceinline__ f32x4 tail_add(f32x4 r, f32x4 p, float inv_p, f32x4 g)
-{
-    return r + (p * inv_p) * g;
-}
-
-__device__ __forceinline__ f32x4 tail_next(f32x4 r, float inv_r, f32x4 g)
-{
-    return (r * inv_r) * g;
-}
-
 // The previous layer's tail, fused into the gate+up kernel's prologue
 // (Ch 10 "The forward pass at a glance", section 10.3: the tail's second
 // output is the next layer's input).
@@ -311,7 +283,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
 #pragma unroll
         for (int j = 0; j < kTailVec; ++j) ss += sumsq4(tp[j]);
         ss = block_sum_fresh(ss, red[0]);
-        const float inv_p = rsqrtf(ss * inv_n + tl.eps_post);
+        const float inv_p = rsqrtf(__builtin_fmaf(ss, inv_n, tl.eps_post));
         float sr = 0.0f;
 #pragma unroll
         for (int j = 0; j < kTailVec; ++j) {
@@ -323,7 +295,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         }
         sr = block_sum_fresh(sr, red[1]);
         ring_prologue();
-        const float inv_r = rsqrtf(sr * inv_n + tl.eps_next);
+        const float inv_r = rsqrtf(__builtin_fmaf(sr, inv_n, tl.eps_next));
         uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
         float *tsc = reinterpret_cast<float *>(smem + LIMBS * plane_bytes(k));
 #pragma unroll
@@ -546,7 +518,7 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
     float ss = 0.0f;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) ss += sumsq4(p4[i]);
     ss = block_sum_fresh(ss, red[0]);
-    const float inv_p = rsqrtf(ss * inv_n + eps_post);
+    const float inv_p = rsqrtf(__builtin_fmaf(ss, inv_n, eps_post));
 
     float sr = 0.0f;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) {
@@ -555,7 +527,7 @@ __global__ __launch_bounds__(1024) void tail_kernel(float *__restrict__ residual
         sr += sumsq4(v);
     }
     sr = block_sum_fresh(sr, red[1]);
-    const float inv_r = rsqrtf(sr * inv_n + eps_next);
+    const float inv_r = rsqrtf(__builtin_fmaf(sr, inv_n, eps_next));
 
     uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
     for (int i = threadIdx.x; i < n4; i += blockDim.x) {
@@ -600,7 +572,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
 #pragma unroll
     for (int j = 0; j < kTailVec; ++j) ss += sumsq4(pv[j]);
     ss = block_sum_fresh(ss, red[0]);
-    const float inv_p = rsqrtf(ss * inv_n + eps_post);
+    const float inv_p = rsqrtf(__builtin_fmaf(ss, inv_n, eps_post));
 
     float sr = 0.0f;
 #pragma unroll
@@ -611,7 +583,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_reg_kernel(
         sr += sumsq4(rv[j]);
     }
     sr = block_sum_fresh(sr, red[1]);
-    const float inv_r = rsqrtf(sr * inv_n + eps_next);
+    const float inv_r = rsqrtf(__builtin_fmaf(sr, inv_n, eps_next));
     uint8_t *xs = xs_out ? xs_out + (int64_t)blockIdx.x * tail_staged_bytes(n, xs_group) : nullptr;
 #pragma unroll
     for (int j = 0; j < kTailVec; ++j) {

@@ -426,3 +426,52 @@ def test_kernel_code_hash_reads_the_built_code_object():
     hashes = {bench.kernel_code_hash(p) for p in bench.PMC_KERNELS.values()}
     assert None not in hashes and len(hashes) == len(bench.PMC_KERNELS)
     assert bench.kernel_code_hash("no_such_kernel_name") is None
+
+
+def test_ffn_pass_validation():
+    """kq_ffn_pass_q4k_q6k rejects bad arguments on the host (the layer table
+    itself is device memory and is not read here)."""
+    L, R, XO, GE, WS = 0x100000, 0x200000, 0x300000, 0x400000, 0x1000000
+    h, f = 6656, 19968
+    need = kq.kq_ffn_pass_workspace_bytes(h, f)
+    # counters (512 B), two [hidden] f32 buffers, staged mid for Q6_K, each
+    # region rounded up to 256 bytes
+    up = lambda b: (b + 255) // 256 * 256
+    assert need == 512 + 2 * up(4 * h) + up(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f))
+
+    def call(layers=L, n=52, r=R, xo=XO, ge=None, ws=WS, wsb=need, hidden=h, ffn=f,
+             ep=1e-8, en=1e-5):
+        return kq.lib().kq_ffn_pass_q4k_q6k(layers, n, r, xo, ge, ws, wsb, hidden, ffn, ep, en,
+                                            None)
+
+    assert call(layers=None) == B.KQ_ERR_NULL
+    assert call(r=None) == B.KQ_ERR_NULL
+    assert call(xo=None) == B.KQ_ERR_NULL
+    assert call(ws=None) == B.KQ_ERR_NULL
+    assert call(n=0) == B.KQ_ERR_SHAPE
+    assert call(hidden=300) == B.KQ_ERR_SHAPE
+    assert call(ffn=1000) == B.KQ_ERR_SHAPE
+    assert call(hidden=B.KQ_MAX_FUSED_TAIL_K + 256) == B.KQ_ERR_UNSUPPORTED
+    assert call(ffn=B.KQ_MAX_PASS_FFN + 256) == B.KQ_ERR_UNSUPPORTED
+    assert call(wsb=need - 1) == B.KQ_ERR_SHAPE
+    assert call(ep=-1.0) == B.KQ_ERR_SHAPE
+    assert call(en=float("inf")) == B.KQ_ERR_SHAPE
+    assert call(layers=L + 4) == B.KQ_ERR_ALIGN
+    assert call(r=R + 4) == B.KQ_ERR_ALIGN
+    assert call(xo=XO + 8) == B.KQ_ERR_ALIGN
+    assert call(ge=GE + 4) == B.KQ_ERR_ALIGN
+    assert call(ws=WS + 128) == B.KQ_ERR_ALIGN
+    assert call(xo=R + 16) == B.KQ_ERR_ALIAS              # x_out inside residual
+    assert call(ge=XO) == B.KQ_ERR_ALIAS                  # g_entry is x_out
+    assert call(ws=R - 256) == B.KQ_ERR_ALIAS             # workspace covers residual
+    assert call(layers=WS + need - 8) == B.KQ_ERR_ALIAS   # table inside the workspace
+    # every check passed: only the device is missing here
+    assert call(ge=GE) in (B.KQ_ERR_DEVICE, B.KQ_ERR_LAUNCH, B.KQ_OK)
+    with pytest.raises(kq.KQError):
+        kq.kq_ffn_pass_workspace_bytes(100, f)
+    with pytest.raises(kq.KQError):
+        kq.kq_ffn_pass_workspace_bytes(h, B.KQ_MAX_PASS_FFN + 256)
+    assert kq.lib().kq_tune_set_pass(8, 2, 2) == B.KQ_OK
+    assert kq.lib().kq_tune_set_pass(12, 2, 1) == B.KQ_OK
+    assert kq.lib().kq_tune_set_pass(7, 2, 2) == B.KQ_ERR_UNSUPPORTED
+    assert kq.lib().kq_tune_set_pass(0, 0, 0) == B.KQ_OK
