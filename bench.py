@@ -74,8 +74,8 @@ STAGED_BYTES = {
     "down_staged": q6k_bytes(HIDDEN, FFN) + staged_bytes(16, FFN) + 4 * HIDDEN,
     "tail_staged": 4 * HIDDEN * 6 + staged_bytes(32, HIDDEN),
     # the previous layer's tail fused into gate+up: the tail's four inputs and
-    # the residual it writes, both matrices, mid f32 and staged
-    "tail_gate_up": 2 * q4k_bytes(FFN, HIDDEN) + 5 * 4 * HIDDEN + 4 * FFN + staged_bytes(16, FFN),
+    # the residual it writes, both matrices, mid staged for the down matvec
+    "tail_gate_up": 2 * q4k_bytes(FFN, HIDDEN) + 5 * 4 * HIDDEN + staged_bytes(16, FFN),
 }
 # one token through the pass: per layer gate+up (x in, mid out), down, tail; plus the entry norm.
 # The same count serves every schedule of the pass, so their rates compare work for work.
@@ -206,6 +206,10 @@ class FFNChain:
                     for _ in range(2)]
         self.mid_s = torch.empty(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, FFN), dtype=u8, device=dev)
         self.R = [self.residual, torch.empty(HIDDEN, device=dev)]  # residual ping-pong
+        self.table = kq.kq_ffn_layer_table([(self.Wg[l], self.Wu[l], self.Wd[l], self.gp[l],
+                                             self.gn[l]) for l in range(layers)])
+        self.pass_ws = torch.empty(kq.kq_ffn_pass_workspace_bytes(HIDDEN, FFN), dtype=torch.uint8,
+                                   device=dev)
 
     def entry_norm(self):
         # x_0 = rms_norm(residual, 1e-5) with unit gain: the tail with a zero
@@ -247,11 +251,17 @@ class FFNChain:
         R = self.R
         return (
             ("tail_gate_up", lambda: kq.kq_ffn_tail_gate_up_q4k(
-                R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, self.Wg[l], self.Wu[l], self.mid,
+                R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, self.Wg[l], self.Wu[l], None,
                 self.mid_s, Q6, FFN, HIDDEN, 1e-8, 1e-5)),
             ("down_staged", lambda: kq.kq_matvec_staged(Q6, self.Wd[l], self.mid_s, self.p,
                                                         HIDDEN, FFN)),
         )
+
+    def lib_pass(self):
+        """The whole pass as one library call: kq_ffn_pass_q4k_q6k enqueues the
+        launches of calls_fusedtail for every layer, then the last tail."""
+        self.kq.kq_ffn_pass_q4k_q6k(self.table, self.R[0], self.x[0], None, self.pass_ws,
+                                    self.pass_ws.numel(), HIDDEN, FFN, 1e-8, 1e-5)
 
     def final_tail(self):
         """The last layer's tail (after the fused pass): residual and x_out."""
@@ -805,9 +815,10 @@ def main():
     # ---- the step as timed: one graph replay of the whole pass: per layer the
     # previous tail (the entry norm for layer 0) fused with gate+up+SiLU, then
     # the down matvec on staged mid; then the last tail
-    ft_pass = lambda: chain.run_pass("fusedtail")
+    ft_pass = chain.lib_pass
     graph_t = capture(ft_pass)
-    log(f"timing {args.steps} steps (graph: 2 launches per layer, tail fused into gate+up)")
+    log(f"timing {args.steps} steps (graph of kq_ffn_pass_q4k_q6k: 2 launches per layer, "
+        "tail fused into gate+up)")
     ms_per_step, wall = timed((lambda: graph_t.replay()) if graph_t is not None else ft_pass,
                               args.steps)
     value = pass_bytes / (ms_per_step * 1e-3) / 1e9
@@ -895,10 +906,10 @@ def main():
                    "hidden": HIDDEN, "ffn": FFN, "layers": args.layers, "tokens_per_step": 1,
                    "weight_bytes_per_step": WEIGHT_BYTES_PASS * args.layers // LAYERS,
                    "algorithmic_bytes_per_step": pass_bytes,
-                   "timing": "one graph replay per step: per layer kq_ffn_tail_gate_up_q4k "
-                             "(the previous layer's tail, or the entry norm, fused with gate, "
-                             "up and SiLU) and kq_matvec_staged (Q6_K down), then the last "
-                             "kq_fused_residual_norm; 105 launches"},
+                   "timing": "one graph replay per step of kq_ffn_pass_q4k_q6k, which enqueues "
+                             "per layer the previous layer's tail (or the entry norm) fused with "
+                             "gate, up and SiLU (writing mid staged) and the Q6_K down matvec on "
+                             "it, then the last dual-eps tail; 105 launches"},
         "alternatives": alternatives,
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "tokens_per_s": round(1e3 / ms_per_step, 2),

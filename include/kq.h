@@ -113,8 +113,6 @@ typedef int kq_status;
 #define KQ_MAX_TAIL_N 32768 /* largest row width of kq_fused_residual_norm */
 #define KQ_STAGED_LIMBS 3   /* byte limbs per input in a staged activation */
 #define KQ_MAX_FUSED_TAIL_K 8192 /* largest k of kq_ffn_tail_gate_up_q4k */
-#define KQ_MAX_PASS_FFN 40960    /* largest ffn of kq_ffn_pass_q4k_q6k */
-#define KQ_FFN_PASS_STATUS_OFFSET 256 /* byte offset of the pass's status word */
 
 /*
  * Q4_K decode matvec: y[r] = sum_i w[r,i] * x[i] for r < n_rows, with an
@@ -405,7 +403,9 @@ kq_status kq_ffn_gate_up_q4k_staged(const void *W_gate, const void *W_up, const 
  *   residual_out  [k] f32 output, 16-byte aligned; must not overlap
  *                 residual_in (every workgroup reads it while one writes).
  *   next_in       NULL or [k] f32 output, 16-byte aligned.
- *   W_gate, W_up, mid, mid_s, mid_qtype  as for kq_ffn_gate_up_q4k_staged.
+ *   W_gate, W_up, mid, mid_s, mid_qtype  as for kq_ffn_gate_up_q4k_staged,
+ *                 except that mid may be NULL when mid_s is given (only the
+ *                 staged form is written).
  *   n_rows        >= 1 (the tail's outputs need a launch), < 2^31.
  *   k             multiple of 256, <= KQ_MAX_FUSED_TAIL_K.
  *   eps_post, eps_next  >= 0 and finite.
@@ -419,9 +419,9 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
                                   float eps_post, float eps_next, void *stream);
 
 /*
- * The decode FFN pass of a whole layer stack in one launch (Ch 10 "The
- * forward pass at a glance", section 10.3: each layer's SiLU-gated FFN on the
- * normed input, then the tail, whose second output is the next layer's input;
+ * The decode FFN pass of a whole layer stack in one call (Ch 10 "The forward
+ * pass at a glance", section 10.3: each layer's SiLU-gated FFN on the normed
+ * input, then the tail, whose second output is the next layer's input;
  * Ch 19 "The down projection + residual", sections 19.1 and 19.4).  From the
  * residual r_0, for l = 0 .. n_layers-1:
  *   x_0     = rms_norm(r_0, eps_next) * g_entry      (unit gain if g_entry is NULL)
@@ -430,45 +430,33 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
  *   r_{l+1} = r_l + rms_norm(p_l, eps_post) * g_post[l]
  *   x_{l+1} = rms_norm(r_{l+1}, eps_next) * g_next[l]
  * and residual <- r_L, x_out <- x_L.  rms_norm(v, eps) = v / sqrt(mean(v^2) + eps).
- * Each step is computed as in the per-layer launches kq_ffn_tail_gate_up_q4k
- * (layer 0: zero projection, unit post gain, g_entry or unit next gain) with
- * mid staged for Q6_K, kq_matvec_staged on the Q6_K down matrix, and a last
- * kq_fused_residual_norm, and the results equal theirs bit for bit whenever
- * that down matvec sums a row over 8 lanes, its launch shape at FFN sizes
- * (ffn > 8192); at other sizes it may associate a row's sum differently and
- * the two agree to rounding (the matvec's accuracy bound holds for both).
- * One cooperative launch runs one workgroup per compute unit for the whole
- * stack; the gate+up and down phases of each layer are separated by
- * grid-wide barriers, whose counter lives in `workspace`.
- *   layers     DEVICE array of n_layers kq_ffn_layer records, 8-byte aligned,
- *              each holding device pointers: W_gate and W_up (Q4_K
- *              [ffn][hidden], 16-byte aligned), W_down (Q6_K [hidden][ffn],
- *              4-byte aligned), g_post and g_next ([hidden] f32, 16-byte
- *              aligned).  The library does not read the array on the host, so
- *              these pointers are not checked: they must stay valid for the
- *              launch and must not overlap residual, x_out or the workspace.
+ * It enqueues two launches per layer and one more: kq_ffn_tail_gate_up_q4k
+ * (layer l's gate, up and SiLU with layer l-1's tail in front; layer 0's
+ * tail is the entry norm) writing mid staged for Q6_K, then kq_matvec_staged
+ * on the Q6_K down matrix; then the last kq_fused_residual_norm.  Results
+ * equal those calls made one by one, bit for bit.
+ *   layers     HOST array of n_layers kq_ffn_layer records holding device
+ *              pointers: W_gate and W_up (Q4_K [ffn][hidden], 16-byte
+ *              aligned), W_down (Q6_K [hidden][ffn], 4-byte aligned), g_post
+ *              and g_next ([hidden] f32, 16-byte aligned).  Read during the
+ *              call only.
  *   n_layers   >= 1.
  *   residual   [hidden] f32, 16-byte aligned: r_0 in, r_L out.
  *   x_out      [hidden] f32 output, 16-byte aligned.
  *   g_entry    NULL or [hidden] f32, 16-byte aligned.
  *   workspace, workspace_bytes
  *              caller-owned device memory of at least
- *              kq_ffn_pass_workspace_bytes(hidden, ffn) bytes, 256-byte aligned,
- *              zero-filled before its first use; each call leaves its
- *              counters at zero, so it can be reused without clearing.  Calls
- *              sharing a workspace must be ordered.  The uint32 at byte
- *              KQ_FFN_PASS_STATUS_OFFSET is the status word: nonzero if a
- *              barrier wait gave up (possible only if the workgroups were not
- *              all resident); the launch still ends and writes NaN to residual
- *              and x_out.  It stays set until the caller clears it.
+ *              kq_ffn_pass_workspace_bytes(hidden, ffn) bytes, 256-byte
+ *              aligned, for the relay buffers (the residual's second buffer,
+ *              the down output and staged mid); no initial contents needed.
+ *              Calls sharing a workspace must be ordered.
  *   hidden     multiple of 256, <= KQ_MAX_FUSED_TAIL_K.
- *   ffn        multiple of 256, <= KQ_MAX_PASS_FFN.
+ *   ffn        multiple of 256, <= KQ_MAX_K.
  *   eps_post, eps_next  >= 0 and finite.
- * residual, x_out, g_entry, the workspace and the layer array must not
- * overlap one another.
+ * No output (residual, x_out, workspace) may overlap another argument's
+ * buffer (weights, gains, g_entry, or another output).
  * Errors as kq_ffn_tail_gate_up_q4k; a workspace that is too small is
- * KQ_ERR_SHAPE; KQ_ERR_LAUNCH also when the device cannot hold one
- * workgroup per compute unit at once.
+ * KQ_ERR_SHAPE.
  */
 typedef struct kq_ffn_layer {
     const void *W_gate, *W_up, *W_down;
@@ -481,9 +469,8 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
                               float eps_post, float eps_next, void *stream);
 
 /*
- * Workspace bytes kq_ffn_pass_q4k_q6k needs (the barrier counters, the
- * residual's second buffer, the down output and staged mid), or a negative
- * kq_status for shapes it would reject.  Host arithmetic only.
+ * Workspace bytes kq_ffn_pass_q4k_q6k needs, or a negative kq_status for
+ * shapes it would reject.  Host arithmetic only.
  */
 int64_t kq_ffn_pass_workspace_bytes(int64_t hidden, int64_t ffn);
 

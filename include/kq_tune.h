@@ -63,17 +63,6 @@ kq_status kq_tune_matvec_plan(int qtype, int64_t n_rows, int64_t k, int staged, 
 kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int cus, int64_t *out);
 
 /*
- * Process-wide launch variant of kq_ffn_pass_q4k_q6k: `waves` wavefronts per
- * workgroup and the half-superblock units in flight per lane in the gate+up
- * phase (`depth_gate_up`) and the down phase (`depth_down`).  Built
- * variants: (8, 2, 2) the default, (8, 3, 2), (8, 2, 3), (12, 2, 2),
- * (12, 2, 1).  All zeros restores the default.  Not thread-safe against
- * concurrent pass calls.
- * Errors: KQ_ERR_UNSUPPORTED for a variant that is not built.
- */
-kq_status kq_tune_set_pass(int waves, int depth_gate_up, int depth_down);
-
-/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of `block` threads and
  * writes grid*block/64 xor-folded words to the device buffer `out` (so the

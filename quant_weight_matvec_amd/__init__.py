@@ -14,6 +14,6 @@ from ._binding import (  # noqa: F401
     kq_matvec_q4k, kq_matvec_q5k, kq_embedding, kq_matvec_q6k, kq_matvec_group, kq_matvec_group_staged, KQ_MAX_GROUP, kq_ffn_gate_up_q4k, kq_probe_read_bw, kq_status_string, kq_tune_get_shape, kq_tune_set_shape, lib,
     kq_staged_bytes, kq_stage_activation, kq_matvec_staged, kq_ffn_gate_up_q4k_staged,
     kq_fused_residual_norm_staged, kq_ffn_tail_gate_up_q4k,
-    kq_ffn_pass_q4k_q6k, kq_ffn_pass_workspace_bytes, kq_ffn_layer_table, kq_tune_set_pass,
-    KQ_MAX_FUSED_TAIL_K, KQ_MAX_PASS_FFN, KQ_FFN_PASS_STATUS_OFFSET,
+    kq_ffn_pass_q4k_q6k, kq_ffn_pass_workspace_bytes, kq_ffn_layer_table, KqFfnLayer,
+    KQ_MAX_FUSED_TAIL_K,
 )

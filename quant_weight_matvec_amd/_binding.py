@@ -34,8 +34,6 @@ KQ_MAX_TAIL_N = 32768
 KQ_MAX_GROUP = 4
 KQ_SMALL_M_SCRATCH_BYTES = 16 * 1024 + 16 * 1024 * 1024
 KQ_MAX_FUSED_TAIL_K = 8192
-KQ_MAX_PASS_FFN = 40960
-KQ_FFN_PASS_STATUS_OFFSET = 256
 
 
 class KQLibraryMissing(RuntimeError):
@@ -46,6 +44,12 @@ class KQError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
         self.status = status
+
+
+class KqFfnLayer(C.Structure):
+    """kq_ffn_layer: device pointers of one layer's matrices and tail gains."""
+    _fields_ = [("W_gate", C.c_void_p), ("W_up", C.c_void_p), ("W_down", C.c_void_p),
+                ("g_post", C.c_void_p), ("g_next", C.c_void_p)]
 
 
 _lib: C.CDLL | None = None
@@ -100,12 +104,11 @@ def lib() -> C.CDLL:
                                                 C.c_float, C.c_float, _vp]
     L.kq_ffn_tail_gate_up_q4k.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           C.c_int, _i64, _i64, C.c_float, C.c_float, _vp]
-    L.kq_ffn_pass_q4k_q6k.argtypes = [_vp, C.c_int, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
-                                      C.c_float, C.c_float, _vp]
+    L.kq_ffn_pass_q4k_q6k.argtypes = [C.POINTER(KqFfnLayer), C.c_int, _vp, _vp, _vp, _vp, _i64,
+                                      _i64, _i64, C.c_float, C.c_float, _vp]
     L.kq_ffn_pass_workspace_bytes.argtypes = [_i64, _i64]
     L.kq_ffn_pass_workspace_bytes.restype = _i64
-    L.kq_tune_set_pass.argtypes = [C.c_int, C.c_int, C.c_int]
-    for fn in ("kq_ffn_pass_q4k_q6k", "kq_tune_set_pass", "kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
+    for fn in ("kq_ffn_pass_q4k_q6k", "kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
                "kq_tune_small_m_plan", "kq_tune_matvec_plan",
@@ -294,19 +297,16 @@ def kq_ffn_tail_gate_up_q4k(residual_in, projected, g_post, g_next, residual_out
     _check(rc, "kq_ffn_tail_gate_up_q4k")
 
 
-def kq_ffn_layer_table(layers, device=None):
-    """The device array of kq_ffn_layer records kq_ffn_pass_q4k_q6k reads:
+def kq_ffn_layer_table(layers):
+    """The host array of kq_ffn_layer records kq_ffn_pass_q4k_q6k reads:
     `layers` is a sequence of (W_gate, W_up, W_down, g_post, g_next) tensors
-    or addresses; returns an int64 tensor of their addresses on `device`
-    (default: that of the first tensor, else the current CUDA device)."""
-    import torch
-    flat = [_ptr(t) for rec in layers for t in rec]
-    if any(len(rec) != 5 for rec in layers) or any(a is None for a in flat):
-        raise ValueError("each layer needs five non-null pointers")
-    if device is None:
-        first = layers[0][0] if layers else None
-        device = first.device if isinstance(first, torch.Tensor) else torch.device("cuda")
-    return torch.tensor(flat, dtype=torch.int64).to(device)
+    or addresses, in layer order."""
+    recs = []
+    for rec in layers:
+        if len(rec) != 5:
+            raise ValueError("each layer is (W_gate, W_up, W_down, g_post, g_next)")
+        recs.append(KqFfnLayer(*[_ptr(t) for t in rec]))
+    return (KqFfnLayer * len(recs))(*recs)
 
 
 def kq_ffn_pass_workspace_bytes(hidden: int, ffn: int) -> int:
@@ -318,19 +318,16 @@ def kq_ffn_pass_workspace_bytes(hidden: int, ffn: int) -> int:
     return int(n)
 
 
-def kq_ffn_pass_q4k_q6k(layers, n_layers: int, residual, x_out, g_entry, workspace,
-                        workspace_bytes: int, hidden: int, ffn: int, eps_post: float = 1e-8,
-                        eps_next: float = 1e-5, stream=None) -> None:
-    rc = lib().kq_ffn_pass_q4k_q6k(_ptr(layers), int(n_layers), _ptr(residual), _ptr(x_out),
-                                   _ptr(g_entry), _ptr(workspace), int(workspace_bytes),
-                                   int(hidden), int(ffn), float(eps_post), float(eps_next),
-                                   _stream(stream))
+def kq_ffn_pass_q4k_q6k(layers, residual, x_out, g_entry, workspace, workspace_bytes: int,
+                        hidden: int, ffn: int, eps_post: float = 1e-8, eps_next: float = 1e-5,
+                        stream=None) -> None:
+    """`layers`: a kq_ffn_layer_table array, or a sequence of
+    (W_gate, W_up, W_down, g_post, g_next) per layer."""
+    table = layers if isinstance(layers, C.Array) else kq_ffn_layer_table(layers)
+    rc = lib().kq_ffn_pass_q4k_q6k(table, len(table), _ptr(residual), _ptr(x_out), _ptr(g_entry),
+                                   _ptr(workspace), int(workspace_bytes), int(hidden), int(ffn),
+                                   float(eps_post), float(eps_next), _stream(stream))
     _check(rc, "kq_ffn_pass_q4k_q6k")
-
-
-def kq_tune_set_pass(waves: int = 0, depth_gate_up: int = 0, depth_down: int = 0) -> None:
-    _check(lib().kq_tune_set_pass(int(waves), int(depth_gate_up), int(depth_down)),
-           "kq_tune_set_pass")
 
 
 def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0,

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkq.so")
-SOURCES = ["kq_kernels.hip", "kq_small_m.hip", "kq_pass.hip", "kq_abi.cpp"]
+SOURCES = ["kq_kernels.hip", "kq_small_m.hip", "kq_abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -497,7 +497,7 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
                                   float eps_post, float eps_next, void *stream)
 {
     if (!residual_in || !projected || !g_post || !g_next || !residual_out || !W_gate || !W_up ||
-        !mid)
+        (!mid && !mid_s))
         return KQ_ERR_NULL;
     if (mid_s && !staged_group(mid_qtype)) return KQ_ERR_SHAPE;
     if (n_rows < 1 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;  // the tail needs a launch
@@ -512,7 +512,7 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
         !aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(mid, 4) || !aligned(mid_s, 16))
         return KQ_ERR_ALIGN;
     const int64_t vb = k * 4, wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
-    const int64_t mb = n_rows * 4, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
+    const int64_t mb = mid ? n_rows * 4 : 0, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
     const void *ins[] = {residual_in, projected, g_post, g_next, W_gate, W_up};
     const int64_t inb[] = {vb, vb, vb, vb, wbytes, wbytes};
     void *outs[] = {residual_out, next_in, mid, mid_s};
@@ -599,13 +599,33 @@ const char *kq_build_info(void)
     return info.c_str();
 }
 
+namespace {
+
+// Relay buffers of kq_ffn_pass_q4k_q6k in its workspace (byte offsets).
+struct PassWs {
+    int64_t res_alt, p, mid_s, total;
+};
+
+PassWs pass_ws_layout(int64_t hidden, int64_t ffn)
+{
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    PassWs w;
+    w.res_alt = 0;
+    w.p = up(4 * hidden);
+    w.mid_s = w.p + up(4 * hidden);
+    w.total = w.mid_s + up(staged_size(KQ_QTYPE_Q6K, ffn));
+    return w;
+}
+
+}  // namespace
+
 int64_t kq_ffn_pass_workspace_bytes(int64_t hidden, int64_t ffn)
 {
     kq_status s = check_k(hidden);
     if (s != KQ_OK) return s;
     if ((s = check_k(ffn)) != KQ_OK) return s;
-    if (hidden > KQ_MAX_FUSED_TAIL_K || ffn > KQ_MAX_PASS_FFN) return KQ_ERR_UNSUPPORTED;
-    return (int64_t)kqi::pass_ws_layout((int)hidden, (int)ffn).total;
+    if (hidden > KQ_MAX_FUSED_TAIL_K) return KQ_ERR_UNSUPPORTED;
+    return pass_ws_layout(hidden, ffn).total;
 }
 
 kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *residual,
@@ -620,25 +640,72 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
     if (workspace_bytes < need) return KQ_ERR_SHAPE;
     if (!(eps_post >= 0.0f) || !(eps_next >= 0.0f) || !isfinite(eps_post) || !isfinite(eps_next))
         return KQ_ERR_SHAPE;
-    if (!aligned(layers, 8) || !aligned(residual, 16) || !aligned(x_out, 16) ||
-        !aligned(g_entry, 16) || !aligned(workspace, 256))
+    if (!aligned(residual, 16) || !aligned(x_out, 16) || !aligned(g_entry, 16) ||
+        !aligned(workspace, 256))
         return KQ_ERR_ALIGN;
-    const int64_t vb = hidden * 4, tb = (int64_t)n_layers * (int64_t)sizeof(kq_ffn_layer);
-    const void *bufs[] = {residual, x_out, g_entry, workspace, layers};
-    const int64_t lens[] = {vb, vb, g_entry ? vb : 0, workspace_bytes, tb};
-    for (int i = 0; i < 5; ++i)
-        for (int j = i + 1; j < 5; ++j)
-            if (overlap(bufs[i], lens[i], bufs[j], lens[j])) return KQ_ERR_ALIAS;
+    const int64_t vb = hidden * 4;
+    const int64_t q4b = ffn * (hidden / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
+    const int64_t q6b = hidden * (ffn / KQ_QK) * KQ_Q6K_BLOCK_BYTES;
+    void *outs[] = {residual, x_out, workspace};
+    const int64_t outb[] = {vb, vb, workspace_bytes};
+    for (int o = 0; o < 3; ++o) {
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return KQ_ERR_ALIAS;
+        if (overlap(outs[o], outb[o], g_entry, g_entry ? vb : 0)) return KQ_ERR_ALIAS;
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        const kq_ffn_layer &L = layers[l];
+        if (!L.W_gate || !L.W_up || !L.W_down || !L.g_post || !L.g_next) return KQ_ERR_NULL;
+        if (!aligned(L.W_gate, 16) || !aligned(L.W_up, 16) || !aligned(L.W_down, 4) ||
+            !aligned(L.g_post, 16) || !aligned(L.g_next, 16))
+            return KQ_ERR_ALIGN;
+        const void *ins[] = {L.W_gate, L.W_up, L.W_down, L.g_post, L.g_next};
+        const int64_t inb[] = {q4b, q4b, q6b, vb, vb};
+        for (int o = 0; o < 3; ++o)
+            for (int i = 0; i < 5; ++i)
+                if (overlap(outs[o], outb[o], ins[i], inb[i])) return KQ_ERR_ALIAS;
+    }
     kq_status s = check_device();
     if (s != KQ_OK) return s;
-    return from_hip(kqi::launch_ffn_pass(layers, n_layers, residual, x_out, g_entry,
-                                         (uint8_t *)workspace, (int)hidden, (int)ffn, eps_post,
-                                         eps_next, (hipStream_t)stream));
-}
-
-kq_status kq_tune_set_pass(int waves, int depth_gate_up, int depth_down)
-{
-    return kqi::set_pass_variant(waves, depth_gate_up, depth_down) ? KQ_OK : KQ_ERR_UNSUPPORTED;
+    const PassWs w = pass_ws_layout(hidden, ffn);
+    uint8_t *ws = (uint8_t *)workspace;
+    float *alt = (float *)(ws + w.res_alt);
+    float *p = (float *)(ws + w.p);
+    uint8_t *mid_s = ws + w.mid_s;
+    const hipStream_t st = (hipStream_t)stream;
+    const int h = (int)hidden, f = (int)ffn;
+    // Layer l's tail reads the current residual buffer and writes the other
+    // one (every workgroup reads the first while one writes the second).
+    // Layer 0's tail is the entry norm, which leaves the residual unchanged:
+    // with an odd layer count it writes nothing, so that the residual after
+    // the last layer sits in `residual`, where the last tail updates it.
+    float *cur = residual, *other = alt;
+    for (int l = 0; l < n_layers; ++l) {
+        const bool skip_write = l == 0 && (n_layers & 1);
+        const kqi::TailArgs t{cur,
+                              l ? p : nullptr,
+                              l ? layers[l - 1].g_post : nullptr,
+                              l ? layers[l - 1].g_next : g_entry,
+                              skip_write ? nullptr : other,
+                              nullptr,
+                              eps_post,
+                              eps_next};
+        s = from_hip(kqi::launch_gate_up_q4k((const uint8_t *)layers[l].W_gate,
+                                             (const uint8_t *)layers[l].W_up, nullptr, nullptr,
+                                             nullptr, mid_s, 16, f, h, &t, st));
+        if (s != KQ_OK) return s;
+        if (!skip_write) {
+            float *tmp = cur;
+            cur = other;
+            other = tmp;
+        }
+        s = from_hip(kqi::launch_matvec_q6k((const uint8_t *)layers[l].W_down, nullptr, mid_s, p,
+                                            h, f, st));
+        if (s != KQ_OK) return s;
+    }
+    return from_hip(kqi::launch_tail(cur, p, x_out, layers[n_layers - 1].g_post,
+                                     layers[n_layers - 1].g_next, 1, h, eps_post, eps_next,
+                                     nullptr, 0, st));
 }
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)

@@ -43,8 +43,8 @@ hipError_t launch_matvec_q4k(const uint8_t *W, const float *x, const uint8_t *xs
 // The previous layer's dual-eps tail, run in the gate+up kernel's prologue in
 // place of a given input (k = the tail's row width).
 struct TailArgs {
-    const float *res_in, *proj, *g_post, *g_next;
-    float *res_out, *x_out;  // x_out nullable
+    const float *res_in, *proj, *g_post, *g_next;  // proj null: zero; gains null: unit
+    float *res_out, *x_out;                        // each nullable (not written)
     float eps_post, eps_next;
 };
 // mid_s (nullable): also write mid staged with scale groups of mid_group (16 or 32).
@@ -87,26 +87,6 @@ hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,
                        float eps_post, float eps_next, uint8_t *xs_out, int xs_group,
                        hipStream_t stream);
-
-// The FFN pass of a layer stack in one cooperative launch (kq_pass.hip): one
-// workgroup per CU, of pass_waves() waves (at most kPassMaxWaves).  The
-// workspace holds the barrier counters and status word, the residual's
-// second buffer, the down output and staged mid, at the byte offsets of
-// pass_ws_layout.
-constexpr int kPassMaxWaves = 12;
-// Launch variant (benchmarks): waves per workgroup and units in flight per
-// lane in each phase; all zeros = the default.  False if not built.
-bool set_pass_variant(int waves, int depth_a, int depth_b);
-int pass_waves();
-struct PassWs {
-    size_t bar, exitc, status, res_alt, p, mid_s, total;
-};
-PassWs pass_ws_layout(int hidden, int ffn);
-size_t pass_lds_bytes(int hidden, int ffn, int grid);
-// layers: device array of n_layers kq_ffn_layer records
-hipError_t launch_ffn_pass(const void *layers, int n_layers, float *residual, float *x_out,
-                           const float *g_entry, uint8_t *ws, int hidden, int ffn, float eps_post,
-                           float eps_next, hipStream_t stream);
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *out, int grid, int block,
                              int unroll, int flags, hipStream_t stream);

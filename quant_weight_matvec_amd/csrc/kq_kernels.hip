@@ -47,8 +47,8 @@ constexpr int kXPre = 80;
 // (Ch 10 "The forward pass at a glance", section 10.3: the tail's second
 // output is the next layer's input).
 struct TailIn {
-    const float *res_in, *proj, *g_post, *g_next;
-    float *res_out, *x_out;  // written by workgroup 0; x_out may be null
+    const float *res_in, *proj, *g_post, *g_next;  // proj null: zero; gains null: unit
+    float *res_out, *x_out;  // written by workgroup 0 unless null
     float eps_post, eps_next;
 };
 
@@ -219,19 +219,22 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         // branch); within them the loads are unconditional (index clamped into
         // the row; slots outside the layout are zeroed at first use), p first:
         // the first sum needs only p.
+        // a null projection is a zero one, a null gain a unit one (the
+        // entry norm of a layer stack); their loads read res_in instead, so
+        // the loads stay unconditional, and the values are replaced below
+        const f32x4 *pp4 = reinterpret_cast<const f32x4 *>(tl.proj ? tl.proj : tl.res_in);
+        const f32x4 *gp4 = reinterpret_cast<const f32x4 *>(tl.g_post ? tl.g_post : tl.res_in);
+        const f32x4 *gn4 = reinterpret_cast<const f32x4 *>(tl.g_next ? tl.g_next : tl.res_in);
         if (tid < tt) {
 #pragma unroll
-            for (int j = 0; j < kTailVec; ++j)
-                tp[j] = reinterpret_cast<const f32x4 *>(tl.proj)[min(tid + j * tt, n4 - 1)];
+            for (int j = 0; j < kTailVec; ++j) tp[j] = pp4[min(tid + j * tt, n4 - 1)];
 #pragma unroll
             for (int j = 0; j < kTailVec; ++j)
                 tr[j] = reinterpret_cast<const f32x4 *>(tl.res_in)[min(tid + j * tt, n4 - 1)];
 #pragma unroll
-            for (int j = 0; j < kTailVec; ++j)
-                tg[j] = reinterpret_cast<const f32x4 *>(tl.g_post)[min(tid + j * tt, n4 - 1)];
+            for (int j = 0; j < kTailVec; ++j) tg[j] = gp4[min(tid + j * tt, n4 - 1)];
 #pragma unroll
-            for (int j = 0; j < kTailVec; ++j)
-                tn[j] = reinterpret_cast<const f32x4 *>(tl.g_next)[min(tid + j * tt, n4 - 1)];
+            for (int j = 0; j < kTailVec; ++j) tn[j] = gn4[min(tid + j * tt, n4 - 1)];
         } else {
 #pragma unroll
             for (int j = 0; j < kTailVec; ++j) tp[j] = tr[j] = tg[j] = tn[j] = z;
@@ -271,13 +274,14 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         // the standalone tail's arithmetic, in its order; threads past its
         // block add exact zeros to the (non-negative) sums
         const float inv_n = 1.0f / (float)k;
+        const f32x4 one = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
         for (int j = 0; j < kTailVec; ++j) {
             const bool ok = tid < tt && tid + j * tt < n4;
-            tp[j] = ok ? tp[j] : z;
+            tp[j] = ok && tl.proj ? tp[j] : z;
             tr[j] = ok ? tr[j] : z;
-            tg[j] = ok ? tg[j] : z;
-            tn[j] = ok ? tn[j] : z;
+            tg[j] = ok ? (tl.g_post ? tg[j] : one) : z;
+            tn[j] = ok ? (tl.g_next ? tn[j] : one) : z;
         }
         float ss = 0.0f;
 #pragma unroll
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         for (int j = 0; j < kTailVec; ++j) {
             const int i = tid + j * tt;
             tr[j] = tail_add(tr[j], tp[j], inv_p, tg[j]);
-            if (blockIdx.x == 0 && tid < tt && i < n4)
+            if (blockIdx.x == 0 && tl.res_out && tid < tt && i < n4)
                 reinterpret_cast<f32x4 *>(tl.res_out)[i] = tr[j];
             sr += sumsq4(tr[j]);
         }
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         acc_u = lane_group_sum<LANES>(acc_u);
         if (sub == 0 && rv) {
             const float m = (acc_g / (1.0f + __expf(-acc_g))) * acc_u;
-            mid[r] = m;
+            if (mid) mid[r] = m;
             if (mid_s) midl[r - r_lo] = m;
         }
         t0 += nwaves * RPT;

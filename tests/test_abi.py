@@ -429,49 +429,65 @@ def test_kernel_code_hash_reads_the_built_code_object():
 
 
 def test_ffn_pass_validation():
-    """kq_ffn_pass_q4k_q6k rejects bad arguments on the host (the layer table
-    itself is device memory and is not read here)."""
-    L, R, XO, GE, WS = 0x100000, 0x200000, 0x300000, 0x400000, 0x1000000
+    """kq_ffn_pass_q4k_q6k checks its arguments and every layer record of its
+    host table before anything is enqueued."""
+    R, XO, GE, WS = 0x100000, 0x200000, 0x300000, 0x1000000
     h, f = 6656, 19968
+    q4b, q6b = f * (h // 256) * 144, h * (f // 256) * 210
     need = kq.kq_ffn_pass_workspace_bytes(h, f)
-    # counters (512 B), two [hidden] f32 buffers, staged mid for Q6_K, each
-    # region rounded up to 256 bytes
+    # the residual's second buffer, the down output, staged mid for Q6_K
     up = lambda b: (b + 255) // 256 * 256
-    assert need == 512 + 2 * up(4 * h) + up(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f))
+    assert need == 2 * up(4 * h) + up(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f))
+    base = 0x10000000
 
-    def call(layers=L, n=52, r=R, xo=XO, ge=None, ws=WS, wsb=need, hidden=h, ffn=f,
+    def layer(l, **kw):
+        o = base + l * 0x10000000
+        d = dict(W_gate=o, W_up=o + 0x4800000, W_down=o + 0x9000000, g_post=o + 0xF000000,
+                 g_next=o + 0xF100000)
+        d.update(kw)
+        return B.KqFfnLayer(**d)
+
+    def call(layers=None, n=2, r=R, xo=XO, ge=None, ws=WS, wsb=need, hidden=h, ffn=f,
              ep=1e-8, en=1e-5):
-        return kq.lib().kq_ffn_pass_q4k_q6k(layers, n, r, xo, ge, ws, wsb, hidden, ffn, ep, en,
+        layers = layers if layers is not None else [layer(i) for i in range(n)]
+        table = (B.KqFfnLayer * max(1, len(layers)))(*layers)
+        return kq.lib().kq_ffn_pass_q4k_q6k(table, n, r, xo, ge, ws, wsb, hidden, ffn, ep, en,
                                             None)
 
-    assert call(layers=None) == B.KQ_ERR_NULL
+    assert kq.lib().kq_ffn_pass_q4k_q6k(None, 1, R, XO, None, WS, need, h, f, 1e-8, 1e-5,
+                                        None) == B.KQ_ERR_NULL
     assert call(r=None) == B.KQ_ERR_NULL
     assert call(xo=None) == B.KQ_ERR_NULL
     assert call(ws=None) == B.KQ_ERR_NULL
-    assert call(n=0) == B.KQ_ERR_SHAPE
+    assert call(layers=[layer(0), layer(1, W_down=None)]) == B.KQ_ERR_NULL
+    assert call(layers=[layer(0, g_next=None), layer(1)]) == B.KQ_ERR_NULL
+    assert call(n=0, layers=[layer(0)]) == B.KQ_ERR_SHAPE
     assert call(hidden=300) == B.KQ_ERR_SHAPE
     assert call(ffn=1000) == B.KQ_ERR_SHAPE
     assert call(hidden=B.KQ_MAX_FUSED_TAIL_K + 256) == B.KQ_ERR_UNSUPPORTED
-    assert call(ffn=B.KQ_MAX_PASS_FFN + 256) == B.KQ_ERR_UNSUPPORTED
+    assert call(ffn=B.KQ_MAX_K + 256) == B.KQ_ERR_UNSUPPORTED
     assert call(wsb=need - 1) == B.KQ_ERR_SHAPE
     assert call(ep=-1.0) == B.KQ_ERR_SHAPE
     assert call(en=float("inf")) == B.KQ_ERR_SHAPE
-    assert call(layers=L + 4) == B.KQ_ERR_ALIGN
     assert call(r=R + 4) == B.KQ_ERR_ALIGN
     assert call(xo=XO + 8) == B.KQ_ERR_ALIGN
     assert call(ge=GE + 4) == B.KQ_ERR_ALIGN
     assert call(ws=WS + 128) == B.KQ_ERR_ALIGN
-    assert call(xo=R + 16) == B.KQ_ERR_ALIAS              # x_out inside residual
-    assert call(ge=XO) == B.KQ_ERR_ALIAS                  # g_entry is x_out
-    assert call(ws=R - 256) == B.KQ_ERR_ALIAS             # workspace covers residual
-    assert call(layers=WS + need - 8) == B.KQ_ERR_ALIAS   # table inside the workspace
+    assert call(layers=[layer(0, W_gate=base + 8), layer(1)]) == B.KQ_ERR_ALIGN
+    assert call(layers=[layer(0), layer(1, W_down=base + 0x10000000 + 0x9000002)]) == B.KQ_ERR_ALIGN
+    assert call(layers=[layer(0, g_post=base + 0xF000004), layer(1)]) == B.KQ_ERR_ALIGN
+    assert call(xo=R + 16) == B.KQ_ERR_ALIAS                      # x_out inside residual
+    assert call(ge=XO) == B.KQ_ERR_ALIAS                          # g_entry is x_out
+    assert call(ws=R - 256) == B.KQ_ERR_ALIAS                     # workspace covers residual
+    assert call(r=base + q4b - 64) == B.KQ_ERR_ALIAS              # residual inside W_gate
+    assert call(ws=base + 0x10000000 + 0x9000000 + q6b - 256) == B.KQ_ERR_ALIAS  # in W_down
+    assert call(xo=base + 0xF100000 + 16) == B.KQ_ERR_ALIAS       # x_out inside g_next
     # every check passed: only the device is missing here
     assert call(ge=GE) in (B.KQ_ERR_DEVICE, B.KQ_ERR_LAUNCH, B.KQ_OK)
+    assert call(n=1, layers=[layer(0)]) in (B.KQ_ERR_DEVICE, B.KQ_ERR_LAUNCH, B.KQ_OK)
     with pytest.raises(kq.KQError):
         kq.kq_ffn_pass_workspace_bytes(100, f)
     with pytest.raises(kq.KQError):
-        kq.kq_ffn_pass_workspace_bytes(h, B.KQ_MAX_PASS_FFN + 256)
-    assert kq.lib().kq_tune_set_pass(8, 2, 2) == B.KQ_OK
-    assert kq.lib().kq_tune_set_pass(12, 2, 1) == B.KQ_OK
-    assert kq.lib().kq_tune_set_pass(7, 2, 2) == B.KQ_ERR_UNSUPPORTED
-    assert kq.lib().kq_tune_set_pass(0, 0, 0) == B.KQ_OK
+        kq.kq_ffn_pass_workspace_bytes(B.KQ_MAX_FUSED_TAIL_K + 256, f)
+    t = kq.kq_ffn_layer_table([(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20)])
+    assert len(t) == 1 and t[0].W_down == 3 << 20 and t[0].g_next == 5 << 20

@@ -118,9 +118,8 @@ class Stack:
         every layer.  mode "f32": 3 launches per layer on f32 activations;
         "staged": the same with staged activations; "fusedtail": 2 launches
         per layer (each layer's tail fused into the next layer's gate+up
-        launch) and a last tail; "onelaunch": kq_ffn_pass_q4k_q6k, the whole
-        stack in one cooperative launch (Q6_K down only), whose barrier
-        counters must be back at zero and status word clear afterwards.  With replays > 0 the pass is also replayed
+        launch) and a last tail; "libpass": the same launches enqueued by the
+        library's kq_ffn_pass_q4k_q6k (Q6_K down only).  With replays > 0 the pass is also replayed
         as a graph, each replay equal to the eager run bit for bit.
         Returns (x_out, residual)."""
         h, f, L = self.hidden, self.ffn, self.layers
@@ -152,24 +151,20 @@ class Stack:
                 for l in range(L):
                     self.ops(l, X[l % 2], X[(l + 1) % 2], R[0], mid, p)
 
-        if mode == "onelaunch":
-            table = kq.kq_ffn_layer_table([(d["wg"], d["wu"], d["wd"], d["gp"], d["gn"]) for d in D])
+        if mode == "libpass":
             wsb = kq.kq_ffn_pass_workspace_bytes(h, f)
-            ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            table = kq.kq_ffn_layer_table([(d["wg"], d["wu"], d["wd"], d["gp"], d["gn"]) for d in D])
 
             def body():  # noqa: F811
-                kq.kq_ffn_pass_q4k_q6k(table, L, R[0], X[0], None, ws, wsb, h, f)
+                kq.kq_ffn_pass_q4k_q6k(table, R[0], X[0], None, ws, wsb, h, f)
 
         out = lambda: ((X[0], R[L % 2]) if mode == "fusedtail" else
-                       (X[0], R[0]) if mode == "onelaunch" else (X[L % 2], R[0]))
+                       (X[0], R[0]) if mode == "libpass" else (X[L % 2], R[0]))
         R[0].copy_(r0)
         body()
         torch.cuda.synchronize()
         xo, ro = (t.cpu().numpy() for t in out())
-        if mode == "onelaunch":
-            c = ws[:512].view(torch.int32).cpu().numpy()
-            assert c[0] == 0 and c[32] == 0, "barrier counters not reset"
-            assert c[64] == 0, "a barrier wait gave up"
         if replays:
             s = torch.cuda.Stream()
             s.wait_stream(torch.cuda.current_stream())
@@ -220,8 +215,9 @@ def test_op_pass_small_end_to_end(layers, hidden, ffn, down):
 @pytest.mark.parametrize("layers,hidden,ffn,down", [(1, 512, 1536, "q6k"), (3, 1024, 4096, "q4k"),
                                                     (2, 768, 2560, "q6k")])
 def test_pass_modes_bitwise(layers, hidden, ffn, down):
-    """f32, staged and fused-tail passes from the same residual: identical bits,
-    and the oracle's stack from the same start within tolerance."""
+    """f32, staged and fused-tail passes from the same residual, and (Q6_K
+    down) the library's kq_ffn_pass_q4k_q6k: identical bits, and the oracle's
+    stack from the same start within tolerance."""
     st = Stack(layers, hidden, ffn, down, cfg=14)
     _, r0 = start_state(hidden, cfg=14)
     a = st.run_pass(r0, "f32", replays=1)
@@ -230,18 +226,8 @@ def test_pass_modes_bitwise(layers, hidden, ffn, down):
     for u, v in ((a, b), (a, c)):
         assert np.array_equal(u[0], v[0]) and np.array_equal(u[1], v[1])
     if down == "q6k":
-        # the one-launch pass sums each down row over 8 lanes, the matvec's own
-        # choice at the FFN shape; at these small shapes the matvec would take
-        # more lanes per row (another association order), so the reference
-        # runs with 8
-        d = st.run_pass(r0, "onelaunch")
-        try:
-            kq.kq_tune_set_shape(kq.KQ_QTYPE_Q6K, lanes=8)
-            e = st.run_pass(r0, "fusedtail")
-        finally:
-            kq.kq_tune_set_shape(kq.KQ_QTYPE_Q6K)
-        assert np.array_equal(e[0], d[0]) and np.array_equal(e[1], d[1])
-        assert np.max(np.abs(d[0] - a[0])) <= 1e-5 and np.max(np.abs(d[1] - a[1])) <= 1e-5
+        d = st.run_pass(r0, "libpass", replays=2)
+        assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1])
     x, r = O.rms_norm(r0.astype(np.float64), 1e-5), r0.astype(np.float64)
     for l in range(layers):
         x, r = st.oracle_layer(l, x, r)
@@ -341,70 +327,56 @@ def test_op_pass_52_layers_full_size(full, teacher_forced):
 
 
 def test_pass_modes_52_layers_full_size(full, teacher_forced):
-    """The decode step as two launches per layer (each tail fused into the
-    next layer's gate+up launch, staged activations, replayed as a graph) and
-    as one launch for the whole stack, against the f32 pass from the same
+    """The timed decode step (each tail fused into the next layer's gate+up
+    launch, staged activations, replayed as a graph; built in Python and by
+    the library's kq_ffn_pass_q4k_q6k) against the f32 pass from the same
     residual: identical bits; and end to end against the oracle."""
     st = full["st"]
     a = st.run_pass(full["r0"], "f32")
     c = st.run_pass(full["r0"], "fusedtail", replays=3)
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
     check_end_to_end(full, c[0], c[1], teacher_forced, "gpu_x0")
-    d = st.run_pass(full["r0"], "onelaunch")
+    d = st.run_pass(full["r0"], "libpass", replays=2)
     assert np.array_equal(a[0], d[0]) and np.array_equal(a[1], d[1])
 
 
 @pytest.mark.parametrize("layers,hidden,ffn", [(3, 512, 1536), (2, 6656, 19968), (1, 256, 256),
                                                (2, 8192, 4096)])
-def test_one_launch_pass_variants_and_reuse(layers, hidden, ffn):
-    """kq_ffn_pass_q4k_q6k with every built launch variant, twice in a row on
-    one workspace (left ready by the previous call) and with an entry gain:
-    the same bits as the two-launch pass with that gain as layer 0's next
-    gain (its down matvec at 8 lanes per row, as in the pass), and the
-    counters back at zero.  The shapes include workgroups
+def test_library_pass_entry_gain_and_reuse(layers, hidden, ffn):
+    """kq_ffn_pass_q4k_q6k with an entry gain, twice in a row on one
+    workspace whose contents start as garbage: the same bits as the per-layer
+    calls with that gain as layer 0's next gain.  Odd and even layer counts
+    (the last residual must land in the caller's buffer either way), workgroups
     without gate+up rows (fewer 16-row groups than compute units), one down
     row per workgroup, and the largest hidden size."""
     st = Stack(layers, hidden, ffn, "q6k", cfg=21)
     _, r0 = start_state(hidden, cfg=21)
     h, f, L, D = hidden, ffn, layers, st.dev
     g_entry = dev(I.gains_f32(h, stream=I.stream_id(21, 99, I.ROLE_GNEXT)))
-    # reference: the two-launch pass with g_entry as layer 0's next gain
-    zeros, ones = torch.zeros(h, device="cuda"), torch.ones(h, device="cuda")
+    ones = torch.ones(h, device="cuda")
+    zeros = torch.zeros(h, device="cuda")
     R = [dev(r0), torch.empty(h, device="cuda")]
     X0 = torch.empty(h, device="cuda")
     mid, p = torch.empty(f, device="cuda"), torch.empty(h, device="cuda")
     mid_s = torch.empty(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f), dtype=torch.uint8, device="cuda")
-    try:
-        kq.kq_tune_set_shape(kq.KQ_QTYPE_Q6K, lanes=8)  # the pass's down layout
-        for l in range(L):
-            pp, gp, gn = (zeros, ones, g_entry) if l == 0 else (p, D[l - 1]["gp"], D[l - 1]["gn"])
-            kq.kq_ffn_tail_gate_up_q4k(R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, D[l]["wg"],
-                                       D[l]["wu"], mid, mid_s, kq.KQ_QTYPE_Q6K, f, h)
-            kq.kq_matvec_staged(kq.KQ_QTYPE_Q6K, D[l]["wd"], mid_s, p, h, f)
-        kq.kq_fused_residual_norm(R[L % 2], p, X0, D[L - 1]["gp"], D[L - 1]["gn"], 1, h)
-    finally:
-        kq.kq_tune_set_shape(kq.KQ_QTYPE_Q6K)
+    for l in range(L):
+        pp, gp, gn = (zeros, ones, g_entry) if l == 0 else (p, D[l - 1]["gp"], D[l - 1]["gn"])
+        kq.kq_ffn_tail_gate_up_q4k(R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, D[l]["wg"],
+                                   D[l]["wu"], mid, mid_s, kq.KQ_QTYPE_Q6K, f, h)
+        kq.kq_matvec_staged(kq.KQ_QTYPE_Q6K, D[l]["wd"], mid_s, p, h, f)
+    kq.kq_fused_residual_norm(R[L % 2], p, X0, D[L - 1]["gp"], D[L - 1]["gn"], 1, h)
     torch.cuda.synchronize()
     want_x, want_r = X0.cpu().numpy(), R[L % 2].cpu().numpy()
     assert np.all(np.isfinite(want_x)) and np.all(np.isfinite(want_r))
 
     table = kq.kq_ffn_layer_table([(d["wg"], d["wu"], d["wd"], d["gp"], d["gn"]) for d in D])
     wsb = kq.kq_ffn_pass_workspace_bytes(h, f)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    ws = torch.full((wsb,), 0xA5, dtype=torch.uint8, device="cuda")
     res, xo = torch.empty(h, device="cuda"), torch.empty(h, device="cuda")
-    variants = [(8, 2, 2), (8, 3, 2), (8, 2, 3), (12, 2, 2), (12, 2, 1)]
-    try:
-        for v in variants:
-            kq.kq_tune_set_pass(*v)
-            for rep in range(2):
-                print(f"variant {v} call {rep}", flush=True)
-                res.copy_(dev(r0))
-                xo.fill_(float("nan"))
-                kq.kq_ffn_pass_q4k_q6k(table, L, res, xo, g_entry, ws, wsb, h, f)
-                torch.cuda.synchronize()
-                c = ws[:512].view(torch.int32).cpu().numpy()
-                assert c[0] == 0 and c[32] == 0 and c[64] == 0, f"{v}: counters {c[[0, 32, 64]]}"
-                assert np.array_equal(xo.cpu().numpy(), want_x), f"{v} call {rep}: x differs"
-                assert np.array_equal(res.cpu().numpy(), want_r), f"{v} call {rep}: residual differs"
-    finally:
-        kq.kq_tune_set_pass(0, 0, 0)
+    for rep in range(2):
+        res.copy_(dev(r0))
+        xo.fill_(float("nan"))
+        kq.kq_ffn_pass_q4k_q6k(table, res, xo, g_entry, ws, wsb, h, f)
+        torch.cuda.synchronize()
+        assert np.array_equal(xo.cpu().numpy(), want_x), f"call {rep}: x differs"
+        assert np.array_equal(res.cpu().numpy(), want_r), f"call {rep}: residual differs"
