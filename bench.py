@@ -74,8 +74,8 @@ STAGED_BYTES = {
     "down_staged": q6k_bytes(HIDDEN, FFN) + staged_bytes(16, FFN) + 4 * HIDDEN,
     "tail_staged": 4 * HIDDEN * 6 + staged_bytes(32, HIDDEN),
     # the previous layer's tail fused into gate+up: the tail's four inputs and
-    # the residual it writes, both matrices, mid staged for the down matvec
-    "tail_gate_up": 2 * q4k_bytes(FFN, HIDDEN) + 5 * 4 * HIDDEN + staged_bytes(16, FFN),
+    # the residual it writes, both matrices, mid f32 and staged
+    "tail_gate_up": 2 * q4k_bytes(FFN, HIDDEN) + 5 * 4 * HIDDEN + 4 * FFN + staged_bytes(16, FFN),
 }
 # one token through the pass: per layer gate+up (x in, mid out), down, tail; plus the entry norm.
 # The same count serves every schedule of the pass, so their rates compare work for work.
@@ -251,7 +251,7 @@ class FFNChain:
         R = self.R
         return (
             ("tail_gate_up", lambda: kq.kq_ffn_tail_gate_up_q4k(
-                R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, self.Wg[l], self.Wu[l], None,
+                R[l % 2], pp, gp, gn, R[(l + 1) % 2], None, self.Wg[l], self.Wu[l], self.mid,
                 self.mid_s, Q6, FFN, HIDDEN, 1e-8, 1e-5)),
             ("down_staged", lambda: kq.kq_matvec_staged(Q6, self.Wd[l], self.mid_s, self.p,
                                                         HIDDEN, FFN)),
@@ -908,7 +908,7 @@ def main():
                    "algorithmic_bytes_per_step": pass_bytes,
                    "timing": "one graph replay per step of kq_ffn_pass_q4k_q6k, which enqueues "
                              "per layer the previous layer's tail (or the entry norm) fused with "
-                             "gate, up and SiLU (writing mid staged) and the Q6_K down matvec on "
+                             "gate, up and SiLU (writing mid, and mid staged) and the Q6_K down matvec on "
                              "it, then the last dual-eps tail; 105 launches"},
         "alternatives": alternatives,
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),

@@ -403,9 +403,7 @@ kq_status kq_ffn_gate_up_q4k_staged(const void *W_gate, const void *W_up, const 
  *   residual_out  [k] f32 output, 16-byte aligned; must not overlap
  *                 residual_in (every workgroup reads it while one writes).
  *   next_in       NULL or [k] f32 output, 16-byte aligned.
- *   W_gate, W_up, mid, mid_s, mid_qtype  as for kq_ffn_gate_up_q4k_staged,
- *                 except that mid may be NULL when mid_s is given (only the
- *                 staged form is written).
+ *   W_gate, W_up, mid, mid_s, mid_qtype  as for kq_ffn_gate_up_q4k_staged.
  *   n_rows        >= 1 (the tail's outputs need a launch), < 2^31.
  *   k             multiple of 256, <= KQ_MAX_FUSED_TAIL_K.
  *   eps_post, eps_next  >= 0 and finite.
@@ -448,7 +446,8 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
  *              caller-owned device memory of at least
  *              kq_ffn_pass_workspace_bytes(hidden, ffn) bytes, 256-byte
  *              aligned, for the relay buffers (the residual's second buffer,
- *              the down output and staged mid); no initial contents needed.
+ *              the down output, mid and its staged form); no initial contents
+ *              needed.
  *              Calls sharing a workspace must be ordered.
  *   hidden     multiple of 256, <= KQ_MAX_FUSED_TAIL_K.
  *   ffn        multiple of 256, <= KQ_MAX_K.

@@ -497,7 +497,7 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
                                   float eps_post, float eps_next, void *stream)
 {
     if (!residual_in || !projected || !g_post || !g_next || !residual_out || !W_gate || !W_up ||
-        (!mid && !mid_s))
+        !mid)
         return KQ_ERR_NULL;
     if (mid_s && !staged_group(mid_qtype)) return KQ_ERR_SHAPE;
     if (n_rows < 1 || n_rows > INT32_MAX) return KQ_ERR_SHAPE;  // the tail needs a launch
@@ -512,7 +512,7 @@ kq_status kq_ffn_tail_gate_up_q4k(const float *residual_in, const float *project
         !aligned(W_gate, 16) || !aligned(W_up, 16) || !aligned(mid, 4) || !aligned(mid_s, 16))
         return KQ_ERR_ALIGN;
     const int64_t vb = k * 4, wbytes = n_rows * (k / KQ_QK) * KQ_Q4K_BLOCK_BYTES;
-    const int64_t mb = mid ? n_rows * 4 : 0, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
+    const int64_t mb = n_rows * 4, msb = mid_s ? staged_size(mid_qtype, n_rows) : 0;
     const void *ins[] = {residual_in, projected, g_post, g_next, W_gate, W_up};
     const int64_t inb[] = {vb, vb, vb, vb, wbytes, wbytes};
     void *outs[] = {residual_out, next_in, mid, mid_s};
@@ -603,7 +603,7 @@ namespace {
 
 // Relay buffers of kq_ffn_pass_q4k_q6k in its workspace (byte offsets).
 struct PassWs {
-    int64_t res_alt, p, mid_s, total;
+    int64_t res_alt, p, mid_s, mid, total;
 };
 
 PassWs pass_ws_layout(int64_t hidden, int64_t ffn)
@@ -613,7 +613,8 @@ PassWs pass_ws_layout(int64_t hidden, int64_t ffn)
     w.res_alt = 0;
     w.p = up(4 * hidden);
     w.mid_s = w.p + up(4 * hidden);
-    w.total = w.mid_s + up(staged_size(KQ_QTYPE_Q6K, ffn));
+    w.mid = w.mid_s + up(staged_size(KQ_QTYPE_Q6K, ffn));
+    w.total = w.mid + up(4 * ffn);
     return w;
 }
 
@@ -672,6 +673,7 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
     float *alt = (float *)(ws + w.res_alt);
     float *p = (float *)(ws + w.p);
     uint8_t *mid_s = ws + w.mid_s;
+    float *mid = (float *)(ws + w.mid);
     const hipStream_t st = (hipStream_t)stream;
     const int h = (int)hidden, f = (int)ffn;
     // Layer l's tail reads the current residual buffer and writes the other
@@ -692,7 +694,7 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
                               eps_next};
         s = from_hip(kqi::launch_gate_up_q4k((const uint8_t *)layers[l].W_gate,
                                              (const uint8_t *)layers[l].W_up, nullptr, nullptr,
-                                             nullptr, mid_s, 16, f, h, &t, st));
+                                             mid, mid_s, 16, f, h, &t, st));
         if (s != KQ_OK) return s;
         if (!skip_write) {
             float *tmp = cur;

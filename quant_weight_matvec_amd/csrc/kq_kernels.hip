@@ -347,7 +347,7 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         acc_u = lane_group_sum<LANES>(acc_u);
         if (sub == 0 && rv) {
             const float m = (acc_g / (1.0f + __expf(-acc_g))) * acc_u;
-            if (mid) mid[r] = m;
+            mid[r] = m;  // (unconditional: a branch on mid here made the kernel 10 % slower)
             if (mid_s) midl[r - r_lo] = m;
         }
         t0 += nwaves * RPT;

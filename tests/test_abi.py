@@ -435,9 +435,9 @@ def test_ffn_pass_validation():
     h, f = 6656, 19968
     q4b, q6b = f * (h // 256) * 144, h * (f // 256) * 210
     need = kq.kq_ffn_pass_workspace_bytes(h, f)
-    # the residual's second buffer, the down output, staged mid for Q6_K
+    # the residual's second buffer, the down output, staged mid for Q6_K, mid
     up = lambda b: (b + 255) // 256 * 256
-    assert need == 2 * up(4 * h) + up(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f))
+    assert need == 2 * up(4 * h) + up(kq.kq_staged_bytes(kq.KQ_QTYPE_Q6K, f)) + up(4 * f)
     base = 0x10000000
 
     def layer(l, **kw):
