@@ -99,8 +99,13 @@ def log(*a):
 
 
 LIB_PATH = os.path.join(ROOT, "quant_weight_matvec_amd", "libkq.so")
-# instantiations whose machine code a committed counter summary covers
-PMC_KERNELS = {"gate_up": "q4k_gate_up_kernel", "down": "q6k_matvec_kernel"}
+# the timed instantiations (mangled-name prefixes) whose machine code a
+# committed counter summary covers: q4k_gate_up_kernel<8, 3, 1, 16, true> and
+# q6k_matvec_kernel<8, 3, 1, 8>.  Only these are hashed, since the compiler
+# may schedule other instantiations of the same template differently when
+# unrelated code in the file changes.
+PMC_KERNELS = {"gate_up": "q4k_gate_up_kernelILi8ELi3ELi1ELi16ELb1E",
+               "down": "q6k_matvec_kernelILi8ELi3ELi1ELi8EE"}
 
 
 def _elf_sections(elf: bytes):
@@ -565,7 +570,7 @@ def decode_shapes(torch, kq, I, reps=5, launches=52, max_launches=1200):
     return out
 
 
-def verify_pass(torch, kq, chain, ms=(1, 2, 4, 8, 16), reps=3):
+def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
     """The speculative-verify batch through the 52-layer FFN pass (Ch 10
     "The forward pass at a glance", sections 10.2-10.3; Ch 36 section 36.4):
     for M activation rows, per layer kq_ffn_gate_up_q4k_small_m (gate, up and
@@ -624,7 +629,7 @@ def embedding_lookup(torch, kq, I, reps=5, launches=52):
     return out
 
 
-def small_m_sweep(torch, kq, I, ms=(1, 2, 4, 8, 16), reps=5, launches=52):
+def small_m_sweep(torch, kq, I, ms=(1, 2, 3, 4, 8, 16), reps=5, launches=52):
     """kq_matmul_small_m at the verify shapes, M = 1..16: per-launch time from a
     graph of 52 launches over >= 1 GiB of rotated weight copies (so the
     Infinity Cache cannot serve them), median and CV of 5 replays, with GB/s

@@ -230,8 +230,10 @@ kq_status kq_matvec_q6k(const void *W, const float *x, float *y, int64_t n_rows,
  * residual", section 19.7, times M = 16): for m < M and r < n_rows,
  *   Y[m * ldy + r] = sum_i w[r,i] * X[m * ldx + i].
  * Each weight is read from memory once and applied to all M rows.  M = 1 runs
- * the matvec of that qtype (identical results); M >= 2 runs the matrix-core
- * kernel, whose partial sums over ranges of k may pass through `workspace`.
+ * the matvec of that qtype (identical results).  Q4_K at M = 2 runs the
+ * matvec's integer dot path on both rows (no workspace); other M >= 2 run the
+ * matrix-core kernel, whose partial sums over ranges of k may pass through
+ * `workspace` (kq_tune_set_small_m_rows moves the boundary).
  *   qtype   KQ_QTYPE_Q4K or KQ_QTYPE_Q6K.
  *   W       weight bytes as for the matvec of that qtype (same alignment).
  *   X       [M][ldx] f32, ldx >= k and ldx % 4 == 0, 16-byte aligned.

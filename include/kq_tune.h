@@ -63,6 +63,22 @@ kq_status kq_tune_matvec_plan(int qtype, int64_t n_rows, int64_t k, int staged, 
 kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int cus, int64_t *out);
 
 /*
+ * Process-wide choice between the two kernels of kq_matmul_small_m (and of
+ * kq_matmul_small_m_noalloc and kq_ffn_gate_up_q4k_small_m): activation
+ * counts 2 <= M <= max_m of `qtype` (KQ_QTYPE_Q4K or KQ_QTYPE_Q6K) run the
+ * matvec's integer dot path (each workgroup stages all M rows into LDS and
+ * applies every weight unit to each; no workspace), where the staged rows fit
+ * the LDS; larger M the matrix-core kernel.  The default max_m is 2 for
+ * Q4_K and 0 for Q6_K; max_m 0 sends every M >= 2 to the matrix-core kernel;
+ * -1 restores the default.  Both give results within the matvec tolerance,
+ * and each row of the dot path equals the 8-lane matvec of that row bit for
+ * bit.  The workspace size follows the choice.  Not thread-safe against
+ * concurrent calls.
+ * Errors: KQ_ERR_SHAPE for an unknown qtype or max_m outside -1..4.
+ */
+kq_status kq_tune_set_small_m_rows(int qtype, int max_m);
+
+/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of `block` threads and
  * writes grid*block/64 xor-folded words to the device buffer `out` (so the

@@ -285,7 +285,7 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
             overlap(workspace, need, W, wbytes))
             return KQ_ERR_ALIAS;
     }
-    return from_hip(kqi::launch_small_m_mfma(qtype, (const uint8_t *)W, X, ldx, Y, ldy,
+    return from_hip(kqi::launch_small_m(qtype, (const uint8_t *)W, X, ldx, Y, ldy,
                                              (int)n_rows, (int)k, m, workspace, workspace_bytes,
                                              (hipStream_t)stream));
 }
@@ -323,10 +323,11 @@ kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const
             overlap(workspace, need, W_gate, wbytes) || overlap(workspace, need, W_up, wbytes))
             return KQ_ERR_ALIAS;
     }
-    hipError_t e = kqi::launch_small_m_mfma(KQ_QTYPE_Q4K, (const uint8_t *)W_gate, X, ldx, Mid, ldm,
+    // gate into Mid, then up with the SiLU of the gate values it overwrites
+    hipError_t e = kqi::launch_small_m(KQ_QTYPE_Q4K, (const uint8_t *)W_gate, X, ldx, Mid, ldm,
                                             (int)n_rows, (int)k, m, workspace, workspace_bytes, st);
     if (e != hipSuccess) return from_hip(e);
-    return from_hip(kqi::launch_small_m_mfma(KQ_QTYPE_Q4K, (const uint8_t *)W_up, X, ldx, Mid, ldm,
+    return from_hip(kqi::launch_small_m(KQ_QTYPE_Q4K, (const uint8_t *)W_up, X, ldx, Mid, ldm,
                                              (int)n_rows, (int)k, m, workspace, workspace_bytes, st,
                                              Mid, ldm));
 }
@@ -708,6 +709,11 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
     return from_hip(kqi::launch_tail(cur, p, x_out, layers[n_layers - 1].g_post,
                                      layers[n_layers - 1].g_next, 1, h, eps_post, eps_next,
                                      nullptr, 0, st));
+}
+
+kq_status kq_tune_set_small_m_rows(int qtype, int max_m)
+{
+    return kqi::set_rows_max_m(qtype, max_m) ? KQ_OK : KQ_ERR_SHAPE;
 }
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)

@@ -77,8 +77,21 @@ bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m);
 hipError_t launch_small_m_noalloc(int qtype, const uint8_t *W, const float *X, int64_t ldx,
                                   float *Y, int64_t ldy, int n_rows, int k, int m,
                                   hipStream_t stream);
+// Small M through the matvec's integer dot path (rows_kernel, kq_kernels.hip):
+// each workgroup stages the m rows into LDS, then dots each weight unit with
+// every row; no workspace.  rows_path says whether (qtype, n_rows, k, m) takes
+// it (the default or overridden largest M per qtype, and the rows fit the
+// LDS).  With gate, Y = silu(gate) * (W X) row by row (gate may be Y).
+int rows_max_m(int qtype);
+bool set_rows_max_m(int qtype, int max_m);  // -1 restores the default
+bool rows_path(int qtype, int n_rows, int k, int m);
+hipError_t launch_rows(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+                       int64_t ldy, int n_rows, int k, int m, const float *gate, int64_t ldg,
+                       hipStream_t stream);
+// Small M (2..16): the dot path where rows_path says so, else the
+// matrix-core kernel.
 // gate (nullable): Y = silu(gate) * (W X), gate [m][ldg]; it may be Y itself.
-hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream,
                                const float *gate = nullptr, int64_t ldg = 0);

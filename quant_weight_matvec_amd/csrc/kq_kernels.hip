@@ -462,6 +462,151 @@ __global__ __launch_bounds__(64 * WMAX) void q6k_matvec_kernel(const MatSegs seg
     }
 }
 
+// Q4_K and Q6_K as seen by rows_kernel: unit load, unit dot, scale group.
+template <int FMT> struct RowsFmt;
+template <> struct RowsFmt<4> {
+    using Unit = Q4Unit;
+    static constexpr int kBytes = kQ4Bytes, kGroup = 32;
+    static __device__ __forceinline__ Unit load(const uint8_t *sb, int h) { return q4_load(sb, h); }
+    template <int LIMBS>
+    static __device__ __forceinline__ float dot(const Unit &u, int h, int base, int k,
+                                                const uint8_t *planes, const float *tscale,
+                                                const float *tsum)
+    {
+        return q4_unit_dot<LIMBS>(u, h, base, k, planes, tscale, tsum);
+    }
+};
+template <> struct RowsFmt<6> {
+    using Unit = Q6Unit;
+    static constexpr int kBytes = kQ6Bytes, kGroup = 16;
+    static __device__ __forceinline__ Unit load(const uint8_t *sb, int h) { return q6_load(sb, h); }
+    template <int LIMBS>
+    static __device__ __forceinline__ float dot(const Unit &u, int, int base, int k,
+                                                const uint8_t *planes, const float *tscale,
+                                                const float *tsum)
+    {
+        return q6_unit_dot<LIMBS>(u, base, k, planes, tscale, tsum);
+    }
+};
+
+// MR activation rows through the matvec's integer dot path (Ch 36 "Prefill vs
+// decode", section 36.4: each weight row is read once and applied to every
+// input column).  Each workgroup stages all MR rows of X (row m at
+// X + m * ldx) into LDS with the matvec's encoding, then loads each weight
+// unit once and dots it with every row.  Per row the arithmetic is that of
+// the 8-lane matvec on the same row, so a row's result does not depend on
+// MR, and the call needs no memory beyond its operands.  At small MR the matvec is bound by its weight stream
+// with the VALU mostly idle, so the extra dot products cost little time,
+// where the matrix-core path spends its VALU on f16 conversions and
+// per-sub-block scaling.  With SILU, Y = silu(gate) * (W X) row by row; gate
+// may be Y itself (each element is read before it is overwritten).
+template <int FMT, int LIMBS, int DEPTH, int WMAX, int MR, bool SILU>
+__global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restrict__ W,
+                                                         const float *__restrict__ X, int64_t ldx,
+                                                         float *Y, int64_t ldy,
+                                                         const float *gate, int64_t ldg,
+                                                         int n_rows, int k)
+{
+    using F = RowsFmt<FMT>;
+    constexpr int LANES = 8, RPT = 64 / LANES;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int nsb = k >> 8;
+    const int units = 2 * nsb;
+    const int64_t row_bytes = (int64_t)nsb * F::kBytes;
+    const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
+    const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+    const int sub = lane % LANES;
+    const int h = sub & 1;
+    const int steps = (units + LANES - 1) / LANES;
+    const int sb = (int)staged_bytes<F::kGroup, LIMBS>(k);  // one staged row (a multiple of 16)
+    // row 0 of X ahead of any weight load (one round trip)
+    constexpr int B = kXPre / WMAX;
+    XPre<B> pre = x_preload<B>(X, k >> 2);
+    int t0 = r_lo + wave * RPT;
+    int r = t0 + lane / LANES;
+    bool rv = r < r_hi;
+    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    auto load = [&](int st) {
+        const int u = min(sub + LANES * st, units - 1);
+        return F::load(rowp + (int64_t)(u >> 1) * F::kBytes, h);
+    };
+    constexpr int R = DEPTH + 1;
+    typename F::Unit ring[R];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+        ring[j] = load(j);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // every row staged as the matvec stages x, row m at smem + m * sb; the
+    // next row's loads go out before the current row is encoded
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        XPre<B> nxt;
+        if (m + 1 < MR) nxt = x_preload<B>(X + (m + 1) * ldx, k >> 2);
+        stage_activation<F::kGroup, LIMBS, B>(pre, X + m * ldx, nullptr, k, smem + m * sb);
+        if (m + 1 < MR) pre = nxt;
+    }
+    __syncthreads();
+    const int P = (int)plane_bytes(k);
+
+    while (t0 < r_hi) {
+        float acc[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+        auto step = [&](int j, int st, bool prefetch) __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (prefetch) ring[(j + DEPTH) % R] = load(st + DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
+            const int u = sub + LANES * st;
+            const int uc = min(u, units - 1);
+            const bool ok = rv && u < units;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const uint8_t *planes = smem + m * sb;
+                const float *tscale = reinterpret_cast<const float *>(planes + LIMBS * P);
+                const float *tsum = tscale + k / F::kGroup;
+                const float d = F::template dot<LIMBS>(ring[j], h, 256 * (uc >> 1) + 128 * h, k,
+                                                       planes, tscale, tsum);
+                acc[m] += ok ? d : 0.0f;
+            }
+        };
+        int s0 = 0;
+        for (; s0 + R <= steps; s0 += R) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) step(j, s0 + j, true);
+        }
+#pragma unroll
+        for (int j = 0; j + 1 < R; ++j)
+            if (s0 + j < steps) step(j, s0 + j, false);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[m] = lane_group_sum<LANES>(acc[m]);
+        if (sub == 0 && rv) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float y = acc[m];
+                if constexpr (SILU) {
+                    const float g = gate[m * ldg + r];
+                    y = (g / (1.0f + __expf(-g))) * y;
+                }
+                Y[m * ldy + r] = y;
+            }
+        }
+        t0 += nwaves * RPT;
+        r = t0 + lane / LANES;
+        rv = r < r_hi;
+        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        if (t0 < r_hi) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; ++j) {
+                ring[j] = load(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
 // Staged form of a plain activation vector (the encoding the matvec kernels
 // otherwise apply per workgroup), for callers that hand the same x to several
 // matvecs.  One float4 per thread; k is a multiple of 256, so the blocks hold
@@ -914,6 +1059,97 @@ MatSegs one_seg(const uint8_t *W, float *y, int n_rows)
 
 }  // namespace
 
+// ---- small M through the matvec's dot path (rows_kernel) ----
+
+namespace {
+
+constexpr int kRowsMaxMr = 4;
+constexpr int kRowsLds = 160 * 1024 - 512;  // beside the kernel's static LDS
+// largest M sent to rows_kernel by default, per qtype (1: Q4_K, 2: Q6_K),
+// from timings against the matrix-core path at the FFN shapes (graphs of 52
+// launches): Q4_K 19968x6656 at M = 2 25.0 against 27.7 us, at M = 3 and 4
+// 31.0 and 37.6 against 26.2 and 26.7 us (each row re-reads its staged planes
+// from LDS, about 416 bytes per weight unit, so LDS bandwidth grows with M);
+// Q6_K 6656x19968 at M = 2 37.1 against 36.7 us
+constexpr int kRowsDefault[3] = {0, 2, 0};
+std::atomic<int> g_rows_override[3] = {{-1}, {-1}, {-1}};
+
+template <int FMT, int WMAX, int MR, bool SILU>
+hipError_t launch_rows_cfg(const uint8_t *W, const float *X, int64_t ldx, float *Y,
+                           int64_t ldy, const float *gate, int64_t ldg, int n_rows, int k,
+                           int grid, size_t lds, hipStream_t stream)
+{
+    constexpr auto kern = rows_kernel<FMT, KQ_LIMBS, 1, WMAX, MR, SILU>;
+    static std::atomic<uint64_t> done{0};
+    if (lds > 65536) {
+        const hipError_t e = kqi::raise_lds_limit(reinterpret_cast<const void *>(kern), done,
+                                                  kRowsLds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WMAX), lds, stream, W, X, ldx, Y, ldy,
+                       gate, ldg, n_rows, k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace kqi {
+
+int rows_max_m(int qtype)
+{
+    if (qtype != 1 && qtype != 2) return 0;
+    const int o = g_rows_override[qtype].load();
+    return o >= 0 ? o : kRowsDefault[qtype];
+}
+
+bool set_rows_max_m(int qtype, int max_m)
+{
+    if (qtype != 1 && qtype != 2) return false;
+    if (max_m < -1 || max_m > kRowsMaxMr) return false;
+    g_rows_override[qtype].store(max_m);
+    return true;
+}
+
+bool rows_path(int qtype, int n_rows, int k, int m)
+{
+    if (m < 2 || m > rows_max_m(qtype) || n_rows < 1) return false;
+    const int64_t sb = qtype == 1 ? staged_bytes<32, KQ_LIMBS>(k) : staged_bytes<16, KQ_LIMBS>(k);
+    return (int64_t)m * sb <= kRowsLds;
+}
+
+hipError_t launch_rows(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+                       int64_t ldy, int n_rows, int k, int m, const float *gate, int64_t ldg,
+                       hipStream_t stream)
+{
+    const int cus = device_cus();
+    const size_t lds = (size_t)m * (size_t)(qtype == 1 ? staged_bytes<32, KQ_LIMBS>(k)
+                                                       : staged_bytes<16, KQ_LIMBS>(k));
+    const int64_t tasks = ((int64_t)n_rows + 7) / 8;  // 8-row wave tasks
+    // one workgroup per CU: Q4_K with 16 waves (within 128 VGPRs), Q6_K with
+    // 8 (its unit ring needs more than 128 VGPRs)
+    int64_t g = cus;
+    if (g > tasks) g = tasks;
+    const int grid = (int)(g > 0 ? g : 1);
+    const bool silu = gate != nullptr;
+#define KQ_RW(F, WM, MR)                                                                        \
+    if (m == MR)                                                                                \
+        return silu ? launch_rows_cfg<F, WM, MR, true>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, \
+                                                       grid, lds, stream)                       \
+                    : launch_rows_cfg<F, WM, MR, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows,   \
+                                                        k, grid, lds, stream);
+    if (qtype == 1) {
+        KQ_RW(4, 16, 2) KQ_RW(4, 16, 3) KQ_RW(4, 16, 4)
+    } else if (!silu) {
+        if (m == 2) return launch_rows_cfg<6, 8, 2, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
+        if (m == 3) return launch_rows_cfg<6, 8, 3, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
+        if (m == 4) return launch_rows_cfg<6, 8, 4, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
+    }
+#undef KQ_RW
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kqi
+
 namespace kqi {
 
 int device_cus()
@@ -1139,7 +1375,7 @@ const char *variant_names()
     return "q4k/q5k_matvec[lanes=4..64,limbs=3,depth=1..3,silu=0/1,x=f32|staged,group<=4] q6k_matvec[lanes=4..64,limbs=3,depth=1..3,x=f32|staged,group<=4] "
            "embedding[q4k,q5k] "
            "gate_up[q4k, mid staged out: 0/16/32] "
-           "small_m[m=1: matvec; m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; q4k: per-lane weight loads, sub-block scale folded into B, 16 waves x 1 16-row tile; q6k: weight tiles through LDS, m<=8: 16 waves x 1 tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
+           "small_m[m=1: matvec; q4k m=2 (tunable to m<=4): matvec dot path over all rows; other m=2..16: f16 MFMA, x split hi+lo, stream-K over 256-row groups; q4k: per-lane weight loads, sub-block scale folded into B, 16 waves x 1 16-row tile; q6k: weight tiles through LDS, m<=8: 16 waves x 1 tile, m>8: 8 waves x 2] tail[n<=8192: registers, 1 round trip; wider: 3 passes]";
 }
 
 }  // namespace kqi

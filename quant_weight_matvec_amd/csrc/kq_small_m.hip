@@ -1166,6 +1166,7 @@ namespace kqi {
 size_t small_m_workspace_bytes(int qtype, int n_rows, int k, int m)
 {
     if (m < 2) return 0;  // m = 1 runs as the matvec
+    if (rows_path(qtype, n_rows, k, m)) return 0;  // the dot path takes no workspace
     return make_plan(qtype, n_rows, k, m, sm_cus()).ws;
 }
 
@@ -1180,11 +1181,13 @@ void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
     out[5] = p.T;
 }
 
-hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
+hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                                int64_t ldy, int n_rows, int k, int m, void *workspace,
                                int64_t workspace_bytes, hipStream_t stream, const float *gate,
                                int64_t ldg)
 {
+    if (rows_path(qtype, n_rows, k, m))
+        return launch_rows(qtype, W, X, ldx, Y, ldy, n_rows, k, m, gate, ldg, stream);
     const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
     if ((int64_t)p.ws > workspace_bytes) return hipErrorInvalidValue;
     return launch_plan(p, qtype, W, X, ldx, Y, ldy, n_rows, k, m,
@@ -1195,6 +1198,7 @@ hipError_t launch_small_m_mfma(int qtype, const uint8_t *W, const float *X, int6
 bool small_m_noalloc_fits(int qtype, int n_rows, int k, int m)
 {
     if (m < 2) return true;
+    if (rows_path(qtype, n_rows, k, m)) return true;  // no scratch
     const SmPlan p = make_plan(qtype, n_rows, k, m, sm_cus());
     if (p.ws == 0) return true;  // no row group is split: the scratch is not used
     const int64_t rgs = ((int64_t)n_rows + kSmRows - 1) / kSmRows;
@@ -1206,6 +1210,8 @@ hipError_t launch_small_m_noalloc(int qtype, const uint8_t *W, const float *X, i
                                   float *Y, int64_t ldy, int n_rows, int k, int m,
                                   hipStream_t stream)
 {
+    if (rows_path(qtype, n_rows, k, m))  // the dot path uses no scratch
+        return launch_rows(qtype, W, X, ldx, Y, ldy, n_rows, k, m, nullptr, 0, stream);
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;

@@ -420,6 +420,7 @@ def test_kernel_code_hash_reads_the_built_code_object():
     assert sorted(n for n, _ in bench.kernel_code("")) == sorted(meta)
     for part in bench.PMC_KERNELS.values():
         code = bench.kernel_code(part)
+        assert len(code) == 1, (part, code)  # exactly the timed instantiation
         assert [n for n, _ in code] == sorted(n for n in meta if part in n)
         assert all(len(body) >= 4 and len(body) % 4 == 0 for _, body in code)
         assert bench.kernel_code_hash(part) == bench.kernel_code_hash(part)
@@ -491,3 +492,12 @@ def test_ffn_pass_validation():
         kq.kq_ffn_pass_workspace_bytes(B.KQ_MAX_FUSED_TAIL_K + 256, f)
     t = kq.kq_ffn_layer_table([(1 << 20, 2 << 20, 3 << 20, 4 << 20, 5 << 20)])
     assert len(t) == 1 and t[0].W_down == 3 << 20 and t[0].g_next == 5 << 20
+
+
+def test_small_m_path_switch_validation():
+    assert kq.lib().kq_tune_set_small_m_rows(B.KQ_QTYPE_Q5K, 2) == B.KQ_ERR_SHAPE
+    assert kq.lib().kq_tune_set_small_m_rows(B.KQ_QTYPE_Q4K, 5) == B.KQ_ERR_SHAPE
+    assert kq.lib().kq_tune_set_small_m_rows(B.KQ_QTYPE_Q4K, -2) == B.KQ_ERR_SHAPE
+    for qt in (B.KQ_QTYPE_Q4K, B.KQ_QTYPE_Q6K):
+        for v in (0, 4, -1):
+            assert kq.lib().kq_tune_set_small_m_rows(qt, v) == B.KQ_OK

@@ -1,8 +1,11 @@
 """kq_matmul_small_m (the batched verify matmul) against the CPU oracle.
 
 Contract per output: |Y[m][r] - Y_ref[m][r]| <= 1e-3 * sum_i |w_ri X_mi|, as for
-the matvec.  M = 1 runs the matvec and must equal it bitwise.  M >= 2 runs the
-matrix-core kernel with its stream-K split; shapes below cover row counts
+the matvec.  M = 1 runs the matvec and must equal it bitwise.  Small M (by
+default M = 2 for Q4_K; up to 4 when tuned, where the staged rows fit the
+LDS) runs the matvec's dot path on every row at once; larger M the
+matrix-core kernel with its stream-K split (both are forced below); shapes
+below cover row counts
 that are not multiples of the 16-row tile or the 256-row group, k from one
 superblock up, workgroups whose range holds one tile, several row groups, or
 parts of two, and the full FFN shapes on sampled rows.  Every output starts
@@ -192,6 +195,61 @@ def test_workspace_errors():
     with pytest.raises(kq.KQError):
         kq.kq_matmul_small_m(QT[qt], W, X, k, Y, n, n, k, m, None, 0)
     with pytest.raises(kq.KQError):  # output inside the workspace
-        kq.kq_matmul_small_m(QT[qt], W, X, k, ws, n, n, k, 2, ws, need)
+        kq.kq_matmul_small_m(QT[qt], W, X, k, ws, n, n, k, m, ws, need)
     torch.cuda.synchronize()
     assert torch.isnan(Y).all(), "a rejected call wrote its output"
+
+
+@pytest.mark.parametrize("qt,n,k,ms", [("q4k", 19968, 6656, (2, 3, 4)), ("q6k", 6656, 19968, (2,))])
+def test_dot_path_rows_equal_the_matvec(qt, n, k, ms):
+    """At the FFN shapes the matvec sums a row over 8 lanes, as the dot path
+    does, so each row of the dot path equals the matvec of that activation
+    row bit for bit (the same staged encoding and per-row arithmetic).  The
+    dot path takes no workspace."""
+    W = weights(qt, n, k, 7700)
+    X = I.normal_f32((4, k), stream=7701)
+    Wd, Xd = dev(W), dev(X)
+    mv = kq.kq_matvec_q4k if qt == "q4k" else kq.kq_matvec_q6k
+    ref = []
+    for i in range(4):
+        y = nan_like(n)
+        mv(Wd, Xd[i], y, n, k)
+        ref.append(y)
+    torch.cuda.synchronize()
+    ref = [y.cpu().numpy().astype(np.float64) for y in ref]
+    try:
+        kq.kq_tune_set_small_m_rows(QT[qt], 4)
+        assert all(kq.kq_matmul_small_m_workspace_bytes(QT[qt], n, k, m) == 0 for m in ms)
+        for m in ms:
+            Yg = run(qt, Wd, Xd, k, n, k, m)
+            for i in range(m):
+                assert np.array_equal(Yg[i], ref[i]), f"{qt} m={m} row {i}"
+    finally:
+        kq.kq_tune_set_small_m_rows(QT[qt], -1)
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_both_small_m_paths_forced(qt, m):
+    """The dot path and the matrix-core kernel, each forced for the same
+    shapes (ragged rows, a k of a few superblocks, the full Q4_K row width),
+    meet the oracle's tolerance; the noalloc form equals the workspace form
+    on each path."""
+    for n, k in ((333, 1280), (4097, 6656)):
+        if qt == "q6k" and k == 6656:
+            k = 5120
+        W, X = weights(qt, n, k, 7800 + m), I.normal_f32((m, k), stream=7810 + m)
+        Wd, Xd = dev(W), dev(X)
+        Yr, S = O.matmul(qt, W, X, n, k, nthreads=NTHREADS)
+        try:
+            for max_m in (4, 0):
+                kq.kq_tune_set_small_m_rows(QT[qt], max_m)
+                Yg = run(qt, Wd, Xd, k, n, k, m)
+                for i in range(m):
+                    assert_matvec_close(Yg[i], Yr[i], S[i], what=f"{qt} {n}x{k} m={m} path {max_m} row {i}")
+                Y2 = nan_like((m, n + 3))
+                kq.kq_matmul_small_m_noalloc(QT[qt], Wd, Xd, k, Y2, n + 3, n, k, m)
+                torch.cuda.synchronize()
+                assert np.array_equal(Y2.cpu().numpy().astype(np.float64)[:, :n], Yg)
+        finally:
+            kq.kq_tune_set_small_m_rows(QT[qt], -1)

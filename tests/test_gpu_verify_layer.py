@@ -47,7 +47,7 @@ def workspace(m):
     return torch.zeros(max(need, 256) // 4, dtype=torch.int32, device="cuda"), need
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 16])
 def test_verify_layer_per_row(layer, m):
     d, h = layer["dev"], layer["host"]
     X, res = layer["X"][:m], layer["res"][:m]
