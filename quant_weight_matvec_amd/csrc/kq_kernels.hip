@@ -266,9 +266,11 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
         }
     };
     // the first weight loads go out before the activation staging; with TAIL
-    // once the tail's operands are in (issued earlier, they delay the tail's
-    // first-touch reads behind the whole chip's weight requests)
-    if constexpr (!TAIL) ring_prologue();
+    // right behind the tail's operand loads (issued before them, they delay
+    // the tail's first-touch reads behind the whole chip's weight requests;
+    // issued after the tail's sums, as they once were, the pass measured
+    // 0.3 % slower)
+    ring_prologue();
 
     if constexpr (TAIL) {
         // the standalone tail's arithmetic, in its order; threads past its
@@ -298,7 +300,6 @@ __global__ __launch_bounds__(64 * WMAX) void q4k_gate_up_kernel(const uint8_t *_
             sr += sumsq4(tr[j]);
         }
         sr = block_sum_fresh(sr, red[1]);
-        ring_prologue();
         const float inv_r = rsqrtf(__builtin_fmaf(sr, inv_n, tl.eps_next));
         uint32_t *plane = reinterpret_cast<uint32_t *>(smem);
         float *tsc = reinterpret_cast<float *>(smem + LIMBS * plane_bytes(k));
