@@ -261,12 +261,16 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
  * for m < M and r < n_rows,
  *   Mid[m * ldm + r] = silu((W_gate X[m])[r]) * (W_up X[m])[r],
  * silu(z) = z / (1 + exp(-z)); both matrices Q4_K, n_rows x k.  M = 1 runs the
- * one-launch gate+up kernel (the result of kq_ffn_gate_up_q4k); M >= 2 runs
- * the matrix-core kernel twice (gate into Mid, then up with the SiLU product
+ * one-launch gate+up kernel (the result of kq_ffn_gate_up_q4k).  M = 2 and 3
+ * run gate and up through the matvec's integer dot path in one launch, and
+ * each row of Mid is then kq_ffn_gate_up_q4k of that row of X, bit for bit
+ * (kq_tune_set_gate_up_rows moves this boundary).  Larger M run
+ * kq_matmul_small_m twice (gate into Mid, then up with the SiLU product
  * applied as each output is stored), each within the kq_matmul_small_m
  * accuracy of its own matvec.
  *   X, ldx, m, workspace, workspace_bytes  as for kq_matmul_small_m with
- *          qtype KQ_QTYPE_Q4K (the same workspace size serves both launches).
+ *          qtype KQ_QTYPE_Q4K (the same workspace size serves both launches;
+ *          the one-launch dot path uses none).
  *   Mid    [M][ldm] f32 output, ldm >= n_rows, 4-byte aligned; must not
  *          overlap W_gate, W_up, X or the workspace.
  * A layer of the verify batch is this call, kq_matmul_small_m on Mid (the

@@ -79,6 +79,18 @@ kq_status kq_tune_small_m_plan(int qtype, int64_t n_rows, int64_t k, int m, int 
 kq_status kq_tune_set_small_m_rows(int qtype, int max_m);
 
 /*
+ * Process-wide choice for kq_ffn_gate_up_q4k_small_m: activation counts
+ * 2 <= M <= max_m (where the staged rows fit the LDS) run gate and up through
+ * the matvec's integer dot path in one launch (each row task streams its gate
+ * row's units, then its up row's; no workspace), and each output row then
+ * equals kq_ffn_gate_up_q4k of that activation row bit for bit.  Larger M run
+ * the two small-M launches.  max_m 0 disables it; -1 restores the default (3).
+ * Not thread-safe against concurrent calls.
+ * Errors: KQ_ERR_SHAPE for max_m outside -1..4.
+ */
+kq_status kq_tune_set_gate_up_rows(int max_m);
+
+/*
  * Read-stream probe (benchmark only): reads every byte of the device buffer
  * `buf` once with 16-byte loads over `grid` workgroups of `block` threads and
  * writes grid*block/64 xor-folded words to the device buffer `out` (so the

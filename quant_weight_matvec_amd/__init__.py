@@ -16,5 +16,6 @@ from ._binding import (  # noqa: F401
     kq_fused_residual_norm_staged, kq_ffn_tail_gate_up_q4k,
     kq_ffn_pass_q4k_q6k, kq_ffn_pass_workspace_bytes, kq_ffn_layer_table, KqFfnLayer,
     kq_tune_set_small_m_rows,
+    kq_tune_set_gate_up_rows,
     KQ_MAX_FUSED_TAIL_K,
 )

@@ -109,7 +109,8 @@ def lib() -> C.CDLL:
     L.kq_ffn_pass_workspace_bytes.argtypes = [_i64, _i64]
     L.kq_ffn_pass_workspace_bytes.restype = _i64
     L.kq_tune_set_small_m_rows.argtypes = [C.c_int, C.c_int]
-    for fn in ("kq_ffn_pass_q4k_q6k", "kq_tune_set_small_m_rows", "kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
+    L.kq_tune_set_gate_up_rows.argtypes = [C.c_int]
+    for fn in ("kq_ffn_pass_q4k_q6k", "kq_tune_set_small_m_rows", "kq_tune_set_gate_up_rows", "kq_stage_activation", "kq_matvec_staged", "kq_ffn_gate_up_q4k_staged",
                "kq_ffn_tail_gate_up_q4k",
                "kq_fused_residual_norm_staged",
                "kq_tune_small_m_plan", "kq_tune_matvec_plan",
@@ -333,6 +334,10 @@ def kq_ffn_pass_q4k_q6k(layers, residual, x_out, g_entry, workspace, workspace_b
 
 def kq_tune_set_small_m_rows(qtype: int, max_m: int = -1) -> None:
     _check(lib().kq_tune_set_small_m_rows(int(qtype), int(max_m)), "kq_tune_set_small_m_rows")
+
+
+def kq_tune_set_gate_up_rows(max_m: int = -1) -> None:
+    _check(lib().kq_tune_set_gate_up_rows(int(max_m)), "kq_tune_set_gate_up_rows")
 
 
 def kq_tune_set_shape(qtype: int, lanes: int = 0, waves: int = 0, grid: int = 0,

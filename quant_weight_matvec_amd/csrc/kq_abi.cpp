@@ -315,6 +315,9 @@ kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const
         return from_hip(kqi::launch_gate_up_q4k((const uint8_t *)W_gate, (const uint8_t *)W_up, X,
                                                 nullptr, Mid, nullptr, 0, (int)n_rows, (int)k,
                                                 nullptr, st));
+    if (kqi::gate_up_rows_path((int)n_rows, (int)k, m))  // one launch, no workspace
+        return from_hip(kqi::launch_rows_gate_up((const uint8_t *)W_gate, (const uint8_t *)W_up, X,
+                                                 ldx, Mid, ldm, (int)n_rows, (int)k, m, st));
     const int64_t need = (int64_t)kqi::small_m_workspace_bytes(KQ_QTYPE_Q4K, (int)n_rows, (int)k, m);
     if (need > 0) {
         if (!workspace) return KQ_ERR_NULL;
@@ -714,6 +717,11 @@ kq_status kq_ffn_pass_q4k_q6k(const kq_ffn_layer *layers, int n_layers, float *r
 kq_status kq_tune_set_small_m_rows(int qtype, int max_m)
 {
     return kqi::set_rows_max_m(qtype, max_m) ? KQ_OK : KQ_ERR_SHAPE;
+}
+
+kq_status kq_tune_set_gate_up_rows(int max_m)
+{
+    return kqi::set_gate_up_rows_max_m(max_m) ? KQ_OK : KQ_ERR_SHAPE;
 }
 
 kq_status kq_tune_set_shape(int qtype, int lanes, int waves, int grid, int depth)

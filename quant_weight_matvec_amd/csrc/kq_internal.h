@@ -88,6 +88,15 @@ bool rows_path(int qtype, int n_rows, int k, int m);
 hipError_t launch_rows(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
                        int64_t ldy, int n_rows, int k, int m, const float *gate, int64_t ldg,
                        hipStream_t stream);
+// The verify gate+up through the dot path in one launch: each row task
+// streams its gate row's units, then its up row's, and Mid = silu(gate X) *
+// (up X); gate_up_rows_path says whether (n_rows, k, m) takes it.
+int gate_up_rows_max_m();
+bool set_gate_up_rows_max_m(int max_m);  // -1 restores the default
+bool gate_up_rows_path(int n_rows, int k, int m);
+hipError_t launch_rows_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *X, int64_t ldx,
+                               float *Mid, int64_t ldm, int n_rows, int k, int m,
+                               hipStream_t stream);
 // Small M (2..16): the dot path where rows_path says so, else the
 // matrix-core kernel.
 // gate (nullable): Y = silu(gate) * (W X), gate [m][ldg]; it may be Y itself.

@@ -496,23 +496,33 @@ template <> struct RowsFmt<6> {
 // X + m * ldx) into LDS with the matvec's encoding, then loads each weight
 // unit once and dots it with every row.  Per row the arithmetic is that of
 // the 8-lane matvec on the same row, so a row's result does not depend on
-// MR, and the call needs no memory beyond its operands.  At small MR the matvec is bound by its weight stream
-// with the VALU mostly idle, so the extra dot products cost little time,
-// where the matrix-core path spends its VALU on f16 conversions and
-// per-sub-block scaling.  With SILU, Y = silu(gate) * (W X) row by row; gate
-// may be Y itself (each element is read before it is overwritten).
-template <int FMT, int LIMBS, int DEPTH, int WMAX, int MR, bool SILU>
+// MR, and the call needs no memory beyond its operands.  At small MR the
+// matvec is bound by its weight stream with the VALU mostly idle, so the
+// extra dot products cost little time, where the matrix-core path spends its
+// VALU on f16 conversions and per-sub-block scaling.
+// MODE kRowsPlain: Y = W X.  kRowsSilu: Y = silu(gate) * (W X) row by row;
+// gate may be Y itself (each element is read before it is overwritten).
+// kRowsGateUp (Q4_K): W is the gate matrix and W2 the up matrix; a row task
+// streams the gate row's units, then the up row's, as q4k_gate_up_kernel
+// does (Ch 10 "The forward pass at a glance", section 10.3: gate and up read
+// the same normed input), and Y = silu(W X) * (W2 X): each output row equals
+// that one-launch kernel's at 8 lanes per row bit for bit.
+constexpr int kRowsPlain = 0, kRowsSilu = 1, kRowsGateUp = 2;
+template <int FMT, int LIMBS, int DEPTH, int WMAX, int MR, int MODE>
 __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restrict__ W,
+                                                         const uint8_t *__restrict__ W2,
                                                          const float *__restrict__ X, int64_t ldx,
                                                          float *Y, int64_t ldy,
                                                          const float *gate, int64_t ldg,
                                                          int n_rows, int k)
 {
+    static_assert(MODE != kRowsGateUp || FMT == 4, "gate and up are Q4_K");
     using F = RowsFmt<FMT>;
     constexpr int LANES = 8, RPT = 64 / LANES;
     extern __shared__ __align__(16) uint8_t smem[];
     const int nsb = k >> 8;
     const int units = 2 * nsb;
+    const int units2 = MODE == kRowsGateUp ? 2 * units : units;  // gate units, then up units
     const int64_t row_bytes = (int64_t)nsb * F::kBytes;
     const int r_lo = (int)((int64_t)blockIdx.x * n_rows / gridDim.x);
     const int r_hi = (int)((int64_t)(blockIdx.x + 1) * n_rows / gridDim.x);
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restri
     const int lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
     const int sub = lane % LANES;
     const int h = sub & 1;
-    const int steps = (units + LANES - 1) / LANES;
+    const int steps = (units2 + LANES - 1) / LANES;
     const int sb = (int)staged_bytes<F::kGroup, LIMBS>(k);  // one staged row (a multiple of 16)
     // row 0 of X ahead of any weight load (one round trip)
     constexpr int B = kXPre / WMAX;
@@ -528,10 +538,15 @@ __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restri
     int t0 = r_lo + wave * RPT;
     int r = t0 + lane / LANES;
     bool rv = r < r_hi;
-    const uint8_t *rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+    int64_t rowoff = (int64_t)(rv ? r : r_lo) * row_bytes;
     auto load = [&](int st) {
-        const int u = min(sub + LANES * st, units - 1);
-        return F::load(rowp + (int64_t)(u >> 1) * F::kBytes, h);
+        const int u = min(sub + LANES * st, units2 - 1);
+        if constexpr (MODE == kRowsGateUp)
+            return F::load(u < units ? W + rowoff + (int64_t)(u >> 1) * F::kBytes
+                                     : W2 + rowoff + (int64_t)((u - units) >> 1) * F::kBytes,
+                           h);
+        else
+            return F::load(W + rowoff + (int64_t)(u >> 1) * F::kBytes, h);
     };
     constexpr int R = DEPTH + 1;
     typename F::Unit ring[R];
@@ -553,24 +568,27 @@ __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restri
     const int P = (int)plane_bytes(k);
 
     while (t0 < r_hi) {
-        float acc[MR];
+        float acc[MR], acc_u[MR];  // acc_u: the up sums (kRowsGateUp)
 #pragma unroll
-        for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+        for (int m = 0; m < MR; ++m) acc[m] = acc_u[m] = 0.0f;
         auto step = [&](int j, int st, bool prefetch) __attribute__((always_inline)) {
             __builtin_amdgcn_sched_barrier(0);
             if (prefetch) ring[(j + DEPTH) % R] = load(st + DEPTH);
             __builtin_amdgcn_sched_barrier(0);
             const int u = sub + LANES * st;
-            const int uc = min(u, units - 1);
+            const int uc = min(u, units2 - 1);
+            const int uu = uc < units ? uc : uc - units;  // the unit within its row
             const bool ok = rv && u < units;
+            const bool ok_u = rv && u >= units && u < units2;
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 const uint8_t *planes = smem + m * sb;
                 const float *tscale = reinterpret_cast<const float *>(planes + LIMBS * P);
                 const float *tsum = tscale + k / F::kGroup;
-                const float d = F::template dot<LIMBS>(ring[j], h, 256 * (uc >> 1) + 128 * h, k,
+                const float d = F::template dot<LIMBS>(ring[j], h, 256 * (uu >> 1) + 128 * h, k,
                                                        planes, tscale, tsum);
                 acc[m] += ok ? d : 0.0f;
+                if constexpr (MODE == kRowsGateUp) acc_u[m] += ok_u ? d : 0.0f;
             }
         };
         int s0 = 0;
@@ -582,14 +600,19 @@ __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restri
         for (int j = 0; j + 1 < R; ++j)
             if (s0 + j < steps) step(j, s0 + j, false);
 #pragma unroll
-        for (int m = 0; m < MR; ++m) acc[m] = lane_group_sum<LANES>(acc[m]);
+        for (int m = 0; m < MR; ++m) {
+            acc[m] = lane_group_sum<LANES>(acc[m]);
+            if constexpr (MODE == kRowsGateUp) acc_u[m] = lane_group_sum<LANES>(acc_u[m]);
+        }
         if (sub == 0 && rv) {
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 float y = acc[m];
-                if constexpr (SILU) {
+                if constexpr (MODE == kRowsSilu) {
                     const float g = gate[m * ldg + r];
                     y = (g / (1.0f + __expf(-g))) * y;
+                } else if constexpr (MODE == kRowsGateUp) {
+                    y = (y / (1.0f + __expf(-y))) * acc_u[m];
                 }
                 Y[m * ldy + r] = y;
             }
@@ -597,7 +620,7 @@ __global__ __launch_bounds__(64 * WMAX) void rows_kernel(const uint8_t *__restri
         t0 += nwaves * RPT;
         r = t0 + lane / LANES;
         rv = r < r_hi;
-        rowp = W + (int64_t)(rv ? r : r_lo) * row_bytes;
+        rowoff = (int64_t)(rv ? r : r_lo) * row_bytes;
         if (t0 < r_hi) {
 #pragma unroll
             for (int j = 0; j < DEPTH; ++j) {
@@ -1074,22 +1097,38 @@ constexpr int kRowsLds = 160 * 1024 - 512;  // beside the kernel's static LDS
 // Q6_K 6656x19968 at M = 2 37.1 against 36.7 us
 constexpr int kRowsDefault[3] = {0, 2, 0};
 std::atomic<int> g_rows_override[3] = {{-1}, {-1}, {-1}};
+// largest M of the verify gate+up (kq_ffn_gate_up_q4k_small_m) sent to the
+// fused dot path (gate and up rows in one launch) by default; measured at
+// 19968 x 6656 (graphs of 52 launches): M = 2 40.2 us against 45.2 us for the
+// two single-matrix dot launches, M = 3 52.2 against 52.6 us on the matrix
+// cores, M = 4 61.2 against 53.1 us
+constexpr int kGuRowsDefault = 3;
+std::atomic<int> g_gu_rows_override{-1};
 
-template <int FMT, int WMAX, int MR, bool SILU>
-hipError_t launch_rows_cfg(const uint8_t *W, const float *X, int64_t ldx, float *Y,
-                           int64_t ldy, const float *gate, int64_t ldg, int n_rows, int k,
-                           int grid, size_t lds, hipStream_t stream)
+template <int FMT, int WMAX, int MR, int MODE>
+hipError_t launch_rows_cfg(const uint8_t *W, const uint8_t *W2, const float *X, int64_t ldx,
+                           float *Y, int64_t ldy, const float *gate, int64_t ldg, int n_rows,
+                           int k, int grid, size_t lds, hipStream_t stream)
 {
-    constexpr auto kern = rows_kernel<FMT, KQ_LIMBS, 1, WMAX, MR, SILU>;
+    constexpr auto kern = rows_kernel<FMT, KQ_LIMBS, 1, WMAX, MR, MODE>;
     static std::atomic<uint64_t> done{0};
     if (lds > 65536) {
         const hipError_t e = kqi::raise_lds_limit(reinterpret_cast<const void *>(kern), done,
                                                   kRowsLds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WMAX), lds, stream, W, X, ldx, Y, ldy,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WMAX), lds, stream, W, W2, X, ldx, Y, ldy,
                        gate, ldg, n_rows, k);
     return hipGetLastError();
+}
+
+// one workgroup per CU, 8-row wave tasks
+int rows_grid(int n_rows)
+{
+    const int64_t tasks = ((int64_t)n_rows + 7) / 8;
+    int64_t g = kqi::device_cus();
+    if (g > tasks) g = tasks;
+    return (int)(g > 0 ? g : 1);
 }
 
 }  // namespace
@@ -1122,30 +1161,61 @@ hipError_t launch_rows(int qtype, const uint8_t *W, const float *X, int64_t ldx,
                        int64_t ldy, int n_rows, int k, int m, const float *gate, int64_t ldg,
                        hipStream_t stream)
 {
-    const int cus = device_cus();
     const size_t lds = (size_t)m * (size_t)(qtype == 1 ? staged_bytes<32, KQ_LIMBS>(k)
                                                        : staged_bytes<16, KQ_LIMBS>(k));
-    const int64_t tasks = ((int64_t)n_rows + 7) / 8;  // 8-row wave tasks
     // one workgroup per CU: Q4_K with 16 waves (within 128 VGPRs), Q6_K with
     // 8 (its unit ring needs more than 128 VGPRs)
-    int64_t g = cus;
-    if (g > tasks) g = tasks;
-    const int grid = (int)(g > 0 ? g : 1);
+    const int grid = rows_grid(n_rows);
     const bool silu = gate != nullptr;
-#define KQ_RW(F, WM, MR)                                                                        \
-    if (m == MR)                                                                                \
-        return silu ? launch_rows_cfg<F, WM, MR, true>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, \
-                                                       grid, lds, stream)                       \
-                    : launch_rows_cfg<F, WM, MR, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows,   \
-                                                        k, grid, lds, stream);
+#define KQ_RW(F, WM, MR)                                                                       \
+    if (m == MR)                                                                               \
+        return silu ? launch_rows_cfg<F, WM, MR, kRowsSilu>(W, nullptr, X, ldx, Y, ldy, gate,  \
+                                                            ldg, n_rows, k, grid, lds, stream) \
+                    : launch_rows_cfg<F, WM, MR, kRowsPlain>(W, nullptr, X, ldx, Y, ldy, gate, \
+                                                             ldg, n_rows, k, grid, lds, stream);
     if (qtype == 1) {
         KQ_RW(4, 16, 2) KQ_RW(4, 16, 3) KQ_RW(4, 16, 4)
     } else if (!silu) {
-        if (m == 2) return launch_rows_cfg<6, 8, 2, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
-        if (m == 3) return launch_rows_cfg<6, 8, 3, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
-        if (m == 4) return launch_rows_cfg<6, 8, 4, false>(W, X, ldx, Y, ldy, gate, ldg, n_rows, k, grid, lds, stream);
+        KQ_RW(6, 8, 2) KQ_RW(6, 8, 3) KQ_RW(6, 8, 4)
     }
 #undef KQ_RW
+    return hipErrorInvalidValue;
+}
+
+int gate_up_rows_max_m()
+{
+    const int o = g_gu_rows_override.load();
+    return o >= 0 ? o : kGuRowsDefault;
+}
+
+bool set_gate_up_rows_max_m(int max_m)
+{
+    if (max_m < -1 || max_m > kRowsMaxMr) return false;
+    g_gu_rows_override.store(max_m);
+    return true;
+}
+
+bool gate_up_rows_path(int n_rows, int k, int m)
+{
+    if (m < 2 || m > gate_up_rows_max_m() || n_rows < 1) return false;
+    return (int64_t)m * staged_bytes<32, KQ_LIMBS>(k) <= kRowsLds;
+}
+
+hipError_t launch_rows_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float *X, int64_t ldx,
+                               float *Mid, int64_t ldm, int n_rows, int k, int m,
+                               hipStream_t stream)
+{
+    const size_t lds = (size_t)m * (size_t)staged_bytes<32, KQ_LIMBS>(k);
+    const int grid = rows_grid(n_rows);
+    // 12 waves: 96 rows per round cover the 78 rows a CU gets at the FFN
+    // shape, and the 168-VGPR budget of 3 waves per SIMD holds two sums per
+    // activation row without spills (16 waves' 128 spill at M = 3 and 4)
+#define KQ_GW(MR)                                                                              \
+    if (m == MR)                                                                               \
+        return launch_rows_cfg<4, 12, MR, kRowsGateUp>(Wg, Wu, X, ldx, Mid, ldm, nullptr, 0,   \
+                                                       n_rows, k, grid, lds, stream);
+    KQ_GW(2) KQ_GW(3) KQ_GW(4)
+#undef KQ_GW
     return hipErrorInvalidValue;
 }
 

@@ -501,3 +501,7 @@ def test_small_m_path_switch_validation():
     for qt in (B.KQ_QTYPE_Q4K, B.KQ_QTYPE_Q6K):
         for v in (0, 4, -1):
             assert kq.lib().kq_tune_set_small_m_rows(qt, v) == B.KQ_OK
+    f = kq.lib().kq_tune_set_gate_up_rows
+    assert f(-2) == B.KQ_ERR_SHAPE and f(5) == B.KQ_ERR_SHAPE
+    for v in (0, 4, -1):
+        assert f(v) == B.KQ_OK

@@ -3,14 +3,16 @@ glance", sections 10.2-10.3; Ch 36 "Prefill vs decode", section 36.4: Y = W X
 with M activation rows): kq_ffn_gate_up_q4k_small_m (gate, up and the SiLU
 product for M rows), kq_matmul_small_m on the product (the Q6_K down
 projection) and kq_fused_residual_norm over the M rows, at the full FFN
-shapes (hidden 6656, ffn 19968), for M in {1, 2, 4, 8, 16}.
+shapes (hidden 6656, ffn 19968), for M in {1, 2, 3, 4, 8, 16}.
 
 Each row is held to the oracle's FFN layer from the same (x, residual): the
 tail's outputs within 2e-3 absolute; mid within the bound derived from the
 two matvec tolerances,
   |dmid| <= 1.1 dg (|u| + du) + |silu(g)| du,  dg = 1e-3 S_g, du = 1e-3 S_u
 (1.1 bounds the derivative of silu).  M = 1 takes the one-launch gate+up
-kernel and must equal kq_ffn_gate_up_q4k bit for bit.
+kernel and must equal kq_ffn_gate_up_q4k bit for bit; so must every row at
+the M (2 and 3 by default, up to 4 when tuned) where gate and up run through
+the matvec's dot path in one launch.
 """
 import numpy as np
 import pytest
@@ -102,3 +104,57 @@ def test_verify_gate_up_rows_independent_of_m(layer):
         torch.cuda.synchronize()
         outs.append(mid.cpu().numpy())
     assert np.all(np.isfinite(outs[0])) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("m", [2, 3, 4])
+def test_verify_gate_up_dot_path_rows_equal_the_one_launch_kernel(layer, m):
+    """The fused dot path (forced up to M = 4) gives, row by row, the bits of
+    kq_ffn_gate_up_q4k on that activation row, needs no workspace, and
+    leaves the padding past n_rows inside ldm untouched."""
+    d = layer["dev"]
+    ref = []
+    for i in range(m):
+        y = nan_like(FFN)
+        kq.kq_ffn_gate_up_q4k(d["wg"], d["wu"], dev(layer["X"][i]), y, FFN, HIDDEN)
+        ref.append(y)
+    try:
+        kq.kq_tune_set_gate_up_rows(4)
+        mid = nan_like((m, FFN + 5))
+        kq.kq_ffn_gate_up_q4k_small_m(d["wg"], d["wu"], dev(layer["X"][:m]), HIDDEN, mid, FFN + 5,
+                                      FFN, HIDDEN, m)
+        torch.cuda.synchronize()
+    finally:
+        kq.kq_tune_set_gate_up_rows(-1)
+    assert torch.isnan(mid[:, FFN:]).all(), "wrote past n_rows inside ldm"
+    for i in range(m):
+        assert torch.equal(mid[i, :FFN], ref[i]), f"m={m} row {i}"
+
+
+@pytest.mark.parametrize("n,k", [(333, 1280), (4100, 2816), (8, 256)])
+def test_verify_gate_up_dot_path_ragged(n, k):
+    """Ragged row counts (not a multiple of the 8-row task or of the grid),
+    a k of one superblock, strided X: each row of the fused dot path equals
+    the one-launch kernel on that row bit for bit (that kernel is held to
+    the oracle in the parity tests)."""
+    Wg = I.q4k_matrix(n, k, stream=7900 + n)
+    Wu = I.q4k_matrix(n, k, stream=7901 + n)
+    ldx = k + 8
+    X = np.zeros((4, ldx), np.float32)
+    X[:, :k] = I.normal_f32((4, k), stream=7902 + n)
+    wg, wu, Xd = dev(Wg), dev(Wu), dev(X)
+    ref = []
+    for i in range(4):
+        y = nan_like(n)
+        kq.kq_ffn_gate_up_q4k(wg, wu, dev(np.ascontiguousarray(X[i, :k])), y, n, k)
+        ref.append(y)
+    try:
+        kq.kq_tune_set_gate_up_rows(4)
+        for m in (2, 3, 4):
+            mid = nan_like((m, n + 3))
+            kq.kq_ffn_gate_up_q4k_small_m(wg, wu, Xd, ldx, mid, n + 3, n, k, m)
+            torch.cuda.synchronize()
+            assert torch.isnan(mid[:, n:]).all()
+            for i in range(m):
+                assert torch.equal(mid[i, :n], ref[i]), f"{n}x{k} m={m} row {i}"
+    finally:
+        kq.kq_tune_set_gate_up_rows(-1)
