@@ -170,6 +170,30 @@ def test_nonfinite_activation_poisons_only_its_row(qt, m):
 
 
 @pytest.mark.parametrize("qt", ["q4k", "q6k"])
+def test_nonfinite_activation_dot_path(qt):
+    """The same rule on the dot path (forced; M = 2 of Q4_K takes it by
+    default): a NaN or an infinity in an activation row makes that output row
+    non-finite (the matvec's staging gives its group a non-finite sum) and
+    leaves the other rows as they are."""
+    n, k, m = 400, 2048, 4
+    W = weights(qt, n, k, 7810)
+    X = I.normal_f32((m, k), stream=7811)
+    X[1, 1500] = np.nan
+    X[2, 37] = -np.inf
+    try:
+        kq.kq_tune_set_small_m_rows(QT[qt], 4)
+        Yg = run(qt, dev(W), dev(X), k, n, k, m)
+    finally:
+        kq.kq_tune_set_small_m_rows(QT[qt], -1)
+    assert np.all(np.isnan(Yg[1])), "NaN input did not propagate"
+    assert not np.any(np.isfinite(Yg[2])), "Inf input did not propagate"
+    rest = [0, 3]
+    Yr, S = O.matmul(qt, W, X[rest], n, k, nthreads=NTHREADS)
+    for j, i in enumerate(rest):
+        assert_matvec_close(Yg[i], Yr[j], S[j], what=f"row {i}")
+
+
+@pytest.mark.parametrize("qt", ["q4k", "q6k"])
 def test_strided_x_and_y(qt):
     n, k, m = 333, 1536, 7
     print("worst |dy|/S", check(qt, n, k, m, 7900, ldx=k + 260))
@@ -232,10 +256,10 @@ def test_dot_path_rows_equal_the_matvec(qt, n, k, ms):
 @pytest.mark.parametrize("m", [2, 3, 4])
 def test_both_small_m_paths_forced(qt, m):
     """The dot path and the matrix-core kernel, each forced for the same
-    shapes (ragged rows, a k of a few superblocks, the full Q4_K row width),
-    meet the oracle's tolerance; the noalloc form equals the workspace form
-    on each path."""
-    for n, k in ((333, 1280), (4097, 6656)):
+    shapes (ragged rows, a k of a few superblocks, the full Q4_K row width,
+    a single row of one superblock, 9 rows), meet the oracle's tolerance;
+    the noalloc form equals the workspace form on each path."""
+    for n, k in ((333, 1280), (4097, 6656), (1, 256), (9, 768)):
         if qt == "q6k" and k == 6656:
             k = 5120
         W, X = weights(qt, n, k, 7800 + m), I.normal_f32((m, k), stream=7810 + m)
