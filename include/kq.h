@@ -69,16 +69,21 @@
  *     3 for N(0,1) inputs).  One input thousands of times larger than the
  *     rest of its group, on a near-zero weight, can exceed 1e-3 * S_r; the
  *     bound above still holds.
- *     kq_matmul_small_m (M >= 2): each input enters as x_i + e_i with
- *     |e_i| <= 2^-22 |x_i| + 2^-39 * max|x| over its 256-input superblock of
- *     its activation row.  The tail's outputs agree within 2e-3 absolute.
+ *     kq_matmul_small_m (M >= 2) on the matrix cores: each input enters as
+ *     x_i + e_i with |e_i| <= 2^-22 |x_i| + 2^-39 * max|x| over its
+ *     256-input superblock of its activation row.  On the matvec's dot path
+ *     (Q4_K at M = 2; the verify gate+up at M = 2 and 3) every row is
+ *     computed as the M = 1 matvec computes it, with the bound above.  The
+ *     tail's outputs agree within 2e-3 absolute.
  *   - Calls hold no per-call state between them.  Process-wide state: the
  *     device attributes each launcher caches, the kernel attribute set on
  *     first use, the launch-shape override of kq_tune.h (benchmarks only; it
  *     changes the split of the work, never the definition of the result),
- *     and the scratch array of kq_matmul_small_m_noalloc.  Calls are safe
- *     from several host threads on different streams, except concurrently
- *     with kq_tune_set_shape.
+ *     the small-M path switches of kq_tune.h (they choose between two
+ *     kernels that both meet the bounds above), and the scratch array of
+ *     kq_matmul_small_m_noalloc.  Calls are safe from several host threads
+ *     on different streams, except concurrently with the kq_tune_set_*
+ *     calls.
  */
 #ifndef KQ_H
 #define KQ_H
