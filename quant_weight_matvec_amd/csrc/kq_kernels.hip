@@ -496,10 +496,11 @@ template <> struct RowsFmt<6> {
 // X + m * ldx) into LDS with the matvec's encoding, then loads each weight
 // unit once and dots it with every row.  Per row the arithmetic is that of
 // the 8-lane matvec on the same row, so a row's result does not depend on
-// MR, and the call needs no memory beyond its operands.  At small MR the
-// matvec is bound by its weight stream with the VALU mostly idle, so the
-// extra dot products cost little time, where the matrix-core path spends its
-// VALU on f16 conversions and per-sub-block scaling.
+// MR, and the call needs no memory beyond its operands.  The matvec is bound
+// by its weight stream with the VALU partly idle, so a second row costs
+// little time; every further row adds its own LDS reads of the staged planes
+// (about 416 bytes per Q4_K unit) and integer dots, which is why the
+// matrix-core path wins from three rows on.
 // MODE kRowsPlain: Y = W X.  kRowsSilu: Y = silu(gate) * (W X) row by row;
 // gate may be Y itself (each element is read before it is overwritten).
 // kRowsGateUp (Q4_K): W is the gate matrix and W2 the up matrix; a row task
