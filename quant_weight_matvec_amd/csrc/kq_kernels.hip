@@ -1316,17 +1316,30 @@ hipError_t launch_gate_up_q4k(const uint8_t *Wg, const uint8_t *Wu, const float 
                               int n_rows, int k, const TailArgs *tail, hipStream_t stream)
 {
     // Measured on MI355X at 19968 x 6656 (sweep of lanes 4/8, waves 4..16,
-    // grid 1-2 per CU, depth 1-3): 8 lanes per row, one 12-wave workgroup per
-    // CU and one unit of look-ahead best (31.4 us, 4.8 TB/s; 16 waves within
-    // 1 %).  A 12-wave workgroup holds 80 rows of 8-row tasks in one round.
+    // grid 1-2 per CU, depth 1-3): 8 lanes per row, one workgroup per CU and
+    // one unit of look-ahead best (31.4 us, 4.8 TB/s).  Waves: one 8-row task
+    // each, so the workgroup's rows take one round (at least 8 waves, which
+    // share the staging of x; at least the tail's layout with the fused
+    // tail): the 80 rows a CU gets at the FFN shape take 10 waves, and the
+    // 52-layer pass measured 2.849 ms with 10 against 2.869 ms with 12 (11:
+    // 2.857 ms; six alternating runs on one box).
     const int tiles = (n_rows + 7) / 8;
-    MatvecShape s{8, 12, tiles < device_cus() ? tiles : device_cus(), 2};
+    MatvecShape s{8, 0, tiles < device_cus() ? tiles : device_cus(), 2};
     const MatvecShape o = g_override[1];
     if (o.lanes) s.lanes = o.lanes;
-    if (o.waves) s.waves = o.waves;
     if (o.grid) s.grid = o.grid;
     if (o.depth) s.depth = o.depth;
     if (mid_s && s.grid > n_rows / mid_group) s.grid = n_rows / mid_group;  // whole groups each
+    if (o.waves) {
+        s.waves = o.waves;
+    } else {
+        const int rows_wg = mid_s ? mid_group * ((n_rows / mid_group + s.grid - 1) / s.grid)
+                                  : (n_rows + s.grid - 1) / s.grid;
+        const int rpt = 64 / s.lanes;  // rows of a wave's task
+        int w = (rows_wg + rpt - 1) / rpt;
+        if (tail && w < tail_threads(k) / 64) w = tail_threads(k) / 64;
+        s.waves = w < 8 ? 8 : (w > 16 ? 16 : w);
+    }
     const bool small = s.waves <= 8;
     if (tail) {
         // the fused tail runs on the first tail_threads(k) threads: 8 lanes per
