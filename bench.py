@@ -601,7 +601,9 @@ def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
         run()
         torch.cuda.synchronize()
         g = graph_of(torch, [run])
-        launches = 1 + L * (3 if m == 1 else 4)
+        # gate+up is one launch up to M = 3 (the one-launch kernel at M = 1,
+        # the dot path at M = 2 and 3 by default), two above
+        launches = 1 + L * (3 if m <= 3 else 4)
         med, cv, _ = time_graph(torch, g, 1, reps)
         del g
         wb = WEIGHT_BYTES_PASS * L // LAYERS
