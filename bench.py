@@ -411,7 +411,7 @@ WINDOWS = {"q4k_19968x6656": q4k_bytes(FFN, HIDDEN), "q6k_6656x19968": q6k_bytes
            "gate_up_pair": 2 * q4k_bytes(FFN, HIDDEN)}
 
 
-def read_ceiling(torch, kq, nbytes=4 << 30, reps=5, launches=52):
+def read_ceiling(torch, kq, nbytes=4 << 30, reps=5, launches=52, layers=LAYERS):
     """The HBM read ceiling the matvecs are compared with.
     (1) One pass over a 4 GiB buffer for a sweep of probe variants (workgroup
     size and count, loads in flight per thread, non-temporal or normal loads,
@@ -419,7 +419,11 @@ def read_ceiling(torch, kq, nbytes=4 << 30, reps=5, launches=52):
     (2) With the best variant and with the chunked one, windows of the sizes
     the matvecs stream, at rotating offsets through the 4 GiB buffer, as a
     graph of `launches` back-to-back launches timed like the isolated matvecs
-    (so the two compare like with like)."""
+    (so the two compare like with like).
+    (3) The pass's own shape with no arithmetic: per layer one window of the
+    gate+up pair's bytes, then one of the down's, for `layers` layers (2 per
+    layer launches back to back in one graph), at offsets advancing through
+    the 4 GiB buffer, so no window is still in the Infinity Cache when read."""
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(7)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -463,10 +467,30 @@ def read_ceiling(torch, kq, nbytes=4 << 30, reps=5, launches=52):
             windows[f"{name}_{label}"] = {"bytes": wb16, "windows_rotated": int(nwin),
                                           "us_median": round(med, 3), "us_cv": round(cv, 4),
                                           "GBps": round(wb16 / med / 1e3, 1)}
+    pass_shaped = {}
+    seq = [WINDOWS["gate_up_pair"], WINDOWS["q6k_6656x19968"]] * layers
+    for label, v in (("best", best), ("chunked", best_chunk)):
+        fl = (1 if v["nontemporal"] else 0) | (2 if v["chunked"] else 0)
+        calls, off, total = [], 0, 0
+        for wb in seq:
+            wb16 = (wb + 4095) // 4096 * 4096
+            if off + wb16 > nbytes:
+                off = 0
+            calls.append(lambda o=off, n=wb16, v=v, fl=fl: kq.kq_probe_read_bw(
+                buf[o // 4:], n, out, v["grid"], v["block"], v["unroll"], fl))
+            off += wb16
+            total += wb16
+        g = graph_of(torch, calls)
+        med, cv, _ = time_graph(torch, g, 1, reps)
+        del g
+        pass_shaped[label] = {"layers": layers, "launches": len(calls), "bytes": total,
+                              "ms_median": round(med / 1e3, 4), "cv": round(cv, 4),
+                              "GBps": round(total / med / 1e3, 1)}
     del buf, out
     torch.cuda.empty_cache()
     return {"GBps_4GiB_best": best["GBps"], "best_variant": best, "best_chunked": best_chunk,
-            "sweep_top": sweep[:8], "sweep_worst": sweep[-3:], "size_matched": windows}
+            "sweep_top": sweep[:8], "sweep_worst": sweep[-3:], "size_matched": windows,
+            "pass_shaped": pass_shaped}
 
 
 def isolated_matvecs(torch, kq, I, reps=5, launches=52):
@@ -879,9 +903,13 @@ def main():
         log("verify batch through the 52-layer pass")
         extras["verify_pass"] = verify_pass(torch, kq, chain)
         log("read-stream ceiling probe")
-        rc = read_ceiling(torch, kq)
+        rc = read_ceiling(torch, kq, layers=layers)
         extras["read_ceiling"] = rc
         extras["read_ceiling_GBps"] = rc["GBps_4GiB_best"]
+        # the timed pass against the same stream read with no arithmetic
+        ro = min(r["ms_median"] for r in rc["pass_shaped"].values())
+        extras["pass_vs_read_only_pass"] = {"read_only_ms": ro, "pass_ms": round(ms_per_step, 4),
+                                            "frac": round(ro / ms_per_step, 4)}
         if roofline is not None:
             roofline["frac_of_read_ceiling"] = round(dk["GBps"] / rc["GBps_4GiB_best"], 4)
             roofline["frac_of_size_matched_read"] = round(
