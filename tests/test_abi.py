@@ -505,3 +505,15 @@ def test_small_m_path_switch_validation():
     assert f(-2) == B.KQ_ERR_SHAPE and f(5) == B.KQ_ERR_SHAPE
     for v in (0, 4, -1):
         assert f(v) == B.KQ_OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and a message,
+    before importing torch or touching a device, and prints no JSON line."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
