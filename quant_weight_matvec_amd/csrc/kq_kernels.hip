@@ -498,9 +498,9 @@ template <> struct RowsFmt<6> {
 // the 8-lane matvec on the same row, so a row's result does not depend on
 // MR, and the call needs no memory beyond its operands.  The matvec is bound
 // by its weight stream with the VALU partly idle, so a second row costs
-// little time; every further row adds its own LDS reads of the staged planes
-// (about 416 bytes per Q4_K unit) and integer dots, which is why the
-// matrix-core path wins from three rows on.
+// little time; every further row adds its own integer dots (about 150 VALU
+// instructions per Q4_K unit, the bound) and LDS reads of the staged planes,
+// which is why the matrix-core path wins from three rows on.
 // MODE kRowsPlain: Y = W X.  kRowsSilu: Y = silu(gate) * (W X) row by row;
 // gate may be Y itself (each element is read before it is overwritten).
 // kRowsGateUp (Q4_K): W is the gate matrix and W2 the up matrix; a row task
@@ -1093,8 +1093,8 @@ constexpr int kRowsLds = 160 * 1024 - 512;  // beside the kernel's static LDS
 // largest M sent to rows_kernel by default, per qtype (1: Q4_K, 2: Q6_K),
 // from timings against the matrix-core path at the FFN shapes (graphs of 52
 // launches): Q4_K 19968x6656 at M = 2 25.0 against 27.7 us, at M = 3 and 4
-// 31.0 and 37.6 against 26.2 and 26.7 us (each row re-reads its staged planes
-// from LDS, about 416 bytes per weight unit, so LDS bandwidth grows with M);
+// 31.0 and 37.6 against 26.2 and 26.7 us (each row adds its own integer dots,
+// whose VALU issue grows with M);
 // Q6_K 6656x19968 at M = 2 37.1 against 36.7 us
 constexpr int kRowsDefault[3] = {0, 2, 0};
 std::atomic<int> g_rows_override[3] = {{-1}, {-1}, {-1}};
