@@ -692,6 +692,59 @@ def small_m_sweep(torch, kq, I, ms=(1, 2, 3, 4, 8, 16), reps=5, launches=52):
     return out
 
 
+def small_m_cases(torch, kq, I, launches=8):
+    """Each small-M kernel choice at the verify shapes, `launches` eager
+    launches per case over rotated weight copies, cases in a fixed order (for
+    a counter run, whose per-dispatch rows follow this order): the M = 1
+    matvec, the dot path and the matrix-core kernel at the same M (each
+    forced where it is not the default), and the verify gate+up."""
+    Q4, Q6 = kq.KQ_QTYPE_Q4K, kq.KQ_QTYPE_Q6K
+    mats = {"q4k": (Q4, FFN, HIDDEN), "q6k": (Q6, HIDDEN, FFN)}
+    cases = [("q4k", 1, None), ("q4k", 2, 4), ("q4k", 2, 0), ("q4k", 4, 4), ("q4k", 4, 0),
+             ("q4k", 16, 0), ("q6k", 1, None), ("q6k", 2, 4), ("q6k", 2, 0), ("q6k", 16, 0),
+             ("gate_up", 1, None), ("gate_up", 2, 3), ("gate_up", 2, 0), ("gate_up", 3, 3),
+             ("gate_up", 3, 0)]
+    W = {}
+    for qt, (qti, n, k) in mats.items():
+        w = torch.from_numpy(I.weight_matrix(qt, n, k, stream=781)).cuda()
+        W[qt] = [w] + [w.clone() for _ in range(max(2, int(np.ceil((1 << 30) / w.numel()))) - 1)]
+    X = torch.from_numpy(I.normal_f32((16, FFN), stream=782)).cuda()
+    Y = torch.empty((16, FFN), device="cuda")
+    order = []
+    for name, m, rows in cases:
+        qt = "q4k" if name == "gate_up" else name
+        qti, n, k = mats[qt]
+        if name == "gate_up":  # the two-launch form on the matrix cores
+            kq.kq_tune_set_gate_up_rows(-1 if rows is None else rows)
+            kq.kq_tune_set_small_m_rows(qti, 0)
+        else:
+            kq.kq_tune_set_small_m_rows(qti, -1 if rows is None else rows)
+        nb = kq.kq_matmul_small_m_workspace_bytes(qti, n, k, m)
+        ws = torch.zeros(max(nb, 256) // 4, dtype=torch.int32, device="cuda")
+        cp = W[qt]
+        for i in range(launches):
+            if name == "gate_up":
+                kq.kq_ffn_gate_up_q4k_small_m(cp[i % len(cp)], cp[(i + 1) % len(cp)], X, k, Y, n, n,
+                                              k, m, ws, nb)
+            else:
+                kq.kq_matmul_small_m(qti, cp[i % len(cp)], X, k, Y, n, n, k, m, ws, nb)
+        torch.cuda.synchronize()
+        if m == 1:
+            path, per = ("one launch" if name == "gate_up" else "matvec"), 1
+        elif rows:
+            path, per = ("dot path, one launch" if name == "gate_up" else "dot path"), 1
+        elif name == "gate_up":
+            path, per = "matrix cores, two launches", 2
+        else:
+            path, per = "matrix cores", 1
+        order.append({"case": f"{name} M={m} {path}", "dispatches": launches * per})
+        del ws
+    kq.kq_tune_set_small_m_rows(Q4, -1)
+    kq.kq_tune_set_small_m_rows(Q6, -1)
+    kq.kq_tune_set_gate_up_rows(-1)
+    return order
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -766,8 +819,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time uncaptured launches instead of a graph")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
-    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "probe", "cpu", "shapes",
-                                       "embedding"),
+    ap.add_argument("--only", choices=("pass", "isolated", "small_m", "small_m_cases", "probe",
+                                       "cpu", "shapes", "embedding"),
                     help="run one section alone (for profiler runs) and print its results")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -799,6 +852,7 @@ def main():
         log(f"section {args.only} only")
         sec = {"isolated": lambda: {"isolated_matvec": isolated_matvecs(torch, kq, I)},
                "small_m": lambda: {"small_m": small_m_sweep(torch, kq, I)},
+               "small_m_cases": lambda: {"small_m_cases": small_m_cases(torch, kq, I)},
                "probe": lambda: {"read_ceiling": read_ceiling(torch, kq)},
                "shapes": lambda: {"decode_shapes": decode_shapes(torch, kq, I)},
                "embedding": lambda: {"embedding": embedding_lookup(torch, kq, I)},
