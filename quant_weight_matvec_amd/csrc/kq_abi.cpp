@@ -285,9 +285,9 @@ kq_status kq_matmul_small_m(int qtype, const void *W, const float *X, int64_t ld
             overlap(workspace, need, W, wbytes))
             return KQ_ERR_ALIAS;
     }
-    return from_hip(kqi::launch_small_m(qtype, (const uint8_t *)W, X, ldx, Y, ldy,
-                                             (int)n_rows, (int)k, m, workspace, workspace_bytes,
-                                             (hipStream_t)stream));
+    return from_hip(kqi::launch_small_m(qtype, (const uint8_t *)W, X, ldx, Y, ldy, (int)n_rows,
+                                        (int)k, m, workspace, workspace_bytes,
+                                        (hipStream_t)stream));
 }
 
 kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const float *X,
@@ -328,11 +328,11 @@ kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const
     }
     // gate into Mid, then up with the SiLU of the gate values it overwrites
     hipError_t e = kqi::launch_small_m(KQ_QTYPE_Q4K, (const uint8_t *)W_gate, X, ldx, Mid, ldm,
-                                            (int)n_rows, (int)k, m, workspace, workspace_bytes, st);
+                                       (int)n_rows, (int)k, m, workspace, workspace_bytes, st);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(kqi::launch_small_m(KQ_QTYPE_Q4K, (const uint8_t *)W_up, X, ldx, Mid, ldm,
-                                             (int)n_rows, (int)k, m, workspace, workspace_bytes, st,
-                                             Mid, ldm));
+                                        (int)n_rows, (int)k, m, workspace, workspace_bytes, st,
+                                        Mid, ldm));
 }
 
 kq_status kq_matmul_small_m_noalloc(int qtype, const void *W, const float *X, int64_t ldx,

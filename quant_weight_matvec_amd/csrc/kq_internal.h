@@ -101,9 +101,9 @@ hipError_t launch_rows_gate_up(const uint8_t *Wg, const uint8_t *Wu, const float
 // matrix-core kernel.
 // gate (nullable): Y = silu(gate) * (W X), gate [m][ldg]; it may be Y itself.
 hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
-                               int64_t ldy, int n_rows, int k, int m, void *workspace,
-                               int64_t workspace_bytes, hipStream_t stream,
-                               const float *gate = nullptr, int64_t ldg = 0);
+                          int64_t ldy, int n_rows, int k, int m, void *workspace,
+                          int64_t workspace_bytes, hipStream_t stream,
+                          const float *gate = nullptr, int64_t ldg = 0);
 // xs_out (nullable): also write next_in staged, groups of xs_group, per row
 hipError_t launch_tail(float *residual, const float *projected, float *next_in,
                        const float *g_post, const float *g_next, int rows, int n,

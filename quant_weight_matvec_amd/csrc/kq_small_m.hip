@@ -1182,9 +1182,9 @@ void small_m_plan(int qtype, int n_rows, int k, int m, int cus, int64_t *out)
 }
 
 hipError_t launch_small_m(int qtype, const uint8_t *W, const float *X, int64_t ldx, float *Y,
-                               int64_t ldy, int n_rows, int k, int m, void *workspace,
-                               int64_t workspace_bytes, hipStream_t stream, const float *gate,
-                               int64_t ldg)
+                          int64_t ldy, int n_rows, int k, int m, void *workspace,
+                          int64_t workspace_bytes, hipStream_t stream, const float *gate,
+                          int64_t ldg)
 {
     if (rows_path(qtype, n_rows, k, m))
         return launch_rows(qtype, W, X, ldx, Y, ldy, n_rows, k, m, gate, ldg, stream);
