@@ -904,9 +904,17 @@ def main():
     graph_t = capture(ft_pass)
     log(f"timing {args.steps} steps (graph of kq_ffn_pass_q4k_q6k: 2 launches per layer, "
         "tail fused into gate+up)")
-    ms_per_step, wall = timed((lambda: graph_t.replay()) if graph_t is not None else ft_pass,
-                              args.steps)
+    step_fn = (lambda: graph_t.replay()) if graph_t is not None else ft_pass
+    ms_per_step, wall = timed(step_fn, args.steps)
     value = pass_bytes / (ms_per_step * 1e-3) / 1e9
+    # the same K steps timed five more times, after the timed region: the
+    # spread of the headline figure (value itself is the timed region's)
+    repeats = [timed(step_fn, args.steps)[0] for _ in range(5)]
+    rep_med = float(np.median(repeats))
+    headline_spread = {"ms_per_step": [round(t, 4) for t in repeats],
+                       "median_ms": round(rep_med, 4),
+                       "cv": round(float(np.std(repeats) / np.mean(repeats)), 5),
+                       "steps_each": args.steps}
 
     # ---- the same pass other ways, reported beside it
     staged_pass = lambda: chain.run_pass("staged")
@@ -1002,6 +1010,7 @@ def main():
         "alternatives": alternatives,
         "frac_peak": round(value / PEAK_HBM_GBPS, 4),
         "tokens_per_s": round(1e3 / ms_per_step, 2),
+        "headline_repeats": headline_spread,
         "full_model_equiv_tokens_per_s": round(value * 1e9 / FULL_MODEL_TOKEN_BYTES, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
