@@ -517,3 +517,38 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_profile_commands_run_committed_sections():
+    """Every rocprofv3 command recorded under profiles/ runs bench.py with a
+    section and flags bench.py accepts, and stays within one counter pass's
+    limits (at most 8 SQ counters and 2 GRBM counters, no trace option with
+    --pmc)."""
+    import glob
+    import re
+    import shlex
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    only = re.search(r'"--only", choices=\(([^)]*)\)', src, re.S).group(1)
+    sections = set(re.findall(r'"([a-z_]+)"', only))
+    cmds = []
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*")):
+        for line in open(path):
+            m = re.search(r"(rocprofv3 [^\"]*)", line)
+            if m and "-- python3 bench.py" in m.group(1):
+                cmds.append((os.path.basename(path), m.group(1).strip().rstrip('",')))
+    assert cmds, "no recorded commands"
+    for name, cmd in cmds:
+        argv = shlex.split(cmd)
+        prof, prog = argv[:argv.index("--")], argv[argv.index("--") + 1:]
+        assert prog[:2] == ["python3", "bench.py"], (name, cmd)
+        rest = prog[2:]
+        assert rest[rest.index("--only") + 1] in sections, (name, cmd)
+        allowed = {"--only", "--steps", "--warmup", "--calibration-copy"}
+        assert {a for a in rest if a.startswith("--")} <= allowed, (name, cmd)
+        if "--pmc" in prof:
+            assert not {"-s", "--sys-trace", "-r", "--runtime-trace", "--kernel-trace"} & set(prof)
+            counters = prof[prof.index("--pmc") + 1:]
+            counters = counters[:next((i for i, c in enumerate(counters) if c.startswith("-")),
+                                      len(counters))]
+            assert sum(c.startswith("SQ_") for c in counters) <= 8, (name, cmd)
+            assert sum(c.startswith("GRBM_") for c in counters) <= 2, (name, cmd)
