@@ -295,7 +295,9 @@ kq_status kq_ffn_gate_up_q4k_small_m(const void *W_gate, const void *W_up, const
  * that the partial tiles and counters of the split over k live in a
  * library-owned device array of KQ_SMALL_M_SCRATCH_BYTES (16 KiB of counters,
  * one per 256-row group, then 16 MiB of partial tiles), one per GPU, held
- * until the process ends.  The call allocates nothing.
+ * until the process ends.  The call allocates nothing.  Where
+ * kq_matmul_small_m takes the matvec's dot path (Q4_K at M = 2 by default),
+ * so does this call, and it uses none of the array.
  *   Returns KQ_ERR_UNSUPPORTED when the shape needs more than that array
  *   holds (more than 4096 row groups of 256 rows, or a split over more than
  *   512 workgroups; kq_matmul_small_m with a workspace takes any shape).
