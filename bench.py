@@ -606,8 +606,12 @@ def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
     "The forward pass at a glance", sections 10.2-10.3; Ch 36 section 36.4):
     for M activation rows, per layer kq_ffn_gate_up_q4k_small_m (gate, up and
     the SiLU product), kq_matmul_small_m (Q6_K down) and kq_fused_residual_norm
-    over the M rows; the entry norm first.  Captured as one graph and replayed;
-    tokens/s = M / time per pass, GB/s = the pass's weight bytes / time."""
+    over the M rows; the entry norm first.  At M = 1 the tail goes into the
+    gate+up launch instead, as in the decode pass: kq_ffn_tail_gate_up_q4k runs
+    layer l-1's tail (layer 0: the entry norm, a zero projection with unit
+    gains) in front of layer l's gate+up, and one kq_fused_residual_norm ends
+    the pass.  Captured as one graph and replayed; tokens/s = M / time per
+    pass, GB/s = the pass's weight bytes / time."""
     Q4, Q6 = kq.KQ_QTYPE_Q4K, kq.KQ_QTYPE_Q6K
     L = chain.layers
     out = {}
@@ -622,6 +626,9 @@ def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
         mid = torch.empty(m, FFN, device="cuda")
         P = torch.empty(m, HIDDEN, device="cuda")
 
+        fused = m == 1
+        R2 = [R, torch.empty_like(R)]
+
         def run():
             kq.kq_fused_residual_norm(R, zeros[:m], X[0], ones, ones, m, HIDDEN)
             for l in range(L):
@@ -629,12 +636,27 @@ def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
                                               FFN, HIDDEN, m, ws, need)
                 kq.kq_matmul_small_m(Q6, chain.Wd[l], mid, FFN, P, HIDDEN, HIDDEN, FFN, m, ws, need)
                 kq.kq_fused_residual_norm(R, P, X[(l + 1) % 2], chain.gp[l], chain.gn[l], m, HIDDEN)
-        run()
+
+        def run_fused():
+            for l in range(L):
+                first = l == 0
+                kq.kq_ffn_tail_gate_up_q4k(
+                    R2[l % 2], zeros[0] if first else P, ones if first else chain.gp[l - 1],
+                    ones if first else chain.gn[l - 1], R2[(l + 1) % 2], None, chain.Wg[l],
+                    chain.Wu[l], mid, None, 0, FFN, HIDDEN)
+                kq.kq_matmul_small_m(Q6, chain.Wd[l], mid, FFN, P, HIDDEN, HIDDEN, FFN, m, ws, need)
+            kq.kq_fused_residual_norm(R2[L % 2], P, X[1], chain.gp[L - 1], chain.gn[L - 1], m,
+                                      HIDDEN)
+        body = run_fused if fused else run
+        body()
         torch.cuda.synchronize()
-        g = graph_of(torch, [run])
-        # gate+up is one launch up to M = 3 (the one-launch kernel at M = 1,
-        # the dot path at M = 2 and 3 by default), two above
-        launches = 1 + L * (3 if m <= 3 else 4)
+        g = graph_of(torch, [body])
+        # M = 1: the tail in front of the one-launch gate+up; M = 2 and 3:
+        # gate+up in one dot-path launch (default), then down and the tail;
+        # above: two gate+up launches.  Running the M tails inside the
+        # dot-path launch measured slower at M = 2 and 3 (4.51 and 5.16 ms
+        # against 4.12-4.23 and 4.61-4.75), so those keep the separate tail.
+        launches = 1 + L * (2 if fused else (3 if m <= 3 else 4))
         med, cv, _ = time_graph(torch, g, 1, reps)
         del g
         wb = WEIGHT_BYTES_PASS * L // LAYERS
