@@ -657,7 +657,9 @@ def verify_pass(torch, kq, chain, ms=(1, 2, 3, 4, 8, 16), reps=3):
         # dot-path launch measured slower at M = 2 and 3 (4.51 and 5.16 ms
         # against 4.12-4.23 and 4.61-4.75), so those keep the separate tail.
         launches = 1 + L * (2 if fused else (3 if m <= 3 else 4))
-        med, cv, _ = time_graph(torch, g, 1, reps)
+        # more warm replays than the default: the first replays of a 3 ms
+        # graph after its capture read up to 4 % slow
+        med, cv, _ = time_graph(torch, g, 1, reps, warm=4)
         del g
         wb = WEIGHT_BYTES_PASS * L // LAYERS
         out[f"m{m}"] = {"us_per_pass": round(med, 1), "us_cv": round(cv, 4),
