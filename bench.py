@@ -124,11 +124,12 @@ def _elf_sections(elf: bytes):
     return secs
 
 
-def kernel_code(name_part: str, lib_path: str = LIB_PATH):
+def kernel_code(name_part: str, lib_path: str = LIB_PATH, objects: bool = False):
     """[(symbol, machine code bytes)] of every gfx950 kernel whose symbol
     contains `name_part`, sorted by symbol, read from the code objects the
     library embeds (uncompressed clang offload bundles in its .hip_fatbin
-    section); [] if the library or the section is missing."""
+    section); [] if the library or the section is missing.  With `objects`
+    the data objects instead (the kernel descriptors)."""
     if not os.path.exists(lib_path):
         return []
     with open(lib_path, "rb") as f:
@@ -158,12 +159,26 @@ def kernel_code(name_part: str, lib_path: str = LIB_PATH):
                     st_name, st_info, _o, shndx, value, sz = struct.unpack_from(
                         "<IBBHQQ", co, symtab["off"] + 24 * i)
                     nm = co[strs + st_name:co.index(b"\0", strs + st_name)].decode()
-                    if (st_info & 0xF) == 2 and sz and name_part in nm:  # STT_FUNC
+                    kind = 1 if objects else 2  # STT_OBJECT (descriptors) or STT_FUNC
+                    if (st_info & 0xF) == kind and sz and name_part in nm:
                         sec = secs[shndx]
                         start = sec["off"] + value - sec["addr"]
                         found.append((nm, co[start:start + sz]))
         pos = fat.find(magic, pos + len(magic))
     return sorted(found)
+
+
+def kernel_descriptors(name_part: str, lib_path: str = LIB_PATH):
+    """{symbol: (LDS bytes, private bytes per lane)} of every gfx950 kernel
+    whose symbol contains `name_part`, from its kernel descriptor (the 64-byte
+    `<symbol>.kd` object of the code object: group_segment_fixed_size at
+    offset 0, private_segment_fixed_size at offset 4).  Private bytes are
+    register spills or per-lane arrays kept in memory."""
+    out = {}
+    for nm, body in kernel_code(name_part, lib_path, objects=True):
+        if nm.endswith(".kd") and len(body) >= 8:
+            out[nm[:-3]] = struct.unpack_from("<II", body, 0)
+    return out
 
 
 def kernel_code_hash(name_part: str, lib_path: str = LIB_PATH):

@@ -552,3 +552,18 @@ def test_profile_commands_run_committed_sections():
                                       len(counters))]
             assert sum(c.startswith("SQ_") for c in counters) <= 8, (name, cmd)
             assert sum(c.startswith("GRBM_") for c in counters) <= 2, (name, cmd)
+
+
+def test_timed_kernels_use_no_private_memory():
+    """The kernels of the timed pass keep every per-lane value in registers:
+    their descriptors give no private (scratch) bytes, while a 16-wave,
+    look-ahead-2 Q6_K form, which cannot fit its registers, does (so the
+    descriptor reading is shown to see spills)."""
+    import bench
+    for part in bench.PMC_KERNELS.values():
+        d = bench.kernel_descriptors(part)
+        assert len(d) == 1, part
+        (lds, private), = d.values()
+        assert private == 0, f"{part}: {private} private bytes per lane"
+    spilled = bench.kernel_descriptors("q6k_matvec_kernelILi8ELi3ELi2ELi16EE")
+    assert len(spilled) == 1 and list(spilled.values())[0][1] > 0
